@@ -1,0 +1,220 @@
+"""Python binding of libheal, the HEAL hot path on AMD Instinct MI355X (gfx950).
+
+The four calls of ``include/heal.h`` under the same names.  This module only marshals arguments: it
+allocates outputs with torch (device memory), passes raw device pointers and the current HIP stream,
+and raises ``RuntimeError`` with the library's status text on any error.  Every step of the path runs in
+the HIP kernels of ``libheal.so``; there is no CPU or PyTorch fallback, and ``load()`` fails loudly when
+the library has not been built.
+
+Sources: gist.science explainer "Demystifying Numerical Instability in LLM Inference: Achieving
+Reproducible Inference for Mission-Critical Tasks with HEAL", Technical Summary, sections 2.A (INT16
+quantisation, Dual-FP16 unpack) and 2.B (algebraic error compensation, overflow handling).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libheal.so")
+
+HEAL_F32, HEAL_BF16, HEAL_F16, HEAL_I16 = 0, 1, 2, 3
+_PARTS = {"f16": HEAL_F16, "bf16": HEAL_BF16}
+
+_lib = None
+
+
+class HealAttnArgs(ctypes.Structure):
+    """Mirror of heal_attn_args in include/heal.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
+        ("n_q_heads", ctypes.c_int64), ("n_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("q_scale", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("q_strides", ctypes.c_int64 * 3), ("kv_strides", ctypes.c_int64 * 3),
+        ("qs_strides", ctypes.c_int64 * 3), ("kvs_strides", ctypes.c_int64 * 3),
+        ("o_strides", ctypes.c_int64 * 3),
+        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def load():
+    """Load libheal.so (built in-tree by ``build.build()``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libheal.so not built ({LIB_PATH}); run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.heal_status_str.restype = ctypes.c_char_p
+    L.heal_status_str.argtypes = [i32]
+    L.heal_abi_version.restype = i32
+    L.heal_abi_version.argtypes = []
+    L.heal_split.restype = i32
+    L.heal_split.argtypes = [p, i32, i64, i64, i64, i32, p, p, i64, p, p]
+    L.heal_gemm_comp.restype = i32
+    L.heal_gemm_comp.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p]
+    L.heal_qkv_quant_i16.restype = i32
+    L.heal_qkv_quant_i16.argtypes = [p, i64, i64, i64, i64, p, i64, p, i64, p]
+    L.heal_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.heal_attn_workspace_bytes.argtypes = [ctypes.POINTER(HealAttnArgs)]
+    L.heal_attn_dual_fp16.restype = i32
+    L.heal_attn_dual_fp16.argtypes = [ctypes.POINTER(HealAttnArgs), p]
+    _lib = L
+    return L
+
+
+EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp", "heal_qkv_quant_i16",
+            "heal_attn_workspace_bytes", "heal_attn_dual_fp16")
+
+
+def _check(status: int):
+    if status != 0:
+        raise RuntimeError(load().heal_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ld(t) -> int:
+    """leading dimension (elements) of a row-major 2-D view"""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+# -------------------------------------------------------------------------------------------------- heal_split
+def heal_split(x, part: str = "f16", prescale: bool = True, residual: bool = True, hi=None, lo=None,
+               exps=None):
+    """Split FP32 / bf16 ``x [rows, cols]`` into 16-bit hi (+ lo) parts with per-row power-of-two exponents,
+    or unpack INT16 ``x`` into its Dual-FP16 halves.  Returns (hi, lo or None, exps or None); parts come
+    back as int16 tensors holding the 16-bit patterns (view them as float16 / bfloat16 as needed)."""
+    import torch
+
+    L = load()
+    rows, cols = x.shape
+    if x.dtype == torch.float32:
+        xt = HEAL_F32
+    elif x.dtype == torch.bfloat16:
+        xt = HEAL_BF16
+    elif x.dtype == torch.int16:
+        xt, prescale, residual, part = HEAL_I16, False, True, "f16"
+    else:
+        raise TypeError(f"heal_split: unsupported dtype {x.dtype}")
+    ld_part = (cols + 7) // 8 * 8
+    if hi is None:
+        hi = torch.empty((rows, ld_part), dtype=torch.int16, device=x.device)[:, :cols]
+    if residual and lo is None:
+        lo = torch.empty((rows, ld_part), dtype=torch.int16, device=x.device)[:, :cols]
+    if prescale and exps is None:
+        exps = torch.empty((rows,), dtype=torch.int32, device=x.device)
+    lo_arg = lo if residual else None
+    ex_arg = exps if prescale else None
+    _check(L.heal_split(_ptr(x), xt, rows, cols, _ld(x), _PARTS[part], _ptr(hi), _ptr(lo_arg),
+                        _ld(hi), _ptr(ex_arg), _stream(x.device)))
+    return hi, lo_arg, ex_arg
+
+
+# ---------------------------------------------------------------------------------------------- heal_gemm_comp
+def heal_gemm_comp(a_hi, a_lo, a_exp, b_hi, b_lo, b_exp, part: str = "f16", c=None):
+    """C [M, N] fp32 = sum of the 16-bit products of A's and B^T's parts, scaled by 2^-(ea_i + eb_j).
+    ``a_*`` are [M, K] and ``b_*`` are parts of B^T [N, K] (both K-contiguous); lo / exp may be None."""
+    import torch
+
+    L = load()
+    M, K = a_hi.shape
+    N = b_hi.shape[0]
+    if c is None:
+        ldc = (N + 3) // 4 * 4
+        c = torch.empty((M, ldc), dtype=torch.float32, device=a_hi.device)[:, :N]
+    if a_lo is not None and (a_lo.shape != a_hi.shape or a_lo.stride() != a_hi.stride()):
+        raise ValueError("a_lo must match a_hi's shape and strides")
+    if b_lo is not None and (b_lo.shape != b_hi.shape or b_lo.stride() != b_hi.stride()):
+        raise ValueError("b_lo must match b_hi's shape and strides")
+    _check(L.heal_gemm_comp(M, N, K, _ptr(a_hi), _ptr(a_lo), _ptr(a_exp), _ld(a_hi), _ptr(b_hi), _ptr(b_lo),
+                            _ptr(b_exp), _ld(b_hi), _PARTS[part], _ptr(c), _ld(c), _stream(a_hi.device)))
+    return c
+
+
+# ------------------------------------------------------------------------------------------ heal_qkv_quant_i16
+def heal_qkv_quant_i16(x, q=None, scale=None):
+    """INT16-quantise fp32 ``x [tokens, heads, head_dim]`` per (token, head).  Returns (q int16, scale fp32).
+    ``q`` / ``scale`` may be views into a larger cache ([tokens, heads, head_dim] with any token stride)."""
+    import torch
+
+    L = load()
+    T, H, D = x.shape
+    if x.stride(2) != 1 or x.stride(1) != D:
+        raise ValueError("x must have heads packed at stride head_dim and a contiguous last axis")
+    if q is None:
+        q = torch.empty((T, H, D), dtype=torch.int16, device=x.device)
+    if scale is None:
+        scale = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if q.stride(2) != 1 or q.stride(1) != D or scale.stride(1) != 1:
+        raise ValueError("q / scale must have heads packed")
+    _check(L.heal_qkv_quant_i16(_ptr(x), T, H, D, x.stride(0), _ptr(q), q.stride(0), _ptr(scale),
+                                scale.stride(0), _stream(x.device)))
+    return q, scale
+
+
+# ----------------------------------------------------------------------------------------- heal_attn_dual_fp16
+def make_attn_args(q, q_scale, k, k_scale, v, v_scale, out, causal: bool = True,
+                   softmax_scale: float | None = None, workspace=None) -> HealAttnArgs:
+    """Fill heal_attn_args from torch tensors q [B, Lq, Hq, D], k/v [B, Lkv, Hkv, D] (int16), scales
+    [B, L, H] (fp32) and out [B, Lq, Hq, D] (fp32).  k and v must share strides, as must their scales."""
+    B, Lq, Hq, D = q.shape
+    Lkv, Hkv = k.shape[1], k.shape[2]
+    if k.stride() != v.stride() or k_scale.stride() != v_scale.stride():
+        raise ValueError("k and v (and their scales) must share strides")
+    for t in (q, k, v, out):
+        if t.stride(3) != 1:
+            raise ValueError("head_dim axis must be contiguous")
+    a = HealAttnArgs()
+    a.batch, a.q_len, a.kv_len, a.n_q_heads, a.n_kv_heads, a.head_dim = B, Lq, Lkv, Hq, Hkv, D
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.q_scale, a.k_scale, a.v_scale = q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr()
+    a.q_strides[:] = list(q.stride()[:3])
+    a.kv_strides[:] = list(k.stride()[:3])
+    a.qs_strides[:] = list(q_scale.stride()[:3])
+    a.kvs_strides[:] = list(k_scale.stride()[:3])
+    a.o_strides[:] = list(out.stride()[:3])
+    a.causal = 1 if causal else 0
+    a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.out = out.data_ptr()
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def heal_attn_workspace_bytes(args: HealAttnArgs) -> int:
+    return int(load().heal_attn_workspace_bytes(ctypes.byref(args)))
+
+
+def heal_attn_dual_fp16(q, q_scale, k, k_scale, v, v_scale, causal: bool = True,
+                        softmax_scale: float | None = None, out=None, workspace=None):
+    """Attention over INT16 Q/K/V with Dual-FP16 products and FP32 softmax; returns out [B, Lq, Hq, D] fp32.
+    A workspace of heal_attn_workspace_bytes() is allocated with torch when none is given."""
+    import torch
+
+    L = load()
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    args = make_attn_args(q, q_scale, k, k_scale, v, v_scale, out, causal, softmax_scale, workspace)
+    need = heal_attn_workspace_bytes(args)
+    if need and workspace is None:
+        workspace = torch.empty((need + 255) // 256 * 256, dtype=torch.uint8, device=q.device)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    _check(L.heal_attn_dual_fp16(ctypes.byref(args), _stream(q.device)))
+    return out

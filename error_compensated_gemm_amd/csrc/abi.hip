@@ -1,0 +1,132 @@
+// abi.hip -- the extern "C" entry points of libheal: argument validation, then the kernel launches.
+// Every check runs on the host before anything is enqueued; the library never allocates, frees or
+// synchronises.  The operations themselves are defined in include/heal.h.
+#include <math.h>
+
+#include "heal_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+heal_status launched(hipError_t e) { return e == hipSuccess ? HEAL_OK : HEAL_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* heal_status_str(int status) {
+  switch (status) {
+    case HEAL_OK: return "HEAL_OK";
+    case HEAL_ERR_NULL: return "HEAL_ERR_NULL: a required pointer is NULL";
+    case HEAL_ERR_SHAPE: return "HEAL_ERR_SHAPE: a size is negative or inconsistent";
+    case HEAL_ERR_STRIDE: return "HEAL_ERR_STRIDE: a leading dimension or stride is too small";
+    case HEAL_ERR_ALIGN: return "HEAL_ERR_ALIGN: pointer not 16-byte aligned or leading dimension not a multiple of 8";
+    case HEAL_ERR_DTYPE: return "HEAL_ERR_DTYPE: dtype not accepted by this call";
+    case HEAL_ERR_UNSUPPORTED: return "HEAL_ERR_UNSUPPORTED: valid request not implemented by this build";
+    case HEAL_ERR_LAUNCH: return "HEAL_ERR_LAUNCH: the HIP runtime refused a kernel launch";
+    case HEAL_ERR_WORKSPACE: return "HEAL_ERR_WORKSPACE: workspace missing or too small";
+    default: return "HEAL: unknown status";
+  }
+}
+
+int heal_abi_version(void) { return HEAL_ABI_VERSION; }
+
+heal_status heal_split(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld_x, int part_type,
+                       void* hi, void* lo, int64_t ld_part, int32_t* exps, void* stream) {
+  if (rows < 0 || cols < 0) return HEAL_ERR_SHAPE;
+  if (x_type != HEAL_F32 && x_type != HEAL_BF16 && x_type != HEAL_I16) return HEAL_ERR_DTYPE;
+  if (part_type != HEAL_F16 && part_type != HEAL_BF16) return HEAL_ERR_DTYPE;
+  if (x_type == HEAL_I16 && (part_type != HEAL_F16 || exps != nullptr)) return HEAL_ERR_DTYPE;
+  if (rows == 0) return HEAL_OK;
+  if (cols > 0 && (!x || !hi)) return HEAL_ERR_NULL;
+  if (x_type == HEAL_I16 && cols > 0 && !lo) return HEAL_ERR_NULL;
+  if (ld_x < cols || ld_part < cols) return HEAL_ERR_STRIDE;
+  // x: element alignment only (rows that start 16-byte aligned take vector loads); parts: 16-byte rows
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
+  if ((x_type == HEAL_F32 ? (xa & 3u) : (xa & 1u)) || (hi && !aligned16(hi)) || (lo && !aligned16(lo)) ||
+      (exps && !aligned4(exps)) || (ld_part & 7))
+    return HEAL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  switch (x_type) {
+    case HEAL_F32:
+      return launched(heal::launch_split_f32((const float*)x, rows, cols, ld_x, part_type, hi, lo, ld_part,
+                                             exps, s));
+    case HEAL_BF16:
+      return launched(heal::launch_split_bf16((const uint16_t*)x, rows, cols, ld_x, part_type, hi, lo,
+                                              ld_part, exps, s));
+    default:
+      return launched(heal::launch_split_i16((const int16_t*)x, rows, cols, ld_x, hi, lo, ld_part, s));
+  }
+}
+
+heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
+                           const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
+                           const int32_t* b_exp, int64_t ldb, int part_type, float* c, int64_t ldc,
+                           void* stream) {
+  if (M < 0 || N < 0 || K < 0) return HEAL_ERR_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
+  if (part_type != HEAL_F16 && part_type != HEAL_BF16) return HEAL_ERR_DTYPE;
+  if (M == 0 || N == 0) return HEAL_OK;
+  if (!c || (K > 0 && (!a_hi || !b_hi))) return HEAL_ERR_NULL;
+  if (lda < K || ldb < K || ldc < N) return HEAL_ERR_STRIDE;
+  if ((a_hi && !aligned16(a_hi)) || (a_lo && !aligned16(a_lo)) || (b_hi && !aligned16(b_hi)) ||
+      (b_lo && !aligned16(b_lo)) || !aligned16(c) || (a_exp && !aligned4(a_exp)) ||
+      (b_exp && !aligned4(b_exp)) || (lda & 7) || (ldb & 7) || (ldc & 3))
+    return HEAL_ERR_ALIGN;
+  return launched(heal::launch_gemm_comp(M, N, K, (const uint16_t*)a_hi, (const uint16_t*)a_lo, a_exp, lda,
+                                         (const uint16_t*)b_hi, (const uint16_t*)b_lo, b_exp, ldb, part_type,
+                                         c, ldc, (hipStream_t)stream));
+}
+
+heal_status heal_qkv_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim,
+                               int64_t ld_x, int16_t* q, int64_t ld_q, float* scale, int64_t ld_s,
+                               void* stream) {
+  if (tokens < 0 || heads < 0 || head_dim < 0) return HEAL_ERR_SHAPE;
+  if (head_dim % 4 != 0 || head_dim > 1024) return HEAL_ERR_UNSUPPORTED;
+  if (tokens == 0 || heads == 0 || head_dim == 0) return HEAL_OK;
+  if (!x || !q || !scale) return HEAL_ERR_NULL;
+  if (ld_x < heads * head_dim || ld_q < heads * head_dim || ld_s < heads) return HEAL_ERR_STRIDE;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u) || !aligned4(scale) || (ld_x & 3) || (ld_q & 3))
+    return HEAL_ERR_ALIGN;
+  return launched(heal::launch_quant_i16(x, tokens, heads, head_dim, ld_x, q, ld_q, scale, ld_s,
+                                         (hipStream_t)stream));
+}
+
+size_t heal_attn_workspace_bytes(const heal_attn_args* a) {
+  if (!a) return 0;
+  return heal::attn_workspace_bytes(*a);
+}
+
+heal_status heal_attn_dual_fp16(const heal_attn_args* a, void* stream) {
+  if (!a) return HEAL_ERR_NULL;
+  if (a->batch < 0 || a->q_len < 0 || a->kv_len < 0 || a->n_q_heads < 0 || a->n_kv_heads < 0 ||
+      a->head_dim < 0)
+    return HEAL_ERR_SHAPE;
+  if (a->head_dim != 128) return HEAL_ERR_UNSUPPORTED;
+  if (a->n_kv_heads == 0 || a->n_q_heads % a->n_kv_heads != 0) return HEAL_ERR_SHAPE;
+  if (a->batch == 0 || a->q_len == 0 || a->n_q_heads == 0) return HEAL_OK;
+  if (!a->q || !a->q_scale || !a->out) return HEAL_ERR_NULL;
+  if (a->kv_len > 0 && (!a->k || !a->v || !a->k_scale || !a->v_scale)) return HEAL_ERR_NULL;
+  if (!(a->softmax_scale >= 0.0f) || isinf(a->softmax_scale)) return HEAL_ERR_SHAPE;
+  const int64_t D = a->head_dim;
+  for (int i = 0; i < 3; ++i)
+    if (a->q_strides[i] < 0 || a->kv_strides[i] < 0 || a->qs_strides[i] < 0 || a->kvs_strides[i] < 0 ||
+        a->o_strides[i] < 0)
+      return HEAL_ERR_STRIDE;
+  if (a->q_strides[2] < D || a->kv_strides[2] < D || a->o_strides[2] < D) return HEAL_ERR_STRIDE;
+  const int64_t* st[3] = {a->q_strides, a->kv_strides, a->o_strides};
+  for (int t = 0; t < 3; ++t)
+    for (int i = 0; i < 3; ++i)
+      if (st[t][i] & 7) return HEAL_ERR_ALIGN;
+  if (!aligned16(a->q) || !aligned16(a->out) || (a->k && !aligned16(a->k)) || (a->v && !aligned16(a->v)) ||
+      !aligned4(a->q_scale) || (a->k_scale && !aligned4(a->k_scale)) || (a->v_scale && !aligned4(a->v_scale)))
+    return HEAL_ERR_ALIGN;
+  const size_t need = heal::attn_workspace_bytes(*a);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need || (reinterpret_cast<uintptr_t>(a->workspace) & 255u)))
+    return HEAL_ERR_WORKSPACE;
+  return launched(heal::launch_attn(*a, (hipStream_t)stream));
+}
+
+}  // extern "C"

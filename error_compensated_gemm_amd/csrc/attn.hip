@@ -1,0 +1,777 @@
+// attn.hip -- Dual-FP16 attention over INT16 Q/K/V on gfx950 matrix cores (HEAL, [TS 2A]).
+//
+// [TS 2A Solution/Mechanism/Benefit]: Q, K and V are stored as INT16; at run time each INT16 value is
+// unpacked into two FP16 values that are exact, so QK^T and PV run on 16-bit matrix units while the
+// stored footprint stays 16 bits.  [TS] = gist.science explainer "Demystifying Numerical Instability in
+// LLM Inference: Achieving Reproducible Inference for Mission-Critical Tasks with HEAL", Technical Summary.
+//
+// Arithmetic (identical in both kernels):
+//   * unpack  q = 256 * (q >> 8) + (q & 0xFF):  H = fp16(q & ~0xFF) (multiple of 256, |H| <= 32768) and
+//     L = fp16(q & 0xFF) (0..255), both exact, H + L = q.
+//   * S_int = q_i . k_j as two FP32 accumulators: Hq.Hk (every partial sum is a multiple of 2^16 below
+//     2^37: exact) and Hq.Lk + Lq.Hk + Lq.Lk (about 2^-7 of the first); S_int = their FP32 sum.
+//   * t_ij = S_int * s_k,j * (s_q,i * softmax_scale * log2 e), carried as an FP32 pair (hi + FMA-captured
+//     rounding error) so that t - max keeps its precision for logits of any size; online softmax in
+//     base 2, FP32 running maximum and sum.
+//   * P~ = p * (s_v,j * 2^E) with E = 14 - ilogb(max_j s_v,j) over the keys a workgroup reads, so P~ < 2^15
+//     and its FP16 split P~ = P~h + P~l (P~l = fp16(P~ - P~h), exact residual) keeps 22 bits;
+//     O += P~h.H + P~h.L + P~l.H + P~l.L (4 products, one FP32 accumulator); O = acc * 2^-E / l.
+//
+// Prefill (q_len > 1): flash-style forward.  A workgroup of 8 wavefronts owns 256 queries of one
+// (batch, head); each wavefront owns 32.  K/V tiles of 64 keys are staged in LDS already unpacked (K as
+// [key][d] H/L planes, V transposed to [d][key] H/L planes), double-buffered, one barrier per tile.
+// Each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16_f16, so the 16 scores a lane holds all
+// belong to ONE query: the softmax maximum/sum are lane-local plus one exchange with lane ^ 32.  The same
+// registers, in MFMA order, are the P^T operand of O^T = V^T P^T, so P never leaves registers.
+// Causal workgroups are dispatched longest first.
+//
+// Decode (q_len = 1): HBM-streaming, split over the keys.  A workgroup of 4 wavefronts owns one
+// (batch, kv-head) and a chunk of 1024 keys; the G = n_q/n_kv query heads of the group are the 16 columns
+// of v_mfma_f32_16x16x32_f16 (G <= 16).  K is loaded straight from HBM into MFMA operand registers; V goes
+// through a wavefront-private LDS transpose.  Register double-buffering keeps the next 32 keys' loads in
+// flight while the current ones are multiplied.  The four wavefronts' partial (max, sum, O) are merged in
+// LDS in a fixed order and written to the workspace; a second kernel merges the chunks of each
+// (batch, head) in a fixed order.  No atomics: results are bitwise reproducible.
+#include <math.h>
+
+#include "heal_internal.h"
+
+namespace heal {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 128;
+
+__device__ __forceinline__ uint32_t pack2(_Float16 a, _Float16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Dual-FP16 unpack of 8 INT16 values (one 16-byte chunk): H = fp16(q & ~0xFF), L = fp16(q & 0xFF)
+__device__ __forceinline__ void unpack8(const uint4& raw, uint4& H, uint4& L) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q0 = (int)(int16_t)(w[i] & 0xFFFFu), q1 = (int)(int16_t)(w[i] >> 16);
+    h[i] = pack2((_Float16)(float)(q0 & ~0xFF), (_Float16)(float)(q1 & ~0xFF));
+    l[i] = pack2((_Float16)(float)(q0 & 0xFF), (_Float16)(float)(q1 & 0xFF));
+  }
+  H = make_uint4(h[0], h[1], h[2], h[3]);
+  L = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// transpose-unpack: 4 keys x 8 d (one 16-byte chunk per key) -> for each of the 8 d, the 4 keys' H and L
+// packed as 8 bytes (uint2)
+__device__ __forceinline__ void unpack_t4x8(const uint4 (&raw)[4], uint2 (&H)[8], uint2 (&L)[8]) {
+  int q[4][8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[k][2 * i] = (int)(int16_t)(w[i] & 0xFFFFu);
+      q[k][2 * i + 1] = (int)(int16_t)(w[i] >> 16);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    H[d] = make_uint2(pack2((_Float16)(float)(q[0][d] & ~0xFF), (_Float16)(float)(q[1][d] & ~0xFF)),
+                      pack2((_Float16)(float)(q[2][d] & ~0xFF), (_Float16)(float)(q[3][d] & ~0xFF)));
+    L[d] = make_uint2(pack2((_Float16)(float)(q[0][d] & 0xFF), (_Float16)(float)(q[1][d] & 0xFF)),
+                      pack2((_Float16)(float)(q[2][d] & 0xFF), (_Float16)(float)(q[3][d] & 0xFF)));
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+
+__device__ __forceinline__ int ilogb_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
+
+// Logit t = (shh + srest) * s_k * cq as an unevaluated pair t_hi + t_lo.  A single FP32 rounding of t
+// costs 2^-24 |t|, which for logits of magnitude 10^3 moves exp2(t - m) by ~1e-4; carrying the product's
+// rounding error (FMA) keeps t - m accurate to ~2^-24 |t - m| instead.
+// S_int = shh + srest is first rounded with its error kept (TwoSum: s_hi + s_lo == shh + srest exactly),
+// so t_hi is the correctly rounded logit and |t_lo| <= ~2^-23 |t_hi| whatever cancellation happens.
+__device__ __forceinline__ void logit2(float shh, float srest, float sk, float cq, float& t_hi, float& t_lo) {
+  const float s_hi = shh + srest;
+  const float bb = s_hi - shh;
+  const float s_lo = (shh - (s_hi - bb)) + (srest - bb);
+  const float c_hi = sk * cq;
+  const float c_lo = __builtin_fmaf(sk, cq, -c_hi);
+  t_hi = s_hi * c_hi;
+  t_lo = __builtin_fmaf(s_hi, c_hi, -t_hi) + (s_hi * c_lo + s_lo * c_hi);
+}
+
+// (hi, lo) maximum: larger hi wins, equal hi -> larger lo.  The rule is symmetric, so lanes that exchange
+// candidates agree on the result, and the arg-max key then gets p = exp2(0 + 0) = 1 exactly.
+__device__ __forceinline__ void pair_max(float& mh, float& ml, float oh, float ol) {
+  if (oh > mh || (oh == mh && ol > ml)) {
+    mh = oh;
+    ml = ol;
+  }
+}
+
+// split p~ into fp16 hi + lo (lo = fp16(p~ - hi), the residual is exact in fp32)
+__device__ __forceinline__ void split_p(float p, _Float16& h, _Float16& l) {
+  h = (_Float16)p;
+  l = (_Float16)(p - (float)h);
+}
+
+// ============================================================================================ prefill
+constexpr int PF_WAVES = 8;
+constexpr int PF_THREADS = 64 * PF_WAVES;
+constexpr int PF_BQ = 32 * PF_WAVES;  // queries per workgroup
+constexpr int PF_BKV = 64;            // keys per LDS stage
+// LDS stage: K H/L planes [64 keys][16 chunks of 8 d] (uint4), V^T H/L planes [128 d][16 groups of 4 keys]
+// (uint2), then the 64 k-scales and the 64 renormalised v-scales.
+constexpr int PF_K_PLANE = PF_BKV * 16;   // uint4 per K plane
+constexpr int PF_V_PLANE = D * 16;        // uint2 per V^T plane
+constexpr int PF_STAGE_BYTES = 2 * PF_K_PLANE * 16 + 2 * PF_V_PLANE * 8 + 2 * PF_BKV * 4;
+
+__device__ __forceinline__ int pf_kpos(int key, int c) { return key * 16 + (c ^ (key & 15)); }
+__device__ __forceinline__ int pf_vpos(int d, int g) { return d * 16 + (g ^ ((d >> 1) & 15)); }
+
+struct AttnParams {
+  const int16_t* q;
+  const int16_t* k;
+  const int16_t* v;
+  const float* qs;
+  const float* ks;
+  const float* vs;
+  float* out;
+  int64_t q_st[3], kv_st[3], qs_st[3], kvs_st[3], o_st[3];
+  int64_t B, Lq, Lkv, Hq, Hkv;
+  float scale_log2;  // softmax_scale * log2(e)
+  int causal;
+};
+
+__global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ float red[PF_WAVES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t bh = blockIdx.x;  // (batch, q-head)
+  const int64_t b = bh / a.Hq, h = bh - b * a.Hq;
+  const int64_t hk = h / (a.Hq / a.Hkv);
+  const int ntq = (int)((a.Lq + PF_BQ - 1) / PF_BQ);
+  const int64_t q0 = (int64_t)(ntq - 1 - (int)blockIdx.y) * PF_BQ;  // longest tiles first
+  const int64_t off = a.Lkv - a.Lq;                                  // bottom-right causal offset
+
+  int64_t kv_end = a.Lkv;
+  if (a.causal) {
+    const int64_t lim = q0 + PF_BQ + off;
+    if (lim < kv_end) kv_end = lim;
+  }
+  if (kv_end < 0) kv_end = 0;
+  const int ntk = (int)((kv_end + PF_BKV - 1) / PF_BKV);
+
+  const int16_t* kbase = a.k + b * a.kv_st[0] + hk * a.kv_st[2];
+  const int16_t* vbase = a.v + b * a.kv_st[0] + hk * a.kv_st[2];
+  const float* ksb = a.ks + b * a.kvs_st[0] + hk * a.kvs_st[2];
+  const float* vsb = a.vs + b * a.kvs_st[0] + hk * a.kvs_st[2];
+
+  // ---- E = 14 - ilogb(max v-scale over the keys this workgroup reads) ----
+  float vmax = 0.0f;
+  for (int64_t j = tid; j < kv_end; j += PF_THREADS) vmax = fmaxf(vmax, vsb[j * a.kvs_st[1]]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, m, 64));
+  if (lane == 0) red[wave] = vmax;
+  __syncthreads();
+  vmax = red[0];
+#pragma unroll
+  for (int w = 1; w < PF_WAVES; ++w) vmax = fmaxf(vmax, red[w]);
+  const int E = vmax > 0.0f ? 14 - ilogb_pos(vmax) : 0;
+
+  // ---- this lane's query and its Dual-FP16 fragments (B operand of S^T = K Q^T) ----
+  const int qcol = lane & 31, half = lane >> 5;
+  const int64_t qi = q0 + 32 * wave + qcol;
+  const bool qvalid = qi < a.Lq;
+  const int64_t qi_c = qvalid ? qi : a.Lq - 1;
+  const int16_t* qrow = a.q + b * a.q_st[0] + qi_c * a.q_st[1] + h * a.q_st[2];
+  uint4 QH[8], QL[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half);
+    unpack8(raw, QH[ks], QL[ks]);
+  }
+  const float cq = a.qs[b * a.qs_st[0] + qi_c * a.qs_st[1] + h * a.qs_st[2]] * a.scale_log2;
+  // queries of this wave: [q0 + 32 wave, q0 + 32 wave + 31]; key j visible to query i iff j <= i + off
+  const int64_t wq_first = q0 + 32 * wave, wq_last = wq_first + 31;
+
+  // ---- staging roles: K: 2 chunks per thread; V: one (2-key pair, 8-d chunk) job per thread ----
+  uint4 kraw[2], vraw[2];
+  auto gload = [&](int t) {
+    const int64_t kb = (int64_t)t * PF_BKV;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + PF_THREADS * i, key = id >> 4, c = id & 15;
+      int64_t j = kb + key;
+      if (j > a.Lkv - 1) j = a.Lkv - 1;
+      kraw[i] = *reinterpret_cast<const uint4*>(kbase + j * a.kv_st[1] + 8 * c);
+    }
+    {
+      const int pair = tid >> 4, c = tid & 15;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int64_t j = kb + 2 * pair + i;
+        if (j > a.Lkv - 1) j = a.Lkv - 1;
+        vraw[i] = *reinterpret_cast<const uint4*>(vbase + j * a.kv_st[1] + 8 * c);
+      }
+    }
+  };
+  float sk_reg = 0.0f, sv_reg = 0.0f;
+  auto sload = [&](int t) {
+    if (tid < PF_BKV) {
+      int64_t j = (int64_t)t * PF_BKV + tid;
+      const bool ok = j < a.Lkv;
+      if (!ok) j = a.Lkv - 1;
+      sk_reg = ksb[j * a.kvs_st[1]];
+      sv_reg = ok ? __builtin_amdgcn_ldexpf(vsb[j * a.kvs_st[1]], E) : 0.0f;
+    }
+  };
+  auto lstore = [&](int buf) {
+    unsigned char* st = smem + (size_t)buf * PF_STAGE_BYTES;
+    uint4* kh = reinterpret_cast<uint4*>(st);
+    uint4* kl = kh + PF_K_PLANE;
+    uint2* vh = reinterpret_cast<uint2*>(kl + PF_K_PLANE);
+    uint2* vl = vh + PF_V_PLANE;
+    float* sks = reinterpret_cast<float*>(vl + PF_V_PLANE);
+    float* svs = sks + PF_BKV;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + PF_THREADS * i, key = id >> 4, c = id & 15;
+      uint4 H, L;
+      unpack8(kraw[i], H, L);
+      kh[pf_kpos(key, c)] = H;
+      kl[pf_kpos(key, c)] = L;
+    }
+    {
+      const int pair = tid >> 4, c = tid & 15;
+      uint4 H0, L0, H1, L1;
+      unpack8(vraw[0], H0, L0);
+      unpack8(vraw[1], H1, L1);
+      const uint32_t h0[4] = {H0.x, H0.y, H0.z, H0.w}, h1[4] = {H1.x, H1.y, H1.z, H1.w};
+      const uint32_t l0[4] = {L0.x, L0.y, L0.z, L0.w}, l1[4] = {L1.x, L1.y, L1.z, L1.w};
+      // keys 2*pair, 2*pair+1 sit in group (2*pair)/4 at half-word slot (2*pair)%4 .. +1
+      const int g = pair >> 1, sub = pair & 1;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int d = 8 * c + dd;
+        const uint32_t sh = (dd & 1) ? 16 : 0;
+        const uint32_t hw = ((h0[dd >> 1] >> sh) & 0xFFFFu) | (((h1[dd >> 1] >> sh) & 0xFFFFu) << 16);
+        const uint32_t lw = ((l0[dd >> 1] >> sh) & 0xFFFFu) | (((l1[dd >> 1] >> sh) & 0xFFFFu) << 16);
+        reinterpret_cast<uint32_t*>(vh + pf_vpos(d, g))[sub] = hw;
+        reinterpret_cast<uint32_t*>(vl + pf_vpos(d, g))[sub] = lw;
+      }
+    }
+    if (tid < PF_BKV) {
+      sks[tid] = sk_reg;
+      svs[tid] = sv_reg;
+    }
+  };
+
+  f32x16 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[dt][r] = 0.0f;
+  float m_run = -INFINITY, m_run_lo = 0.0f, l_run = 0.0f;
+
+  if (ntk > 0) {
+    gload(0);
+    sload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntk; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntk) {
+      gload(t + 1);
+      sload(t + 1);
+    }
+    const unsigned char* st = smem + (size_t)buf * PF_STAGE_BYTES;
+    const uint4* kh = reinterpret_cast<const uint4*>(st);
+    const uint4* kl = kh + PF_K_PLANE;
+    const uint2* vh = reinterpret_cast<const uint2*>(kl + PF_K_PLANE);
+    const uint2* vl = vh + PF_V_PLANE;
+    const float* sks = reinterpret_cast<const float*>(vl + PF_V_PLANE);
+    const float* svs = sks + PF_BKV;
+    const int64_t kb = (int64_t)t * PF_BKV;
+
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int64_t kfirst = kb + 32 * sub;
+      if (a.causal && kfirst > wq_last + off) continue;  // every key masked for this wave (wave-uniform)
+      if (kfirst >= a.Lkv) continue;
+      // ---- S^T tile [32 keys x 32 queries] = K Q^T, two accumulators ----
+      f32x16 shh, srest;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { shh[r] = 0.0f; srest[r] = 0.0f; }
+      const int krow = 32 * sub + qcol;  // A-operand row of this lane (a key)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int c = 2 * ks + half;
+        const uint4 KH = kh[pf_kpos(krow, c)];
+        const uint4 KL = kl[pf_kpos(krow, c)];
+        shh = mfma32(KH, QH[ks], shh);
+        srest = mfma32(KH, QL[ks], srest);
+        srest = mfma32(KL, QH[ks], srest);
+        srest = mfma32(KL, QL[ks], srest);
+      }
+      // ---- scores of this lane's query for its 16 keys: key = 32 sub + 8 (r/4) + 4 half + r%4 ----
+      const bool need_mask = (a.causal && kfirst + 31 > wq_first + off) || (kfirst + 31 >= a.Lkv);
+      float tv[16], tl[16];
+      float tmax = -INFINITY, tmax_lo = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 32 * sub + 8 * (r >> 2) + 4 * half + (r & 3);
+        float s, sl;
+        logit2(shh[r], srest[r], sks[kk], cq, s, sl);
+        if (need_mask) {
+          const int64_t j = kb + kk;
+          if (j >= a.Lkv || (a.causal && j > qi + off)) {
+            s = -INFINITY;
+            sl = 0.0f;
+          }
+        }
+        tv[r] = s;
+        tl[r] = sl;
+        pair_max(tmax, tmax_lo, s, sl);
+      }
+      pair_max(tmax, tmax_lo, __shfl_xor(tmax, 32, 64), __shfl_xor(tmax_lo, 32, 64));
+      float m_new = m_run, m_new_lo = m_run_lo;
+      pair_max(m_new, m_new_lo, tmax, tmax_lo);
+      const bool none = m_new == -INFINITY;
+      const float m_use = none ? 0.0f : m_new, m_use_lo = none ? 0.0f : m_new_lo;
+      // 0 on the first visible tile (m_run = -inf)
+      const float alpha = exp2f((m_run - m_use) + (m_run_lo - m_use_lo));
+      m_run = m_new;
+      m_run_lo = m_new_lo;
+      float psum = 0.0f;
+      uint32_t ph[8], pl[8];  // P~ fragments: k-step kk2 uses registers 8 kk2 .. 8 kk2 + 7
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int kk0 = 32 * sub + 8 * (r >> 2) + 4 * half + (r & 3);
+        const float p0 = exp2f((tv[r] - m_use) + (tl[r] - m_use_lo));
+        const float p1 = exp2f((tv[r + 1] - m_use) + (tl[r + 1] - m_use_lo));
+        psum += p0 + p1;
+        _Float16 h0, l0, h1, l1;
+        split_p(p0 * svs[kk0], h0, l0);
+        split_p(p1 * svs[kk0 + 1], h1, l1);
+        ph[r >> 1] = pack2(h0, h1);
+        pl[r >> 1] = pack2(l0, l1);
+      }
+      l_run = l_run * alpha + psum;
+      if (alpha != 1.0f) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+      }
+      // ---- O^T [128 d x 32 queries] += V^T P~^T over these 32 keys (2 k-steps of 16) ----
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const uint4 PH = make_uint4(ph[4 * kk2], ph[4 * kk2 + 1], ph[4 * kk2 + 2], ph[4 * kk2 + 3]);
+        const uint4 PL = make_uint4(pl[4 * kk2], pl[4 * kk2 + 1], pl[4 * kk2 + 2], pl[4 * kk2 + 3]);
+        // key groups (of 4) of this k-step for this half: 8 sub + 4 kk2 + half, and that + 2
+        const int g1 = 8 * sub + 4 * kk2 + half, g2 = g1 + 2;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = 32 * dt + qcol;
+          const uint2 a1 = vh[pf_vpos(d, g1)], a2 = vh[pf_vpos(d, g2)];
+          const uint2 b1 = vl[pf_vpos(d, g1)], b2 = vl[pf_vpos(d, g2)];
+          const uint4 VH = make_uint4(a1.x, a1.y, a2.x, a2.y);
+          const uint4 VL = make_uint4(b1.x, b1.y, b2.x, b2.y);
+          O[dt] = mfma32(VH, PH, O[dt]);
+          O[dt] = mfma32(VL, PH, O[dt]);
+          O[dt] = mfma32(VH, PL, O[dt]);
+          O[dt] = mfma32(VL, PL, O[dt]);
+        }
+      }
+    }
+    if (t + 1 < ntk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc * 2^-E / l; lane holds query qcol, d = 32 dt + 8 (r/4) + 4 half + r%4 ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!qvalid) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  float* orow = a.out + b * a.o_st[0] + qi * a.o_st[1] + h * a.o_st[2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float4 o;
+      o.x = __builtin_amdgcn_ldexpf(O[dt][4 * g + 0], -E) * inv;
+      o.y = __builtin_amdgcn_ldexpf(O[dt][4 * g + 1], -E) * inv;
+      o.z = __builtin_amdgcn_ldexpf(O[dt][4 * g + 2], -E) * inv;
+      o.w = __builtin_amdgcn_ldexpf(O[dt][4 * g + 3], -E) * inv;
+      *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * half) = o;
+    }
+}
+
+// ============================================================================================= decode
+constexpr int DC_WAVES = 4;
+constexpr int DC_THREADS = 64 * DC_WAVES;
+constexpr int DC_KPW = 256;                   // keys per wavefront
+constexpr int DC_CHUNK = DC_KPW * DC_WAVES;   // keys per workgroup
+constexpr int DC_SUB = 32;                    // keys per step
+// wavefront-private V^T planes: [128 d][8 groups of 4 keys] uint2, H and L
+constexpr int DC_V_PLANE = D * 8;
+constexpr int DC_PART = 4 + D;  // floats per partial: m_hi, m_lo, l, (pad), O[128]
+
+__device__ __forceinline__ int dc_vpos(int d, int g) { return d * 8 + (g ^ (((d >> 2) & 3) << 1)); }
+
+size_t decode_workspace(int64_t B, int64_t Hq, int64_t Lkv) {
+  const int64_t nsplit = (Lkv + DC_CHUNK - 1) / DC_CHUNK;
+  return (size_t)(B * Hq * (nsplit > 0 ? nsplit : 1) * DC_PART) * sizeof(float);
+}
+
+__global__ __launch_bounds__(DC_THREADS) void attn_decode_kernel(AttnParams a, float* __restrict__ ws,
+                                                                 int nsplit) {
+  // V^T staging during the key loop; the same bytes hold the wavefront partials afterwards
+  __shared__ uint2 vlds[DC_WAVES][2][DC_V_PLANE];
+  __shared__ float red[DC_WAVES];
+  static_assert(sizeof(float) * DC_WAVES * 16 * DC_PART <= sizeof(uint2) * DC_WAVES * 2 * DC_V_PLANE,
+                "partials must fit in the staging planes");
+  float(*part)[16][DC_PART] = reinterpret_cast<float(*)[16][DC_PART]>(&vlds[0][0][0]);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int64_t bk = blockIdx.y;  // (batch, kv-head)
+  const int64_t b = bk / a.Hkv, hk = bk - b * a.Hkv;
+  const int G = (int)(a.Hq / a.Hkv);
+  const int64_t c0 = (int64_t)split * DC_CHUNK;
+  int64_t c1 = c0 + DC_CHUNK;
+  if (c1 > a.Lkv) c1 = a.Lkv;
+  const int64_t w0 = c0 + (int64_t)wave * DC_KPW;
+  int64_t w1 = w0 + DC_KPW;
+  if (w1 > c1) w1 = c1;
+
+  const int16_t* kbase = a.k + b * a.kv_st[0] + hk * a.kv_st[2];
+  const int16_t* vbase = a.v + b * a.kv_st[0] + hk * a.kv_st[2];
+  const float* ksb = a.ks + b * a.kvs_st[0] + hk * a.kvs_st[2];
+  const float* vsb = a.vs + b * a.kvs_st[0] + hk * a.kvs_st[2];
+
+  // E over this workgroup's chunk
+  float vmax = 0.0f;
+  for (int64_t j = c0 + tid; j < c1; j += DC_THREADS) vmax = fmaxf(vmax, vsb[j * a.kvs_st[1]]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, m, 64));
+  if (lane == 0) red[wave] = vmax;
+  __syncthreads();
+  vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int E = vmax > 0.0f ? 14 - ilogb_pos(vmax) : 0;
+
+  // query column of this lane: head hk*G + qc for qc < G (other columns are zero padding)
+  const int qc = lane & 15, grp = lane >> 4;
+  const bool qvalid = qc < G;
+  const int64_t hq = hk * G + (qvalid ? qc : 0);
+  uint4 QH[4], QL[4];
+  {
+    const int16_t* qrow = a.q + b * a.q_st[0] + hq * a.q_st[2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * grp);
+      if (!qvalid) raw = make_uint4(0u, 0u, 0u, 0u);
+      unpack8(raw, QH[ks], QL[ks]);
+    }
+  }
+  const float cq = qvalid ? a.qs[b * a.qs_st[0] + hq * a.qs_st[2]] * a.scale_log2 : 0.0f;
+
+  // loads of one 32-key step: K in operand layout (2 key tiles x 4 d-steps), V as 2 jobs of 4 keys x 8 d
+  uint4 kr[2][4], vr[2][4];
+  float skr[2][4], svr[2][4];
+  auto gload = [&](int64_t j0, uint4 (&k_)[2][4], uint4 (&v_)[2][4], float (&sk_)[2][4], float (&sv_)[2][4]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      int64_t j = j0 + 16 * mt + qc;
+      if (j > a.Lkv - 1) j = a.Lkv - 1;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        k_[mt][ks] = *reinterpret_cast<const uint4*>(kbase + j * a.kv_st[1] + 32 * ks + 8 * grp);
+    }
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int job = lane + 64 * jb, g = job >> 4, c = job & 15;  // keys 4g..4g+3, d-chunk c
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        int64_t j = j0 + 4 * g + kk;
+        if (j > a.Lkv - 1) j = a.Lkv - 1;
+        v_[jb][kk] = *reinterpret_cast<const uint4*>(vbase + j * a.kv_st[1] + 8 * c);
+      }
+    }
+    // scales of the keys this lane's score registers hold: key = j0 + 16 mt + 4 grp + i
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int64_t j = j0 + 16 * mt + 4 * grp + i;
+        const bool ok = j < a.Lkv;
+        if (!ok) j = a.Lkv - 1;
+        sk_[mt][i] = ksb[j * a.kvs_st[1]];
+        sv_[mt][i] = ok ? vsb[j * a.kvs_st[1]] : 0.0f;
+      }
+  };
+
+  f32x4 O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, m_run_lo = 0.0f, l_run = 0.0f;
+  uint2* vh = vlds[wave][0];
+  uint2* vl = vlds[wave][1];
+
+  const int nsteps = w1 > w0 ? (int)((w1 - w0 + DC_SUB - 1) / DC_SUB) : 0;
+  uint4 kr2[2][4], vr2[2][4];
+  float skr2[2][4], svr2[2][4];
+  if (nsteps > 0) gload(w0, kr, vr, skr, svr);
+  for (int st = 0; st < nsteps; ++st) {
+    const int64_t j0 = w0 + (int64_t)st * DC_SUB;
+    if (st + 1 < nsteps) gload(j0 + DC_SUB, kr2, vr2, skr2, svr2);
+    // ---- V^T of these 32 keys into this wave's LDS planes ----
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int job = lane + 64 * jb, g = job >> 4, c = job & 15;
+      uint2 H[8], L[8];
+      unpack_t4x8(vr[jb], H, L);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        vh[dc_vpos(8 * c + dd, g)] = H[dd];
+        vl[dc_vpos(8 * c + dd, g)] = L[dd];
+      }
+    }
+    // ---- S^T [32 keys x 16 query columns] ----
+    f32x4 shh[2], srest[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      shh[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      srest[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        uint4 KH, KL;
+        unpack8(kr[mt][ks], KH, KL);
+        shh[mt] = mfma16(KH, QH[ks], shh[mt]);
+        srest[mt] = mfma16(KH, QL[ks], srest[mt]);
+        srest[mt] = mfma16(KL, QH[ks], srest[mt]);
+        srest[mt] = mfma16(KL, QL[ks], srest[mt]);
+      }
+    }
+    float tv[2][4], tl[2][4];
+    float tmax = -INFINITY, tmax_lo = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t j = j0 + 16 * mt + 4 * grp + i;
+        float s, sl;
+        logit2(shh[mt][i], srest[mt][i], skr[mt][i], cq, s, sl);
+        if (j >= w1) {
+          s = -INFINITY;
+          sl = 0.0f;
+        }
+        tv[mt][i] = s;
+        tl[mt][i] = sl;
+        pair_max(tmax, tmax_lo, s, sl);
+      }
+    pair_max(tmax, tmax_lo, __shfl_xor(tmax, 16, 64), __shfl_xor(tmax_lo, 16, 64));
+    pair_max(tmax, tmax_lo, __shfl_xor(tmax, 32, 64), __shfl_xor(tmax_lo, 32, 64));
+    float m_new = m_run, m_new_lo = m_run_lo;
+    pair_max(m_new, m_new_lo, tmax, tmax_lo);
+    const bool none = m_new == -INFINITY;
+    const float m_use = none ? 0.0f : m_new, m_use_lo = none ? 0.0f : m_new_lo;
+    const float alpha = exp2f((m_run - m_use) + (m_run_lo - m_use_lo));
+    m_run = m_new;
+    m_run_lo = m_new_lo;
+    float psum = 0.0f;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float p0 = exp2f((tv[mt][i] - m_use) + (tl[mt][i] - m_use_lo));
+        const float p1 = exp2f((tv[mt][i + 1] - m_use) + (tl[mt][i + 1] - m_use_lo));
+        psum += p0 + p1;
+        _Float16 h0, l0, h1, l1;
+        split_p(p0 * __builtin_amdgcn_ldexpf(svr[mt][i], E), h0, l0);
+        split_p(p1 * __builtin_amdgcn_ldexpf(svr[mt][i + 1], E), h1, l1);
+        ph[2 * mt + (i >> 1)] = pack2(h0, h1);
+        pl[2 * mt + (i >> 1)] = pack2(l0, l1);
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+    // ---- O^T [128 d x 16 columns] += V^T P~^T over the 32 keys (virtual order: 4 grp.., 16 + 4 grp..) ----
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint4 PH = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    const uint4 PL = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + qc;
+      const uint2 a1 = vh[dc_vpos(d, grp)], a2 = vh[dc_vpos(d, grp + 4)];
+      const uint2 b1 = vl[dc_vpos(d, grp)], b2 = vl[dc_vpos(d, grp + 4)];
+      const uint4 VH = make_uint4(a1.x, a1.y, a2.x, a2.y);
+      const uint4 VL = make_uint4(b1.x, b1.y, b2.x, b2.y);
+      O[dt] = mfma16(VH, PH, O[dt]);
+      O[dt] = mfma16(VL, PH, O[dt]);
+      O[dt] = mfma16(VH, PL, O[dt]);
+      O[dt] = mfma16(VL, PL, O[dt]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kr[mt][ks] = kr2[mt][ks];
+        vr[mt][ks] = vr2[mt][ks];
+        skr[mt][ks] = skr2[mt][ks];
+        svr[mt][ks] = svr2[mt][ks];
+      }
+  }
+
+  // ---- wave partial: the sum over the 4 lane groups, O^T un-renormalised by 2^-E ----
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  __syncthreads();  // every wavefront is done with its V^T planes before they are reused
+  {
+    float* pw = part[wave][qc];
+    if (grp == 0) {
+      pw[0] = m_run;
+      pw[1] = m_run_lo;
+      pw[2] = l_tot;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[4 + 16 * dt + 4 * grp + i] = __builtin_amdgcn_ldexpf(O[dt][i], -E);
+  }
+  __syncthreads();
+  // ---- merge the 4 wavefronts in order: thread -> (column, 8 d values) ----
+  for (int idx = tid; idx < G * 16; idx += DC_THREADS) {
+    const int col = idx >> 4, d0 = (idx & 15) * 8;
+    float m = -INFINITY, ml = 0.0f;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) pair_max(m, ml, part[w][col][0], part[w][col][1]);
+    const bool none = m == -INFINITY;
+    const float mu = none ? 0.0f : m, mul = none ? 0.0f : ml;
+    float l = 0.0f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) {
+      const float f = exp2f((part[w][col][0] - mu) + (part[w][col][1] - mul));
+      l += part[w][col][2] * f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] += part[w][col][4 + d0 + u] * f;
+    }
+    float* dst = ws + (((b * a.Hq + hk * G + col) * nsplit) + split) * DC_PART;
+    if (d0 == 0) {
+      dst[0] = m;
+      dst[1] = ml;
+      dst[2] = l;
+      dst[3] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[4 + d0 + u] = o[u];
+  }
+}
+
+// merge the nsplit partials of each (batch, q-head) in split order
+__global__ __launch_bounds__(128) void attn_decode_merge_kernel(AttnParams a, const float* __restrict__ ws,
+                                                                int nsplit) {
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / a.Hq, h = bh - b * a.Hq;
+  const int d = threadIdx.x;
+  const float* src = ws + bh * nsplit * DC_PART;
+  float m = -INFINITY, ml = 0.0f;
+  for (int s = 0; s < nsplit; ++s) pair_max(m, ml, src[s * DC_PART], src[s * DC_PART + 1]);
+  const bool none = m == -INFINITY;
+  const float mu = none ? 0.0f : m, mul = none ? 0.0f : ml;
+  float l = 0.0f, o = 0.0f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float f = exp2f((src[s * DC_PART] - mu) + (src[s * DC_PART + 1] - mul));
+    l += src[s * DC_PART + 2] * f;
+    o += src[s * DC_PART + 4 + d] * f;
+  }
+  a.out[b * a.o_st[0] + h * a.o_st[2] + d] = l > 0.0f ? o / l : 0.0f;
+}
+
+AttnParams make_params(const heal_attn_args& x) {
+  AttnParams p;
+  p.q = x.q; p.k = x.k; p.v = x.v;
+  p.qs = x.q_scale; p.ks = x.k_scale; p.vs = x.v_scale;
+  p.out = x.out;
+  for (int i = 0; i < 3; ++i) {
+    p.q_st[i] = x.q_strides[i];
+    p.kv_st[i] = x.kv_strides[i];
+    p.qs_st[i] = x.qs_strides[i];
+    p.kvs_st[i] = x.kvs_strides[i];
+    p.o_st[i] = x.o_strides[i];
+  }
+  p.B = x.batch; p.Lq = x.q_len; p.Lkv = x.kv_len; p.Hq = x.n_q_heads; p.Hkv = x.n_kv_heads;
+  const double sm = x.softmax_scale > 0.0f ? (double)x.softmax_scale : 1.0 / sqrt((double)x.head_dim);
+  p.scale_log2 = (float)(sm * 1.4426950408889634);
+  p.causal = x.causal != 0;
+  return p;
+}
+
+bool use_decode(const heal_attn_args& x) {
+  return x.q_len == 1 && x.kv_len > 0 && x.n_kv_heads > 0 && (x.n_q_heads / x.n_kv_heads) <= 16;
+}
+
+__global__ void zero_rows_kernel(AttnParams a) {
+  // kv_len == 0: every query sees no key; the output is defined as 0
+  const int64_t row = blockIdx.x;  // (b, i, h)
+  const int64_t h = row % a.Hq, i = (row / a.Hq) % a.Lq, b = row / (a.Hq * a.Lq);
+  a.out[b * a.o_st[0] + i * a.o_st[1] + h * a.o_st[2] + threadIdx.x] = 0.0f;
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(const heal_attn_args& x) {
+  if (!use_decode(x) || x.batch <= 0 || x.n_q_heads <= 0) return 0;
+  return decode_workspace(x.batch, x.n_q_heads, x.kv_len);
+}
+
+hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
+  const AttnParams p = make_params(x);
+  if (x.kv_len == 0) {
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)(x.batch * x.q_len * x.n_q_heads)), dim3(D), 0, stream,
+                       p);
+    return hipGetLastError();
+  }
+  if (use_decode(x)) {
+    const int nsplit = (int)((x.kv_len + DC_CHUNK - 1) / DC_CHUNK);
+    float* ws = reinterpret_cast<float*>(x.workspace);
+    hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads)),
+                       dim3(DC_THREADS), 0, stream, p, ws, nsplit);
+    hipLaunchKernelGGL(attn_decode_merge_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream,
+                       p, (const float*)ws, nsplit);
+    return hipGetLastError();
+  }
+  static bool attr_set = false;  // benign race: every caller sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * PF_STAGE_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned ntq = (unsigned)((x.q_len + PF_BQ - 1) / PF_BQ);
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)(x.batch * x.n_q_heads), ntq), dim3(PF_THREADS),
+                     2 * PF_STAGE_BYTES, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace heal

@@ -1,0 +1,26 @@
+// heal_internal.h -- declarations shared by the HIP translation units of libheal (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/heal.h"
+
+namespace heal {
+
+// Launchers (host side).  Each enqueues its kernels on `stream` and returns hipGetLastError().
+hipError_t launch_split_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
+                            void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream);
+hipError_t launch_split_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
+                             void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream);
+hipError_t launch_split_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, void* hi, void* lo,
+                            int64_t ld_part, hipStream_t stream);
+hipError_t launch_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim, int64_t ld_x,
+                            int16_t* q, int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream);
+hipError_t launch_gemm_comp(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,
+                            const int32_t* a_exp, int64_t lda, const uint16_t* b_hi, const uint16_t* b_lo,
+                            const int32_t* b_exp, int64_t ldb, int part, float* c, int64_t ldc,
+                            hipStream_t stream);
+size_t attn_workspace_bytes(const heal_attn_args& a);
+hipError_t launch_attn(const heal_attn_args& a, hipStream_t stream);
+
+}  // namespace heal

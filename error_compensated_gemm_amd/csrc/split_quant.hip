@@ -1,0 +1,322 @@
+// split_quant.hip -- the HBM-bound passes of the HEAL hot path on gfx950:
+//   * the split of an FP32 / bf16 matrix into a 16-bit primary value and a 16-bit residual, with an exact
+//     power-of-two row prescale ([TS 2B Mechanism, Overflow Handling]);
+//   * the Dual-FP16 byte split of an INT16 matrix ([TS 2A Mechanism]);
+//   * the INT16 quantisation of Q/K/V per (token, head) ([TS 2A Solution]).
+// [TS] = gist.science explainer "Demystifying Numerical Instability in LLM Inference: Achieving
+// Reproducible Inference for Mission-Critical Tasks with HEAL", Technical Summary.
+//
+// Layout of the work: one 64-lane wavefront per matrix row (split) or one 32-lane half-wave per
+// (token, head) row (quantise), 16-byte vector loads and stores, the row maximum reduced with cross-lane
+// shuffles, no LDS and no atomics.  Each pass reads every input byte once from HBM (the split's second
+// read of a row hits the cache it was just read into) and writes every output byte once.
+#include "heal_internal.h"
+
+namespace heal {
+namespace {
+
+constexpr int kPartF16 = HEAL_F16;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ __forceinline__ float halfwave_max(float v) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 32));
+  return v;
+}
+
+// ilogb of a positive finite float (subnormals included): v_frexp_exp gives e with x = m * 2^e,
+// m in [0.5, 1).
+__device__ __forceinline__ int ilogb_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
+
+// round-to-nearest-even into the 16-bit part type; returns the bit pattern and the value back in fp32
+template <int PART>
+__device__ __forceinline__ uint16_t round16(float x, float* back) {
+  if constexpr (PART == kPartF16) {
+    const _Float16 h = (_Float16)x;
+    *back = (float)h;
+    return __builtin_bit_cast(uint16_t, h);
+  } else {
+    const __bf16 h = (__bf16)x;
+    *back = (float)h;
+    return __builtin_bit_cast(uint16_t, h);
+  }
+}
+
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float v[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float v[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const uint16_t* p) {
+  return __builtin_bit_cast(float, (uint32_t)(*p) << 16);
+}
+
+// One wavefront per row.  PRESCALE: e = 14 - ilogb(rowmax) (else 0).  RESID: write lo.
+// vec: every row of x starts 16-byte aligned (else every element takes the scalar path).
+template <typename TIn, int PART, bool PRESCALE, bool RESID>
+__global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__ x, int64_t rows,
+                                                         int64_t cols, int64_t ld_x, int vec,
+                                                         uint16_t* __restrict__ hi,
+                                                         uint16_t* __restrict__ lo, int64_t ld_part,
+                                                         int32_t* __restrict__ exps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // the whole wave leaves together
+  const TIn* xr = x + row * ld_x;
+  const int64_t nvec = vec ? cols >> 3 : 0;
+  const int64_t tail0 = nvec << 3;
+
+  int e = 0;
+  if constexpr (PRESCALE) {
+    float amax = 0.0f;
+#pragma unroll 4
+    for (int64_t c = lane; c < nvec; c += 64) {
+      float v[8];
+      load8(xr + (c << 3), v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    for (int64_t c = tail0 + lane; c < cols; c += 64) amax = fmaxf(amax, fabsf(load1(xr + c)));
+    amax = wave_max(amax);
+    e = amax > 0.0f ? 14 - ilogb_pos(amax) : 0;
+    if (lane == 0) exps[row] = e;
+  }
+
+  uint16_t* hr = hi + row * ld_part;
+  uint16_t* lr = RESID ? lo + row * ld_part : nullptr;
+#pragma unroll 2
+  for (int64_t c = lane; c < nvec; c += 64) {
+    float v[8];
+    load8(xr + (c << 3), v);
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t h2[2], l2[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float xs = PRESCALE ? __builtin_amdgcn_ldexpf(v[2 * i + j], e) : v[2 * i + j];
+        float hb;
+        h2[j] = round16<PART>(xs, &hb);
+        if constexpr (RESID) {
+          float lb;
+          l2[j] = round16<PART>(xs - hb, &lb);
+        }
+      }
+      hw[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+      if constexpr (RESID) lw[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(hr + (c << 3)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    if constexpr (RESID) *reinterpret_cast<uint4*>(lr + (c << 3)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+  for (int64_t c = tail0 + lane; c < cols; c += 64) {
+    const float xv = load1(xr + c);
+    const float xs = PRESCALE ? __builtin_amdgcn_ldexpf(xv, e) : xv;
+    float hb;
+    hr[c] = round16<PART>(xs, &hb);
+    if constexpr (RESID) {
+      float lb;
+      lr[c] = round16<PART>(xs - hb, &lb);
+    }
+  }
+}
+
+// Dual-FP16 byte split: hi = q >> 8 (arithmetic shift = floor), lo = q & 0xFF; both exact in FP16.
+__global__ __launch_bounds__(256) void split_i16_kernel(const int16_t* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t ld_x, int vec,
+                                                        uint16_t* __restrict__ hi,
+                                                        uint16_t* __restrict__ lo, int64_t ld_part) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int16_t* xr = x + row * ld_x;
+  uint16_t* hr = hi + row * ld_part;
+  uint16_t* lr = lo + row * ld_part;
+  const int64_t nvec = vec ? cols >> 3 : 0;
+  for (int64_t c = lane; c < nvec; c += 64) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(xr + (c << 3));
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q0 = (int)(int16_t)(w[i] & 0xFFFFu);
+      const int q1 = (int)(int16_t)(w[i] >> 16);
+      const _Float16 h0 = (_Float16)(float)(q0 >> 8), h1 = (_Float16)(float)(q1 >> 8);
+      const _Float16 l0 = (_Float16)(float)(q0 & 0xFF), l1 = (_Float16)(float)(q1 & 0xFF);
+      hw[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      lw[i] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    *reinterpret_cast<uint4*>(hr + (c << 3)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *reinterpret_cast<uint4*>(lr + (c << 3)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+  for (int64_t c = (nvec << 3) + lane; c < cols; c += 64) {
+    const int q = xr[c];
+    hr[c] = __builtin_bit_cast(uint16_t, (_Float16)(float)(q >> 8));
+    lr[c] = __builtin_bit_cast(uint16_t, (_Float16)(float)(q & 0xFF));
+  }
+}
+
+// INT16 quantisation, one 32-lane half-wave per (token, head) row of head_dim elements; each lane owns
+// NV float4 groups of the row (head_dim <= 128 * NV).
+template <int NV>
+__global__ __launch_bounds__(256) void quant_i16_kernel(const float* __restrict__ x, int64_t tokens,
+                                                        int64_t heads, int64_t D, int64_t ld_x,
+                                                        int16_t* __restrict__ q, int64_t ld_q,
+                                                        float* __restrict__ s, int64_t ld_s) {
+  const int sub = threadIdx.x & 31;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
+  if (row >= tokens * heads) return;  // both halves of a wave test their own row; shuffles stay in-half
+  const int64_t t = row / heads, h = row - t * heads;
+  const float* xr = x + t * ld_x + h * D;
+  float4 v[NV];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t d = (int64_t)(sub + 32 * i) * 4;
+    if (d < D) {
+      v[i] = *reinterpret_cast<const float4*>(xr + d);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    } else {
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  amax = halfwave_max(amax);
+  const float sc = amax / 32767.0f;  // IEEE fp32 division (correctly rounded build flag)
+  if (sub == 0) s[t * ld_s + h] = sc;
+  int16_t* qr = q + t * ld_q + h * D;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t d = (int64_t)(sub + 32 * i) * 4;
+    if (d < D) {
+      const float in[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      uint32_t packed[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        int16_t o[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float r = 0.0f;
+          if (sc > 0.0f) {
+            r = rintf(in[2 * j + u] / sc);
+            r = fminf(fmaxf(r, -32767.0f), 32767.0f);
+          }
+          o[u] = (int16_t)r;
+        }
+        packed[j] = (uint32_t)(uint16_t)o[0] | ((uint32_t)(uint16_t)o[1] << 16);
+      }
+      *reinterpret_cast<uint2*>(qr + d) = make_uint2(packed[0], packed[1]);
+    }
+  }
+}
+
+inline unsigned blocks_for_rows(int64_t rows, int64_t per_block) {
+  return (unsigned)((rows + per_block - 1) / per_block);
+}
+
+inline int rows_vectorisable(const void* x, int64_t ld_x, int64_t elem_bytes) {
+  return ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && ((ld_x * elem_bytes) & 15) == 0) ? 1 : 0;
+}
+
+template <typename TIn>
+hipError_t launch_split_any(const TIn* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
+                            void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream) {
+  const int vec = rows_vectorisable(x, ld_x, (int64_t)sizeof(TIn));
+  if (rows == 0 || cols == 0) {
+    // an empty row still has a defined exponent (0); set it with a one-wave launch of the kernel
+    if (rows > 0 && exps) {
+      hipLaunchKernelGGL((split_rows_kernel<TIn, kPartF16, true, false>), dim3(blocks_for_rows(rows, 4)),
+                         dim3(256), 0, stream, x, rows, (int64_t)0, ld_x, vec, (uint16_t*)hi,
+                         (uint16_t*)lo, ld_part, exps);
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid(blocks_for_rows(rows, 4)), block(256);
+  uint16_t* h = (uint16_t*)hi;
+  uint16_t* l = (uint16_t*)lo;
+  const bool pre = exps != nullptr, res = lo != nullptr;
+#define HEAL_SPLIT_CASE(PART, PRE, RES)                                                                \
+  if (part == PART && pre == PRE && res == RES) {                                                       \
+    hipLaunchKernelGGL((split_rows_kernel<TIn, PART, PRE, RES>), grid, block, 0, stream, x, rows, cols, \
+                       ld_x, vec, h, l, ld_part, exps);                                                 \
+    return hipGetLastError();                                                                           \
+  }
+  HEAL_SPLIT_CASE(HEAL_F16, true, true)
+  HEAL_SPLIT_CASE(HEAL_F16, true, false)
+  HEAL_SPLIT_CASE(HEAL_F16, false, true)
+  HEAL_SPLIT_CASE(HEAL_F16, false, false)
+  HEAL_SPLIT_CASE(HEAL_BF16, true, true)
+  HEAL_SPLIT_CASE(HEAL_BF16, true, false)
+  HEAL_SPLIT_CASE(HEAL_BF16, false, true)
+  HEAL_SPLIT_CASE(HEAL_BF16, false, false)
+#undef HEAL_SPLIT_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_split_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
+                            void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream) {
+  return launch_split_any<float>(x, rows, cols, ld_x, part, hi, lo, ld_part, exps, stream);
+}
+
+hipError_t launch_split_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int part,
+                             void* hi, void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream) {
+  return launch_split_any<uint16_t>(x, rows, cols, ld_x, part, hi, lo, ld_part, exps, stream);
+}
+
+hipError_t launch_split_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, void* hi, void* lo,
+                            int64_t ld_part, hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_i16_kernel, dim3(blocks_for_rows(rows, 4)), dim3(256), 0, stream, x, rows, cols,
+                     ld_x, rows_vectorisable(x, ld_x, 2), (uint16_t*)hi, (uint16_t*)lo, ld_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim, int64_t ld_x,
+                            int16_t* q, int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream) {
+  const int64_t rows = tokens * heads;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(blocks_for_rows(rows, 8)), block(256);
+  const int nv = (int)((head_dim + 127) / 128);
+  switch (nv) {
+    case 0:
+    case 1:
+      hipLaunchKernelGGL(quant_i16_kernel<1>, grid, block, 0, stream, x, tokens, heads, head_dim, ld_x, q,
+                         ld_q, scale, ld_s);
+      break;
+    case 2:
+      hipLaunchKernelGGL(quant_i16_kernel<2>, grid, block, 0, stream, x, tokens, heads, head_dim, ld_x, q,
+                         ld_q, scale, ld_s);
+      break;
+    case 3:
+    case 4:
+      hipLaunchKernelGGL(quant_i16_kernel<4>, grid, block, 0, stream, x, tokens, heads, head_dim, ld_x, q,
+                         ld_q, scale, ld_s);
+      break;
+    default:
+      hipLaunchKernelGGL(quant_i16_kernel<8>, grid, block, 0, stream, x, tokens, heads, head_dim, ld_x, q,
+                         ld_q, scale, ld_s);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace heal

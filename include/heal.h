@@ -1,0 +1,185 @@
+/*
+ * heal.h -- C ABI of the HEAL hot path on AMD Instinct MI355X (gfx950).
+ *
+ * HEAL gets near-FP32 results out of 16-bit matrix units and keeps the attention inputs at 16 bits:
+ *   - an FP32 operand is split into a primary 16-bit value and a residual, and the 16-bit products are
+ *     summed into one FP32 accumulator (the "algebraic error compensation" GEMM);
+ *   - Q, K and V are stored as INT16, and each INT16 value is unpacked into two exactly representable
+ *     FP16 halves ("Dual-FP16") for the QK^T and PV products, with FP32 softmax.
+ *
+ * Sources (cited by page and section):
+ *   [TS]  gist.science explainer "Demystifying Numerical Instability in LLM Inference: Achieving
+ *         Reproducible Inference for Mission-Critical Tasks with HEAL", section "Technical Summary";
+ *         [TS 2A] "Mitigating Attention Truncation via INT16 Quantization" (Solution, Mechanism, Benefit);
+ *         [TS 2B] "Mitigating GEMM Truncation via Algebraic Error Compensation" (Solution, Mechanism,
+ *         Overflow Handling).
+ *   [ABS] the authors' abstract, arXiv 2606.21023 v2.
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library never allocates, frees or
+ *     synchronises; work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and the call
+ *     returns at once.
+ *   - Arguments are validated before anything is launched; on any error nothing is enqueued and the
+ *     status says why.  A launch failure reported by the runtime gives HEAL_ERR_LAUNCH.
+ *   - Matrices are row-major.  Leading dimensions are in ELEMENTS.  Base pointers must be 16-byte aligned
+ *     and leading dimensions must be multiples of 8 elements (16 bytes for 16-bit data); otherwise
+ *     HEAL_ERR_ALIGN.  There is no slow fallback path.
+ *   - NaN or infinite inputs are outside the contract: they are not detected and the result is
+ *     unspecified.  Zero-sized problems are valid and enqueue nothing (or only the zero fill they imply).
+ *   - Results are bitwise deterministic: no floating-point atomics, fixed reduction orders.
+ *   - Calls are stateless and may be made from several host threads at once.
+ */
+#ifndef HEAL_H
+#define HEAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HEAL_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define HEAL_API __attribute__((visibility("default")))
+#else
+#define HEAL_API
+#endif
+
+typedef enum {
+  HEAL_OK = 0,
+  HEAL_ERR_NULL = 1,        /* a required pointer is NULL */
+  HEAL_ERR_SHAPE = 2,       /* a size is negative or inconsistent */
+  HEAL_ERR_STRIDE = 3,      /* a leading dimension / stride is smaller than the row it must hold */
+  HEAL_ERR_ALIGN = 4,       /* pointer not 16-byte aligned, or leading dimension not a multiple of 8 */
+  HEAL_ERR_DTYPE = 5,       /* a dtype code that the call does not accept */
+  HEAL_ERR_UNSUPPORTED = 6, /* a valid request this build does not implement (e.g. head_dim != 128) */
+  HEAL_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
+  HEAL_ERR_WORKSPACE = 8    /* workspace missing or smaller than heal_attn_workspace_bytes() */
+} heal_status;
+
+typedef enum { HEAL_F32 = 0, HEAL_BF16 = 1, HEAL_F16 = 2, HEAL_I16 = 3 } heal_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+HEAL_API const char* heal_status_str(int status);
+/* HEAL_ABI_VERSION of the loaded library. */
+HEAL_API int heal_abi_version(void);
+
+/*
+ * heal_split -- the operand decomposition of [TS 2B Mechanism] (FP32/bf16 in) and the Dual-FP16 unpack
+ * of [TS 2A Mechanism] (INT16 in).
+ *
+ * x_type = HEAL_F32 or HEAL_BF16 (x is [rows, cols], leading dimension ld_x):
+ *   per row r:  e_r = 14 - ilogb(max_c |x_rc|)  (0 for an all-zero row; 0 for every row if exps == NULL)
+ *               x'  = fl32(x * 2^e_r)                      (exact unless x' falls below the fp32 normals)
+ *               hi  = round16(x'),  lo = round16(x' - hi)  (x' - hi is exact in fp32)
+ *   round16 is IEEE round-to-nearest-even into part_type (HEAL_F16, the graded mode, or HEAL_BF16, the
+ *   contrast mode), gradual underflow, overflow to infinity.  The prescale is the exact power-of-two form
+ *   of the "targeted rescaling" of [TS 2B Overflow Handling]: each row's maximum lands in [2^14, 2^15), so
+ *   no FP16 part overflows and the residual keeps 11 more bits.  exps[r] receives e_r (int32) when
+ *   exps != NULL.  lo == NULL drops the residual (used for weights that are exact in 16 bits).
+ * x_type = HEAL_I16 (x is int16 [rows, cols]): the byte split hi = x >> 8 (floor), lo = x & 0xFF, written
+ *   as FP16 values with x = 256*hi + lo exactly.  part_type must be HEAL_F16, lo must be non-NULL and
+ *   exps must be NULL.
+ * hi and lo are [rows, cols] 16-bit, leading dimension ld_part.  Rows are independent; hi/lo must not
+ * overlap x.  Alignment: x needs only its element alignment and any ld_x >= cols (rows that start on a
+ * 16-byte boundary are read with 16-byte loads, others element by element); hi and lo must be 16-byte
+ * aligned with ld_part a multiple of 8.
+ * Errors: HEAL_ERR_NULL (x or hi NULL with rows*cols > 0; lo NULL for I16), HEAL_ERR_SHAPE (negative
+ * sizes), HEAL_ERR_STRIDE (ld < cols), HEAL_ERR_ALIGN, HEAL_ERR_DTYPE (bad x_type/part_type pairing).
+ */
+HEAL_API heal_status heal_split(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld_x, int part_type,
+                       void* hi, void* lo, int64_t ld_part, int32_t* exps, void* stream);
+
+/*
+ * heal_gemm_comp -- the error-compensated GEMM of [TS 2B Solution/Mechanism]:
+ *   C[i, j] = 2^-(ea_i + eb_j) * sum_k ( ah*bh + [b_lo] ah*bl + [a_lo] al*bh )[i, k, j]
+ * with A [M, K] given as parts a_hi / a_lo (leading dimension lda) and B given TRANSPOSED as parts
+ * b_hi / b_lo of B^T [N, K] (leading dimension ldb): both operands are K-contiguous.  Parts are what
+ * heal_split writes (16-bit, part_type HEAL_F16 or HEAL_BF16).  A NULL a_lo / b_lo drops the products
+ * that need it: P = 1 + (a_lo != NULL) + (b_lo != NULL) products of 16-bit inputs, all accumulated in
+ * ONE FP32 accumulator per output; lo*lo is never formed.  a_exp / b_exp are the int32 row exponents of
+ * heal_split (NULL means 0).  C is FP32 [M, N] (leading dimension ldc, a multiple of 4 elements): the
+ * accumulator scaled by the exact power of two is the only rounding at the kernel boundary.
+ * K = 0 writes zeros.  Errors: HEAL_ERR_NULL (a_hi, b_hi or c NULL with M*N > 0), HEAL_ERR_SHAPE,
+ * HEAL_ERR_STRIDE (lda, ldb < K or ldc < N), HEAL_ERR_ALIGN, HEAL_ERR_DTYPE.
+ */
+HEAL_API heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
+                           const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
+                           const int32_t* b_exp, int64_t ldb, int part_type, float* c, int64_t ldc,
+                           void* stream);
+
+/*
+ * heal_qkv_quant_i16 -- INT16 quantisation of Q, K or V per (token, head) ([TS 2A Solution]; [ABS]):
+ *   a = max_d |x|;  s = fl32(a / 32767);  q = clamp(rint(fl32(x / s)), -32767, 32767)   (IEEE division,
+ *   ties-to-even rint, symmetric, no zero point);  s = 0 (an all-zero row, or one so small that s
+ *   underflows) gives q = 0.
+ * x is fp32 [tokens, heads, head_dim] with token stride ld_x (elements; heads packed at head_dim).
+ * q is int16 with token stride ld_q and heads packed; scale is fp32 with token stride ld_s and heads
+ * packed.  The strides let a caller quantise new tokens straight into a larger KV cache (fold the batch
+ * into `tokens` with the cache's per-sequence stride).  head_dim must be a multiple of 4 and at most 1024.
+ * Errors: HEAL_ERR_NULL, HEAL_ERR_SHAPE, HEAL_ERR_STRIDE (ld_x or ld_q < heads*head_dim, ld_s < heads),
+ * HEAL_ERR_ALIGN (x 16-byte and q 8-byte aligned; ld_x, ld_q multiples of 4; scale 4-byte aligned),
+ * HEAL_ERR_UNSUPPORTED (head_dim).
+ */
+HEAL_API heal_status heal_qkv_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim,
+                               int64_t ld_x, int16_t* q, int64_t ld_q, float* scale, int64_t ld_s,
+                               void* stream);
+
+/*
+ * Arguments of heal_attn_dual_fp16.  Strides are in elements; the last (head_dim) axis is contiguous.
+ *   q        int16 [batch, q_len, n_q_heads, head_dim]     strides q_strides  = {batch, token, head}
+ *   k, v     int16 [batch, kv_len, n_kv_heads, head_dim]   strides kv_strides (shared by k and v)
+ *   q_scale  fp32  [batch, q_len, n_q_heads]               strides qs_strides
+ *   k_scale, v_scale fp32 [batch, kv_len, n_kv_heads]      strides kvs_strides
+ *   out      fp32  [batch, q_len, n_q_heads, head_dim]     strides o_strides
+ * causal != 0 masks key j for query i unless j <= i + (kv_len - q_len) (bottom-right alignment, so a
+ * decode step with q_len = 1 sees the whole cache).  softmax_scale = 0 means 1/sqrt(head_dim).
+ * Query head h reads key/value head h / (n_q_heads / n_kv_heads) (grouped-query attention).
+ * workspace: device scratch of at least heal_attn_workspace_bytes(args) bytes (may be NULL when that is
+ * 0), 256-byte aligned, owned by the caller, not shared by calls that may run concurrently.
+ */
+typedef struct {
+  int64_t batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim;
+  const int16_t* q;
+  const int16_t* k;
+  const int16_t* v;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  int64_t q_strides[3];
+  int64_t kv_strides[3];
+  int64_t qs_strides[3];
+  int64_t kvs_strides[3];
+  int64_t o_strides[3];
+  int32_t causal;
+  float softmax_scale;
+  float* out;
+  void* workspace;
+  size_t workspace_bytes;
+} heal_attn_args;
+
+/* Workspace bytes heal_attn_dual_fp16 needs for these arguments (0 when none). */
+HEAL_API size_t heal_attn_workspace_bytes(const heal_attn_args* args);
+
+/*
+ * heal_attn_dual_fp16 -- attention over INT16 Q/K/V with Dual-FP16 products ([TS 2A Mechanism, Benefit]):
+ *   x^ = s * q  (per-(token, head) scale);  S = softmax_scale * Q^ K^T;  P = softmax(S) over the visible
+ *   keys (FP32, running maximum and sum);  O = P V^.
+ * Each INT16 operand is unpacked in registers into FP16 halves (hi = q >> 8, lo = q & 0xFF), QK^T is the
+ * sum of the four 16-bit products of the halves, and PV is formed from P * s_v (renormalised by an exact
+ * power of two and split into FP16 hi + lo) against the halves of V: 4 + 4 16-bit matrix products,
+ * FP32 accumulation, FP32 output.  q_len = 1 takes the decode path (split over the keys, partial results
+ * merged in a fixed order); q_len > 1 the prefill path.
+ * Errors: HEAL_ERR_NULL, HEAL_ERR_SHAPE (sizes, n_q_heads % n_kv_heads != 0), HEAL_ERR_STRIDE,
+ * HEAL_ERR_ALIGN (q/k/v/out 16-byte aligned, strides multiples of 8), HEAL_ERR_UNSUPPORTED
+ * (head_dim != 128), HEAL_ERR_WORKSPACE.
+ */
+HEAL_API heal_status heal_attn_dual_fp16(const heal_attn_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HEAL_H */

@@ -24,7 +24,8 @@
  *   R-prod    the compensated product sums hi*hi + hi*lo + lo*hi (lo*lo dropped) when both operands are
  *             split, hi*hi + lo*hi when only the activations are ([TS 2B Mechanism]: "two" products).
  *   R-quant   symmetric INT16 per (token, head): s = fl32(max|x| / 32767), q = clamp(rint(fl32(x / s)),
- *             -32767, 32767), max|x| = 0 gives s = 0 and q = 0 ([TS 2A Solution] names only "INT16").
+ *             -32767, 32767); s = 0 (an all-zero row, or max|x| so small that s underflows) gives q = 0
+ *             ([TS 2A Solution] names only "INT16").
  *   R-dual    Dual-FP16 unpack is the byte split hi = q >> 8 (floor), lo = q & 0xFF, q = 256*hi + lo;
  *             the pages write the pair with a 2^10 shift ([TS 2A Mechanism]); any shift that keeps both
  *             halves integer is exact, and 8 keeps every FP32 partial sum exact at head_dim 128.
@@ -185,13 +186,12 @@ void orc_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t d, int
         const float a = fabsf(row[i]);
         if (a > amax) amax = a;
       }
-      if (amax == 0.0f) {
-        s[t * heads + h] = 0.0f;
+      const float sc = amax / 32767.0f;
+      s[t * heads + h] = sc;
+      if (sc == 0.0f) { /* an all-zero row (or one whose scale underflows) codes every element as 0 */
         for (int64_t i = 0; i < d; ++i) qrow[i] = 0;
         continue;
       }
-      const float sc = amax / 32767.0f;
-      s[t * heads + h] = sc;
       for (int64_t i = 0; i < d; ++i) {
         float r = rintf(row[i] / sc);
         if (r > 32767.0f) r = 32767.0f;

@@ -1,0 +1,153 @@
+"""The C ABI on the CPU: libheal.so loads, exports every entry point include/heal.h declares, the
+ctypes mirror of heal_attn_args matches the C layout, and every validation error is returned before any
+device work (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "heal.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"HEAL_API\s+[\w\s\*]+?\b(heal_\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("heal_split", "heal_gemm_comp", "heal_qkv_quant_i16", "heal_attn_dual_fp16",
+              "heal_attn_workspace_bytes", "heal_status_str", "heal_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(heal):
+    lib = heal.load()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", heal.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (heal_\w+)$", out, re.M))
+    assert set(_declared()) <= exported
+    # nothing else leaks out of the library's namespace
+    assert all(s.startswith("heal_") for s in exported)
+
+
+def test_version_and_status_strings(heal):
+    lib = heal.load()
+    assert lib.heal_abi_version() == 1
+    for s in range(9):
+        assert lib.heal_status_str(s).decode().startswith("HEAL")
+    assert b"unknown" in lib.heal_status_str(99)
+
+
+def test_attn_args_layout_matches_c(heal, tmp_path):
+    fields = [f for f, _ in heal.HealAttnArgs._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(f'  printf("{f} %zu\\n", offsetof(heal_attn_args, {f}));\n' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "heal.h"\nint main(void) {\n'
+                   f'  printf("size %zu\\n", sizeof(heal_attn_args));\n{body}  return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split("\n")
+               if line)
+    assert int(got["size"]) == ctypes.sizeof(heal.HealAttnArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(heal.HealAttnArgs, f).offset, f
+
+
+P = ctypes.c_void_p
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: each call below fails validation first
+MIS = FAKE + 2
+
+
+def test_split_validation(heal):
+    lib = heal.load()
+    F32, BF16, F16, I16 = 0, 1, 2, 3
+    assert lib.heal_split(None, F32, 4, 8, 8, F16, P(FAKE), P(FAKE), 8, P(FAKE), None) == 1   # NULL x
+    assert lib.heal_split(P(FAKE), F32, -1, 8, 8, F16, P(FAKE), None, 8, None, None) == 2     # shape
+    assert lib.heal_split(P(FAKE), F32, 4, 8, 4, F16, P(FAKE), None, 8, None, None) == 3      # ld_x < cols
+    assert lib.heal_split(P(MIS), F32, 4, 8, 8, F16, P(FAKE), None, 8, None, None) == 4       # f32 misaligned
+    assert lib.heal_split(P(FAKE), F32, 4, 8, 8, F16, P(MIS), None, 8, None, None) == 4       # parts misaligned
+    assert lib.heal_split(P(FAKE), F32, 4, 8, 8, F16, P(FAKE), None, 12, None, None) == 4     # ld_part % 8
+    assert lib.heal_split(P(FAKE), 7, 4, 8, 8, F16, P(FAKE), None, 8, None, None) == 5        # x dtype
+    assert lib.heal_split(P(FAKE), F32, 4, 8, 8, F32, P(FAKE), None, 8, None, None) == 5      # part dtype
+    assert lib.heal_split(P(FAKE), I16, 4, 8, 8, F16, P(FAKE), P(FAKE), 8, P(FAKE), None) == 5  # I16 + exps
+    assert lib.heal_split(P(FAKE), I16, 4, 8, 8, F16, P(FAKE), None, 8, None, None) == 1      # I16 needs lo
+    assert lib.heal_split(None, F32, 0, 8, 8, F16, None, None, 8, None, None) == 0            # empty: OK
+
+
+def test_gemm_validation(heal):
+    lib = heal.load()
+    F16, F32 = 2, 0
+    ok = dict(M=4, N=4, K=8)
+    args = lambda M=4, N=4, K=8, ah=FAKE, bh=FAKE, c=FAKE, lda=8, ldb=8, ldc=4, part=F16, al=None: (
+        M, N, K, P(ah) if ah else None, P(al) if al else None, None, lda, P(bh) if bh else None, None, None,
+        ldb, part, P(c) if c else None, ldc, None)
+    assert lib.heal_gemm_comp(*args(M=-1)) == 2
+    assert lib.heal_gemm_comp(*args(ah=None)) == 1
+    assert lib.heal_gemm_comp(*args(c=None)) == 1
+    assert lib.heal_gemm_comp(*args(lda=4)) == 3
+    assert lib.heal_gemm_comp(*args(ldc=2)) == 3
+    assert lib.heal_gemm_comp(*args(ah=MIS)) == 4
+    assert lib.heal_gemm_comp(*args(al=MIS)) == 4
+    assert lib.heal_gemm_comp(*args(ldb=12)) == 4
+    assert lib.heal_gemm_comp(*args(ldc=6)) == 4
+    assert lib.heal_gemm_comp(*args(part=F32)) == 5
+    assert lib.heal_gemm_comp(*args(M=0)) == 0
+
+
+def test_quant_validation(heal):
+    lib = heal.load()
+    assert lib.heal_qkv_quant_i16(P(FAKE), 4, 2, 130, 512, P(FAKE), 512, P(FAKE), 2, None) == 6  # head_dim % 4
+    assert lib.heal_qkv_quant_i16(P(FAKE), 4, 2, 2048, 4096, P(FAKE), 4096, P(FAKE), 2, None) == 6
+    assert lib.heal_qkv_quant_i16(None, 4, 2, 128, 256, P(FAKE), 256, P(FAKE), 2, None) == 1
+    assert lib.heal_qkv_quant_i16(P(FAKE), 4, 2, 128, 128, P(FAKE), 256, P(FAKE), 2, None) == 3
+    assert lib.heal_qkv_quant_i16(P(FAKE), 4, 2, 128, 256, P(FAKE), 256, P(FAKE), 1, None) == 3
+    assert lib.heal_qkv_quant_i16(P(MIS), 4, 2, 128, 256, P(FAKE), 256, P(FAKE), 2, None) == 4
+    assert lib.heal_qkv_quant_i16(P(FAKE), 4, 2, 128, 258, P(FAKE), 256, P(FAKE), 2, None) == 4
+    assert lib.heal_qkv_quant_i16(P(FAKE), -4, 2, 128, 256, P(FAKE), 256, P(FAKE), 2, None) == 2
+    assert lib.heal_qkv_quant_i16(P(FAKE), 0, 2, 128, 256, P(FAKE), 256, P(FAKE), 2, None) == 0
+
+
+def _attn_args(heal, **kw):
+    a = heal.HealAttnArgs()
+    a.batch, a.q_len, a.kv_len, a.n_q_heads, a.n_kv_heads, a.head_dim = 1, 4, 4, 2, 1, 128
+    a.q = a.k = a.v = a.out = FAKE
+    a.q_scale = a.k_scale = a.v_scale = FAKE
+    a.q_strides[:] = [4 * 2 * 128, 2 * 128, 128]
+    a.kv_strides[:] = [4 * 128, 128, 128]
+    a.qs_strides[:] = [8, 2, 1]
+    a.kvs_strides[:] = [4, 1, 1]
+    a.o_strides[:] = [4 * 2 * 128, 2 * 128, 128]
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_attn_validation(heal):
+    lib = heal.load()
+    call = lambda **kw: lib.heal_attn_dual_fp16(ctypes.byref(_attn_args(heal, **kw)), None)
+    assert lib.heal_attn_dual_fp16(None, None) == 1
+    assert call(head_dim=64) == 6
+    assert call(n_q_heads=3, n_kv_heads=2) == 2
+    assert call(batch=-1) == 2
+    assert call(q=0) == 1
+    assert call(k=0) == 1
+    assert call(out=MIS) == 4
+    assert call(softmax_scale=-1.0) == 2
+    a = _attn_args(heal)
+    a.q_strides[1] = 100  # not a multiple of 8
+    assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 4
+    a = _attn_args(heal)
+    a.kv_strides[2] = 64  # smaller than head_dim
+    assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 3
+    # decode needs a workspace: none given -> HEAL_ERR_WORKSPACE before any launch
+    a = _attn_args(heal, q_len=1, kv_len=5000)
+    assert lib.heal_attn_workspace_bytes(ctypes.byref(a)) > 0
+    assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 8
+    a = _attn_args(heal, q_len=1, kv_len=5000, workspace=FAKE, workspace_bytes=16)
+    assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 8
+    assert call(batch=0) == 0

@@ -1,0 +1,146 @@
+"""GPU parity of the Dual-FP16 attention (prefill and decode) against the FP64 oracle on the dequantised
+INT16 inputs.  Bar: normwise relative error <= 2e-6 over the checked rows; closed forms; decode equals
+the last prefill row; run-to-run bit determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import banner, dev, host, normwise
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-6
+
+
+def _run(heal, q, qs, k, ks, v, vs, causal, scale=None):
+    out = heal.heal_attn_dual_fp16(dev(q), dev(qs), dev(k), dev(ks), dev(v), dev(vs), causal=causal,
+                                   softmax_scale=scale)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("B,Lq,Lkv,Hq,Hkv,causal", [
+    (1, 300, 300, 4, 2, True), (2, 64, 64, 2, 2, False), (1, 77, 333, 3, 1, True), (1, 513, 513, 2, 1, True),
+    (1, 5, 5, 1, 1, True), (1, 40, 17, 2, 2, True), (2, 33, 129, 4, 4, False)])
+def test_prefill_small(heal, B, Lq, Lkv, Hq, Hkv, causal):
+    banner(f"prefill B={B} Lq={Lq} Lkv={Lkv} Hq={Hq} Hkv={Hkv} causal={causal}")
+    q, qs = workloads.int16_cache_host(B, Lq, Hq, 128, seed=11)
+    k, ks = workloads.int16_cache_host(B, Lkv, Hkv, 128, seed=12)
+    v, vs = workloads.int16_cache_host(B, Lkv, Hkv, 128, seed=13)
+    o = _run(heal, q, qs, k, ks, v, vs, causal)
+    ref = oracle.attn_i16_f64(q, qs, k, ks, v, vs, causal)
+    err = normwise(o, ref)
+    print(f"[attn] prefill {B},{Lq},{Lkv},{Hq},{Hkv},{causal} normwise {err:.3e}")
+    assert err <= TOL
+
+
+def test_prefill_quantized_fp32_inputs(heal):
+    banner("prefill from fp32 Q/K/V through the GPU quantiser")
+    Q, K, V = workloads.qkv_fp32(1, 384, 4, 128, seed=2)
+    qd, kd, vd = dev(Q[0]), dev(K[0]), dev(V[0])
+    (q, qs), (k, ks), (v, vs) = (heal.heal_qkv_quant_i16(t) for t in (qd, kd, vd))
+    out = heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None], causal=True)
+    torch.cuda.synchronize()
+    oq, oqs = oracle.quant_i16(Q[0])
+    ok_, oks = oracle.quant_i16(K[0])
+    ov, ovs = oracle.quant_i16(V[0])
+    ref = oracle.attn_i16_f64(oq[None], oqs[None], ok_[None], oks[None], ov[None], ovs[None], causal=True)
+    err = normwise(host(out), ref)
+    raw = oracle.attn_f64(Q, K, V, causal=True)
+    qerr = normwise(host(out), raw)
+    print(f"[attn] quantised prefill normwise {err:.3e} (vs raw fp32 inputs: {qerr:.3e})")
+    assert err <= TOL
+
+
+def test_closed_forms(heal):
+    banner("attention closed forms")
+    # one key with a power-of-two scale: O = s_v * v exactly
+    q, qs = workloads.int16_cache_host(1, 4, 2, 128, seed=1)
+    k, ks = workloads.int16_cache_host(1, 1, 2, 128, seed=2)
+    v, _ = workloads.int16_cache_host(1, 1, 2, 128, seed=3)
+    vs = np.full((1, 1, 2), 2.0 ** -13, np.float32)
+    o = _run(heal, q, qs, k, ks, v, vs, causal=False)
+    assert np.array_equal(o, np.broadcast_to(v.astype(np.float64) * 2.0 ** -13, o.shape).astype(np.float32))
+    # identical value rows: O equals that row (decode and prefill)
+    for Lq in (1, 70):
+        k, ks = workloads.int16_cache_host(1, 200, 1, 128, seed=4)
+        v1, _ = workloads.int16_cache_host(1, 1, 1, 128, seed=5)
+        v = np.repeat(v1, 200, axis=1)
+        vs = np.full((1, 200, 1), 3.0e-4, np.float32)
+        q, qs = workloads.int16_cache_host(1, Lq, 4, 128, seed=6)
+        o = _run(heal, q, qs, k, ks, v, vs, causal=True)
+        want = (v1[0, 0, 0].astype(np.float64) * np.float64(np.float32(3.0e-4)))
+        assert normwise(o.reshape(-1, 128), np.broadcast_to(want, (Lq * 4, 128))) <= 1e-6
+
+
+def test_decode_matches_last_prefill_row(heal):
+    banner("decode == last row of prefill")
+    B, L, Hq, Hkv = 2, 1500, 8, 2
+    q, qs = workloads.int16_cache_host(B, L, Hq, 128, seed=21)
+    k, ks = workloads.int16_cache_host(B, L, Hkv, 128, seed=22)
+    v, vs = workloads.int16_cache_host(B, L, Hkv, 128, seed=23)
+    full = _run(heal, q, qs, k, ks, v, vs, causal=True)
+    dec = _run(heal, q[:, -1:], qs[:, -1:], k, ks, v, vs, causal=True)
+    ref = oracle.attn_i16_f64(q[:, -1:], qs[:, -1:], k, ks, v, vs, causal=True)
+    e_dec, e_full = normwise(dec, ref), normwise(full[:, -1:], ref)
+    print(f"[attn] decode {e_dec:.3e}, last prefill row {e_full:.3e}")
+    assert e_dec <= TOL and e_full <= TOL
+    assert normwise(dec, full[:, -1:]) <= 2 * TOL
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv", [(3, 1000, 32, 8), (1, 1, 4, 4), (2, 4097, 16, 1), (1, 33, 8, 8)])
+def test_decode_small(heal, B, L, Hq, Hkv):
+    banner(f"decode B={B} L={L} Hq={Hq} Hkv={Hkv}")
+    q, qs = workloads.int16_cache_host(B, 1, Hq, 128, seed=31)
+    k, ks = workloads.int16_cache_host(B, L, Hkv, 128, seed=32)
+    v, vs = workloads.int16_cache_host(B, L, Hkv, 128, seed=33)
+    o = _run(heal, q, qs, k, ks, v, vs, causal=True)
+    ref = oracle.attn_i16_f64(q, qs, k, ks, v, vs, causal=True)
+    err = normwise(o, ref)
+    print(f"[attn] decode {B},{L},{Hq},{Hkv} normwise {err:.3e}")
+    assert err <= TOL
+
+
+def test_prefill_config_sampled_and_deterministic(heal):
+    banner("prefill 1x4096x32x128 causal, sampled rows")
+    B, L, H = 1, 4096, 32
+    Q, K, V = workloads.qkv_fp32(B, L, H, 128, seed=2)
+    qd, kd, vd = dev(Q[0]), dev(K[0]), dev(V[0])
+    (q, qs), (k, ks), (v, vs) = (heal.heal_qkv_quant_i16(t) for t in (qd, kd, vd))
+    args = (q[None], qs[None], k[None], ks[None], v[None], vs[None])
+    o1 = heal.heal_attn_dual_fp16(*args, causal=True)
+    o2 = heal.heal_attn_dual_fp16(*args, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    oq, oqs = oracle.quant_i16(Q[0])
+    ok_, oks = oracle.quant_i16(K[0])
+    ov, ovs = oracle.quant_i16(V[0])
+    assert np.array_equal(host(q), oq) and np.array_equal(host(k), ok_) and np.array_equal(host(v), ov)
+    rng = np.random.default_rng(0)
+    rows = np.stack([np.zeros(384, np.int64), rng.integers(0, L, 384), rng.integers(0, H, 384)], 1)
+    rows[:8, 1] = [0, 1, 255, 256, 4094, 4095, 63, 64]
+    ref = oracle.attn_i16_f64(oq[None], oqs[None], ok_[None], oks[None], ov[None], ovs[None], True, rows=rows)
+    got = host(o1)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    err = normwise(got, ref)
+    print(f"[attn] prefill 4096 sampled normwise {err:.3e}")
+    assert err <= TOL
+
+
+def test_decode_config_sampled(heal):
+    banner("decode 64x8192 GQA 32/8, sampled heads")
+    B, L, Hq, Hkv = 64, 8192, 32, 8
+    k, ks = workloads.int16_cache_device(B, L, Hkv, 128, seed=3)
+    v, vs = workloads.int16_cache_device(B, L, Hkv, 128, seed=4)
+    qh, qsh = workloads.int16_cache_host(B, 1, Hq, 128, seed=5)
+    q, qs = dev(qh), dev(qsh)
+    out = heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True)
+    torch.cuda.synchronize()
+    o = host(out)
+    errs = []
+    for b in (0, 17, 63):
+        kb, ksb, vb, vsb = (host(t[b:b + 1]) for t in (k, ks, v, vs))
+        ref = oracle.attn_i16_f64(qh[b:b + 1], qsh[b:b + 1], kb, ksb, vb, vsb, causal=True)
+        errs.append(normwise(o[b:b + 1], ref))
+    print(f"[attn] decode 64x8192 sampled normwise {max(errs):.3e}")
+    assert max(errs) <= TOL
