@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark of the HEAL hot path on one MI355X.
+
+Headline (one JSON line on stdout): FP32-equivalent TFLOP/s of the error-compensated GEMM on the
+Llama-3-8B projection shapes -- M in {1, 16, 2048} tokens x (K, N) in {(4096, 4096), (4096, 14336),
+(14336, 4096)} -- with FP32 activations N(0, 1) carrying 1 % outlier channels x50 and bf16 weights N(0, 0.02)
+(exact in FP16 after the per-row power-of-two prescale, so P = 2 products).  One step = for each of the
+9 shapes: heal_split of the activations (FP32 -> FP16 hi + lo + row exponents) and heal_gemm_comp.  The
+weights are split once at load time, outside the timed region.  Inputs are synthetic, seeded, resident in
+HBM before timing starts.
+
+Also reported in the same line:
+  * "roofline" -- the dominant kernel of the step (the GEMM instantiation with the most time), its
+    16-bit MFMA work per launch (P x 2MNK) over its average launch duration, measured with HIP events on
+    the launch stream inside the timed region, against the 2516.6 TFLOP/s dense FP16 peak;
+  * "cpu_baseline" -- the FP64 CPU oracle on a bounded row sample of the same 9 shapes (all host threads),
+    and the GPU's error against it on those rows;
+  * "rows" -- the other hot-path steps, timed after the headline loop: the activation split, the INT16
+    quantiser, Dual-FP16 prefill (1 x 4096 x 32 heads x 128, causal), decode (64 x 8192 keys, GQA 32/8)
+    and the 8192^3 FP32 x FP32 GEMM (P = 3).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6  # MI355X dense FP16/BF16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-step measurements of the other rows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of each M=2048 shape in the CPU sample")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the current (launch) stream."""
+
+    def __init__(self):
+        import torch
+
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, key, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((key, e0, e1))
+
+    def durations(self):
+        out = {}
+        for key, a, b in self.pairs:
+            out.setdefault(key, []).append(a.elapsed_time(b) * 1e-3)
+        return out
+
+
+def time_fn(fn, reps, warm=2):
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / reps
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the hot path shards without communication and multi-GPU runs are not part of it",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import error_compensated_gemm_amd as heal
+    import workloads
+
+    heal.load()
+    torch.cuda.set_device(0)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    # ---------------------------------------------------------------- set-up (untimed): weights split once
+    shapes = [(M, K, N) for M in workloads.LLAMA3_8B_M for (K, N) in workloads.LLAMA3_8B_KN]
+    weights = {}
+    host_w = {}
+    for (K, N) in workloads.LLAMA3_8B_KN:
+        W = workloads.llama_weights_bf16(N, K, seed=1)
+        host_w[(K, N)] = W
+        wt = dev(W.view(np.int16)).view(torch.bfloat16)
+        bh, _, eb = heal.heal_split(wt, residual=False)
+        weights[(K, N)] = (bh, eb)
+        del wt
+    bufs = []
+    host_x = {}
+    for (M, K, N) in shapes:
+        X = workloads.llama_activations(M, K, seed=1)
+        host_x[(M, K)] = X
+        x = dev(X)
+        ah, al, ea = heal.heal_split(x)
+        c = heal.heal_gemm_comp(ah, al, ea, *weights[(K, N)][:1], None, weights[(K, N)][1])
+        bufs.append((M, K, N, x, ah, al, ea, c))
+    torch.cuda.synchronize()
+    variants = {(M, K, N): heal.heal_gemm_comp_variant(M, N, K, 2) for (M, K, N) in shapes}
+
+    timer = Timer()
+
+    def step(record):
+        for (M, K, N, x, ah, al, ea, c) in bufs:
+            bh, eb = weights[(K, N)]
+            heal.heal_split(x, hi=ah, lo=al, exps=ea)
+            if record:
+                e0 = timer.start()
+            heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
+            if record:
+                timer.stop((M, K, N), e0)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    total_s = t0.elapsed_time(t1) * 1e-3
+    ms_per_step = total_s / args.steps * 1e3
+    flops_step = sum(2.0 * M * N * K for (M, K, N) in shapes)
+    value = flops_step / (total_s / args.steps) / 1e12
+
+    durs = timer.durations()
+    per_shape = {}
+    by_variant = {}
+    for (M, K, N) in shapes:
+        d = durs[(M, K, N)]
+        avg = sum(d) / len(d)
+        per_shape[f"{M}x{K}x{N}"] = {
+            "us": round(avg * 1e6, 2),
+            "tflops_fp32eq": round(2.0 * M * N * K / avg / 1e12, 2),
+            "hbm_gbs": round((2.0 * N * K + 8.0 * M * K + 4.0 * M * N) / avg / 1e9, 1),
+            "kernel": variants[(M, K, N)],
+        }
+        v = by_variant.setdefault(variants[(M, K, N)], {"time": 0.0, "launches": 0, "mfma_flop": 0.0})
+        v["time"] += sum(d)
+        v["launches"] += len(d)
+        v["mfma_flop"] += 2 * 2.0 * M * N * K * len(d)
+    dom_name, dom = max(by_variant.items(), key=lambda kv: kv[1]["time"])
+    avg_dur = dom["time"] / dom["launches"]
+    achieved = dom["mfma_flop"] / dom["launches"] / avg_dur / 1e12
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_F16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+        "traffic": None,
+        "kernel": dom_name,
+        "avg_launch_us": round(avg_dur * 1e6, 2),
+        "launches_per_step": dom["launches"] // args.steps,
+        "work_per_launch": "P x 2MNK 16-bit MFMA flop (P = 2), averaged over the launches of this kernel",
+    }
+
+    result = {
+        "metric": "FP32-equiv TFLOP/s of compensated GEMM + % of MFMA roofline; max rel err vs FP64",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3_8b_linear: split(fp32 X) + compensated GEMM, P=2, 9 shapes",
+            "shapes_MKN": [list(s) for s in shapes],
+            "activations": "fp32 N(0,1), 1% channels x50",
+            "weights": "bf16 N(0,0.02), pre-split to fp16 once",
+            "flop_per_step_fp32eq": flops_step,
+        },
+        "roofline": roofline,
+        "per_shape": per_shape,
+    }
+
+    # ------------------------------------------------------------------ CPU baseline: the FP64 oracle
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args, shapes, host_x, host_w, bufs, flops_step)
+
+    if not args.no_rows:
+        result["rows"] = other_rows(heal, workloads, dev)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, shapes, host_x, host_w, bufs, flops_step):
+    import ctypes
+
+    import numpy as np
+
+    import oracle
+
+    lib = oracle.lib()
+    try:
+        threads = ctypes.CDLL("libgomp.so.1").omp_get_max_threads()
+    except OSError:
+        threads = os.cpu_count()
+    wd = {}
+    for (K, N), W in host_w.items():
+        wd[(K, N)] = (W.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    flops = 0.0
+    t_cpu = 0.0
+    errs, comps = [], []
+    gpu_c = {(M, K, N): c for (M, K, N, x, ah, al, ea, c) in bufs}
+    for (M, K, N) in shapes:
+        rows = min(M, args.cpu_rows)
+        X = host_x[(M, K)][:rows].astype(np.float64)
+        t = time.perf_counter()
+        C = oracle.gemm_f64(X, wd[(K, N)])
+        t_cpu += time.perf_counter() - t
+        flops += 2.0 * rows * K * N
+        G = gpu_c[(M, K, N)][:rows].cpu().numpy().astype(np.float64)
+        errs.append(float(np.linalg.norm(G - C) / np.linalg.norm(C)))
+        absab = np.abs(X) @ np.abs(wd[(K, N)]).T
+        comps.append(float(np.max(np.abs(G - C) / absab)))
+    return {
+        "value": round(flops / t_cpu / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"FP64 plain-C GEMM on the first min(M, {args.cpu_rows}) rows of each of the 9 shapes "
+                  f"({flops:.3e} flop, {t_cpu:.1f} s)",
+        "gpu_err_vs_fp64_on_sample": {"normwise_max": max(errs), "componentwise_max": max(comps)},
+    }
+
+
+def other_rows(heal, workloads, dev):
+    """The remaining hot-path steps, each timed on its own workload with HIP events."""
+    import numpy as np
+    import torch
+
+    rows = {}
+    # a1: activation split, 2048 x 14336 fp32 -> fp16 hi + lo + exps (read 4 B, write 4 B per element)
+    x = dev(workloads.llama_activations(2048, 14336, seed=1))
+    hi, lo, e = heal.heal_split(x)
+    t = time_fn(lambda: heal.heal_split(x, hi=hi, lo=lo, exps=e), 20)
+    rows["a1_split_2048x14336"] = {"us": round(t * 1e6, 2), "gbs": round(x.numel() * 8 / t / 1e9, 1)}
+    del x, hi, lo, e
+    # a4 + a6: quantise Q, K, V [4096, 32, 128] then causal Dual-FP16 prefill
+    Q, K, V = workloads.qkv_fp32(1, 4096, 32, 128, seed=2)
+    qd, kd, vd = dev(Q[0]), dev(K[0]), dev(V[0])
+    qkv = [heal.heal_qkv_quant_i16(t) for t in (qd, kd, vd)]
+    def quant_all():
+        for src, (q, s) in zip((qd, kd, vd), qkv):
+            heal.heal_qkv_quant_i16(src, q=q, scale=s)
+    t = time_fn(quant_all, 20)
+    nel = 3 * qd.numel()
+    rows["a4_quant_3x4096x32x128"] = {"us": round(t * 1e6, 2), "gbs": round(nel * (4 + 2 + 4 / 128) / t / 1e9, 1)}
+    (q, qs), (k, ks), (v, vs) = qkv
+    out = heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None], causal=True)
+    t = time_fn(lambda: heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None],
+                                                 causal=True, out=out), 10)
+    fl = 4.0 * 128 * 32 * (4096 * 4097 / 2)
+    rows["a6_prefill_1x4096x32x128_causal"] = {
+        "us": round(t * 1e6, 2), "tflops_fp32eq": round(fl / t / 1e12, 2),
+        "mfma_frac": round(8 * fl / 2 / t / 1e12 / PEAK_F16_TFLOPS, 4)}
+    del qd, kd, vd, qkv, q, k, v, out
+    # a7: decode over an INT16 cache, 64 x 8192 keys, 32 q-heads / 8 kv-heads
+    B, L, Hq, Hkv = 64, 8192, 32, 8
+    k, ks = workloads.int16_cache_device(B, L, Hkv, 128, seed=3)
+    v, vs = workloads.int16_cache_device(B, L, Hkv, 128, seed=4)
+    q, qs = [dev(a) for a in workloads.int16_cache_host(B, 1, Hq, 128, seed=5)]
+    out = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device="cuda")
+    args = heal.make_attn_args(q, qs, k, ks, v, vs, out, True)
+    ws = torch.empty(heal.heal_attn_workspace_bytes(args), dtype=torch.uint8, device="cuda")
+    t = time_fn(lambda: heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws), 10)
+    by = 2.0 * B * L * Hkv * 128 * 2 + 2.0 * B * L * Hkv * 4 + B * Hq * 128 * (2 + 4)
+    rows["a7_decode_64x8192_gqa32_8"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
+                                         "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
+    del k, v, ks, vs, q, qs, out, ws
+    torch.cuda.empty_cache()
+    # config 5a: 8192^3 FP32 x FP32, rows scaled by 10^U(-3,3), P = 3
+    A, Bt = workloads.gemm_rowscaled(8192, 8192, 8192, seed=4)
+    ah, al, ea = heal.heal_split(dev(A))
+    bh, bl, eb = heal.heal_split(dev(Bt))
+    c = heal.heal_gemm_comp(ah, al, ea, bh, bl, eb)
+    t = time_fn(lambda: heal.heal_gemm_comp(ah, al, ea, bh, bl, eb, c=c), 5)
+    fl = 2.0 * 8192 ** 3
+    rows["gemm_8192cube_p3"] = {"us": round(t * 1e6, 1), "tflops_fp32eq": round(fl / t / 1e12, 1),
+                                "mfma_frac": round(3 * fl / t / 1e12 / PEAK_F16_TFLOPS, 4),
+                                "kernel": heal.heal_gemm_comp_variant(8192, 8192, 8192, 3)}
+    return rows
+
+
+if __name__ == "__main__":
+    main()

@@ -57,6 +57,8 @@ def load():
     L.heal_split.argtypes = [p, i32, i64, i64, i64, i32, p, p, i64, p, p]
     L.heal_gemm_comp.restype = i32
     L.heal_gemm_comp.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p]
+    L.heal_gemm_comp_variant.restype = ctypes.c_char_p
+    L.heal_gemm_comp_variant.argtypes = [i64, i64, i64, i32]
     L.heal_qkv_quant_i16.restype = i32
     L.heal_qkv_quant_i16.argtypes = [p, i64, i64, i64, i64, p, i64, p, i64, p]
     L.heal_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -67,8 +69,8 @@ def load():
     return L
 
 
-EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp", "heal_qkv_quant_i16",
-            "heal_attn_workspace_bytes", "heal_attn_dual_fp16")
+EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp", "heal_gemm_comp_variant",
+            "heal_qkv_quant_i16", "heal_attn_workspace_bytes", "heal_attn_dual_fp16")
 
 
 def _check(status: int):
@@ -144,6 +146,11 @@ def heal_gemm_comp(a_hi, a_lo, a_exp, b_hi, b_lo, b_exp, part: str = "f16", c=No
     _check(L.heal_gemm_comp(M, N, K, _ptr(a_hi), _ptr(a_lo), _ptr(a_exp), _ld(a_hi), _ptr(b_hi), _ptr(b_lo),
                             _ptr(b_exp), _ld(b_hi), _PARTS[part], _ptr(c), _ld(c), _stream(a_hi.device)))
     return c
+
+
+def heal_gemm_comp_variant(M: int, N: int, K: int, products: int) -> str:
+    """Name of the kernel instantiation heal_gemm_comp launches for this shape and product count."""
+    return load().heal_gemm_comp_variant(M, N, K, products).decode()
 
 
 # ------------------------------------------------------------------------------------------ heal_qkv_quant_i16

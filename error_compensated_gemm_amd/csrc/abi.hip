@@ -80,6 +80,10 @@ heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, co
                                          c, ldc, (hipStream_t)stream));
 }
 
+const char* heal_gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
+  return heal::gemm_comp_variant(M, N, K, products);
+}
+
 heal_status heal_qkv_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim,
                                int64_t ld_x, int16_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                                void* stream) {

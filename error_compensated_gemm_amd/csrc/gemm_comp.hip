@@ -44,18 +44,36 @@ constexpr int kBK = 32;          // K per stage
 constexpr int kCPR = kBK / 8;    // 16-byte chunks per row of a stage
 constexpr int kThreads = 256;
 
-// chunk c of tile row r lives at r * kCPR + (c ^ swz(r)): rows that one fragment read touches together
-// land in distinct 16-byte bank groups for both 8- and 16-lane read phases.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & (kCPR - 1); }
+// chunk c of tile row r lives at r * kCPR + (c ^ swz(r)).  With 64-byte rows, XOR-ing the chunk index
+// with bits 2..3 of the row makes the 32-row x 2-chunk fragment reads (ds_read_b128) conflict-free on
+// gfx950: SQ_LDS_BANK_CONFLICT measured 0 for this layout against 4 cycles per read for (r >> 1) & 3 and
+// 12 for r & 3 in an LDS probe of the same access pattern.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & (kCPR - 1); }
 
-// 8 consecutive 16-bit values of one row starting at column k (k a multiple of 8); zeros past K
-__device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ row, int64_t k, int64_t K) {
-  if (k + 8 <= K) return *reinterpret_cast<const uint4*>(row + k);
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+// Loads stay branch-free: a chunk start k (a multiple of 8) is clamped to klast, the last chunk that
+// starts inside the row (every row holds ld >= roundup8(K) elements), and the elements at or past K are
+// zeroed afterwards, only for the one partial K tile.  (A per-element tail branch here makes the compiler
+// wait for each global load in turn, which serialises the prefetch.)
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ row, int64_t k, int64_t klast) {
+  return *reinterpret_cast<const uint4*>(row + (k < klast ? k : klast));
+}
+// keep the first `valid` of the 8 values (valid <= 0 clears the chunk)
+__device__ __forceinline__ uint4 mask_chunk(uint4 v, int64_t valid) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (k + i < K) w[i >> 1] |= (uint32_t)row[k + i] << (16 * (i & 1));
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t m = (2 * d < valid ? 0x0000FFFFu : 0u) | (2 * d + 1 < valid ? 0xFFFF0000u : 0u);
+    w[d] &= m;
+  }
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// one 16-byte direct global -> LDS transfer per lane: lane l's bytes land at lds_wave_base + 16 l
+__device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                   (lds_void_t*)(lds_wave_base), 16, 0, 0);
 }
 
 template <int PART, int BM, int BN, bool ALO, bool BLO>
@@ -67,9 +85,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int NA = ALO ? 2 : 1, NB = BLO ? 2 : 1;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_PER_T = BM * kCPR / kThreads, B_PER_T = BN * kCPR / kThreads;
-  constexpr int STAGE = (NA * BM + NB * BN) * kCPR;  // uint4 chunks per stage
+  constexpr int APLANE = BM * kCPR, BPLANE = BN * kCPR;  // uint4 chunks per operand plane
+  constexpr int STAGE = NA * APLANE + NB * BPLANE;
   static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small for the loader");
-  __shared__ uint4 lds[2 * STAGE];
+  // two stages as two distinct objects: the compiler can tell the stage being read from the one the
+  // direct-to-LDS loads are filling, so no wait on those loads is placed before the fragment reads
+  __shared__ uint4 lds0[STAGE];
+  __shared__ uint4 lds1[STAGE];
+  __shared__ int exps_s[BM + BN];
 
   // ---- tile of this workgroup (XCD-contiguous, then grouped by 4 tile rows) ----
   const int ntm = (int)((M + BM - 1) / BM), ntn = (int)((N + BN - 1) / BN);
@@ -90,59 +113,85 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- loader: per thread, A_PER_T chunks of each A part and B_PER_T of each B part ----
-  const uint16_t* a_rows[A_PER_T];
-  const uint16_t* al_rows[A_PER_T];
-  int a_slot[A_PER_T];
+  for (int i = tid; i < BM + BN; i += kThreads) {
+    if (i < BM) {
+      const int64_t r = (m0 + i < M) ? m0 + i : M - 1;
+      exps_s[i] = ea ? ea[r] : 0;
+    } else {
+      const int64_t r = (n0 + i - BM < N) ? n0 + i - BM : N - 1;
+      exps_s[i] = eb ? eb[r] : 0;
+    }
+  }
+
+  // ---- loader: LDS position p = tid + 256 i of a plane holds row p / kCPR, chunk (p % kCPR) ^ swz(row);
+  //      a wavefront's 64 consecutive positions are one direct-to-LDS transfer ----
+  const uint16_t* a_src[A_PER_T];
+  const uint16_t* al_src[A_PER_T];
   int a_col[A_PER_T];
 #pragma unroll
   for (int i = 0; i < A_PER_T; ++i) {
-    const int id = tid + kThreads * i, r = id / kCPR, c = id % kCPR;
+    const int p = tid + kThreads * i, r = p / kCPR, c = (p % kCPR) ^ swz(r);
     int64_t gr = m0 + r;
     if (gr > M - 1) gr = M - 1;  // rows past M only feed outputs that are never stored
-    a_rows[i] = ah + gr * lda;
-    al_rows[i] = ALO ? al + gr * lda : nullptr;
-    a_slot[i] = r * kCPR + (c ^ swz(r));
-    a_col[i] = c * 8;
+    a_col[i] = 8 * c;
+    a_src[i] = ah + gr * lda + 8 * c;
+    al_src[i] = ALO ? al + gr * lda + 8 * c : nullptr;
   }
-  const uint16_t* b_rows[B_PER_T];
-  const uint16_t* bl_rows[B_PER_T];
-  int b_slot[B_PER_T];
+  const uint16_t* b_src[B_PER_T];
+  const uint16_t* bl_src[B_PER_T];
   int b_col[B_PER_T];
 #pragma unroll
   for (int i = 0; i < B_PER_T; ++i) {
-    const int id = tid + kThreads * i, r = id / kCPR, c = id % kCPR;
+    const int p = tid + kThreads * i, r = p / kCPR, c = (p % kCPR) ^ swz(r);
     int64_t gr = n0 + r;
     if (gr > N - 1) gr = N - 1;
-    b_rows[i] = bh + gr * ldb;
-    bl_rows[i] = BLO ? bl + gr * ldb : nullptr;
-    b_slot[i] = r * kCPR + (c ^ swz(r));
-    b_col[i] = c * 8;
+    b_col[i] = 8 * c;
+    b_src[i] = bh + gr * ldb + 8 * c;
+    bl_src[i] = BLO ? bl + gr * ldb + 8 * c : nullptr;
   }
-
-  uint4 ra[NA][A_PER_T], rb[NB][B_PER_T];
-  auto gload = [&](int64_t k0) {
+  // full K tiles: direct-to-LDS
+  auto dma_stage = [&](uint4* s, int64_t k0) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
-      ra[0][i] = load_chunk(a_rows[i], k0 + a_col[i], K);
-      if constexpr (ALO) ra[NA - 1][i] = load_chunk(al_rows[i], k0 + a_col[i], K);
+      uint4* dst = s + kThreads * i + 64 * wave;
+      dma16(a_src[i] + k0, dst);
+      if constexpr (ALO) dma16(al_src[i] + k0, dst + APLANE);
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
-      rb[0][i] = load_chunk(b_rows[i], k0 + b_col[i], K);
-      if constexpr (BLO) rb[NB - 1][i] = load_chunk(bl_rows[i], k0 + b_col[i], K);
+      uint4* dst = s + NA * APLANE + kThreads * i + 64 * wave;
+      dma16(b_src[i] + k0, dst);
+      if constexpr (BLO) dma16(bl_src[i] + k0, dst + BPLANE);
     }
   };
-  auto lstore = [&](int buf) {
-    uint4* s = lds + buf * STAGE;
+  // the partial last K tile: through registers, zeroing the columns at or past K
+  const int64_t klast = ((K + 7) / 8 - 1) * 8;
+  auto tail_stage = [&](uint4* s, int64_t k0) {
 #pragma unroll
-    for (int p = 0; p < NA; ++p)
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int64_t k = k0 + a_col[i];
+      const int64_t kc = k < klast ? k : klast;
+      s[kThreads * i + tid] = mask_chunk(*reinterpret_cast<const uint4*>(a_src[i] - a_col[i] + kc), K - k);
+      if constexpr (ALO)
+        s[APLANE + kThreads * i + tid] =
+            mask_chunk(*reinterpret_cast<const uint4*>(al_src[i] - a_col[i] + kc), K - k);
+    }
 #pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) s[p * BM * kCPR + a_slot[i]] = ra[p][i];
-#pragma unroll
-    for (int p = 0; p < NB; ++p)
-#pragma unroll
-      for (int i = 0; i < B_PER_T; ++i) s[NA * BM * kCPR + p * BN * kCPR + b_slot[i]] = rb[p][i];
+    for (int i = 0; i < B_PER_T; ++i) {
+      const int64_t k = k0 + b_col[i];
+      const int64_t kc = k < klast ? k : klast;
+      s[NA * APLANE + kThreads * i + tid] =
+          mask_chunk(*reinterpret_cast<const uint4*>(b_src[i] - b_col[i] + kc), K - k);
+      if constexpr (BLO)
+        s[NA * APLANE + BPLANE + kThreads * i + tid] =
+            mask_chunk(*reinterpret_cast<const uint4*>(bl_src[i] - b_col[i] + kc), K - k);
+    }
+  };
+  const int nk = (int)((K + kBK - 1) / kBK);
+  const int nfull = (int)(K / kBK);
+  auto fill = [&](uint4* s, int kt) {
+    if (kt < nfull) dma_stage(s, (int64_t)kt * kBK);
+    else tail_stage(s, (int64_t)kt * kBK);
   };
 
   f32x16 acc[TM][TN];
@@ -153,33 +202,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (int)((K + kBK - 1) / kBK);
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
   const int frow = lane & 31, fhalf = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((int64_t)(kt + 1) * kBK);
-    const uint4* s = lds + buf * STAGE;
+  auto compute = [&](const uint4* s) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int c = 2 * ks + fhalf;
       uint4 fa[NA][TM], fb[NB][TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + frow;
-#pragma unroll
-        for (int p = 0; p < NA; ++p) fa[p][i] = s[p * BM * kCPR + r * kCPR + (c ^ swz(r))];
-      }
-#pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = wn * WN + j * 32 + frow;
 #pragma unroll
-        for (int p = 0; p < NB; ++p) fb[p][j] = s[NA * BM * kCPR + p * BN * kCPR + r * kCPR + (c ^ swz(r))];
+        for (int p = 0; p < NB; ++p) fb[p][j] = s[NA * APLANE + p * BPLANE + r * kCPR + (c ^ swz(r))];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 32 + frow;
+#pragma unroll
+        for (int p = 0; p < NA; ++p) fa[p][i] = s[p * APLANE + r * kCPR + (c ^ swz(r))];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -190,28 +229,162 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           if constexpr (ALO) acc[i][j] = mfma32<PART>(fa[NA - 1][i], fb[0][j], acc[i][j]);
         }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  };
+
+  // ---- main loop, two stages per trip so each stage is a fixed LDS object ----
+  if (nk > 0) fill(lds0, 0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    fill(lds1, kt + 1);
+    compute(lds0);
+    __syncthreads();
+    if (kt + 2 < nk) fill(lds0, kt + 2);
+    compute(lds1);
     __syncthreads();
   }
+  if (kt < nk) compute(lds0);  // odd tile count: the last tile sits in stage 0
 
   // ---- epilogue: C = acc * 2^-(ea_i + eb_j), one rounding (exact unless the result is subnormal) ----
+  const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
-    if (col >= N) continue;
-    const int ebj = eb ? eb[col] : 0;
+    const int cl = wn * WN + j * 32 + (lane & 31);
+    const int64_t col = n0 + cl;
+    const int ebj = exps_s[BM + cl];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) {
-          const int e = (ea ? ea[row] : 0) + ebj;
-          C[row * ldc + col] = __builtin_amdgcn_ldexpf(acc[i][j][r], -e);
-        }
+        const int rl = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t row = m0 + rl;
+        const float v = __builtin_amdgcn_ldexpf(acc[i][j][r], -(exps_s[rl] + ebj));
+        if (interior || (row < M && col < N)) C[row * ldc + col] = v;
       }
     }
   }
+}
+
+// ------------------------------------------------------------------------------------------- skinny M
+// M <= 64: the problem is a stream over B (N x K 16-bit values read once from HBM) with a small A that
+// stays in L2.  A workgroup of 8 wavefronts owns 16 output columns; its wavefronts split K in 32-wide steps
+// and each accumulates a 16 x 16 block per 16 rows of A with v_mfma_f32_16x16x32; the 8 partial blocks
+// are added in wavefront order through LDS (fixed order: bitwise reproducible).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int PART>
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f32x4& c) {
+  if constexpr (PART == HEAL_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+}
+
+constexpr int kSkWaves = 8;
+
+template <int PART, int MT, bool ALO, bool BLO>
+__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
+    int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
+    const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
+    const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
+    int64_t ldc) {
+  __shared__ float red[kSkWaves][MT][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cl = lane & 15, kg = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  int64_t n = n0 + cl;
+  if (n > N - 1) n = N - 1;  // columns past N feed outputs that are never stored
+  const uint16_t* brow = bh + n * ldb;
+  const uint16_t* blrow = BLO ? bl + n * ldb : nullptr;
+  const uint16_t* arow[MT];
+  const uint16_t* alrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    int64_t m = 16 * mt + cl;
+    if (m > M - 1) m = M - 1;
+    arow[mt] = ah + m * lda;
+    alrow[mt] = ALO ? al + m * lda : nullptr;
+  }
+  const int64_t nsteps = (K + 31) / 32, nfull = K / 32;
+  const int64_t klast = ((K + 7) / 8 - 1) * 8;
+  const int64_t s0 = nsteps * wave / kSkWaves, s1 = nsteps * (wave + 1) / kSkWaves;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](int64_t s, bool tail) {
+    const int64_t k = s * 32 + 8 * kg;
+    uint4 b = load_chunk(brow, k, klast);
+    uint4 b2 = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (BLO) b2 = load_chunk(blrow, k, klast);
+    if (tail) {  // padding past K may hold any bits (even NaN patterns): clear both operands
+      b = mask_chunk(b, K - k);
+      if constexpr (BLO) b2 = mask_chunk(b2, K - k);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      uint4 a = load_chunk(arow[mt], k, klast);
+      if (tail) a = mask_chunk(a, K - k);
+      acc[mt] = mfma16<PART>(a, b, acc[mt]);
+      if constexpr (BLO) acc[mt] = mfma16<PART>(a, b2, acc[mt]);
+      if constexpr (ALO) {
+        uint4 a2 = load_chunk(alrow[mt], k, klast);
+        if (tail) a2 = mask_chunk(a2, K - k);
+        acc[mt] = mfma16<PART>(a2, b, acc[mt]);
+      }
+    }
+  };
+  const int64_t s1f = s1 < nfull ? s1 : nfull;
+#pragma unroll 4
+  for (int64_t s = s0; s < s1f; ++s) step(s, false);
+  if (s1 > s1f) step(s1f, true);  // the one partial step (K % 32 != 0) belongs to the last wavefront
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][mt][i][lane] = acc[mt][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MT * 4 * 64; idx += 64 * kSkWaves) {
+    const int mt = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSkWaves; ++w) s += red[w][mt][i][l];
+    const int64_t row = 16 * mt + 4 * (l >> 4) + i, col = n0 + (l & 15);
+    if (row < M && col < N) {
+      const int e = (ea ? ea[row] : 0) + (eb ? eb[col] : 0);
+      C[row * ldc + col] = __builtin_amdgcn_ldexpf(s, -e);
+    }
+  }
+}
+
+template <int PART, int MT>
+hipError_t launch_skinny_mt(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
+                            const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
+                            const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * kSkWaves);
+  if (al && bl)
+    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, true, true>), grid, block, 0, stream, M, N, K, ah, al, ea,
+                       lda, bh, bl, eb, ldb, c, ldc);
+  else if (al)
+    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, true, false>), grid, block, 0, stream, M, N, K, ah, al, ea,
+                       lda, bh, bl, eb, ldb, c, ldc);
+  else if (bl)
+    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, false, true>), grid, block, 0, stream, M, N, K, ah, al, ea,
+                       lda, bh, bl, eb, ldb, c, ldc);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, false, false>), grid, block, 0, stream, M, N, K, ah, al,
+                       ea, lda, bh, bl, eb, ldb, c, ldc);
+  return hipGetLastError();
+}
+
+template <int PART>
+hipError_t launch_skinny(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
+                         const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
+                         const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
+  if (M <= 16) return launch_skinny_mt<PART, 1>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  if (M <= 32) return launch_skinny_mt<PART, 2>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  return launch_skinny_mt<PART, 4>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
 }
 
 template <int PART, int BM, int BN>
@@ -235,21 +408,55 @@ hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const uint16_t* ah, cons
   return hipGetLastError();
 }
 
+// Kernel choice: M <= 64 streams B (skinny kernel); otherwise the largest block tile that still gives
+// every CU a workgroup.
+constexpr int64_t kSkinnyMaxM = 64;
+enum TileKind { kTile256x256 = 0, kTile256x128 = 1, kTile128x128 = 2, kSkinny = 3 };
+TileKind choose_tile(int64_t M, int64_t N) {
+  if (M <= kSkinnyMaxM) return kSkinny;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
+  if (t256 >= 256) return kTile256x256;
+  if (t128 >= 256) return kTile256x128;
+  return kTile128x128;
+}
+
 template <int PART>
 hipError_t launch_part(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
                        const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
                        const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
-  // the largest tile that still gives every CU a workgroup
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
-  if (t256 >= 256)
-    return launch_tile<PART, 256, 256>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
-  if (t128 >= 256)
-    return launch_tile<PART, 256, 128>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
-  return launch_tile<PART, 128, 128>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  switch (choose_tile(M, N)) {
+    case kSkinny:
+      return launch_skinny<PART>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    case kTile256x256:
+      return launch_tile<PART, 256, 256>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    case kTile256x128:
+      return launch_tile<PART, 256, 128>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    default:
+      return launch_tile<PART, 128, 128>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  }
 }
 
 }  // namespace
+
+const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
+  (void)K;
+  static const char* names[4][3] = {
+      {"gemm_comp_kernel 256x256 P1", "gemm_comp_kernel 256x256 P2", "gemm_comp_kernel 256x256 P3"},
+      {"gemm_comp_kernel 256x128 P1", "gemm_comp_kernel 256x128 P2", "gemm_comp_kernel 256x128 P3"},
+      {"gemm_comp_kernel 128x128 P1", "gemm_comp_kernel 128x128 P2", "gemm_comp_kernel 128x128 P3"},
+      {"gemm_skinny_kernel P1", "gemm_skinny_kernel P2", "gemm_skinny_kernel P3"}};
+  if (M <= 0 || N <= 0 || products < 1 || products > 3) return "none";
+  const TileKind kind = choose_tile(M, N);
+  if (kind == kSkinny) {
+    static const char* sk[3][3] = {
+        {"gemm_skinny_kernel M<=16 P1", "gemm_skinny_kernel M<=16 P2", "gemm_skinny_kernel M<=16 P3"},
+        {"gemm_skinny_kernel M<=32 P1", "gemm_skinny_kernel M<=32 P2", "gemm_skinny_kernel M<=32 P3"},
+        {"gemm_skinny_kernel M<=64 P1", "gemm_skinny_kernel M<=64 P2", "gemm_skinny_kernel M<=64 P3"}};
+    return sk[M <= 16 ? 0 : (M <= 32 ? 1 : 2)][products - 1];
+  }
+  return names[kind][products - 1];
+}
 
 hipError_t launch_gemm_comp(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,
                             const int32_t* a_exp, int64_t lda, const uint16_t* b_hi, const uint16_t* b_lo,

@@ -102,13 +102,23 @@ HEAL_API heal_status heal_split(const void* x, int x_type, int64_t rows, int64_t
  * ONE FP32 accumulator per output; lo*lo is never formed.  a_exp / b_exp are the int32 row exponents of
  * heal_split (NULL means 0).  C is FP32 [M, N] (leading dimension ldc, a multiple of 4 elements): the
  * accumulator scaled by the exact power of two is the only rounding at the kernel boundary.
- * K = 0 writes zeros.  Errors: HEAL_ERR_NULL (a_hi, b_hi or c NULL with M*N > 0), HEAL_ERR_SHAPE,
+ * Each part buffer holds its rows x ld elements (the padding columns K .. ld-1 may hold anything; they are
+ * read as whole 16-byte chunks and never contribute).  K = 0 writes zeros.
+ * Errors: HEAL_ERR_NULL (a_hi, b_hi or c NULL with M*N > 0), HEAL_ERR_SHAPE,
  * HEAL_ERR_STRIDE (lda, ldb < K or ldc < N), HEAL_ERR_ALIGN, HEAL_ERR_DTYPE.
  */
 HEAL_API heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
                            const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
                            const int32_t* b_exp, int64_t ldb, int part_type, float* c, int64_t ldc,
                            void* stream);
+
+/*
+ * heal_gemm_comp_variant -- the name of the kernel instantiation heal_gemm_comp launches for an M x N x K
+ * problem with `products` (1..3) 16-bit products, e.g. "gemm_comp_kernel 256x128 P2" (static storage;
+ * "none" for an empty problem).  For profiling: it lets a caller attribute a profiler's per-kernel times
+ * to problem shapes.  Pure host function, no device work.
+ */
+HEAL_API const char* heal_gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products);
 
 /*
  * heal_qkv_quant_i16 -- INT16 quantisation of Q, K or V per (token, head) ([TS 2A Solution]; [ABS]):

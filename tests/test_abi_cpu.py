@@ -151,3 +151,9 @@ def test_attn_validation(heal):
     a = _attn_args(heal, q_len=1, kv_len=5000, workspace=FAKE, workspace_bytes=16)
     assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 8
     assert call(batch=0) == 0
+
+
+def test_gemm_variant_names(heal):
+    assert heal.heal_gemm_comp_variant(0, 5, 5, 2) == "none"
+    assert heal.heal_gemm_comp_variant(8192, 8192, 8192, 3).startswith("gemm_comp_kernel")
+    assert heal.heal_gemm_comp_variant(8192, 8192, 8192, 3).endswith("P3")
