@@ -26,12 +26,16 @@
 // Causal workgroups are dispatched longest first.
 //
 // Decode (q_len = 1): HBM-streaming, split over the keys.  A workgroup of 4 wavefronts owns one
-// (batch, kv-head) and a chunk of 1024 keys; the G = n_q/n_kv query heads of the group are the 16 columns
-// of v_mfma_f32_16x16x32_f16 (G <= 16).  K is loaded straight from HBM into MFMA operand registers; V goes
-// through a wavefront-private LDS transpose.  Register double-buffering keeps the next 32 keys' loads in
-// flight while the current ones are multiplied.  The four wavefronts' partial (max, sum, O) are merged in
-// LDS in a fixed order and written to the workspace; a second kernel merges the chunks of each
-// (batch, head) in a fixed order.  No atomics: results are bitwise reproducible.
+// (batch, kv-head) and a chunk of 2048 keys; the G = n_q/n_kv query heads of the group are the 16 columns
+// of v_mfma_f32_16x16x32_f16 (G <= 16).  Each wavefront streams its 512 keys in steps of 32: K straight
+// into MFMA operand registers, V and the scales through two private LDS stages filled by direct-to-LDS
+// transfers, so the next step's 16 KB are in flight while the current step is multiplied (66 KB of LDS
+// per workgroup: two workgroups, eight wavefronts, per CU); the V^T operand comes straight from the
+// [key][d] rows through gfx950's transposing LDS read.  The P~
+// renormalisation exponent is kept as a running value (O rescaled by an exact power of two when a larger
+// v-scale arrives), so no pre-pass over the scales is needed.  The four wavefronts' partial (max, sum, O)
+// are merged in LDS in a fixed order and written to the workspace; a second kernel merges the chunks of
+// each (batch, head) in a fixed order.  No atomics: results are bitwise reproducible.
 #include <math.h>
 
 #include "heal_internal.h"
@@ -424,28 +428,52 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 // ============================================================================================= decode
 constexpr int DC_WAVES = 4;
 constexpr int DC_THREADS = 64 * DC_WAVES;
-constexpr int DC_KPW = 256;                   // keys per wavefront
+constexpr int DC_KPW = 512;                   // keys per wavefront
 constexpr int DC_CHUNK = DC_KPW * DC_WAVES;   // keys per workgroup
 constexpr int DC_SUB = 32;                    // keys per step
-// wavefront-private V^T planes: [128 d][8 groups of 4 keys] uint2, H and L
-constexpr int DC_V_PLANE = D * 8;
-constexpr int DC_PART = 4 + D;  // floats per partial: m_hi, m_lo, l, (pad), O[128]
+constexpr int DC_PART = 4 + D;                // floats per partial: m_hi, m_lo, l, (pad), O[128]
+constexpr int DC_NDMA = 17;                   // direct-to-LDS transfers per lane per step
 
-__device__ __forceinline__ int dc_vpos(int d, int g) { return d * 8 + (g ^ (((d >> 2) & 3) << 1)); }
+// One step's V in a wavefront-private LDS stage, filled by direct-to-LDS transfers: [32 keys][16 chunks of
+// 8 d] INT16 (chunk c of key j at j * 16 + (c ^ (j & 15)), so the rows one transposing read touches sit
+// in different bank groups), then the 32 k-scales and 32 v-scales.  K needs no LDS: its MFMA operand
+// layout (one key's 8 consecutive d per lane) is a plain 16-byte load into registers.
+struct DcStage {
+  uint4 v[DC_SUB * 16];
+  float sc[2 * DC_SUB];
+};
+__device__ __forceinline__ int dc_pos(int key, int c) { return key * 16 + (c ^ (key & 15)); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, 0);
+}
+// s_waitcnt immediate: at most N vector-memory operations outstanding, all LDS operations done
+template <int N>
+constexpr int waitcnt_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
+}
 
 size_t decode_workspace(int64_t B, int64_t Hq, int64_t Lkv) {
   const int64_t nsplit = (Lkv + DC_CHUNK - 1) / DC_CHUNK;
   return (size_t)(B * Hq * (nsplit > 0 ? nsplit : 1) * DC_PART) * sizeof(float);
 }
 
-__global__ __launch_bounds__(DC_THREADS) void attn_decode_kernel(AttnParams a, float* __restrict__ ws,
-                                                                 int nsplit) {
-  // V^T staging during the key loop; the same bytes hold the wavefront partials afterwards
-  __shared__ uint2 vlds[DC_WAVES][2][DC_V_PLANE];
-  __shared__ float red[DC_WAVES];
-  static_assert(sizeof(float) * DC_WAVES * 16 * DC_PART <= sizeof(uint2) * DC_WAVES * 2 * DC_V_PLANE,
-                "partials must fit in the staging planes");
-  float(*part)[16][DC_PART] = reinterpret_cast<float(*)[16][DC_PART]>(&vlds[0][0][0]);
+__global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_decode_kernel(
+    AttnParams a, float* __restrict__ ws, int nsplit) {
+  // two stages per wavefront, each stage its own object (the compiler can tell the stage being read
+  // from the one being filled); after the key loop the same bytes hold the wavefront partials
+  __shared__ DcStage st0[DC_WAVES];
+  __shared__ DcStage st1[DC_WAVES];
+  static_assert(sizeof(float) * DC_WAVES * 16 * DC_PART <= sizeof(DcStage) * DC_WAVES,
+                "partials must fit in one stage array");
+  float(*part)[16][DC_PART] = reinterpret_cast<float(*)[16][DC_PART]>(&st0[0]);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x;
@@ -464,16 +492,6 @@ __global__ __launch_bounds__(DC_THREADS) void attn_decode_kernel(AttnParams a, f
   const float* ksb = a.ks + b * a.kvs_st[0] + hk * a.kvs_st[2];
   const float* vsb = a.vs + b * a.kvs_st[0] + hk * a.kvs_st[2];
 
-  // E over this workgroup's chunk
-  float vmax = 0.0f;
-  for (int64_t j = c0 + tid; j < c1; j += DC_THREADS) vmax = fmaxf(vmax, vsb[j * a.kvs_st[1]]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, m, 64));
-  if (lane == 0) red[wave] = vmax;
-  __syncthreads();
-  vmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const int E = vmax > 0.0f ? 14 - ilogb_pos(vmax) : 0;
-
   // query column of this lane: head hk*G + qc for qc < G (other columns are zero padding)
   const int qc = lane & 15, grp = lane >> 4;
   const bool qvalid = qc < G;
@@ -490,66 +508,58 @@ __global__ __launch_bounds__(DC_THREADS) void attn_decode_kernel(AttnParams a, f
   }
   const float cq = qvalid ? a.qs[b * a.qs_st[0] + hq * a.qs_st[2]] * a.scale_log2 : 0.0f;
 
-  // loads of one 32-key step: K in operand layout (2 key tiles x 4 d-steps), V as 2 jobs of 4 keys x 8 d
-  uint4 kr[2][4], vr[2][4];
-  float skr[2][4], svr[2][4];
-  auto gload = [&](int64_t j0, uint4 (&k_)[2][4], uint4 (&v_)[2][4], float (&sk_)[2][4], float (&sv_)[2][4]) {
+  // one step's loads: K straight into operand registers (key 16 mt + qc, d 32 ks + 8 grp .. + 7), V and the
+  // scales direct-to-LDS (position p = 64 i + l holds key p / 16, chunk (p % 16) ^ key)
+  const int64_t kvs1 = a.kv_st[1], ss1 = a.kvs_st[1];
+  auto issue = [&](DcStage& S, uint4 (&kr)[2][4], int64_t j0) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       int64_t j = j0 + 16 * mt + qc;
       if (j > a.Lkv - 1) j = a.Lkv - 1;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        k_[mt][ks] = *reinterpret_cast<const uint4*>(kbase + j * a.kv_st[1] + 32 * ks + 8 * grp);
+        kr[mt][ks] = *reinterpret_cast<const uint4*>(kbase + j * kvs1 + 32 * ks + 8 * grp);
     }
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      const int job = lane + 64 * jb, g = job >> 4, c = job & 15;  // keys 4g..4g+3, d-chunk c
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        int64_t j = j0 + 4 * g + kk;
-        if (j > a.Lkv - 1) j = a.Lkv - 1;
-        v_[jb][kk] = *reinterpret_cast<const uint4*>(vbase + j * a.kv_st[1] + 8 * c);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int p = 64 * i + lane, key = p >> 4, c = (p & 15) ^ (key & 15);
+      int64_t j = j0 + key;
+      if (j > a.Lkv - 1) j = a.Lkv - 1;
+      dma16(vbase + j * kvs1 + 8 * c, &S.v[64 * i]);
     }
-    // scales of the keys this lane's score registers hold: key = j0 + 16 mt + 4 grp + i
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int64_t j = j0 + 16 * mt + 4 * grp + i;
-        const bool ok = j < a.Lkv;
-        if (!ok) j = a.Lkv - 1;
-        sk_[mt][i] = ksb[j * a.kvs_st[1]];
-        sv_[mt][i] = ok ? vsb[j * a.kvs_st[1]] : 0.0f;
-      }
+    int64_t j = j0 + (lane & 31);
+    if (j > a.Lkv - 1) j = a.Lkv - 1;
+    dma4((lane < 32 ? ksb : vsb) + j * ss1, &S.sc[0]);
   };
 
   f32x4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, m_run_lo = 0.0f, l_run = 0.0f;
-  uint2* vh = vlds[wave][0];
-  uint2* vl = vlds[wave][1];
+  int E = 0;            // O is held in units of 2^-E (running P~ renormalisation)
+  float sv_seen = 0.0f;  // largest v-scale seen so far
 
-  const int nsteps = w1 > w0 ? (int)((w1 - w0 + DC_SUB - 1) / DC_SUB) : 0;
-  uint4 kr2[2][4], vr2[2][4];
-  float skr2[2][4], svr2[2][4];
-  if (nsteps > 0) gload(w0, kr, vr, skr, svr);
-  for (int st = 0; st < nsteps; ++st) {
-    const int64_t j0 = w0 + (int64_t)st * DC_SUB;
-    if (st + 1 < nsteps) gload(j0 + DC_SUB, kr2, vr2, skr2, svr2);
-    // ---- V^T of these 32 keys into this wave's LDS planes ----
+  auto compute = [&](const DcStage& S, const uint4 (&kraw)[2][4], int64_t j0) {
+    // ---- every LDS read of the step first (one round of latency): V^T fragments through the
+    //      transposing read, the scales of this lane's 8 keys ----
+    // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element (i % 4) of the 8-byte rows read
+    // by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  Lane r of group grp reads V[key 16 hh + 4 grp + r/4]
+    // [d 16 dt + 4 (r % 4) .. + 3], so lane i gets V[keys 16 hh + 4 grp + 0..3][16 dt + i]: the V^T
+    // operand rows in the score registers' key order.
+    v4i16 vtr[8][2];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      const int job = lane + 64 * jb, g = job >> 4, c = job & 15;
-      uint2 H[8], L[8];
-      unpack_t4x8(vr[jb], H, L);
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        vh[dc_vpos(8 * c + dd, g)] = H[dd];
-        vl[dc_vpos(8 * c + dd, g)] = L[dd];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = 16 * hh + 4 * grp + (qc >> 2), d = 16 * dt + 4 * (qc & 3);
+        const char* src = reinterpret_cast<const char*>(S.v) + dc_pos(key, d >> 3) * 16 + (d & 7) * 2;
+        vtr[dt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src));
       }
+    float4 skq[2], svq[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      skq[mt] = *reinterpret_cast<const float4*>(&S.sc[16 * mt + 4 * grp]);
+      svq[mt] = *reinterpret_cast<const float4*>(&S.sc[DC_SUB + 16 * mt + 4 * grp]);
     }
     // ---- S^T [32 keys x 16 query columns] ----
     f32x4 shh[2], srest[2];
@@ -560,23 +570,45 @@ __global__ __launch_bounds__(DC_THREADS) void attn_decode_kernel(AttnParams a, f
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         uint4 KH, KL;
-        unpack8(kr[mt][ks], KH, KL);
+        unpack8(kraw[mt][ks], KH, KL);
         shh[mt] = mfma16(KH, QH[ks], shh[mt]);
         srest[mt] = mfma16(KH, QL[ks], srest[mt]);
         srest[mt] = mfma16(KL, QH[ks], srest[mt]);
         srest[mt] = mfma16(KL, QL[ks], srest[mt]);
       }
     }
+    float skr[2][4] = {{skq[0].x, skq[0].y, skq[0].z, skq[0].w}, {skq[1].x, skq[1].y, skq[1].z, skq[1].w}};
+    float svr[2][4] = {{svq[0].x, svq[0].y, svq[0].z, svq[0].w}, {svq[1].x, svq[1].y, svq[1].z, svq[1].w}};
+    // ---- running exponent of the v-scales: P~ = p * s_v * 2^E < 2^15 ----
+    float svm = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (j0 + 16 * mt + 4 * grp + i >= w1) svr[mt][i] = 0.0f;
+        svm = fmaxf(svm, svr[mt][i]);
+      }
+    svm = fmaxf(svm, __shfl_xor(svm, 16, 64));
+    svm = fmaxf(svm, __shfl_xor(svm, 32, 64));
+    if (svm > sv_seen) {
+      sv_seen = svm;
+      const int En = 14 - ilogb_pos(svm);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[dt][i] = __builtin_amdgcn_ldexpf(O[dt][i], En - E);
+      E = En;
+    }
+    // ---- scores, online softmax (FP32 pairs) ----
     float tv[2][4], tl[2][4];
     float tmax = -INFINITY, tmax_lo = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t j = j0 + 16 * mt + 4 * grp + i;
         float s, sl;
         logit2(shh[mt][i], srest[mt][i], skr[mt][i], cq, s, sl);
-        if (j >= w1) {
+        if (j0 + 16 * mt + 4 * grp + i >= w1) {
           s = -INFINITY;
           sl = 0.0f;
         }
@@ -611,42 +643,45 @@ __global__ __launch_bounds__(DC_THREADS) void attn_decode_kernel(AttnParams a, f
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
-    // ---- O^T [128 d x 16 columns] += V^T P~^T over the 32 keys (virtual order: 4 grp.., 16 + 4 grp..) ----
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- O^T [128 d x 16 columns] += V^T P~^T ----
     const uint4 PH = make_uint4(ph[0], ph[1], ph[2], ph[3]);
     const uint4 PL = make_uint4(pl[0], pl[1], pl[2], pl[3]);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + qc;
-      const uint2 a1 = vh[dc_vpos(d, grp)], a2 = vh[dc_vpos(d, grp + 4)];
-      const uint2 b1 = vl[dc_vpos(d, grp)], b2 = vl[dc_vpos(d, grp + 4)];
-      const uint4 VH = make_uint4(a1.x, a1.y, a2.x, a2.y);
-      const uint4 VL = make_uint4(b1.x, b1.y, b2.x, b2.y);
+      const uint2 a0 = __builtin_bit_cast(uint2, vtr[dt][0]), a1 = __builtin_bit_cast(uint2, vtr[dt][1]);
+      uint4 VH, VL;
+      unpack8(make_uint4(a0.x, a0.y, a1.x, a1.y), VH, VL);
       O[dt] = mfma16(VH, PH, O[dt]);
       O[dt] = mfma16(VL, PH, O[dt]);
       O[dt] = mfma16(VH, PL, O[dt]);
       O[dt] = mfma16(VL, PL, O[dt]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        kr[mt][ks] = kr2[mt][ks];
-        vr[mt][ks] = vr2[mt][ks];
-        skr[mt][ks] = skr2[mt][ks];
-        svr[mt][ks] = svr2[mt][ks];
-      }
-  }
+  };
 
-  // ---- wave partial: the sum over the 4 lane groups, O^T un-renormalised by 2^-E ----
+  // ---- key loop: the next step's transfers are in flight while the current step is computed.  The
+  //      body is straight-line: a transfer past the last step re-reads valid keys (clamped) into the
+  //      idle stage and is drained after the loop. ----
+  const int nsteps = w1 > w0 ? (int)((w1 - w0 + DC_SUB - 1) / DC_SUB) : 0;
+  uint4 kr0[2][4], kr1[2][4];
+  if (nsteps > 0) issue(st0[wave], kr0, w0);
+  for (int s = 0; s < nsteps; s += 2) {
+    const int64_t j0 = w0 + (int64_t)s * DC_SUB;
+    issue(st1[wave], kr1, j0 + DC_SUB);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<DC_NDMA>());
+    __asm__ __volatile__("" ::: "memory");
+    compute(st0[wave], kr0, j0);
+    if (s + 1 >= nsteps) break;
+    issue(st0[wave], kr0, j0 + 2 * DC_SUB);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<DC_NDMA>());
+    __asm__ __volatile__("" ::: "memory");
+    compute(st1[wave], kr1, j0 + DC_SUB);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+
+  // ---- wave partial: the sum over the 4 lane groups, O^T brought back from units of 2^-E ----
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  __syncthreads();  // every wavefront is done with its V^T planes before they are reused
+  __syncthreads();  // every wavefront is done with its stages before they are reused
   {
     float* pw = part[wave][qc];
     if (grp == 0) {
