@@ -18,8 +18,10 @@
 //     O += P~h.H + P~h.L + P~l.H + P~l.L (4 products, one FP32 accumulator); O = acc * 2^-E / l.
 //
 // Prefill (q_len > 1): flash-style forward.  A workgroup of 8 wavefronts owns 256 queries of one
-// (batch, head); each wavefront owns 32.  K/V tiles of 64 keys are staged in LDS already unpacked (K as
-// [key][d] H/L planes, V transposed to [d][key] H/L planes), double-buffered, one barrier per tile.
+// (batch, head); each wavefront owns 32.  K/V tiles of 64 keys arrive in LDS as raw INT16 rows by
+// direct-to-LDS transfers (double-buffered, one barrier per tile); K fragments are 16-byte LDS reads and
+// the V^T operand comes from the same [key][d] rows through gfx950's transposing LDS read, both unpacked
+// into their FP16 halves in registers.
 // Each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16_f16, so the 16 scores a lane holds all
 // belong to ONE query: the softmax maximum/sum are lane-local plus one exchange with lane ^ 32.  The same
 // registers, in MFMA order, are the P^T operand of O^T = V^T P^T, so P never leaves registers.
@@ -53,40 +55,25 @@ __device__ __forceinline__ uint32_t pack2(_Float16 a, _Float16 b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Dual-FP16 unpack of 8 INT16 values (one 16-byte chunk): H = fp16(q & ~0xFF), L = fp16(q & 0xFF)
-__device__ __forceinline__ void unpack8(const uint4& raw, uint4& H, uint4& L) {
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q0 = (int)(int16_t)(w[i] & 0xFFFFu), q1 = (int)(int16_t)(w[i] >> 16);
-    h[i] = pack2((_Float16)(float)(q0 & ~0xFF), (_Float16)(float)(q1 & ~0xFF));
-    l[i] = pack2((_Float16)(float)(q0 & 0xFF), (_Float16)(float)(q1 & 0xFF));
-  }
-  H = make_uint4(h[0], h[1], h[2], h[3]);
-  L = make_uint4(l[0], l[1], l[2], l[3]);
+// Dual-FP16 unpack of 8 INT16 values (one 16-byte chunk): H = fp16(q & ~0xFF) = 256 * (q >> 8) and
+// L = fp16(q & 0xFF), two values per 32-bit word with packed FP16 arithmetic, exact by construction:
+//   L: the FP16 pattern 0x5C00 | (l << 2) is 256 + l (exponent 2^8, l in the top 8 mantissa bits), minus 256.
+//   H: with b = the signed high byte, 0x6400 | (b ^ 0x80) is 1024 + b + 128; minus 1152 gives b, times 256
+//      gives H (|H| <= 2^15).  Every intermediate is an integer below 2^11, so no step rounds.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t& h, uint32_t& l) {
+  const f16x2 lo = __builtin_bit_cast(f16x2, ((w & 0x00FF00FFu) << 2) | 0x5C005C00u);
+  const f16x2 hb = __builtin_bit_cast(f16x2, ((w >> 8) & 0x00FF00FFu) ^ 0x64806480u);
+  const f16x2 c256 = {(_Float16)256.0f, (_Float16)256.0f};
+  const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+  l = __builtin_bit_cast(uint32_t, lo - c256);
+  h = __builtin_bit_cast(uint32_t, (hb - c1152) * c256);
 }
-
-// transpose-unpack: 4 keys x 8 d (one 16-byte chunk per key) -> for each of the 8 d, the 4 keys' H and L
-// packed as 8 bytes (uint2)
-__device__ __forceinline__ void unpack_t4x8(const uint4 (&raw)[4], uint2 (&H)[8], uint2 (&L)[8]) {
-  int q[4][8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      q[k][2 * i] = (int)(int16_t)(w[i] & 0xFFFFu);
-      q[k][2 * i + 1] = (int)(int16_t)(w[i] >> 16);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    H[d] = make_uint2(pack2((_Float16)(float)(q[0][d] & ~0xFF), (_Float16)(float)(q[1][d] & ~0xFF)),
-                      pack2((_Float16)(float)(q[2][d] & ~0xFF), (_Float16)(float)(q[3][d] & ~0xFF)));
-    L[d] = make_uint2(pack2((_Float16)(float)(q[0][d] & 0xFF), (_Float16)(float)(q[1][d] & 0xFF)),
-                      pack2((_Float16)(float)(q[2][d] & 0xFF), (_Float16)(float)(q[3][d] & 0xFF)));
-  }
+__device__ __forceinline__ void unpack8(const uint4& raw, uint4& H, uint4& L) {
+  unpack_word(raw.x, H.x, L.x);
+  unpack_word(raw.y, H.y, L.y);
+  unpack_word(raw.z, H.z, L.z);
+  unpack_word(raw.w, H.w, L.w);
 }
 
 __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
@@ -118,10 +105,9 @@ __device__ __forceinline__ void logit2(float shh, float srest, float sk, float c
 // (hi, lo) maximum: larger hi wins, equal hi -> larger lo.  The rule is symmetric, so lanes that exchange
 // candidates agree on the result, and the arg-max key then gets p = exp2(0 + 0) = 1 exactly.
 __device__ __forceinline__ void pair_max(float& mh, float& ml, float oh, float ol) {
-  if (oh > mh || (oh == mh && ol > ml)) {
-    mh = oh;
-    ml = ol;
-  }
+  const bool take = (oh > mh) | ((oh == mh) & (ol > ml));
+  mh = take ? oh : mh;
+  ml = take ? ol : ml;
 }
 
 // split p~ into fp16 hi + lo (lo = fp16(p~ - hi), the residual is exact in fp32)
@@ -130,19 +116,66 @@ __device__ __forceinline__ void split_p(float p, _Float16& h, _Float16& l) {
   l = (_Float16)(p - (float)h);
 }
 
+// ================================================================================ direct-to-LDS helpers
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, 0);
+}
+// s_waitcnt immediate: at most N vector-memory operations outstanding, all LDS operations done
+template <int N>
+constexpr int waitcnt_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
+}
+// INT16 K rows in LDS: [key][16 chunks of 8 d], chunk c of key j at j * 16 + (c ^ (j & 15)), so the 16
+// keys one 16-byte fragment read touches sit in 16 different bank groups
+__device__ __forceinline__ int kv_pos(int key, int c) { return key * 16 + (c ^ (key & 15)); }
+// INT16 V rows: chunk c of key j at j * 16 + (c ^ (j & 3)).  A transposing read touches 4 consecutive keys,
+// which this spreads over 4 chunk slots; XOR-ing only the low two chunk bits leaves the d-tile and key-block
+// offsets of every read plain immediates, so one address register per lane serves all of them.
+__device__ __forceinline__ int v_pos(int key, int c) { return key * 16 + (c ^ (key & 3)); }
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane i receives element (i % 4) of the 8-byte rows read by
+// lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  So when lane r of a group reads V[k0 + r/4][d0 + 4 (r % 4) .. + 3]
+// (4 keys x 16 d), lane i receives V[k0 .. k0 + 3][d0 + i]: four keys of one d, the V^T operand layout.
+__device__ __forceinline__ v4i16 read_vt(const uint4* v_rows, int k0, int d0, int r) {
+  const int key = k0 + (r >> 2), d = d0 + 4 * (r & 3);
+  const char* src = reinterpret_cast<const char*>(v_rows) + v_pos(key, d >> 3) * 16 + (d & 7) * 2;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src));
+}
+__device__ __forceinline__ uint4 join_v4i16(const v4i16& a, const v4i16& b) {
+  const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+  return make_uint4(x.x, x.y, y.x, y.y);
+}
+
 // ============================================================================================ prefill
 constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_BQ = 32 * PF_WAVES;  // queries per workgroup
-constexpr int PF_BKV = 64;            // keys per LDS stage
-// LDS stage: K H/L planes [64 keys][16 chunks of 8 d] (uint4), V^T H/L planes [128 d][16 groups of 4 keys]
-// (uint2), then the 64 k-scales and the 64 renormalised v-scales.
-constexpr int PF_K_PLANE = PF_BKV * 16;   // uint4 per K plane
-constexpr int PF_V_PLANE = D * 16;        // uint2 per V^T plane
-constexpr int PF_STAGE_BYTES = 2 * PF_K_PLANE * 16 + 2 * PF_V_PLANE * 8 + 2 * PF_BKV * 4;
-
-__device__ __forceinline__ int pf_kpos(int key, int c) { return key * 16 + (c ^ (key & 15)); }
-__device__ __forceinline__ int pf_vpos(int d, int g) { return d * 16 + (g ^ ((d >> 1) & 15)); }
+constexpr int PF_BKV = 32;            // keys per tile
+static_assert(PF_BKV * 16 == PF_THREADS, "one 16-byte chunk of K and one of V per thread and tile");
+// A tile as the direct-to-LDS transfers leave it: thread tid's chunk (key tid / 16, chunk tid % 16) of K and
+// of V at slot tid, then the tile's 32 k-scales and 32 v-scales (brought by wavefront 0).  Every slot is
+// written and read by the same thread, so only that thread's own transfer count guards it.
+struct PfRaw {
+  uint4 k[PF_THREADS];
+  uint4 v[PF_THREADS];
+  float sc[64];
+};
+// The tile's Dual-FP16 operands, unpacked once for all wavefronts: K halves in the kv_pos layout, V halves
+// in the v_pos layout, the k-scales, then the v-scales times 2^E.
+struct PfPlanes {
+  uint4 kh[PF_BKV * 16];
+  uint4 kl[PF_BKV * 16];
+  uint4 vh[PF_BKV * 16];
+  uint4 vl[PF_BKV * 16];
+  float sc[64];
+};
 
 struct AttnParams {
   const int16_t* q;
@@ -159,7 +192,10 @@ struct AttnParams {
 };
 
 __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ PfRaw r0;
+  __shared__ PfRaw r1;
+  __shared__ PfPlanes p0;
+  __shared__ PfPlanes p1;
   __shared__ float red[PF_WAVES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -182,10 +218,31 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
   const int16_t* vbase = a.v + b * a.kv_st[0] + hk * a.kv_st[2];
   const float* ksb = a.ks + b * a.kvs_st[0] + hk * a.kvs_st[2];
   const float* vsb = a.vs + b * a.kvs_st[0] + hk * a.kvs_st[2];
+  const int64_t kvs1 = a.kv_st[1], ss1 = a.kvs_st[1];
+
+  // ---- one tile's transfers: wavefront 0 brings the scales first, then every thread its K and V chunk, so
+  //      "at most 2 outstanding" after issuing tile t + 1 means this thread's part of tile t has landed.
+  //      Keys past the end are clamped to the last key (read, never used). ----
+  const int ckey = tid >> 4, cchunk = tid & 15;
+  auto issue = [&](PfRaw& R, int t) {
+    if (wave == 0) {
+      int64_t js = (int64_t)t * PF_BKV + (lane & 31);
+      if (js > a.Lkv - 1) js = a.Lkv - 1;
+      dma4((lane < 32 ? ksb : vsb) + js * ss1, &R.sc[0]);
+    }
+    int64_t j = (int64_t)t * PF_BKV + ckey;
+    if (j > a.Lkv - 1) j = a.Lkv - 1;
+    dma16(kbase + j * kvs1 + 8 * cchunk, &R.k[64 * wave]);
+    dma16(vbase + j * kvs1 + 8 * cchunk, &R.v[64 * wave]);
+  };
+  if (ntk > 0) {
+    issue(r0, 0);
+    issue(r1, 1);
+  }
 
   // ---- E = 14 - ilogb(max v-scale over the keys this workgroup reads) ----
   float vmax = 0.0f;
-  for (int64_t j = tid; j < kv_end; j += PF_THREADS) vmax = fmaxf(vmax, vsb[j * a.kvs_st[1]]);
+  for (int64_t j = tid; j < kv_end; j += PF_THREADS) vmax = fmaxf(vmax, vsb[j * ss1]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, m, 64));
   if (lane == 0) red[wave] = vmax;
@@ -195,7 +252,22 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
   for (int w = 1; w < PF_WAVES; ++w) vmax = fmaxf(vmax, red[w]);
   const int E = vmax > 0.0f ? 14 - ilogb_pos(vmax) : 0;
 
-  // ---- this lane's query and its Dual-FP16 fragments (B operand of S^T = K Q^T) ----
+  // ---- unpack this thread's chunks of a landed tile into the Dual-FP16 planes ----
+  auto unpack = [&](const PfRaw& R, PfPlanes& P) {
+    uint4 hi, lo;
+    unpack8(R.k[tid], hi, lo);
+    P.kh[kv_pos(ckey, cchunk)] = hi;
+    P.kl[kv_pos(ckey, cchunk)] = lo;
+    unpack8(R.v[tid], hi, lo);
+    P.vh[v_pos(ckey, cchunk)] = hi;
+    P.vl[v_pos(ckey, cchunk)] = lo;
+    if (wave == 0) {
+      const float s = R.sc[lane];
+      P.sc[lane] = lane < 32 ? s : __builtin_amdgcn_ldexpf(s, E);
+    }
+  };
+
+  // ---- this lane's query and its Dual-FP16 fragments (B operand of S^T = K Q^T), unpacked once ----
   const int qcol = lane & 31, half = lane >> 5;
   const int64_t qi = q0 + 32 * wave + qcol;
   const bool qvalid = qi < a.Lq;
@@ -203,85 +275,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
   const int16_t* qrow = a.q + b * a.q_st[0] + qi_c * a.q_st[1] + h * a.q_st[2];
   uint4 QH[8], QL[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half);
-    unpack8(raw, QH[ks], QL[ks]);
-  }
+  for (int ks = 0; ks < 8; ++ks) unpack8(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half), QH[ks], QL[ks]);
   const float cq = a.qs[b * a.qs_st[0] + qi_c * a.qs_st[1] + h * a.qs_st[2]] * a.scale_log2;
   // queries of this wave: [q0 + 32 wave, q0 + 32 wave + 31]; key j visible to query i iff j <= i + off
   const int64_t wq_first = q0 + 32 * wave, wq_last = wq_first + 31;
-
-  // ---- staging roles: K: 2 chunks per thread; V: one (2-key pair, 8-d chunk) job per thread ----
-  uint4 kraw[2], vraw[2];
-  auto gload = [&](int t) {
-    const int64_t kb = (int64_t)t * PF_BKV;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + PF_THREADS * i, key = id >> 4, c = id & 15;
-      int64_t j = kb + key;
-      if (j > a.Lkv - 1) j = a.Lkv - 1;
-      kraw[i] = *reinterpret_cast<const uint4*>(kbase + j * a.kv_st[1] + 8 * c);
-    }
-    {
-      const int pair = tid >> 4, c = tid & 15;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int64_t j = kb + 2 * pair + i;
-        if (j > a.Lkv - 1) j = a.Lkv - 1;
-        vraw[i] = *reinterpret_cast<const uint4*>(vbase + j * a.kv_st[1] + 8 * c);
-      }
-    }
-  };
-  float sk_reg = 0.0f, sv_reg = 0.0f;
-  auto sload = [&](int t) {
-    if (tid < PF_BKV) {
-      int64_t j = (int64_t)t * PF_BKV + tid;
-      const bool ok = j < a.Lkv;
-      if (!ok) j = a.Lkv - 1;
-      sk_reg = ksb[j * a.kvs_st[1]];
-      sv_reg = ok ? __builtin_amdgcn_ldexpf(vsb[j * a.kvs_st[1]], E) : 0.0f;
-    }
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* st = smem + (size_t)buf * PF_STAGE_BYTES;
-    uint4* kh = reinterpret_cast<uint4*>(st);
-    uint4* kl = kh + PF_K_PLANE;
-    uint2* vh = reinterpret_cast<uint2*>(kl + PF_K_PLANE);
-    uint2* vl = vh + PF_V_PLANE;
-    float* sks = reinterpret_cast<float*>(vl + PF_V_PLANE);
-    float* svs = sks + PF_BKV;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + PF_THREADS * i, key = id >> 4, c = id & 15;
-      uint4 H, L;
-      unpack8(kraw[i], H, L);
-      kh[pf_kpos(key, c)] = H;
-      kl[pf_kpos(key, c)] = L;
-    }
-    {
-      const int pair = tid >> 4, c = tid & 15;
-      uint4 H0, L0, H1, L1;
-      unpack8(vraw[0], H0, L0);
-      unpack8(vraw[1], H1, L1);
-      const uint32_t h0[4] = {H0.x, H0.y, H0.z, H0.w}, h1[4] = {H1.x, H1.y, H1.z, H1.w};
-      const uint32_t l0[4] = {L0.x, L0.y, L0.z, L0.w}, l1[4] = {L1.x, L1.y, L1.z, L1.w};
-      // keys 2*pair, 2*pair+1 sit in group (2*pair)/4 at half-word slot (2*pair)%4 .. +1
-      const int g = pair >> 1, sub = pair & 1;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int d = 8 * c + dd;
-        const uint32_t sh = (dd & 1) ? 16 : 0;
-        const uint32_t hw = ((h0[dd >> 1] >> sh) & 0xFFFFu) | (((h1[dd >> 1] >> sh) & 0xFFFFu) << 16);
-        const uint32_t lw = ((l0[dd >> 1] >> sh) & 0xFFFFu) | (((l1[dd >> 1] >> sh) & 0xFFFFu) << 16);
-        reinterpret_cast<uint32_t*>(vh + pf_vpos(d, g))[sub] = hw;
-        reinterpret_cast<uint32_t*>(vl + pf_vpos(d, g))[sub] = lw;
-      }
-    }
-    if (tid < PF_BKV) {
-      sks[tid] = sk_reg;
-      svs[tid] = sv_reg;
-    }
-  };
 
   f32x16 O[4];
 #pragma unroll
@@ -289,60 +286,42 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[dt][r] = 0.0f;
   float m_run = -INFINITY, m_run_lo = 0.0f, l_run = 0.0f;
+  const int vq = lane >> 4, vi = lane & 15;  // 16-lane group and position for the transposing reads
 
-  if (ntk > 0) {
-    gload(0);
-    sload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntk; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntk) {
-      gload(t + 1);
-      sload(t + 1);
-    }
-    const unsigned char* st = smem + (size_t)buf * PF_STAGE_BYTES;
-    const uint4* kh = reinterpret_cast<const uint4*>(st);
-    const uint4* kl = kh + PF_K_PLANE;
-    const uint2* vh = reinterpret_cast<const uint2*>(kl + PF_K_PLANE);
-    const uint2* vl = vh + PF_V_PLANE;
-    const float* sks = reinterpret_cast<const float*>(vl + PF_V_PLANE);
-    const float* svs = sks + PF_BKV;
+  auto compute = [&](const PfPlanes& P, int t) {
     const int64_t kb = (int64_t)t * PF_BKV;
-
+    if (a.causal && kb > wq_last + off) return;  // every key masked for this wave (wave-uniform)
+    // ---- S^T tile [32 keys x 32 queries] = K Q^T, two accumulators ----
+    f32x16 shh, srest;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int64_t kfirst = kb + 32 * sub;
-      if (a.causal && kfirst > wq_last + off) continue;  // every key masked for this wave (wave-uniform)
-      if (kfirst >= a.Lkv) continue;
-      // ---- S^T tile [32 keys x 32 queries] = K Q^T, two accumulators ----
-      f32x16 shh, srest;
+    for (int r = 0; r < 16; ++r) {
+      shh[r] = 0.0f;
+      srest[r] = 0.0f;
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { shh[r] = 0.0f; srest[r] = 0.0f; }
-      const int krow = 32 * sub + qcol;  // A-operand row of this lane (a key)
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 KH = P.kh[kv_pos(qcol, 2 * ks + half)];
+      const uint4 KL = P.kl[kv_pos(qcol, 2 * ks + half)];
+      shh = mfma32(KH, QH[ks], shh);
+      srest = mfma32(KH, QL[ks], srest);
+      srest = mfma32(KL, QH[ks], srest);
+      srest = mfma32(KL, QL[ks], srest);
+    }
+    // ---- scores of this lane's query for its 16 keys: key = 8 (r/4) + 4 half + r%4 ----
+    const bool need_mask = (a.causal && kb + 31 > wq_first + off) || (kb + 31 >= a.Lkv);
+    float tv[16], tl[16];
+    float tmax = -INFINITY, tmax_lo = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int c = 2 * ks + half;
-        const uint4 KH = kh[pf_kpos(krow, c)];
-        const uint4 KL = kl[pf_kpos(krow, c)];
-        shh = mfma32(KH, QH[ks], shh);
-        srest = mfma32(KH, QL[ks], srest);
-        srest = mfma32(KL, QH[ks], srest);
-        srest = mfma32(KL, QL[ks], srest);
-      }
-      // ---- scores of this lane's query for its 16 keys: key = 32 sub + 8 (r/4) + 4 half + r%4 ----
-      const bool need_mask = (a.causal && kfirst + 31 > wq_first + off) || (kfirst + 31 >= a.Lkv);
-      float tv[16], tl[16];
-      float tmax = -INFINITY, tmax_lo = 0.0f;
+    for (int g = 0; g < 4; ++g) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&P.sc[8 * g + 4 * half]);
+      const float skv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 32 * sub + 8 * (r >> 2) + 4 * half + (r & 3);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
         float s, sl;
-        logit2(shh[r], srest[r], sks[kk], cq, s, sl);
+        logit2(shh[r], srest[r], skv[i], cq, s, sl);
         if (need_mask) {
-          const int64_t j = kb + kk;
+          const int64_t j = kb + 8 * g + 4 * half + i;
           if (j >= a.Lkv || (a.causal && j > qi + off)) {
             s = -INFINITY;
             sl = 0.0f;
@@ -352,60 +331,86 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
         tl[r] = sl;
         pair_max(tmax, tmax_lo, s, sl);
       }
-      pair_max(tmax, tmax_lo, __shfl_xor(tmax, 32, 64), __shfl_xor(tmax_lo, 32, 64));
-      float m_new = m_run, m_new_lo = m_run_lo;
-      pair_max(m_new, m_new_lo, tmax, tmax_lo);
-      const bool none = m_new == -INFINITY;
-      const float m_use = none ? 0.0f : m_new, m_use_lo = none ? 0.0f : m_new_lo;
-      // 0 on the first visible tile (m_run = -inf)
-      const float alpha = exp2f((m_run - m_use) + (m_run_lo - m_use_lo));
-      m_run = m_new;
-      m_run_lo = m_new_lo;
-      float psum = 0.0f;
-      uint32_t ph[8], pl[8];  // P~ fragments: k-step kk2 uses registers 8 kk2 .. 8 kk2 + 7
+    }
+    pair_max(tmax, tmax_lo, __shfl_xor(tmax, 32, 64), __shfl_xor(tmax_lo, 32, 64));
+    float m_new = m_run, m_new_lo = m_run_lo;
+    pair_max(m_new, m_new_lo, tmax, tmax_lo);
+    const bool none = m_new == -INFINITY;
+    const float m_use = none ? 0.0f : m_new, m_use_lo = none ? 0.0f : m_new_lo;
+    // 0 on the first visible tile (m_run = -inf)
+    const float alpha = exp2f((m_run - m_use) + (m_run_lo - m_use_lo));
+    m_run = m_new;
+    m_run_lo = m_new_lo;
+    float psum = 0.0f;
+    uint32_t ph[8], pl[8];  // P~ fragments: k-step kk2 uses registers 4 kk2 .. 4 kk2 + 3
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int kk0 = 32 * sub + 8 * (r >> 2) + 4 * half + (r & 3);
+    for (int g = 0; g < 4; ++g) {
+      const float4 v4 = *reinterpret_cast<const float4*>(&P.sc[32 + 8 * g + 4 * half]);
+      const float svv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int r = 4 * g + i;
         const float p0 = exp2f((tv[r] - m_use) + (tl[r] - m_use_lo));
         const float p1 = exp2f((tv[r + 1] - m_use) + (tl[r + 1] - m_use_lo));
         psum += p0 + p1;
         _Float16 h0, l0, h1, l1;
-        split_p(p0 * svs[kk0], h0, l0);
-        split_p(p1 * svs[kk0 + 1], h1, l1);
+        split_p(p0 * svv[i], h0, l0);
+        split_p(p1 * svv[i + 1], h1, l1);
         ph[r >> 1] = pack2(h0, h1);
         pl[r >> 1] = pack2(l0, l1);
       }
-      l_run = l_run * alpha + psum;
-      if (alpha != 1.0f) {
+    }
+    l_run = l_run * alpha + psum;
+    if (alpha != 1.0f) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-      }
-      // ---- O^T [128 d x 32 queries] += V^T P~^T over these 32 keys (2 k-steps of 16) ----
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+    }
+    // ---- O^T [128 d x 32 queries] += V^T P~^T over these 32 keys (2 k-steps of 16).  The V^T operand of
+    //      lane (d = 32 dt + l % 32, k-group g = l / 32) holds keys 16 kk2 + 4 g + 0..3 and
+    //      16 kk2 + 8 + 4 g + 0..3: the same keys, in the same order, as the P~ registers ----
 #pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2) {
-        const uint4 PH = make_uint4(ph[4 * kk2], ph[4 * kk2 + 1], ph[4 * kk2 + 2], ph[4 * kk2 + 3]);
-        const uint4 PL = make_uint4(pl[4 * kk2], pl[4 * kk2 + 1], pl[4 * kk2 + 2], pl[4 * kk2 + 3]);
-        // key groups (of 4) of this k-step for this half: 8 sub + 4 kk2 + half, and that + 2
-        const int g1 = 8 * sub + 4 * kk2 + half, g2 = g1 + 2;
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const uint4 PH = make_uint4(ph[4 * kk2], ph[4 * kk2 + 1], ph[4 * kk2 + 2], ph[4 * kk2 + 3]);
+      const uint4 PL = make_uint4(pl[4 * kk2], pl[4 * kk2 + 1], pl[4 * kk2 + 2], pl[4 * kk2 + 3]);
+      const int k1 = 16 * kk2 + 4 * (vq >> 1);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + qcol;
-          const uint2 a1 = vh[pf_vpos(d, g1)], a2 = vh[pf_vpos(d, g2)];
-          const uint2 b1 = vl[pf_vpos(d, g1)], b2 = vl[pf_vpos(d, g2)];
-          const uint4 VH = make_uint4(a1.x, a1.y, a2.x, a2.y);
-          const uint4 VL = make_uint4(b1.x, b1.y, b2.x, b2.y);
-          O[dt] = mfma32(VH, PH, O[dt]);
-          O[dt] = mfma32(VL, PH, O[dt]);
-          O[dt] = mfma32(VH, PL, O[dt]);
-          O[dt] = mfma32(VL, PL, O[dt]);
-        }
+      for (int dt = 0; dt < 4; ++dt) {
+        const int d0 = 32 * dt + 16 * (vq & 1);
+        const uint4 VH = join_v4i16(read_vt(P.vh, k1, d0, vi), read_vt(P.vh, k1 + 8, d0, vi));
+        const uint4 VL = join_v4i16(read_vt(P.vl, k1, d0, vi), read_vt(P.vl, k1 + 8, d0, vi));
+        O[dt] = mfma32(VH, PH, O[dt]);
+        O[dt] = mfma32(VL, PH, O[dt]);
+        O[dt] = mfma32(VH, PL, O[dt]);
+        O[dt] = mfma32(VL, PL, O[dt]);
       }
     }
-    if (t + 1 < ntk) lstore(buf ^ 1);
+  };
+
+  // ---- key loop.  In the step for tile t: tile t + 2's transfers are issued, tile t + 1 (landed) is
+  //      unpacked into the other plane set, and tile t is multiplied; one barrier per tile.  The body is
+  //      straight-line: transfers and unpacks past the last tile touch valid (clamped) keys and idle
+  //      buffers only, and the transfers are drained before the epilogue. ----
+  if (ntk > 0) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<2>());
+    unpack(r0, p0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntk; t += 2) {
+    issue(r0, t + 2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<2>());
+    unpack(r1, p1);
+    compute(p0, t);
+    __syncthreads();
+    if (t + 1 >= ntk) break;
+    issue(r1, t + 3);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<2>());
+    unpack(r0, p0);
+    compute(p1, t + 1);
     __syncthreads();
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
 
   // ---- epilogue: O = acc * 2^-E / l; lane holds query qcol, d = 32 dt + 8 (r/4) + 4 half + r%4 ----
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -435,30 +440,12 @@ constexpr int DC_PART = 4 + D;                // floats per partial: m_hi, m_lo,
 constexpr int DC_NDMA = 17;                   // direct-to-LDS transfers per lane per step
 
 // One step's V in a wavefront-private LDS stage, filled by direct-to-LDS transfers: [32 keys][16 chunks of
-// 8 d] INT16 (chunk c of key j at j * 16 + (c ^ (j & 15)), so the rows one transposing read touches sit
-// in different bank groups), then the 32 k-scales and 32 v-scales.  K needs no LDS: its MFMA operand
+// 8 d] INT16 in the v_pos layout, then the 32 k-scales and 32 v-scales.  K needs no LDS: its MFMA operand
 // layout (one key's 8 consecutive d per lane) is a plain 16-byte load into registers.
 struct DcStage {
   uint4 v[DC_SUB * 16];
   float sc[2 * DC_SUB];
 };
-__device__ __forceinline__ int dc_pos(int key, int c) { return key * 16 + (c ^ (key & 15)); }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, 0);
-}
-// s_waitcnt immediate: at most N vector-memory operations outstanding, all LDS operations done
-template <int N>
-constexpr int waitcnt_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
-  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
-}
 
 size_t decode_workspace(int64_t B, int64_t Hq, int64_t Lkv) {
   const int64_t nsplit = (Lkv + DC_CHUNK - 1) / DC_CHUNK;
@@ -522,7 +509,7 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int p = 64 * i + lane, key = p >> 4, c = (p & 15) ^ (key & 15);
+      const int p = 64 * i + lane, key = p >> 4, c = (p & 15) ^ (key & 3);
       int64_t j = j0 + key;
       if (j > a.Lkv - 1) j = a.Lkv - 1;
       dma16(vbase + j * kvs1 + 8 * c, &S.v[64 * i]);
@@ -550,11 +537,7 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int key = 16 * hh + 4 * grp + (qc >> 2), d = 16 * dt + 4 * (qc & 3);
-        const char* src = reinterpret_cast<const char*>(S.v) + dc_pos(key, d >> 3) * 16 + (d & 7) * 2;
-        vtr[dt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src));
-      }
+      for (int hh = 0; hh < 2; ++hh) vtr[dt][hh] = read_vt(S.v, 16 * hh + 4 * grp, 16 * dt, qc);
     float4 skq[2], svq[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -648,9 +631,8 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint4 PL = make_uint4(pl[0], pl[1], pl[2], pl[3]);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint2 a0 = __builtin_bit_cast(uint2, vtr[dt][0]), a1 = __builtin_bit_cast(uint2, vtr[dt][1]);
       uint4 VH, VL;
-      unpack8(make_uint4(a0.x, a0.y, a1.x, a1.y), VH, VL);
+      unpack8(join_v4i16(vtr[dt][0], vtr[dt][1]), VH, VL);
       O[dt] = mfma16(VH, PH, O[dt]);
       O[dt] = mfma16(VL, PH, O[dt]);
       O[dt] = mfma16(VH, PL, O[dt]);
@@ -796,16 +778,9 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
                        p, (const float*)ws, nsplit);
     return hipGetLastError();
   }
-  static bool attr_set = false;  // benign race: every caller sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * PF_STAGE_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const unsigned ntq = (unsigned)((x.q_len + PF_BQ - 1) / PF_BQ);
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)(x.batch * x.n_q_heads), ntq), dim3(PF_THREADS),
-                     2 * PF_STAGE_BYTES, stream, p);
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)(x.batch * x.n_q_heads), ntq), dim3(PF_THREADS), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
