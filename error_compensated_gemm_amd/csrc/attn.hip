@@ -90,17 +90,23 @@ __device__ __forceinline__ int ilogb_pos(float x) { return __builtin_amdgcn_frex
 // Logit t = (shh + srest) * s_k * cq as an unevaluated pair t_hi + t_lo.  A single FP32 rounding of t
 // costs 2^-24 |t|, which for logits of magnitude 10^3 moves exp2(t - m) by ~1e-4; carrying the product's
 // rounding error (FMA) keeps t - m accurate to ~2^-24 |t - m| instead.
-// S_int = shh + srest is first rounded with its error kept (TwoSum: s_hi + s_lo == shh + srest exactly),
-// so t_hi is the correctly rounded logit and |t_lo| <= ~2^-23 |t_hi| whatever cancellation happens.
+// S_int = shh + srest is first rounded with its error kept: s_hi + s_lo == shh + srest exactly.  Fast2Sum
+// suffices here although |srest| may exceed |shh|: shh sums products of two multiples of 256, so it is a
+// multiple of 2^16, while |srest| < 2^31 makes ulp(srest) <= 2^8; an addend that is a multiple of the
+// other's ulp makes the error term exact in either order.  t_hi is then the correctly rounded logit and
+// |t_lo| <= ~2^-23 |t_hi| whatever cancellation happens.
 __device__ __forceinline__ void logit2(float shh, float srest, float sk, float cq, float& t_hi, float& t_lo) {
   const float s_hi = shh + srest;
-  const float bb = s_hi - shh;
-  const float s_lo = (shh - (s_hi - bb)) + (srest - bb);
+  const float s_lo = srest - (s_hi - shh);
   const float c_hi = sk * cq;
   const float c_lo = __builtin_fmaf(sk, cq, -c_hi);
   t_hi = s_hi * c_hi;
-  t_lo = __builtin_fmaf(s_hi, c_hi, -t_hi) + (s_hi * c_lo + s_lo * c_hi);
+  t_lo = __builtin_fmaf(s_hi, c_hi, -t_hi) + __builtin_fmaf(s_lo, c_hi, s_hi * c_lo);
 }
+
+// 2^x by the hardware instruction (about 1 ulp; results below 2^-126 flush to 0).  Softmax weights are
+// at most about 1, so a flushed weight is below the rounding error of the largest one.
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // (hi, lo) maximum: larger hi wins, equal hi -> larger lo.  The rule is symmetric, so lanes that exchange
 // candidates agree on the result, and the arg-max key then gets p = exp2(0 + 0) = 1 exactly.
@@ -158,6 +164,7 @@ constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_BQ = 32 * PF_WAVES;  // queries per workgroup
 constexpr int PF_BKV = 32;            // keys per tile
+constexpr int PF_TAU = 8;             // slack of the lazy running maximum (log2 units)
 static_assert(PF_BKV * 16 == PF_THREADS, "one 16-byte chunk of K and one of V per thread and tile");
 // A tile as the direct-to-LDS transfers leave it: thread tid's chunk (key tid / 16, chunk tid % 16) of K and
 // of V at slot tid, then the tile's 32 k-scales and 32 v-scales (brought by wavefront 0).  Every slot is
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
     issue(r1, 1);
   }
 
-  // ---- E = 14 - ilogb(max v-scale over the keys this workgroup reads) ----
+  // ---- E = 14 - PF_TAU - ilogb(max v-scale over the keys this workgroup reads) ----
   float vmax = 0.0f;
   for (int64_t j = tid; j < kv_end; j += PF_THREADS) vmax = fmaxf(vmax, vsb[j * ss1]);
 #pragma unroll
@@ -250,7 +257,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
   vmax = red[0];
 #pragma unroll
   for (int w = 1; w < PF_WAVES; ++w) vmax = fmaxf(vmax, red[w]);
-  const int E = vmax > 0.0f ? 14 - ilogb_pos(vmax) : 0;
+  // p <= 2^PF_TAU under the lazy running maximum, so P~ = p s_v 2^E stays below 2^15
+  const int E = vmax > 0.0f ? 14 - PF_TAU - ilogb_pos(vmax) : 0;
 
   // ---- unpack this thread's chunks of a landed tile into the Dual-FP16 planes ----
   auto unpack = [&](const PfRaw& R, PfPlanes& P) {
@@ -307,10 +315,14 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
       srest = mfma32(KL, QH[ks], srest);
       srest = mfma32(KL, QL[ks], srest);
     }
-    // ---- scores of this lane's query for its 16 keys: key = 8 (r/4) + 4 half + r%4 ----
-    const bool need_mask = (a.causal && kb + 31 > wq_first + off) || (kb + 31 >= a.Lkv);
+    // ---- scores of this lane's query for its 16 keys: key = 8 (r/4) + 4 half + r%4.  Keys past the end
+    //      or above this query's causal limit are hidden: tile key kk is visible iff kk < lim, so the lane's
+    //      key 8 (r/4) + 4 half + r%4 is hidden iff 8 (r/4) + r%4 >= lim - 4 half.  A hidden key's lo stays
+    //      finite, so its p = exp2(-inf + ...) is 0 all the same. ----
+    int64_t lim = a.Lkv - kb;
+    if (a.causal && qi + off + 1 - kb < lim) lim = qi + off + 1 - kb;
+    const int lim2 = (int)(lim < 0 ? 0 : (lim > PF_BKV ? PF_BKV : lim)) - 4 * half;
     float tv[16], tl[16];
-    float tmax = -INFINITY, tmax_lo = 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 k4 = *reinterpret_cast<const float4*>(&P.sc[8 * g + 4 * half]);
@@ -318,29 +330,36 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
-        float s, sl;
-        logit2(shh[r], srest[r], skv[i], cq, s, sl);
-        if (need_mask) {
-          const int64_t j = kb + 8 * g + 4 * half + i;
-          if (j >= a.Lkv || (a.causal && j > qi + off)) {
-            s = -INFINITY;
-            sl = 0.0f;
-          }
-        }
-        tv[r] = s;
-        tl[r] = sl;
-        pair_max(tmax, tmax_lo, s, sl);
+        logit2(shh[r], srest[r], skv[i], cq, tv[r], tl[r]);
+        tv[r] = 8 * g + i >= lim2 ? -INFINITY : tv[r];
       }
     }
+    // (hi, lo) maximum of the 16: the largest hi, then the lo of a key attaining it.  When keys tie in hi,
+    // one with a larger lo than the chosen key gets p a few ulp above 1, which is harmless.
+    float tmax = tv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, tv[r]);
+    float tmax_lo = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax_lo = tv[r] == tmax ? tl[r] : tmax_lo;
     pair_max(tmax, tmax_lo, __shfl_xor(tmax, 32, 64), __shfl_xor(tmax_lo, 32, 64));
-    float m_new = m_run, m_new_lo = m_run_lo;
-    pair_max(m_new, m_new_lo, tmax, tmax_lo);
-    const bool none = m_new == -INFINITY;
-    const float m_use = none ? 0.0f : m_new, m_use_lo = none ? 0.0f : m_new_lo;
-    // 0 on the first visible tile (m_run = -inf)
-    const float alpha = exp2f((m_run - m_use) + (m_run_lo - m_use_lo));
-    m_run = m_new;
-    m_run_lo = m_new_lo;
+    // ---- lazy running maximum: it moves to the tile maximum only where that exceeds it by more than
+    //      PF_TAU, and then for the whole wavefront at once, so most tiles skip rescaling O.  Otherwise
+    //      every p <= 2^PF_TAU, which the P~ scale 2^E leaves room for.  The first visible tile always
+    //      moves it (m_run = -inf), so a key that is alone at the maximum still gets p = 1 exactly. ----
+    const bool grow = tmax > m_run + PF_TAU;
+    if (__ballot(grow)) {  // wave-uniform
+      const float alpha = grow ? exp2_raw((m_run - tmax) + (m_run_lo - tmax_lo)) : 1.0f;  // 0 from -inf
+      m_run = grow ? tmax : m_run;
+      m_run_lo = grow ? tmax_lo : m_run_lo;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+    }
+    const bool none = m_run == -INFINITY;  // no visible key yet: every p below is exp2(-inf) = 0
+    const float m_use = none ? 0.0f : m_run, m_use_lo = none ? 0.0f : m_run_lo;
     float psum = 0.0f;
     uint32_t ph[8], pl[8];  // P~ fragments: k-step kk2 uses registers 4 kk2 .. 4 kk2 + 3
 #pragma unroll
@@ -350,8 +369,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
         const int r = 4 * g + i;
-        const float p0 = exp2f((tv[r] - m_use) + (tl[r] - m_use_lo));
-        const float p1 = exp2f((tv[r + 1] - m_use) + (tl[r + 1] - m_use_lo));
+        const float p0 = exp2_raw((tv[r] - m_use) + (tl[r] - m_use_lo));
+        const float p1 = exp2_raw((tv[r + 1] - m_use) + (tl[r + 1] - m_use_lo));
         psum += p0 + p1;
         _Float16 h0, l0, h1, l1;
         split_p(p0 * svv[i], h0, l0);
@@ -360,13 +379,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
         pl[r >> 1] = pack2(l0, l1);
       }
     }
-    l_run = l_run * alpha + psum;
-    if (alpha != 1.0f) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-    }
+    l_run += psum;
     // ---- O^T [128 d x 32 queries] += V^T P~^T over these 32 keys (2 k-steps of 16).  The V^T operand of
     //      lane (d = 32 dt + l % 32, k-group g = l / 32) holds keys 16 kk2 + 4 g + 0..3 and
     //      16 kk2 + 8 + 4 g + 0..3: the same keys, in the same order, as the P~ registers ----
@@ -605,7 +618,7 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     pair_max(m_new, m_new_lo, tmax, tmax_lo);
     const bool none = m_new == -INFINITY;
     const float m_use = none ? 0.0f : m_new, m_use_lo = none ? 0.0f : m_new_lo;
-    const float alpha = exp2f((m_run - m_use) + (m_run_lo - m_use_lo));
+    const float alpha = exp2_raw((m_run - m_use) + (m_run_lo - m_use_lo));
     m_run = m_new;
     m_run_lo = m_new_lo;
     float psum = 0.0f;
@@ -614,8 +627,8 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
-        const float p0 = exp2f((tv[mt][i] - m_use) + (tl[mt][i] - m_use_lo));
-        const float p1 = exp2f((tv[mt][i + 1] - m_use) + (tl[mt][i + 1] - m_use_lo));
+        const float p0 = exp2_raw((tv[mt][i] - m_use) + (tl[mt][i] - m_use_lo));
+        const float p1 = exp2_raw((tv[mt][i + 1] - m_use) + (tl[mt][i + 1] - m_use_lo));
         psum += p0 + p1;
         _Float16 h0, l0, h1, l1;
         split_p(p0 * __builtin_amdgcn_ldexpf(svr[mt][i], E), h0, l0);
