@@ -138,20 +138,29 @@ constexpr int waitcnt_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
   return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
 }
-// INT16 K rows in LDS: [key][16 chunks of 8 d], chunk c of key j at j * 16 + (c ^ (j & 15)), so the 16
-// keys one 16-byte fragment read touches sit in 16 different bank groups
+// K rows (FP16 halves) in LDS: [key][16 chunks of 8 d], chunk c of key j at j * 16 + (c ^ (j & 15)), so the
+// 16 keys one 16-byte fragment read touches sit in 16 different bank groups
 __device__ __forceinline__ int kv_pos(int key, int c) { return key * 16 + (c ^ (key & 15)); }
-// INT16 V rows: chunk c of key j at j * 16 + (c ^ (j & 3)).  A transposing read touches 4 consecutive keys,
-// which this spreads over 4 chunk slots; XOR-ing only the low two chunk bits leaves the d-tile and key-block
-// offsets of every read plain immediates, so one address register per lane serves all of them.
-__device__ __forceinline__ int v_pos(int key, int c) { return key * 16 + (c ^ (key & 3)); }
+// V rows for the transposing reads: chunk c of key j at j * 16 + (c ^ vt_swz(j)).  A ds_read_b64_tr_b16 of a
+// wavefront moves 512 bytes in two halves of 32 lanes; the swizzle spreads each half's 16 chunks over the 16
+// distinct 16-byte bank groups of a 256-byte row, per read pattern:
+//   VT_PREFILL: each half reads 4 consecutive keys x 4 consecutive chunks: XOR the chunk's top 2 bits with j % 4;
+//   VT_DECODE:  each half reads 8 consecutive keys x 2 consecutive chunks: XOR chunk bits 1..3 with j % 8.
+constexpr int VT_PREFILL = 0, VT_DECODE = 1;
+template <int L>
+__device__ __forceinline__ int vt_swz(int key) {
+  return L == VT_PREFILL ? (key & 3) << 2 : (key & 7) << 1;
+}
+template <int L>
+__device__ __forceinline__ int vt_pos(int key, int c) { return key * 16 + (c ^ vt_swz<L>(key)); }
 
 // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element (i % 4) of the 8-byte rows read by
 // lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  So when lane r of a group reads V[k0 + r/4][d0 + 4 (r % 4) .. + 3]
 // (4 keys x 16 d), lane i receives V[k0 .. k0 + 3][d0 + i]: four keys of one d, the V^T operand layout.
+template <int L>
 __device__ __forceinline__ v4i16 read_vt(const uint4* v_rows, int k0, int d0, int r) {
   const int key = k0 + (r >> 2), d = d0 + 4 * (r & 3);
-  const char* src = reinterpret_cast<const char*>(v_rows) + v_pos(key, d >> 3) * 16 + (d & 7) * 2;
+  const char* src = reinterpret_cast<const char*>(v_rows) + vt_pos<L>(key, d >> 3) * 16 + (d & 7) * 2;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src));
 }
 __device__ __forceinline__ uint4 join_v4i16(const v4i16& a, const v4i16& b) {
@@ -175,7 +184,7 @@ struct PfRaw {
   float sc[64];
 };
 // The tile's Dual-FP16 operands, unpacked once for all wavefronts: K halves in the kv_pos layout, V halves
-// in the v_pos layout, the k-scales, then the v-scales times 2^E.
+// in the VT_PREFILL layout, the k-scales, then the v-scales times 2^E.
 struct PfPlanes {
   uint4 kh[PF_BKV * 16];
   uint4 kl[PF_BKV * 16];
@@ -267,8 +276,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
     P.kh[kv_pos(ckey, cchunk)] = hi;
     P.kl[kv_pos(ckey, cchunk)] = lo;
     unpack8(R.v[tid], hi, lo);
-    P.vh[v_pos(ckey, cchunk)] = hi;
-    P.vl[v_pos(ckey, cchunk)] = lo;
+    P.vh[vt_pos<VT_PREFILL>(ckey, cchunk)] = hi;
+    P.vl[vt_pos<VT_PREFILL>(ckey, cchunk)] = lo;
     if (wave == 0) {
       const float s = R.sc[lane];
       P.sc[lane] = lane < 32 ? s : __builtin_amdgcn_ldexpf(s, E);
@@ -391,8 +400,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const int d0 = 32 * dt + 16 * (vq & 1);
-        const uint4 VH = join_v4i16(read_vt(P.vh, k1, d0, vi), read_vt(P.vh, k1 + 8, d0, vi));
-        const uint4 VL = join_v4i16(read_vt(P.vl, k1, d0, vi), read_vt(P.vl, k1 + 8, d0, vi));
+        const uint4 VH = join_v4i16(read_vt<VT_PREFILL>(P.vh, k1, d0, vi), read_vt<VT_PREFILL>(P.vh, k1 + 8, d0, vi));
+        const uint4 VL = join_v4i16(read_vt<VT_PREFILL>(P.vl, k1, d0, vi), read_vt<VT_PREFILL>(P.vl, k1 + 8, d0, vi));
         O[dt] = mfma32(VH, PH, O[dt]);
         O[dt] = mfma32(VL, PH, O[dt]);
         O[dt] = mfma32(VH, PL, O[dt]);
@@ -453,7 +462,7 @@ constexpr int DC_PART = 4 + D;                // floats per partial: m_hi, m_lo,
 constexpr int DC_NDMA = 17;                   // direct-to-LDS transfers per lane per step
 
 // One step's V in a wavefront-private LDS stage, filled by direct-to-LDS transfers: [32 keys][16 chunks of
-// 8 d] INT16 in the v_pos layout, then the 32 k-scales and 32 v-scales.  K needs no LDS: its MFMA operand
+// 8 d] INT16 in the VT_DECODE layout, then the 32 k-scales and 32 v-scales.  K needs no LDS: its MFMA operand
 // layout (one key's 8 consecutive d per lane) is a plain 16-byte load into registers.
 struct DcStage {
   uint4 v[DC_SUB * 16];
@@ -509,7 +518,7 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   const float cq = qvalid ? a.qs[b * a.qs_st[0] + hq * a.qs_st[2]] * a.scale_log2 : 0.0f;
 
   // one step's loads: K straight into operand registers (key 16 mt + qc, d 32 ks + 8 grp .. + 7), V and the
-  // scales direct-to-LDS (position p = 64 i + l holds key p / 16, chunk (p % 16) ^ key)
+  // scales direct-to-LDS (position p = 64 i + l holds key p / 16 in the VT_DECODE layout)
   const int64_t kvs1 = a.kv_st[1], ss1 = a.kvs_st[1];
   auto issue = [&](DcStage& S, uint4 (&kr)[2][4], int64_t j0) {
 #pragma unroll
@@ -522,7 +531,7 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int p = 64 * i + lane, key = p >> 4, c = (p & 15) ^ (key & 3);
+      const int p = 64 * i + lane, key = p >> 4, c = (p & 15) ^ vt_swz<VT_DECODE>(key);
       int64_t j = j0 + key;
       if (j > a.Lkv - 1) j = a.Lkv - 1;
       dma16(vbase + j * kvs1 + 8 * c, &S.v[64 * i]);
@@ -550,7 +559,7 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) vtr[dt][hh] = read_vt(S.v, 16 * hh + 4 * grp, 16 * dt, qc);
+      for (int hh = 0; hh < 2; ++hh) vtr[dt][hh] = read_vt<VT_DECODE>(S.v, 16 * hh + 4 * grp, 16 * dt, qc);
     float4 skq[2], svq[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
