@@ -42,7 +42,118 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="skip the per-step measurements of the other rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of each M=2048 shape in the CPU sample")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (scale run for the HBM byte counters)")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="only print the HBM traffic summary of the rocprofv3 --pmc runs under DIR "
+                         "(fetch/, write/, copy_fetch/, copy_write/)")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (MiB)")
     return ap.parse_args()
+
+
+# ------------------------------------------------------------------ HBM traffic from stored counters
+GEMM_SRC = os.path.join(ROOT, "error_compensated_gemm_amd", "csrc", "gemm_comp.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_comp_llama3_8b_hbm_traffic.md")
+TRAFFIC_TAG = "traffic-json: "
+
+
+def source_sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def kernel_symbol(variant):
+    """Template symbol of a GEMM variant name, as rocprofv3 prints it ("gemm_comp_kernel 256x128 P2" ->
+    "gemm_comp_kernel<2, 256, 128, true, false>": FP16 parts, block tile, a_lo used, b_lo used)."""
+    parts = variant.split()
+    if len(parts) != 3 or parts[0] != "gemm_comp_kernel":
+        return None
+    bm, bn = parts[1].split("x")
+    p = int(parts[2][1:])
+    return f"gemm_comp_kernel<2, {bm}, {bn}, {str(p >= 2).lower()}, {str(p >= 3).lower()}>"
+
+
+def stored_traffic(variant):
+    """HBM bytes per launch of `variant` from the committed counter summary, or None when there is none or
+    the GEMM source changed since the counters were taken."""
+    sym = kernel_symbol(variant)
+    if sym is None or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = next((json.loads(l[len(TRAFFIC_TAG):]) for l in f if l.startswith(TRAFFIC_TAG)), None)
+    if rec is None or rec.get("source_sha256") != source_sha256(GEMM_SRC):
+        return None
+    k = rec.get("kernels", {}).get(sym)
+    return None if k is None else k["traffic_bytes_per_launch"]
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy calibration: 5 copies of {mib} MiB done", flush=True)
+
+
+def summarize_pmc(d, copy_mib):
+    """Markdown summary of FETCH_SIZE / WRITE_SIZE (KiB per dispatch) for every GEMM kernel of a bench run,
+    each scaled by the ratio of known bytes to the counter's reading for a plain copy of copy_mib MiB."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def read(sub):
+        vals = defaultdict(list)
+        for f in glob.glob(os.path.join(d, sub, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write, cf, cw = read("fetch"), read("write"), read("copy_fetch"), read("copy_write")
+    copy_name = lambda v: max((k for k in v if "copyBuffer" in k), key=lambda k: len(v[k]))
+    nbytes = copy_mib * (1 << 20)
+    cfk = sum(cf[copy_name(cf)]) / len(cf[copy_name(cf)])
+    cwk = sum(cw[copy_name(cw)]) / len(cw[copy_name(cw)])
+    ff, fw = nbytes / (cfk * 1024), nbytes / (cwk * 1024)
+    kernels = {}
+    rows = []
+    for name in sorted(fetch):
+        if "gemm_comp_kernel<" not in name and "gemm_skinny_kernel<" not in name:
+            continue
+        sym = name[name.index("gemm_"):].split(">")[0] + ">"
+        fk = sum(fetch[name]) / len(fetch[name])
+        wk = sum(write[name]) / len(write[name]) if name in write else float("nan")
+        tb = fk * 1024 * ff + wk * 1024 * fw
+        kernels[sym] = {"dispatches": len(fetch[name]), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                        "traffic_bytes_per_launch": round(tb)}
+        rows.append(f"| `{sym}` | {len(fetch[name])} | {fk:.1f} | {wk:.1f} | {tb / 1e6:.2f} |")
+    rec = {"source_sha256": source_sha256(GEMM_SRC), "fetch_factor": round(ff, 4), "write_factor": round(fw, 4),
+           "copy_mib": copy_mib, "kernels": kernels}
+    print("# HBM traffic of the compensated-GEMM kernels: bench.py (Llama-3-8B linear shapes)\n")
+    print("Commands (from the repository root on one MI355X, ROCm 7.2; D = gpurun_out/traffic):\n")
+    print("```")
+    print("cd /tmp && export TMPDIR=/tmp")
+    for c, sub, prog in (("FETCH_SIZE", "fetch", "--steps 2 --warmup 1 --no-cpu --no-rows"),
+                         ("WRITE_SIZE", "write", "--steps 2 --warmup 1 --no-cpu --no-rows"),
+                         ("FETCH_SIZE", "copy_fetch", f"--copy-calibration {copy_mib}"),
+                         ("WRITE_SIZE", "copy_write", f"--copy-calibration {copy_mib}")):
+        print(f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $D/{sub} -o pmc -- "
+              f"python3 /root/repo/bench.py {prog}")
+    print(f"python3 /root/repo/bench.py --summarize-pmc $D --copy-mib {copy_mib}")
+    print("```\n")
+    print(f"Scale: a plain device copy of {copy_mib} MiB reads {cfk:.0f} KiB by FETCH_SIZE and writes {cwk:.0f} KiB "
+          f"by WRITE_SIZE per dispatch, so FETCH_SIZE x {ff:.3f} and WRITE_SIZE x {fw:.3f} give bytes.  The "
+          "counters see traffic below the L2 (to the memory-side cache and HBM).\n")
+    print("| kernel | dispatches | FETCH_SIZE (KiB/launch) | WRITE_SIZE (KiB/launch) | traffic (MB/launch) |")
+    print("|---|---|---|---|---|")
+    print("\n".join(rows))
+    print("\nbench.py reads the record below and reports the traffic of its dominant kernel only while "
+          "gemm_comp.hip still has this SHA-256.\n")
+    print(TRAFFIC_TAG + json.dumps(rec))
 
 
 class Timer:
@@ -88,9 +199,12 @@ def time_fn(fn, reps, warm=2):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.copy_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the hot path shards without communication and multi-GPU runs are not part of it",
               file=sys.stderr)
         sys.exit(2)
@@ -101,6 +215,9 @@ def main():
     import error_compensated_gemm_amd as heal
     import workloads
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     heal.load()
     torch.cuda.set_device(0)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
@@ -180,7 +297,7 @@ def main():
         "peak": PEAK_F16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": stored_traffic(dom_name),
         "kernel": dom_name,
         "avg_launch_us": round(avg_dur * 1e6, 2),
         "launches_per_step": dom["launches"] // args.steps,

@@ -24,7 +24,7 @@ const char* heal_status_str(int status) {
     case HEAL_ERR_STRIDE: return "HEAL_ERR_STRIDE: a leading dimension or stride is too small";
     case HEAL_ERR_ALIGN: return "HEAL_ERR_ALIGN: pointer not 16-byte aligned or leading dimension not a multiple of 8";
     case HEAL_ERR_DTYPE: return "HEAL_ERR_DTYPE: dtype not accepted by this call";
-    case HEAL_ERR_UNSUPPORTED: return "HEAL_ERR_UNSUPPORTED: valid request not implemented by this build";
+    case HEAL_ERR_UNSUPPORTED: return "HEAL_ERR_UNSUPPORTED: valid request not implemented by this library";
     case HEAL_ERR_LAUNCH: return "HEAL_ERR_LAUNCH: the HIP runtime refused a kernel launch";
     case HEAL_ERR_WORKSPACE: return "HEAL_ERR_WORKSPACE: workspace missing or too small";
     default: return "HEAL: unknown status";

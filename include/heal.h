@@ -54,7 +54,7 @@ typedef enum {
   HEAL_ERR_STRIDE = 3,      /* a leading dimension / stride is smaller than the row it must hold */
   HEAL_ERR_ALIGN = 4,       /* pointer not 16-byte aligned, or leading dimension not a multiple of 8 */
   HEAL_ERR_DTYPE = 5,       /* a dtype code that the call does not accept */
-  HEAL_ERR_UNSUPPORTED = 6, /* a valid request this build does not implement (e.g. head_dim != 128) */
+  HEAL_ERR_UNSUPPORTED = 6, /* a valid request this library does not implement (e.g. head_dim != 128) */
   HEAL_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
   HEAL_ERR_WORKSPACE = 8    /* workspace missing or smaller than heal_attn_workspace_bytes() */
 } heal_status;
