@@ -299,9 +299,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 // ------------------------------------------------------------------------------------------- skinny M
 // M <= 64: the problem is a stream over B (N x K 16-bit values read once from HBM) with a small A that
-// stays in L2.  A workgroup of 8 wavefronts owns 16 output columns; its wavefronts split K in 32-wide steps
-// and each accumulates a 16 x 16 block per 16 rows of A with v_mfma_f32_16x16x32; the 8 partial blocks
-// are added in wavefront order through LDS (fixed order: bitwise reproducible).
+// stays in L2.  A workgroup of 8 wavefronts owns 16 NC output columns; its wavefronts split K in 32-wide
+// steps and each accumulates 16 x 16 blocks (16 rows of A x 16 columns) with v_mfma_f32_16x16x32, so each
+// A fragment loaded feeds NC MFMAs and A is re-read from L2 once per workgroup.  The 8 partial blocks are
+// added in wavefront order through LDS (fixed order: bitwise reproducible).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int PART>
@@ -317,20 +318,25 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f3
 
 constexpr int kSkWaves = 8;
 
-template <int PART, int MT, bool ALO, bool BLO>
+template <int PART, int MT, int NC, bool ALO, bool BLO>
 __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
     const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
     const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
     int64_t ldc) {
-  __shared__ float red[kSkWaves][MT][4][64];
+  __shared__ float red[kSkWaves][MT * NC][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cl = lane & 15, kg = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  int64_t n = n0 + cl;
-  if (n > N - 1) n = N - 1;  // columns past N feed outputs that are never stored
-  const uint16_t* brow = bh + n * ldb;
-  const uint16_t* blrow = BLO ? bl + n * ldb : nullptr;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NC;
+  const uint16_t* brow[NC];
+  const uint16_t* blrow[NC];
+#pragma unroll
+  for (int nc = 0; nc < NC; ++nc) {
+    int64_t n = n0 + 16 * nc + cl;
+    if (n > N - 1) n = N - 1;  // columns past N feed outputs that are never stored
+    brow[nc] = bh + n * ldb;
+    blrow[nc] = BLO ? bl + n * ldb : nullptr;
+  }
   const uint16_t* arow[MT];
   const uint16_t* alrow[MT];
 #pragma unroll
@@ -343,46 +349,103 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   const int64_t nsteps = (K + 31) / 32, nfull = K / 32;
   const int64_t klast = ((K + 7) / 8 - 1) * 8;
   const int64_t s0 = nsteps * wave / kSkWaves, s1 = nsteps * (wave + 1) / kSkWaves;
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto step = [&](int64_t s, bool tail) {
-    const int64_t k = s * 32 + 8 * kg;
-    uint4 b = load_chunk(brow, k, klast);
-    uint4 b2 = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (BLO) b2 = load_chunk(blrow, k, klast);
-    if (tail) {  // padding past K may hold any bits (even NaN patterns): clear both operands
-      b = mask_chunk(b, K - k);
-      if constexpr (BLO) b2 = mask_chunk(b2, K - k);
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      uint4 a = load_chunk(arow[mt], k, klast);
-      if (tail) a = mask_chunk(a, K - k);
-      acc[mt] = mfma16<PART>(a, b, acc[mt]);
-      if constexpr (BLO) acc[mt] = mfma16<PART>(a, b2, acc[mt]);
-      if constexpr (ALO) {
-        uint4 a2 = load_chunk(alrow[mt], k, klast);
-        if (tail) a2 = mask_chunk(a2, K - k);
-        acc[mt] = mfma16<PART>(a2, b, acc[mt]);
-      }
-    }
-  };
-  const int64_t s1f = s1 < nfull ? s1 : nfull;
-#pragma unroll 4
-  for (int64_t s = s0; s < s1f; ++s) step(s, false);
-  if (s1 > s1f) step(s1f, true);  // the one partial step (K % 32 != 0) belongs to the last wavefront
+  f32x4 acc[MT][NC];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][mt][i][lane] = acc[mt][i];
+    for (int nc = 0; nc < NC; ++nc) acc[mt][nc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma1 = [&](const uint4 (&a)[MT], const uint4 (&a2)[ALO ? MT : 1], const uint4 (&b)[NC],
+                  const uint4 (&b2)[BLO ? NC : 1]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        acc[mt][nc] = mfma16<PART>(a[mt], b[nc], acc[mt][nc]);
+        if constexpr (BLO) acc[mt][nc] = mfma16<PART>(a[mt], b2[nc], acc[mt][nc]);
+        if constexpr (ALO) acc[mt][nc] = mfma16<PART>(a2[mt], b[nc], acc[mt][nc]);
+      }
+  };
+  // one K step with the columns at or past K cleared (the partial last step; padding past K may hold any
+  // bits, even NaN patterns, so both operands are cleared)
+  auto tail_step = [&](int64_t s) {
+    const int64_t k = s * 32 + 8 * kg;
+    uint4 a[MT], a2[ALO ? MT : 1], b[NC], b2[BLO ? NC : 1];
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) {
+      b[nc] = mask_chunk(load_chunk(brow[nc], k, klast), K - k);
+      if constexpr (BLO) b2[nc] = mask_chunk(load_chunk(blrow[nc], k, klast), K - k);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      a[mt] = mask_chunk(load_chunk(arow[mt], k, klast), K - k);
+      if constexpr (ALO) a2[mt] = mask_chunk(load_chunk(alrow[mt], k, klast), K - k);
+    }
+    mma1(a, a2, b, b2);
+  };
+  const int64_t s1f = s1 < nfull ? s1 : nfull;
+  // Full steps in groups of U, software-pipelined through registers: the next group's loads are issued
+  // before the current group's MFMAs, so two groups of B (the HBM stream) are in flight per wavefront.  The
+  // prefetch address is clamped to the last full group instead of branching (a conditional load block
+  // makes the compiler wait for every outstanding load at its boundary).
+  constexpr int U = (MT * NC) >= 4 ? 1 : 4 / (MT * NC);
+  struct Grp {
+    uint4 b[U][NC], b2[U][BLO ? NC : 1], a[U][MT], a2[U][ALO ? MT : 1];
+  };
+  auto load = [&](Grp& g, int64_t s) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (s + u) * 32 + 8 * kg;
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        g.b[u][nc] = load_chunk(brow[nc], k, klast);
+        if constexpr (BLO) g.b2[u][nc] = load_chunk(blrow[nc], k, klast);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        g.a[u][mt] = load_chunk(arow[mt], k, klast);
+        if constexpr (ALO) g.a2[u][mt] = load_chunk(alrow[mt], k, klast);
+      }
+    }
+  };
+  auto mma = [&](const Grp& g) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) mma1(g.a[u], g.a2[u], g.b[u], g.b2[u]);
+  };
+  const int64_t ng = s1f > s0 ? (s1f - s0) / U : 0;  // full groups of this wavefront
+  const int64_t s_last = s0 + (ng - 1) * U;           // first step of the last full group
+  if (ng > 0) {
+    Grp g0, g1;
+    load(g0, s0);
+    int64_t gi = 0;
+    for (; gi + 1 < ng; gi += 2) {
+      load(g1, s0 + (gi + 1) * U);
+      mma(g0);
+      const int64_t sn = s0 + (gi + 2) * U;
+      load(g0, sn < s_last ? sn : s_last);  // past the end: a re-read of the last group, never used
+      mma(g1);
+    }
+    if (gi < ng) mma(g0);
+  }
+  for (int64_t s = s0 + ng * U; s < s1f; ++s) {  // fewer than U full steps left
+    Grp g;
+    load(g, s);
+    mma1(g.a[0], g.a2[0], g.b[0], g.b2[0]);
+  }
+  if (s1 > s1f) tail_step(s1f);  // the one partial step (K % 32 != 0) belongs to the last wavefront
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][mt * NC + nc][i][lane] = acc[mt][nc][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < MT * 4 * 64; idx += 64 * kSkWaves) {
-    const int mt = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
+  for (int idx = threadIdx.x; idx < MT * NC * 4 * 64; idx += 64 * kSkWaves) {
+    const int blk = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
+    const int mt = blk / NC, nc = blk % NC;
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kSkWaves; ++w) s += red[w][mt][i][l];
-    const int64_t row = 16 * mt + 4 * (l >> 4) + i, col = n0 + (l & 15);
+    for (int w = 0; w < kSkWaves; ++w) s += red[w][blk][i][l];
+    const int64_t row = 16 * mt + 4 * (l >> 4) + i, col = n0 + 16 * nc + (l & 15);
     if (row < M && col < N) {
       const int e = (ea ? ea[row] : 0) + (eb ? eb[col] : 0);
       C[row * ldc + col] = __builtin_amdgcn_ldexpf(s, -e);
@@ -390,23 +453,34 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   }
 }
 
-template <int PART, int MT>
-hipError_t launch_skinny_mt(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
+// Column blocks per skinny workgroup.  Each workgroup re-reads A (M x K) from L2, so more columns per
+// workgroup save that traffic, but fewer workgroups keep fewer loads in flight.  Measured on MI355X at
+// K = 4096 / 14336 (M = 1, 16, 32): N = 4096 runs best with 1 block (256 workgroups), N = 14336 with 4
+// blocks for M <= 16 (224 workgroups: M = 16 36 -> 28 us) and 2 for M <= 32.
+int skinny_nc(int64_t M, int64_t N) {
+  const int64_t cap = M <= 16 ? 4 : (M <= 32 ? 2 : 1);
+  int64_t nc = 1;
+  while (nc < cap && N / (16 * 2 * nc) >= 224) nc *= 2;
+  return (int)nc;
+}
+
+template <int PART, int MT, int NC>
+hipError_t launch_skinny_nc(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
                             const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
                             const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * kSkWaves);
+  const dim3 grid((unsigned)((N + 16 * NC - 1) / (16 * NC))), block(64 * kSkWaves);
   if (al && bl)
-    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, true, true>), grid, block, 0, stream, M, N, K, ah, al, ea,
-                       lda, bh, bl, eb, ldb, c, ldc);
-  else if (al)
-    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, true, false>), grid, block, 0, stream, M, N, K, ah, al, ea,
-                       lda, bh, bl, eb, ldb, c, ldc);
-  else if (bl)
-    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, false, true>), grid, block, 0, stream, M, N, K, ah, al, ea,
-                       lda, bh, bl, eb, ldb, c, ldc);
-  else
-    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, false, false>), grid, block, 0, stream, M, N, K, ah, al,
+    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, NC, true, true>), grid, block, 0, stream, M, N, K, ah, al,
                        ea, lda, bh, bl, eb, ldb, c, ldc);
+  else if (al)
+    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, NC, true, false>), grid, block, 0, stream, M, N, K, ah, al,
+                       ea, lda, bh, bl, eb, ldb, c, ldc);
+  else if (bl)
+    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, NC, false, true>), grid, block, 0, stream, M, N, K, ah, al,
+                       ea, lda, bh, bl, eb, ldb, c, ldc);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, NC, false, false>), grid, block, 0, stream, M, N, K, ah,
+                       al, ea, lda, bh, bl, eb, ldb, c, ldc);
   return hipGetLastError();
 }
 
@@ -414,9 +488,17 @@ template <int PART>
 hipError_t launch_skinny(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
                          const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
                          const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
-  if (M <= 16) return launch_skinny_mt<PART, 1>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
-  if (M <= 32) return launch_skinny_mt<PART, 2>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
-  return launch_skinny_mt<PART, 4>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  const int nc = skinny_nc(M, N);
+  if (M <= 16) {
+    if (nc >= 4) return launch_skinny_nc<PART, 1, 4>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    if (nc == 2) return launch_skinny_nc<PART, 1, 2>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    return launch_skinny_nc<PART, 1, 1>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  }
+  if (M <= 32) {
+    if (nc >= 2) return launch_skinny_nc<PART, 2, 2>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    return launch_skinny_nc<PART, 2, 1>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  }
+  return launch_skinny_nc<PART, 4, 1>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
 }
 
 template <int PART, int BM, int BN>
@@ -481,11 +563,19 @@ const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
   if (M <= 0 || N <= 0 || products < 1 || products > 3) return "none";
   const TileKind kind = choose_tile(M, N);
   if (kind == kSkinny) {
-    static const char* sk[3][3] = {
-        {"gemm_skinny_kernel M<=16 P1", "gemm_skinny_kernel M<=16 P2", "gemm_skinny_kernel M<=16 P3"},
-        {"gemm_skinny_kernel M<=32 P1", "gemm_skinny_kernel M<=32 P2", "gemm_skinny_kernel M<=32 P3"},
-        {"gemm_skinny_kernel M<=64 P1", "gemm_skinny_kernel M<=64 P2", "gemm_skinny_kernel M<=64 P3"}};
-    return sk[M <= 16 ? 0 : (M <= 32 ? 1 : 2)][products - 1];
+    // [rows class][column blocks 1, 2, 4][products]
+    static const char* sk[3][3][3] = {
+        {{"gemm_skinny_kernel M<=16 NC1 P1", "gemm_skinny_kernel M<=16 NC1 P2", "gemm_skinny_kernel M<=16 NC1 P3"},
+         {"gemm_skinny_kernel M<=16 NC2 P1", "gemm_skinny_kernel M<=16 NC2 P2", "gemm_skinny_kernel M<=16 NC2 P3"},
+         {"gemm_skinny_kernel M<=16 NC4 P1", "gemm_skinny_kernel M<=16 NC4 P2", "gemm_skinny_kernel M<=16 NC4 P3"}},
+        {{"gemm_skinny_kernel M<=32 NC1 P1", "gemm_skinny_kernel M<=32 NC1 P2", "gemm_skinny_kernel M<=32 NC1 P3"},
+         {"gemm_skinny_kernel M<=32 NC2 P1", "gemm_skinny_kernel M<=32 NC2 P2", "gemm_skinny_kernel M<=32 NC2 P3"},
+         {"none", "none", "none"}},
+        {{"gemm_skinny_kernel M<=64 NC1 P1", "gemm_skinny_kernel M<=64 NC1 P2", "gemm_skinny_kernel M<=64 NC1 P3"},
+         {"none", "none", "none"},
+         {"none", "none", "none"}}};
+    const int nc = skinny_nc(M, N);
+    return sk[M <= 16 ? 0 : (M <= 32 ? 1 : 2)][nc == 4 ? 2 : nc - 1][products - 1];
   }
   return names[kind][products - 1];
 }
