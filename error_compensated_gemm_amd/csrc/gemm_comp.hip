@@ -70,6 +70,13 @@ __device__ __forceinline__ uint4 mask_chunk(uint4 v, int64_t valid) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// s_waitcnt immediate: at most N vector-memory operations outstanding, all LDS operations done
+template <int N>
+constexpr int waitcnt_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
+}
+
 // one 16-byte direct global -> LDS transfer per lane: lane l's bytes land at lds_wave_base + 16 l
 __device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
@@ -88,10 +95,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int APLANE = BM * kCPR, BPLANE = BN * kCPR;  // uint4 chunks per operand plane
   constexpr int STAGE = NA * APLANE + NB * BPLANE;
   static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small for the loader");
-  // two stages as two distinct objects: the compiler can tell the stage being read from the one the
-  // direct-to-LDS loads are filling, so no wait on those loads is placed before the fragment reads
+  // Stages as distinct objects: the compiler can tell the stage being read from the ones the
+  // direct-to-LDS loads are filling, so no wait on those loads is placed before the fragment reads.  Three
+  // stages where they fit in the 160 KB of LDS, so each stage's transfers have two stages of MFMAs to land
+  // (a transfer's round trip under load is longer than one stage of MFMAs).
+  constexpr int NST = (3 * STAGE * 16 + (BM + BN) * 4 <= 160 * 1024) ? 3 : 2;
   __shared__ uint4 lds0[STAGE];
   __shared__ uint4 lds1[STAGE];
+  __shared__ uint4 lds2[NST == 3 ? STAGE : 1];
   __shared__ int exps_s[BM + BN];
 
   // ---- tile of this workgroup (XCD-contiguous, then grouped by 4 tile rows) ----
@@ -203,35 +214,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int frow = lane & 31, fhalf = lane >> 5;
+  // the MFMA operand fragments of one 16-wide k step of a stage
+  struct Frag {
+    uint4 a[NA][TM], b[NB][TN];
+  };
+  auto read_frags = [&](const uint4* s, int ks, Frag& F) {
+    const int c = 2 * ks + fhalf;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * WN + j * 32 + frow;
+#pragma unroll
+      for (int p = 0; p < NB; ++p) F.b[p][j] = s[NA * APLANE + p * BPLANE + r * kCPR + (c ^ swz(r))];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WM + i * 32 + frow;
+#pragma unroll
+      for (int p = 0; p < NA; ++p) F.a[p][i] = s[p * APLANE + r * kCPR + (c ^ swz(r))];
+    }
+  };
+  auto mma = [&](const Frag& F) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        acc[i][j] = mfma32<PART>(F.a[0][i], F.b[0][j], acc[i][j]);
+        if constexpr (BLO) acc[i][j] = mfma32<PART>(F.a[0][i], F.b[NB - 1][j], acc[i][j]);
+        if constexpr (ALO) acc[i][j] = mfma32<PART>(F.a[NA - 1][i], F.b[0][j], acc[i][j]);
+      }
+  };
   auto compute = [&](const uint4* s) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int c = 2 * ks + fhalf;
-      uint4 fa[NA][TM], fb[NB][TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * WN + j * 32 + frow;
-#pragma unroll
-        for (int p = 0; p < NB; ++p) fb[p][j] = s[NA * APLANE + p * BPLANE + r * kCPR + (c ^ swz(r))];
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + frow;
-#pragma unroll
-        for (int p = 0; p < NA; ++p) fa[p][i] = s[p * APLANE + r * kCPR + (c ^ swz(r))];
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          acc[i][j] = mfma32<PART>(fa[0][i], fb[0][j], acc[i][j]);
-          if constexpr (BLO) acc[i][j] = mfma32<PART>(fa[0][i], fb[NB - 1][j], acc[i][j]);
-          if constexpr (ALO) acc[i][j] = mfma32<PART>(fa[NA - 1][i], fb[0][j], acc[i][j]);
-        }
+      Frag F;
+      read_frags(s, ks, F);
+      mma(F);
     }
   };
 
-  // ---- main loop, two stages per trip so each stage is a fixed LDS object.  The steady state (both
+  // ---- main loop, unrolled over the stages so each stage is a fixed LDS object.  The steady state (all
   //      prefetched tiles full) is branch-free, so the transfers, fragment reads and MFMAs of a stage
   //      share one scheduling region and are interleaved: reads of the first 16-wide k step, then one
   //      transfer, a few MFMAs and the next k step's reads in turn.  Issuing the transfers ahead of the
@@ -252,30 +273,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);  // the remaining MFMAs
   };
-  if (nk > 0) fill(lds0, 0);
-  __syncthreads();
-  int kt = 0;
-  // (measured on 256-wide tiles only; the 256 x 128 tiles ran 5 % slower with it, so they keep the
-  // plain loop below)
-  for (; BN == 256 && kt + 2 < nfull; kt += 2) {
-    dma_stage(lds1, (int64_t)(kt + 1) * kBK);
-    compute(lds0);
-    interleave();
+  if constexpr (NST == 3) {
+    // Three stages: the step for tile kt issues tile kt + 2's transfers, multiplies tile kt, then waits
+    // only until this thread's transfers of tile kt + 1 have landed (tile kt + 2's may still fly) and
+    // meets the other wavefronts at a plain barrier (__syncthreads would also drain tile kt + 2).
+    auto wait_then_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NDMA>());
+      __builtin_amdgcn_s_barrier();
+    };
+    if (nk > 0) fill(lds0, 0);
+    if (nk > 1) fill(lds1, 1);
     __syncthreads();
-    dma_stage(lds0, (int64_t)(kt + 2) * kBK);
-    compute(lds1);
-    interleave();
+    int kt = 0;
+    for (; kt + 4 < nfull; kt += 3) {
+      dma_stage(lds2, (int64_t)(kt + 2) * kBK);
+      compute(lds0);
+      interleave();
+      wait_then_barrier();
+      dma_stage(lds0, (int64_t)(kt + 3) * kBK);
+      compute(lds1);
+      interleave();
+      wait_then_barrier();
+      dma_stage(lds1, (int64_t)(kt + 4) * kBK);
+      compute(lds2);
+      interleave();
+      wait_then_barrier();
+    }
+    for (; kt < nk; ++kt) {  // the last tiles (tiles kt and kt + 1 are already in their stages)
+      const int si = kt % 3;
+      if (kt + 2 < nk) fill(si == 0 ? lds2 : (si == 1 ? lds0 : lds1), kt + 2);
+      compute(si == 0 ? lds0 : (si == 1 ? lds1 : lds2));
+      __syncthreads();
+    }
+  } else {
+    if (nk > 0) fill(lds0, 0);
     __syncthreads();
+    int kt = 0;
+    // (measured on 256-wide tiles only; the 256 x 128 tiles ran 5 % slower with it, so they keep the
+    // plain loop below)
+    for (; BN == 256 && kt + 2 < nfull; kt += 2) {
+      dma_stage(lds1, (int64_t)(kt + 1) * kBK);
+      compute(lds0);
+      interleave();
+      __syncthreads();
+      dma_stage(lds0, (int64_t)(kt + 2) * kBK);
+      compute(lds1);
+      interleave();
+      __syncthreads();
+    }
+    for (; kt + 1 < nk; kt += 2) {
+      fill(lds1, kt + 1);
+      compute(lds0);
+      __syncthreads();
+      if (kt + 2 < nk) fill(lds0, kt + 2);
+      compute(lds1);
+      __syncthreads();
+    }
+    if (kt < nk) compute(lds0);  // odd tile count: the last tile sits in stage 0
   }
-  for (; kt + 1 < nk; kt += 2) {
-    fill(lds1, kt + 1);
-    compute(lds0);
-    __syncthreads();
-    if (kt + 2 < nk) fill(lds0, kt + 2);
-    compute(lds1);
-    __syncthreads();
-  }
-  if (kt < nk) compute(lds0);  // odd tile count: the last tile sits in stage 0
 
   // ---- epilogue: C = acc * 2^-(ea_i + eb_j), one rounding (exact unless the result is subnormal) ----
   const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
