@@ -16,8 +16,9 @@ Also reported in the same line:
   * "cpu_baseline" -- the FP64 CPU oracle on a bounded row sample of the same 9 shapes (all host threads),
     and the GPU's error against it on those rows;
   * "rows" -- the other hot-path steps, timed after the headline loop: the activation split, the INT16
-    quantiser, Dual-FP16 prefill (1 x 4096 x 32 heads x 128, causal), decode (64 x 8192 keys, GQA 32/8)
-    and the 8192^3 FP32 x FP32 GEMM (P = 3).
+    quantiser, Dual-FP16 prefill (1 x 4096 x 32 heads x 128, causal), decode (64 x 8192 keys, GQA 32/8),
+    the same decode over a paged cache (64-key pages, shuffled pool) and the 8192^3 FP32 x FP32 GEMM
+    (P = 3).
 """
 from __future__ import annotations
 
@@ -422,7 +423,29 @@ def other_rows(heal, workloads, dev):
     by = 2.0 * B * L * Hkv * 128 * 2 + 2.0 * B * L * Hkv * 4 + B * Hq * 128 * (2 + 4)
     rows["a7_decode_64x8192_gqa32_8"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
                                          "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
-    del k, v, ks, vs, q, qs, out, ws
+    # the same cache in 64-key pages of a shuffled pool (paged decode): pages gathered by index, no copy
+    # of the keys on the timed path
+    ps, npg = 64, L // 64
+    g = torch.Generator(device="cpu")
+    g.manual_seed(6)
+    tab = torch.randperm(B * npg, generator=g).to(torch.int32).view(B, npg).to("cuda")
+    def pool(t):
+        p = torch.empty((B * npg, ps) + tuple(t.shape[2:]), dtype=t.dtype, device="cuda")
+        p.index_copy_(0, tab.view(-1).long(), t.reshape((B * npg, ps) + tuple(t.shape[2:])))
+        return p
+    kp, ksp = pool(k), pool(ks)
+    del k, ks
+    vp, vsp = pool(v), pool(vs)
+    del v, vs
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    q1, qs1, o1 = q[:, 0].contiguous(), qs[:, 0].contiguous(), out[:, 0].contiguous()
+    pargs = heal.make_paged_args(q1, qs1, kp, ksp, vp, vsp, tab, lens, L, o1)
+    pws = torch.empty(heal.heal_attn_paged_workspace_bytes(pargs), dtype=torch.uint8, device="cuda")
+    t = time_fn(lambda: heal.heal_attn_decode_paged(q1, qs1, kp, ksp, vp, vsp, tab, lens, L, out=o1,
+                                                    workspace=pws), 10)
+    rows["a7p_paged_decode_64x8192_page64"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
+                                               "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
+    del kp, ksp, vp, vsp, tab, lens, q, qs, out, ws, q1, qs1, o1, pws
     torch.cuda.empty_cache()
     # config 5a: 8192^3 FP32 x FP32, rows scaled by 10^U(-3,3), P = 3
     A, Bt = workloads.gemm_rowscaled(8192, 8192, 8192, seed=4)

@@ -40,6 +40,24 @@ class HealAttnArgs(ctypes.Structure):
     ]
 
 
+class HealPagedDecodeArgs(ctypes.Structure):
+    """Mirror of heal_paged_decode_args in include/heal.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("n_q_heads", ctypes.c_int64), ("n_kv_heads", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64), ("page_size", ctypes.c_int64), ("num_pages", ctypes.c_int64),
+        ("max_pages_per_seq", ctypes.c_int64), ("max_kv_len", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("q_strides", ctypes.c_int64 * 2), ("qs_strides", ctypes.c_int64 * 2),
+        ("kv_strides", ctypes.c_int64 * 3), ("kvs_strides", ctypes.c_int64 * 3),
+        ("o_strides", ctypes.c_int64 * 2), ("bt_stride", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 def load():
     """Load libheal.so (built in-tree by ``build.build()``); raise if it is missing."""
     global _lib
@@ -65,12 +83,17 @@ def load():
     L.heal_attn_workspace_bytes.argtypes = [ctypes.POINTER(HealAttnArgs)]
     L.heal_attn_dual_fp16.restype = i32
     L.heal_attn_dual_fp16.argtypes = [ctypes.POINTER(HealAttnArgs), p]
+    L.heal_attn_paged_workspace_bytes.restype = ctypes.c_size_t
+    L.heal_attn_paged_workspace_bytes.argtypes = [ctypes.POINTER(HealPagedDecodeArgs)]
+    L.heal_attn_decode_paged.restype = i32
+    L.heal_attn_decode_paged.argtypes = [ctypes.POINTER(HealPagedDecodeArgs), p]
     _lib = L
     return L
 
 
 EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp", "heal_gemm_comp_variant",
-            "heal_qkv_quant_i16", "heal_attn_workspace_bytes", "heal_attn_dual_fp16")
+            "heal_qkv_quant_i16", "heal_attn_workspace_bytes", "heal_attn_dual_fp16",
+            "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged")
 
 
 def _check(status: int):
@@ -224,4 +247,61 @@ def heal_attn_dual_fp16(q, q_scale, k, k_scale, v, v_scale, causal: bool = True,
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = workspace.numel()
     _check(L.heal_attn_dual_fp16(ctypes.byref(args), _stream(q.device)))
+    return out
+
+
+def make_paged_args(q, q_scale, k_pages, k_scale, v_pages, v_scale, block_table, seq_lens, max_kv_len: int,
+                    out, softmax_scale: float | None = None, workspace=None) -> HealPagedDecodeArgs:
+    """Fill heal_paged_decode_args from torch tensors: q [B, Hq, D] int16, q_scale [B, Hq] fp32, k/v pages
+    [P, page_size, Hkv, D] int16, their scales [P, page_size, Hkv] fp32, block_table [B, max_pages] int32,
+    seq_lens [B] int32 and out [B, Hq, D] fp32.  k and v pages (and their scales) must share strides."""
+    B, Hq, D = q.shape
+    P, ps, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if k_pages.stride() != v_pages.stride() or k_scale.stride() != v_scale.stride():
+        raise ValueError("k and v pages (and their scales) must share strides")
+    for t in (q, k_pages, v_pages, out):
+        if t.stride(-1) != 1:
+            raise ValueError("head_dim axis must be contiguous")
+    a = HealPagedDecodeArgs()
+    a.batch, a.n_q_heads, a.n_kv_heads, a.head_dim = B, Hq, Hkv, D
+    a.page_size, a.num_pages, a.max_pages_per_seq, a.max_kv_len = ps, P, block_table.shape[1], int(max_kv_len)
+    a.q, a.q_scale = q.data_ptr(), q_scale.data_ptr()
+    a.k_pages, a.v_pages = k_pages.data_ptr(), v_pages.data_ptr()
+    a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+    a.block_table, a.seq_lens = block_table.data_ptr(), seq_lens.data_ptr()
+    a.q_strides[:] = list(q.stride()[:2])
+    a.qs_strides[:] = list(q_scale.stride()[:2])
+    a.kv_strides[:] = list(k_pages.stride()[:3])
+    a.kvs_strides[:] = list(k_scale.stride()[:3])
+    a.o_strides[:] = list(out.stride()[:2])
+    a.bt_stride = block_table.stride(0)
+    a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.out = out.data_ptr()
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def heal_attn_paged_workspace_bytes(args: HealPagedDecodeArgs) -> int:
+    return int(load().heal_attn_paged_workspace_bytes(ctypes.byref(args)))
+
+
+def heal_attn_decode_paged(q, q_scale, k_pages, k_scale, v_pages, v_scale, block_table, seq_lens,
+                           max_kv_len: int, softmax_scale: float | None = None, out=None, workspace=None):
+    """Decode attention (one query token per sequence) over a paged INT16 KV cache; returns out [B, Hq, D]
+    fp32.  A workspace of heal_attn_paged_workspace_bytes() is allocated with torch when none is given."""
+    import torch
+
+    L = load()
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    args = make_paged_args(q, q_scale, k_pages, k_scale, v_pages, v_scale, block_table, seq_lens, max_kv_len,
+                           out, softmax_scale, workspace)
+    need = heal_attn_paged_workspace_bytes(args)
+    if need and workspace is None:
+        workspace = torch.empty((need + 255) // 256 * 256, dtype=torch.uint8, device=q.device)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    _check(L.heal_attn_decode_paged(ctypes.byref(args), _stream(q.device)))
     return out

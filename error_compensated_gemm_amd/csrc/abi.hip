@@ -133,4 +133,50 @@ heal_status heal_attn_dual_fp16(const heal_attn_args* a, void* stream) {
   return launched(heal::launch_attn(*a, (hipStream_t)stream));
 }
 
+size_t heal_attn_paged_workspace_bytes(const heal_paged_decode_args* a) {
+  if (!a) return 0;
+  return heal::paged_workspace_bytes(*a);
+}
+
+heal_status heal_attn_decode_paged(const heal_paged_decode_args* a, void* stream) {
+  if (!a) return HEAL_ERR_NULL;
+  if (a->batch < 0 || a->n_q_heads < 0 || a->n_kv_heads < 0 || a->head_dim < 0 || a->page_size < 0 ||
+      a->num_pages < 0 || a->max_pages_per_seq < 0 || a->max_kv_len < 0)
+    return HEAL_ERR_SHAPE;
+  if (a->head_dim != 128) return HEAL_ERR_UNSUPPORTED;
+  if (a->page_size < 32 || (a->page_size & (a->page_size - 1)) || a->page_size > (int64_t(1) << 30))
+    return HEAL_ERR_UNSUPPORTED;
+  if (a->n_kv_heads == 0 || a->n_q_heads % a->n_kv_heads != 0) return HEAL_ERR_SHAPE;
+  if (a->n_q_heads / a->n_kv_heads > 16) return HEAL_ERR_UNSUPPORTED;
+  // the table must be able to hold max_kv_len keys (checked without overflow)
+  if (a->max_kv_len > 0 && (a->max_pages_per_seq == 0 || a->max_pages_per_seq < (a->max_kv_len + a->page_size - 1) / a->page_size))
+    return HEAL_ERR_SHAPE;
+  if (a->max_kv_len > 0 && a->num_pages == 0) return HEAL_ERR_SHAPE;
+  if (a->batch == 0 || a->n_q_heads == 0) return HEAL_OK;
+  if (!a->q || !a->q_scale || !a->out || !a->seq_lens) return HEAL_ERR_NULL;
+  if (a->max_kv_len > 0 && (!a->k_pages || !a->v_pages || !a->k_scale || !a->v_scale || !a->block_table))
+    return HEAL_ERR_NULL;
+  if (!(a->softmax_scale >= 0.0f) || isinf(a->softmax_scale)) return HEAL_ERR_SHAPE;
+  const int64_t D = a->head_dim;
+  for (int i = 0; i < 2; ++i)
+    if (a->q_strides[i] < 0 || a->qs_strides[i] < 0 || a->o_strides[i] < 0) return HEAL_ERR_STRIDE;
+  for (int i = 0; i < 3; ++i)
+    if (a->kv_strides[i] < 0 || a->kvs_strides[i] < 0) return HEAL_ERR_STRIDE;
+  if (a->q_strides[1] < D || a->o_strides[1] < D || a->kv_strides[2] < D || a->bt_stride < a->max_pages_per_seq)
+    return HEAL_ERR_STRIDE;
+  for (int i = 0; i < 2; ++i)
+    if ((a->q_strides[i] & 7) || (a->o_strides[i] & 7)) return HEAL_ERR_ALIGN;
+  for (int i = 0; i < 3; ++i)
+    if (a->kv_strides[i] & 7) return HEAL_ERR_ALIGN;
+  if (!aligned16(a->q) || !aligned16(a->out) || (a->k_pages && !aligned16(a->k_pages)) ||
+      (a->v_pages && !aligned16(a->v_pages)) || !aligned4(a->q_scale) || !aligned4(a->seq_lens) ||
+      (a->k_scale && !aligned4(a->k_scale)) || (a->v_scale && !aligned4(a->v_scale)) ||
+      (a->block_table && !aligned4(a->block_table)))
+    return HEAL_ERR_ALIGN;
+  const size_t need = heal::paged_workspace_bytes(*a);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need || (reinterpret_cast<uintptr_t>(a->workspace) & 255u)))
+    return HEAL_ERR_WORKSPACE;
+  return launched(heal::launch_attn_paged(*a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -205,6 +205,13 @@ struct AttnParams {
   int64_t B, Lq, Lkv, Hq, Hkv;
   float scale_log2;  // softmax_scale * log2(e)
   int causal;
+  // paged KV cache (decode): Lkv bounds the lengths lens[b]; key j of sequence b is slot
+  // j & ((1 << page_shift) - 1) of page bt[b * bt_st + (j >> page_shift)], and kv_st[0] / kvs_st[0] are
+  // the page strides
+  const int32_t* bt;
+  const int32_t* lens;
+  int64_t bt_st, num_pages;
+  int page_shift;
 };
 
 __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) {
@@ -474,6 +481,9 @@ size_t decode_workspace(int64_t B, int64_t Hq, int64_t Lkv) {
   return (size_t)(B * Hq * (nsplit > 0 ? nsplit : 1) * DC_PART) * sizeof(float);
 }
 
+// PAGED: the keys of each sequence are in pages of a shared pool (AttnParams::bt / lens) and every sequence
+// has its own length; otherwise one contiguous run of a.Lkv keys per (batch, kv head).
+template <bool PAGED>
 __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_decode_kernel(
     AttnParams a, float* __restrict__ ws, int nsplit) {
   // two stages per wavefront, each stage its own object (the compiler can tell the stage being read
@@ -484,22 +494,27 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
                 "partials must fit in one stage array");
   float(*part)[16][DC_PART] = reinterpret_cast<float(*)[16][DC_PART]>(&st0[0]);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x;
   const int64_t bk = blockIdx.y;  // (batch, kv-head)
   const int64_t b = bk / a.Hkv, hk = bk - b * a.Hkv;
   const int G = (int)(a.Hq / a.Hkv);
+  // keys of this sequence (paged: its own length, clamped into [0, a.Lkv])
+  int64_t L = a.Lkv;
+  if constexpr (PAGED) {
+    const int64_t len = a.lens[b];
+    L = len < 0 ? 0 : (len > a.Lkv ? a.Lkv : len);
+  }
   const int64_t c0 = (int64_t)split * DC_CHUNK;
   int64_t c1 = c0 + DC_CHUNK;
-  if (c1 > a.Lkv) c1 = a.Lkv;
+  if (c1 > L) c1 = L;
   const int64_t w0 = c0 + (int64_t)wave * DC_KPW;
   int64_t w1 = w0 + DC_KPW;
   if (w1 > c1) w1 = c1;
 
-  const int16_t* kbase = a.k + b * a.kv_st[0] + hk * a.kv_st[2];
-  const int16_t* vbase = a.v + b * a.kv_st[0] + hk * a.kv_st[2];
-  const float* ksb = a.ks + b * a.kvs_st[0] + hk * a.kvs_st[2];
-  const float* vsb = a.vs + b * a.kvs_st[0] + hk * a.kvs_st[2];
+  // contiguous: the (batch, kv head) runs; paged: the kv head's offset inside a page
+  const int64_t kvoff = (PAGED ? 0 : b * a.kv_st[0]) + hk * a.kv_st[2];
+  const int64_t soff = (PAGED ? 0 : b * a.kvs_st[0]) + hk * a.kvs_st[2];
 
   // query column of this lane: head hk*G + qc for qc < G (other columns are zero padding)
   const int qc = lane & 15, grp = lane >> 4;
@@ -519,26 +534,53 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // one step's loads: K straight into operand registers (key 16 mt + qc, d 32 ks + 8 grp .. + 7), V and the
   // scales direct-to-LDS (position p = 64 i + l holds key p / 16 in the VT_DECODE layout)
+  //  A step's keys past this wavefront's range are clamped to its last key (read, never used).  Paged: the
+  //  page size is a power of two >= 32 and steps start at multiples of 32, so after that clamp every key of
+  //  a step lies in the page of its first (clamped) key.  The wavefront's range (512 keys, 512-aligned)
+  //  spans at most 16 pages, whose ids lane l holds from the start (pid_lane); a step takes its page id from
+  //  the lane of its page, so no table read waits in front of the step's loads.
   const int64_t kvs1 = a.kv_st[1], ss1 = a.kvs_st[1];
+  const int64_t jmax = w1 - 1;
+  int pid_lane = 0;
+  int64_t p0 = 0;
+  if constexpr (PAGED) {
+    p0 = w0 >> a.page_shift;
+    const int64_t pend = (w1 + ((int64_t)1 << a.page_shift) - 1) >> a.page_shift;  // pages of [w0, w1)
+    if (w1 > w0 && p0 + lane < pend) pid_lane = a.bt[b * a.bt_st + p0 + lane];
+  }
   auto issue = [&](DcStage& S, uint4 (&kr)[2][4], int64_t j0) {
+    int64_t row0 = 0, srow0 = 0;  // element offsets of the step's page (paged) or run (contiguous)
+    int64_t jmask = -1;           // key -> slot within that page
+    if constexpr (PAGED) {
+      const int64_t jc = j0 < jmax ? j0 : jmax;
+      int64_t pg = __builtin_amdgcn_readlane(pid_lane, (int)((jc >> a.page_shift) - p0));
+      pg = pg < 0 ? 0 : (pg > a.num_pages - 1 ? a.num_pages - 1 : pg);
+      row0 = pg * a.kv_st[0];
+      srow0 = pg * a.kvs_st[0];
+      jmask = ((int64_t)1 << a.page_shift) - 1;
+    }
+    const int16_t* kb = a.k + kvoff + row0;
+    const int16_t* vb = a.v + kvoff + row0;
+    const float* ksp = a.ks + soff + srow0;
+    const float* vsp = a.vs + soff + srow0;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       int64_t j = j0 + 16 * mt + qc;
-      if (j > a.Lkv - 1) j = a.Lkv - 1;
+      if (j > jmax) j = jmax;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        kr[mt][ks] = *reinterpret_cast<const uint4*>(kbase + j * kvs1 + 32 * ks + 8 * grp);
+        kr[mt][ks] = *reinterpret_cast<const uint4*>(kb + (j & jmask) * kvs1 + 32 * ks + 8 * grp);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int p = 64 * i + lane, key = p >> 4, c = (p & 15) ^ vt_swz<VT_DECODE>(key);
       int64_t j = j0 + key;
-      if (j > a.Lkv - 1) j = a.Lkv - 1;
-      dma16(vbase + j * kvs1 + 8 * c, &S.v[64 * i]);
+      if (j > jmax) j = jmax;
+      dma16(vb + (j & jmask) * kvs1 + 8 * c, &S.v[64 * i]);
     }
     int64_t j = j0 + (lane & 31);
-    if (j > a.Lkv - 1) j = a.Lkv - 1;
-    dma4((lane < 32 ? ksb : vsb) + j * ss1, &S.sc[0]);
+    if (j > jmax) j = jmax;
+    dma4((lane < 32 ? ksp : vsp) + (j & jmask) * ss1, &S.sc[0]);
   };
 
   f32x4 O[8];
@@ -763,6 +805,38 @@ AttnParams make_params(const heal_attn_args& x) {
   const double sm = x.softmax_scale > 0.0f ? (double)x.softmax_scale : 1.0 / sqrt((double)x.head_dim);
   p.scale_log2 = (float)(sm * 1.4426950408889634);
   p.causal = x.causal != 0;
+  p.bt = nullptr;
+  p.lens = nullptr;
+  p.bt_st = 0;
+  p.num_pages = 0;
+  p.page_shift = 0;
+  return p;
+}
+
+AttnParams make_params_paged(const heal_paged_decode_args& x) {
+  AttnParams p;
+  p.q = x.q; p.k = x.k_pages; p.v = x.v_pages;
+  p.qs = x.q_scale; p.ks = x.k_scale; p.vs = x.v_scale;
+  p.out = x.out;
+  // (batch, token, head) triples with a single query token; kv / kvs: (page, slot, head)
+  p.q_st[0] = x.q_strides[0]; p.q_st[1] = 0; p.q_st[2] = x.q_strides[1];
+  p.qs_st[0] = x.qs_strides[0]; p.qs_st[1] = 0; p.qs_st[2] = x.qs_strides[1];
+  p.o_st[0] = x.o_strides[0]; p.o_st[1] = 0; p.o_st[2] = x.o_strides[1];
+  for (int i = 0; i < 3; ++i) {
+    p.kv_st[i] = x.kv_strides[i];
+    p.kvs_st[i] = x.kvs_strides[i];
+  }
+  p.B = x.batch; p.Lq = 1; p.Lkv = x.max_kv_len; p.Hq = x.n_q_heads; p.Hkv = x.n_kv_heads;
+  const double sm = x.softmax_scale > 0.0f ? (double)x.softmax_scale : 1.0 / sqrt((double)x.head_dim);
+  p.scale_log2 = (float)(sm * 1.4426950408889634);
+  p.causal = 0;
+  p.bt = x.block_table;
+  p.lens = x.seq_lens;
+  p.bt_st = x.bt_stride;
+  p.num_pages = x.num_pages;
+  int sh = 0;
+  while (((int64_t)1 << sh) < x.page_size) ++sh;
+  p.page_shift = sh;
   return p;
 }
 
@@ -794,7 +868,7 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
   if (use_decode(x)) {
     const int nsplit = (int)((x.kv_len + DC_CHUNK - 1) / DC_CHUNK);
     float* ws = reinterpret_cast<float*>(x.workspace);
-    hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads)),
+    hipLaunchKernelGGL(attn_decode_kernel<false>, dim3((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads)),
                        dim3(DC_THREADS), 0, stream, p, ws, nsplit);
     hipLaunchKernelGGL(attn_decode_merge_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream,
                        p, (const float*)ws, nsplit);
@@ -803,6 +877,27 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
   const unsigned ntq = (unsigned)((x.q_len + PF_BQ - 1) / PF_BQ);
   hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)(x.batch * x.n_q_heads), ntq), dim3(PF_THREADS), 0,
                      stream, p);
+  return hipGetLastError();
+}
+
+size_t paged_workspace_bytes(const heal_paged_decode_args& x) {
+  if (x.batch <= 0 || x.n_q_heads <= 0) return 0;
+  return decode_workspace(x.batch, x.n_q_heads, x.max_kv_len);
+}
+
+hipError_t launch_attn_paged(const heal_paged_decode_args& x, hipStream_t stream) {
+  const AttnParams p = make_params_paged(x);
+  if (x.max_kv_len == 0) {
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream, p);
+    return hipGetLastError();
+  }
+  // the grid covers max_kv_len; splits past a sequence's own length write empty partials
+  const int nsplit = (int)((x.max_kv_len + DC_CHUNK - 1) / DC_CHUNK);
+  float* ws = reinterpret_cast<float*>(x.workspace);
+  hipLaunchKernelGGL(attn_decode_kernel<true>, dim3((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads)),
+                     dim3(DC_THREADS), 0, stream, p, ws, nsplit);
+  hipLaunchKernelGGL(attn_decode_merge_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream, p,
+                     (const float*)ws, nsplit);
   return hipGetLastError();
 }
 

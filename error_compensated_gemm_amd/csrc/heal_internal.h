@@ -23,5 +23,7 @@ hipError_t launch_gemm_comp(int64_t M, int64_t N, int64_t K, const uint16_t* a_h
 const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products);
 size_t attn_workspace_bytes(const heal_attn_args& a);
 hipError_t launch_attn(const heal_attn_args& a, hipStream_t stream);
+size_t paged_workspace_bytes(const heal_paged_decode_args& a);
+hipError_t launch_attn_paged(const heal_paged_decode_args& a, hipStream_t stream);
 
 }  // namespace heal

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define HEAL_ABI_VERSION 1
+#define HEAL_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define HEAL_API __attribute__((visibility("default")))
@@ -187,6 +187,61 @@ HEAL_API size_t heal_attn_workspace_bytes(const heal_attn_args* args);
  * (head_dim != 128), HEAL_ERR_WORKSPACE.
  */
 HEAL_API heal_status heal_attn_dual_fp16(const heal_attn_args* args, void* stream);
+
+/*
+ * Paged, variable-length INT16 KV cache for decode (one query token per sequence): the attention of
+ * heal_attn_dual_fp16 with q_len = 1, the same Dual-FP16 arithmetic ([TS 2A Mechanism]) and the same
+ * 16-bit cache footprint ([TS 2A Benefit]), with the keys of each sequence held in fixed-size pages of a
+ * shared pool instead of one contiguous run.
+ *
+ * Layout (all device memory, owned by the caller):
+ *   q        int16 [batch, n_q_heads, 128]            element (b, h, d) at q[b*q_strides[0] + h*q_strides[1] + d]
+ *   q_scale  fp32  [batch, n_q_heads]                 at q_scale[b*qs_strides[0] + h*qs_strides[1]]
+ *   k_pages, v_pages  int16 [num_pages, page_size, n_kv_heads, 128]
+ *                                                     (p, t, h, d) at [p*kv_strides[0] + t*kv_strides[1] + h*kv_strides[2] + d]
+ *   k_scale, v_scale  fp32 [num_pages, page_size, n_kv_heads]
+ *                                                     (p, t, h) at [p*kvs_strides[0] + t*kvs_strides[1] + h*kvs_strides[2]]
+ *   block_table int32 [batch, max_pages_per_seq]: key j of sequence b lives in page
+ *            block_table[b*bt_stride + j / page_size], slot j % page_size
+ *   seq_lens int32 [batch]: keys of each sequence (0 gives an all-zero output row)
+ *   out      fp32  [batch, n_q_heads, 128]            at out[b*o_strides[0] + h*o_strides[1] + d]
+ * Query head h reads kv head h / (n_q_heads / n_kv_heads).  Every key of a sequence is visible.
+ * page_size must be a power of two >= 32 (HEAL_ERR_UNSUPPORTED otherwise); head_dim must be 128.
+ * max_kv_len bounds seq_lens and sizes the launch (no device read on the host): a length outside
+ * [0, max_kv_len] is clamped into it, and a page id outside [0, num_pages) is clamped into it, so no
+ * access leaves the pool whatever the table holds; the result for such entries is unspecified.
+ * The workspace (heal_attn_paged_workspace_bytes) holds the partial results of the key splits.
+ * Errors: HEAL_ERR_NULL, HEAL_ERR_SHAPE (sizes, n_q_heads % n_kv_heads != 0, max_pages_per_seq *
+ * page_size < max_kv_len), HEAL_ERR_STRIDE, HEAL_ERR_ALIGN (q/pages/out 16-byte aligned, q/kv/o strides
+ * multiples of 8), HEAL_ERR_UNSUPPORTED (head_dim, page_size, n_q_heads / n_kv_heads > 16),
+ * HEAL_ERR_WORKSPACE.
+ */
+typedef struct {
+  int64_t batch, n_q_heads, n_kv_heads, head_dim;
+  int64_t page_size, num_pages, max_pages_per_seq, max_kv_len;
+  const int16_t* q;
+  const float* q_scale;
+  const int16_t* k_pages;
+  const int16_t* v_pages;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int64_t q_strides[2];
+  int64_t qs_strides[2];
+  int64_t kv_strides[3];
+  int64_t kvs_strides[3];
+  int64_t o_strides[2];
+  int64_t bt_stride;
+  float softmax_scale; /* 0 selects 1/sqrt(head_dim) */
+  float* out;
+  void* workspace;
+  size_t workspace_bytes;
+} heal_paged_decode_args;
+
+/* Workspace bytes heal_attn_decode_paged needs for these arguments. */
+HEAL_API size_t heal_attn_paged_workspace_bytes(const heal_paged_decode_args* args);
+HEAL_API heal_status heal_attn_decode_paged(const heal_paged_decode_args* args, void* stream);
 
 #ifdef __cplusplus
 }

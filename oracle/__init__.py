@@ -248,3 +248,29 @@ def attn_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: f
 def attn_i16_f64(q, qs, k, ks, v, vs, causal: bool, scale: float | None = None, rows=None):
     """[TS 2A] attention graded on the dequantised INT16 inputs x = s * q (reading R-attn)."""
     return attn_f64(dequant_i16(q, qs), dequant_i16(k, ks), dequant_i16(v, vs), causal, scale, rows)
+
+
+def gather_pages(pool: np.ndarray, table_row: np.ndarray, seq_len: int, page_size: int) -> np.ndarray:
+    """The first seq_len keys of one sequence from a page pool [P, page_size, ...]: key j is slot
+    j % page_size of page table_row[j // page_size] (the paged layout of the decode KV cache)."""
+    j = np.arange(int(seq_len))
+    return pool[np.asarray(table_row)[j // page_size], j % page_size]
+
+
+def attn_paged_i16_f64(q, qs, k_pages, ks_pages, v_pages, vs_pages, block_table, seq_lens, scale=None):
+    """Decode attention (one query token per sequence) over a paged INT16 cache, graded like
+    attn_i16_f64: each sequence's keys are gathered from its pages and the FP64 definition is applied to
+    the dequantised values.  q [B, Hq, D] int16, qs [B, Hq]; returns [B, Hq, D] (0 for an empty sequence)."""
+    B, Hq, D = q.shape
+    ps = k_pages.shape[1]
+    out = np.zeros((B, Hq, D), np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        k = gather_pages(k_pages, block_table[b], n, ps)[None]
+        ks = gather_pages(ks_pages, block_table[b], n, ps)[None]
+        v = gather_pages(v_pages, block_table[b], n, ps)[None]
+        vs = gather_pages(vs_pages, block_table[b], n, ps)[None]
+        out[b] = attn_i16_f64(q[b][None, None], qs[b][None, None], k, ks, v, vs, causal=False, scale=scale)[0, 0]
+    return out

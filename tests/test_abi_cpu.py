@@ -20,7 +20,8 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("heal_split", "heal_gemm_comp", "heal_qkv_quant_i16", "heal_attn_dual_fp16",
-              "heal_attn_workspace_bytes", "heal_status_str", "heal_abi_version"):
+              "heal_attn_workspace_bytes", "heal_status_str", "heal_abi_version", "heal_attn_decode_paged",
+              "heal_attn_paged_workspace_bytes"):
         assert n in names
 
 
@@ -37,25 +38,28 @@ def test_library_exports_every_declared_symbol(heal):
 
 def test_version_and_status_strings(heal):
     lib = heal.load()
-    assert lib.heal_abi_version() == 1
+    assert lib.heal_abi_version() == 2
     for s in range(9):
         assert lib.heal_status_str(s).decode().startswith("HEAL")
     assert b"unknown" in lib.heal_status_str(99)
 
 
-def test_attn_args_layout_matches_c(heal, tmp_path):
-    fields = [f for f, _ in heal.HealAttnArgs._fields_]
+@pytest.mark.parametrize("cname,pyname", [("heal_attn_args", "HealAttnArgs"),
+                                          ("heal_paged_decode_args", "HealPagedDecodeArgs")])
+def test_args_layout_matches_c(heal, tmp_path, cname, pyname):
+    cls = getattr(heal, pyname)
+    fields = [f for f, _ in cls._fields_]
     src = tmp_path / "layout.c"
-    body = "".join(f'  printf("{f} %zu\\n", offsetof(heal_attn_args, {f}));\n' for f in fields)
+    body = "".join(f'  printf("{f} %zu\\n", offsetof({cname}, {f}));\n' for f in fields)
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "heal.h"\nint main(void) {\n'
-                   f'  printf("size %zu\\n", sizeof(heal_attn_args));\n{body}  return 0;\n}}\n')
+                   f'  printf("size %zu\\n", sizeof({cname}));\n{body}  return 0;\n}}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split("\n")
                if line)
-    assert int(got["size"]) == ctypes.sizeof(heal.HealAttnArgs)
+    assert int(got["size"]) == ctypes.sizeof(cls)
     for f in fields:
-        assert int(got[f]) == getattr(heal.HealAttnArgs, f).offset, f
+        assert int(got[f]) == getattr(cls, f).offset, f
 
 
 P = ctypes.c_void_p
@@ -157,3 +161,52 @@ def test_gemm_variant_names(heal):
     assert heal.heal_gemm_comp_variant(0, 5, 5, 2) == "none"
     assert heal.heal_gemm_comp_variant(8192, 8192, 8192, 3).startswith("gemm_comp_kernel")
     assert heal.heal_gemm_comp_variant(8192, 8192, 8192, 3).endswith("P3")
+
+
+def _paged_args(heal, **kw):
+    a = heal.HealPagedDecodeArgs()
+    a.batch, a.n_q_heads, a.n_kv_heads, a.head_dim = 2, 8, 2, 128
+    a.page_size, a.num_pages, a.max_pages_per_seq, a.max_kv_len = 64, 10, 4, 256
+    a.q = a.k_pages = a.v_pages = a.out = FAKE
+    a.q_scale = a.k_scale = a.v_scale = a.block_table = a.seq_lens = FAKE
+    a.q_strides[:] = [8 * 128, 128]
+    a.qs_strides[:] = [8, 1]
+    a.kv_strides[:] = [64 * 2 * 128, 2 * 128, 128]
+    a.kvs_strides[:] = [64 * 2, 2, 1]
+    a.o_strides[:] = [8 * 128, 128]
+    a.bt_stride = 4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_paged_decode_validation(heal):
+    lib = heal.load()
+    call = lambda **kw: lib.heal_attn_decode_paged(ctypes.byref(_paged_args(heal, **kw)), None)
+    assert lib.heal_attn_decode_paged(None, None) == 1
+    assert call(head_dim=64) == 6
+    assert call(page_size=16) == 6      # below 32
+    assert call(page_size=96) == 6      # not a power of two
+    assert call(n_q_heads=34, n_kv_heads=2) == 6  # more than 16 query heads per kv head
+    assert call(n_q_heads=9) == 2       # n_q_heads % n_kv_heads
+    assert call(max_pages_per_seq=3) == 2   # 3 pages of 64 cannot hold 256 keys
+    assert call(num_pages=0) == 2
+    assert call(batch=-1) == 2
+    assert call(seq_lens=0) == 1
+    assert call(block_table=0) == 1
+    assert call(k_pages=0) == 1
+    assert call(bt_stride=3) == 3
+    assert call(softmax_scale=float("inf")) == 2
+    assert call(v_pages=MIS) == 4
+    assert call(block_table=FAKE + 2) == 4
+    a = _paged_args(heal)
+    a.kv_strides[1] = 260  # not a multiple of 8
+    assert lib.heal_attn_decode_paged(ctypes.byref(a), None) == 4
+    a = _paged_args(heal)
+    a.q_strides[1] = 64  # smaller than head_dim
+    assert lib.heal_attn_decode_paged(ctypes.byref(a), None) == 3
+    # the partials need a workspace: none, then too small -> HEAL_ERR_WORKSPACE before any launch
+    assert lib.heal_attn_paged_workspace_bytes(ctypes.byref(_paged_args(heal))) > 0
+    assert call() == 8
+    assert call(workspace=FAKE, workspace_bytes=16) == 8
+    assert call(batch=0) == 0

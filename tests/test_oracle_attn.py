@@ -84,3 +84,43 @@ def test_dequant_exact():
     x = oracle.dequant_i16(q, s)
     sd = float(np.float32(1.0) / np.float32(3.0))
     assert list(x[0, 0, 0]) == [32767 * sd, -32767 * sd, sd, 0.0]
+
+
+def test_gather_pages_by_hand():
+    # 2 sequences, page_size 4: sequence 0 = pages [2, 0], sequence 1 = page [1]
+    pool = np.arange(3 * 4 * 2).reshape(3, 4, 2)  # [page, slot, feature]
+    table = np.array([[2, 0], [1, -1]])
+    g0 = oracle.gather_pages(pool, table[0], 6, 4)
+    assert np.array_equal(g0, np.concatenate([pool[2], pool[0, :2]]))
+    g1 = oracle.gather_pages(pool, table[1], 3, 4)
+    assert np.array_equal(g1, pool[1, :3])
+    # scatter then gather is the identity on a shuffled pool (the two are written independently)
+    x = np.random.default_rng(0).integers(-9, 9, (3, 70, 2, 5)).astype(np.int16)
+    lens = [70, 1, 33]
+    P, tab = workloads.paged_layout(lens, 32, spare_pages=2, seed=1)
+    pool = workloads.pages_from_contiguous(x, lens, tab, P, 32)
+    for b, n in enumerate(lens):
+        assert np.array_equal(oracle.gather_pages(pool, tab[b], n, 32), x[b, :n])
+
+
+def test_paged_decode_matches_sdpa_on_the_contiguous_keys():
+    B, Hq, Hkv, D, ps = 3, 8, 2, 128, 32
+    lens = [1, 77, 130]
+    Lmax = max(lens)
+    q, qs = workloads.int16_cache_host(B, 1, Hq, D, seed=11)
+    k, ks = workloads.int16_cache_host(B, Lmax, Hkv, D, seed=12)
+    v, vs = workloads.int16_cache_host(B, Lmax, Hkv, D, seed=13)
+    P, tab = workloads.paged_layout(lens, ps, seed=2)
+    kp = workloads.pages_from_contiguous(k, lens, tab, P, ps)
+    vp = workloads.pages_from_contiguous(v, lens, tab, P, ps)
+    ksp = workloads.pages_from_contiguous(ks, lens, tab, P, ps, fill=1.0)
+    vsp = workloads.pages_from_contiguous(vs, lens, tab, P, ps, fill=1.0)
+    got = oracle.attn_paged_i16_f64(q[:, 0], qs[:, 0], kp, ksp, vp, vsp, tab, np.array(lens))
+    for b, n in enumerate(lens):
+        deq = lambda t, s: t[b:b + 1, :n].astype(np.float64) * s[b:b + 1, :n, :, None].astype(np.float64)
+        want = _sdpa(q[b:b + 1].astype(np.float64) * qs[b:b + 1, :, :, None].astype(np.float64),
+                     deq(k, ks), deq(v, vs), causal=False)
+        assert np.allclose(got[b], want[0, 0], rtol=1e-12, atol=1e-12)
+    # an empty sequence gives zeros
+    z = oracle.attn_paged_i16_f64(q[:1, 0], qs[:1, 0], kp, ksp, vp, vsp, tab[:1], np.array([0]))
+    assert np.all(z == 0)

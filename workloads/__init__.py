@@ -110,3 +110,34 @@ def int16_cache_device(B: int, L: int, H: int, D: int, seed: int = 3, device: st
     sig = torch.exp(torch.randn((B, L, 1), generator=g, device=device, dtype=torch.float32))
     s = (sig / INT16_SIGMA).expand(B, L, H).contiguous()
     return q, s
+
+
+def paged_layout(seq_lens, page_size: int, spare_pages: int = 3, seed: int = 7):
+    """A shuffled page assignment for sequences of the given lengths: returns (num_pages, block_table
+    [B, max_pages] int32).  Every page of every sequence is a distinct pool page in random order, the pool
+    holds spare_pages unused pages besides, and table columns past a sequence's pages hold -1."""
+    rng = np.random.default_rng(seed)
+    seq_lens = [int(n) for n in seq_lens]
+    need = [(n + page_size - 1) // page_size for n in seq_lens]
+    max_pages = max(1, max(need) if need else 1)
+    num_pages = sum(need) + spare_pages
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((len(seq_lens), max_pages), -1, np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[at:at + n]
+        at += n
+    return num_pages, table
+
+
+def pages_from_contiguous(x: np.ndarray, seq_lens, table: np.ndarray, num_pages: int, page_size: int,
+                          fill=0):
+    """Scatter a contiguous per-sequence tensor x [B, L, ...] into a page pool [num_pages, page_size, ...]
+    following `table` (key j of sequence b -> slot j % page_size of page table[b, j // page_size]); slots
+    no sequence uses hold `fill`."""
+    pool = np.full((num_pages, page_size) + x.shape[2:], fill, x.dtype)
+    for b, n in enumerate(seq_lens):
+        for j0 in range(0, int(n), page_size):
+            j1 = min(int(n), j0 + page_size)
+            pool[table[b, j0 // page_size], :j1 - j0] = x[b, j0:j1]
+    return pool
