@@ -17,8 +17,8 @@ Also reported in the same line:
     and the GPU's error against it on those rows;
   * "rows" -- the other hot-path steps, timed after the headline loop: the activation split, the INT16
     quantiser, Dual-FP16 prefill (1 x 4096 x 32 heads x 128, causal), decode (64 x 8192 keys, GQA 32/8),
-    the same decode over a paged cache (64-key pages, shuffled pool) and the 8192^3 FP32 x FP32 GEMM
-    (P = 3).
+    the same decode over a paged cache (64-key pages, shuffled pool), the QKV projection with the INT16
+    quantisation fused into the GEMM (against GEMM + quantiser) and the 8192^3 FP32 x FP32 GEMM (P = 3).
 """
 from __future__ import annotations
 
@@ -447,6 +447,25 @@ def other_rows(heal, workloads, dev):
                                                "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
     del kp, ksp, vp, vsp, tab, lens, q, qs, out, ws, q1, qs1, o1, pws
     torch.cuda.empty_cache()
+    # quantise-on-append: the Llama-3-8B QKV projection (2048 tokens x 4096 -> 6144 = 48 heads of 128, bf16
+    # weights, P = 2) with the INT16 quantisation fused into the GEMM epilogue, against GEMM + quantiser
+    X = dev(workloads.llama_activations(2048, 4096, seed=7))
+    Wq = dev(workloads.llama_weights_bf16(6144, 4096, seed=7).view(np.int16)).view(torch.bfloat16)
+    ah, al, ea = heal.heal_split(X)
+    bh, _, eb = heal.heal_split(Wq, residual=False)
+    qf, sf = heal.heal_gemm_comp_quant_i16(ah, al, ea, bh, None, eb)
+    c = heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
+    qu, su = heal.heal_qkv_quant_i16(c.view(2048, 48, 128))
+    t_f = time_fn(lambda: heal.heal_gemm_comp_quant_i16(ah, al, ea, bh, None, eb, q=qf, scale=sf), 20)
+    def unfused():
+        heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
+        heal.heal_qkv_quant_i16(c.view(2048, 48, 128), q=qu, scale=su)
+    t_u = time_fn(unfused, 20)
+    fl = 2.0 * 2048 * 4096 * 6144
+    rows["qkv_proj_quant_fused_2048x4096x6144"] = {
+        "us": round(t_f * 1e6, 2), "unfused_us": round(t_u * 1e6, 2), "tflops_fp32eq": round(fl / t_f / 1e12, 1),
+        "kernel": heal.heal_gemm_comp_variant(2048, 6144, 4096, 2)}
+    del X, Wq, ah, al, ea, bh, eb, qf, sf, c, qu, su
     # config 5a: 8192^3 FP32 x FP32, rows scaled by 10^U(-3,3), P = 3
     A, Bt = workloads.gemm_rowscaled(8192, 8192, 8192, seed=4)
     ah, al, ea = heal.heal_split(dev(A))

@@ -75,6 +75,8 @@ def load():
     L.heal_split.argtypes = [p, i32, i64, i64, i64, i32, p, p, i64, p, p]
     L.heal_gemm_comp.restype = i32
     L.heal_gemm_comp.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p]
+    L.heal_gemm_comp_quant_i16.restype = i32
+    L.heal_gemm_comp_quant_i16.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p, i64, p]
     L.heal_gemm_comp_variant.restype = ctypes.c_char_p
     L.heal_gemm_comp_variant.argtypes = [i64, i64, i64, i32]
     L.heal_qkv_quant_i16.restype = i32
@@ -93,7 +95,7 @@ def load():
 
 EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp", "heal_gemm_comp_variant",
             "heal_qkv_quant_i16", "heal_attn_workspace_bytes", "heal_attn_dual_fp16",
-            "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged")
+            "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged", "heal_gemm_comp_quant_i16")
 
 
 def _check(status: int):
@@ -169,6 +171,28 @@ def heal_gemm_comp(a_hi, a_lo, a_exp, b_hi, b_lo, b_exp, part: str = "f16", c=No
     _check(L.heal_gemm_comp(M, N, K, _ptr(a_hi), _ptr(a_lo), _ptr(a_exp), _ld(a_hi), _ptr(b_hi), _ptr(b_lo),
                             _ptr(b_exp), _ld(b_hi), _PARTS[part], _ptr(c), _ld(c), _stream(a_hi.device)))
     return c
+
+
+def heal_gemm_comp_quant_i16(a_hi, a_lo, a_exp, b_hi, b_lo, b_exp, q=None, scale=None):
+    """The compensated GEMM with INT16 quantisation per (row, 128-column head) in its epilogue.  Returns
+    (q int16 [M, N], scale fp32 [M, N / 128]); ``q`` / ``scale`` may be row-strided views into a cache."""
+    import torch
+
+    L = load()
+    M, K = a_hi.shape
+    N = b_hi.shape[0]
+    if q is None:
+        q = torch.empty((M, N), dtype=torch.int16, device=a_hi.device)
+    if scale is None:
+        scale = torch.empty((M, N // 128), dtype=torch.float32, device=a_hi.device)
+    if a_lo is not None and (a_lo.shape != a_hi.shape or a_lo.stride() != a_hi.stride()):
+        raise ValueError("a_lo must match a_hi's shape and strides")
+    if b_lo is not None and (b_lo.shape != b_hi.shape or b_lo.stride() != b_hi.stride()):
+        raise ValueError("b_lo must match b_hi's shape and strides")
+    _check(L.heal_gemm_comp_quant_i16(M, N, K, _ptr(a_hi), _ptr(a_lo), _ptr(a_exp), _ld(a_hi), _ptr(b_hi),
+                                      _ptr(b_lo), _ptr(b_exp), _ld(b_hi), _PARTS["f16"], _ptr(q), _ld(q),
+                                      _ptr(scale), _ld(scale), _stream(a_hi.device)))
+    return q, scale
 
 
 def heal_gemm_comp_variant(M: int, N: int, K: int, products: int) -> str:

@@ -80,6 +80,26 @@ heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, co
                                          c, ldc, (hipStream_t)stream));
 }
 
+heal_status heal_gemm_comp_quant_i16(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
+                                     const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
+                                     const int32_t* b_exp, int64_t ldb, int part_type, int16_t* q, int64_t ldq,
+                                     float* scale, int64_t ld_s, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return HEAL_ERR_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
+  if (N % 128 != 0) return HEAL_ERR_SHAPE;
+  if (part_type != HEAL_F16) return HEAL_ERR_DTYPE;
+  if (M == 0 || N == 0) return HEAL_OK;
+  if (!q || !scale || (K > 0 && (!a_hi || !b_hi))) return HEAL_ERR_NULL;
+  if (lda < K || ldb < K || ldq < N || ld_s < N / 128) return HEAL_ERR_STRIDE;
+  if ((a_hi && !aligned16(a_hi)) || (a_lo && !aligned16(a_lo)) || (b_hi && !aligned16(b_hi)) ||
+      (b_lo && !aligned16(b_lo)) || !aligned16(q) || !aligned4(scale) || (a_exp && !aligned4(a_exp)) ||
+      (b_exp && !aligned4(b_exp)) || (lda & 7) || (ldb & 7) || (ldq & 7))
+    return HEAL_ERR_ALIGN;
+  return launched(heal::launch_gemm_comp_quant(M, N, K, (const uint16_t*)a_hi, (const uint16_t*)a_lo, a_exp, lda,
+                                               (const uint16_t*)b_hi, (const uint16_t*)b_lo, b_exp, ldb, q, ldq,
+                                               scale, ld_s, (hipStream_t)stream));
+}
+
 const char* heal_gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
   return heal::gemm_comp_variant(M, N, K, products);
 }

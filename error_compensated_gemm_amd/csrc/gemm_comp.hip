@@ -70,6 +70,25 @@ __device__ __forceinline__ uint4 mask_chunk(uint4 v, int64_t valid) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// maximum over the 32 lanes of each half-wavefront, with DPP and one swizzle (no LDS traffic): quad
+// swaps (lane ^ 1, lane ^ 2), mirrors within 8 and within 16 lanes, then lane ^ 16
+__device__ __forceinline__ float halfwave_max32(float m) {
+  auto dpp = [](float v, int ctrl) -> float {
+    switch (ctrl) {  // the control must be a constant
+      case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+      case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+      case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+      default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+    }
+  };
+  m = fmaxf(m, dpp(m, 0xB1));   // quad_perm [1, 0, 3, 2]
+  m = fmaxf(m, dpp(m, 0x4E));   // quad_perm [2, 3, 0, 1]
+  m = fmaxf(m, dpp(m, 0x141));  // row_half_mirror: lane i <-> 7 - i within 8
+  m = fmaxf(m, dpp(m, 0x140));  // row_mirror: lane i <-> 15 - i within 16
+  // ds_swizzle bit mode, and_mask 0x1f, or_mask 0, xor_mask 0x10: lane ^ 16 within each 32 lanes
+  return fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m), 0x401F)));
+}
+
 // s_waitcnt immediate: at most N vector-memory operations outstanding, all LDS operations done
 template <int N>
 constexpr int waitcnt_vm() {
@@ -83,12 +102,16 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_wave_base)
                                    (lds_void_t*)(lds_wave_base), 16, 0, 0);
 }
 
-template <int PART, int BM, int BN, bool ALO, bool BLO>
+// QUANT: instead of storing C, quantise each (row, 128-column head) of it to INT16 exactly as
+// heal_qkv_quant_i16 does (s = fl32(max |c| / 32767), q = clamp(rint(fl32(c / s)), +-32767)) and store the
+// codes in Qo [M, N] and the scales in So [M, N / 128].
+template <int PART, int BM, int BN, bool ALO, bool BLO, bool QUANT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_comp_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
     const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
     const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
-    int64_t ldc) {
+    int64_t ldc, int16_t* __restrict__ Qo = nullptr, int64_t ldq = 0, float* __restrict__ So = nullptr,
+    int64_t ld_s = 0) {
   constexpr int NA = ALO ? 2 : 1, NB = BLO ? 2 : 1;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_PER_T = BM * kCPR / kThreads, B_PER_T = BN * kCPR / kThreads;
@@ -333,20 +356,87 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 
   // ---- epilogue: C = acc * 2^-(ea_i + eb_j), one rounding (exact unless the result is subnormal) ----
-  const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+  if constexpr (!QUANT) {
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int cl = wn * WN + j * 32 + (lane & 31);
-    const int64_t col = n0 + cl;
-    const int ebj = exps_s[BM + cl];
+    for (int j = 0; j < TN; ++j) {
+      const int cl = wn * WN + j * 32 + (lane & 31);
+      const int64_t col = n0 + cl;
+      const int ebj = exps_s[BM + cl];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t row = m0 + rl;
-        const float v = __builtin_amdgcn_ldexpf(acc[i][j][r], -(exps_s[rl] + ebj));
-        if (interior || (row < M && col < N)) C[row * ldc + col] = v;
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t row = m0 + rl;
+          const float v = __builtin_amdgcn_ldexpf(acc[i][j][r], -(exps_s[rl] + ebj));
+          if (interior || (row < M && col < N)) C[row * ldc + col] = v;
+        }
+      }
+    }
+  } else {
+    // A lane holds rows wm*WM + 32 i + 8 (r/4) + 4 (lane/32) + r%4 at columns wn*WN + 32 j + lane%32, so a
+    // row's values inside this wavefront sit in the 32 lanes of one half.  A head (128 columns) is 4
+    // column blocks of one wavefront (WN >= 128) or 2 blocks in each of the wavefronts wn = 0, 1 (WN = 64),
+    // whose partial maxima meet in LDS.  N is a multiple of 128, so a head is wholly in or out of range.
+    static_assert(WN % 128 == 0 || WN == 64, "a head is 128 columns");
+    constexpr int HW = WN >= 128 ? WN / 128 : 1;  // heads (or half heads) per wavefront
+    constexpr int JH = WN >= 128 ? 4 : TN;        // column blocks per head in this wavefront
+    auto cval = [&](int i, int j, int r) {
+      const int rl = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int cl = wn * WN + j * 32 + (lane & 31);
+      return __builtin_amdgcn_ldexpf(acc[i][j][r], -(exps_s[rl] + exps_s[BM + cl]));
+    };
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+      const int64_t c0h = n0 + wn * WN + hh * 128;  // first column of the head (WN = 64: of its half)
+      const int64_t head = c0h / 128;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {  // one 32-row block at a time keeps 16 maxima per lane live
+        float amax[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float m = 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < JH; ++jj) m = fmaxf(m, fabsf(cval(i, hh * JH + jj, r)));
+          amax[r] = halfwave_max32(m);
+        }
+        if constexpr (WN < 128) {
+          // the other half of the head is in wavefront (wm, wn ^ 1): exchange the row maxima through LDS
+          float* hred = reinterpret_cast<float*>(lds0);  // the stages are idle after the main loop
+          __syncthreads();
+          if ((lane & 31) == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rl = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              hred[2 * rl + wn] = amax[r];
+            }
+          }
+          __syncthreads();
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            amax[r] = fmaxf(amax[r], hred[2 * rl + (wn ^ 1)]);
+          }
+        }
+        if (c0h >= N) continue;  // wave-uniform
+        const bool all_rows = m0 + wm * WM + i * 32 + 32 <= M;  // wave-uniform: no per-row test needed
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t row = m0 + rl;
+          if (!all_rows && row >= M) continue;
+          const float sc = amax[r] / 32767.0f;  // IEEE fp32 division (correctly rounded build flag)
+          if ((lane & 31) == 0 && (WN >= 128 || wn == 0)) So[row * ld_s + head] = sc;
+          int16_t* qrow = Qo + row * ldq + n0 + wn * WN + (lane & 31);
+#pragma unroll
+          for (int jj = 0; jj < JH; ++jj) {
+            const int j = hh * JH + jj;
+            // a zero scale (all-zero row) gives zero codes: computed branch-free, then selected
+            const float q = fminf(fmaxf(rintf(cval(i, j, r) / sc), -32767.0f), 32767.0f);
+            qrow[j * 32] = (int16_t)(sc > 0.0f ? q : 0.0f);
+          }
+        }
       }
     }
   }
@@ -633,6 +723,48 @@ const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
     return sk[M <= 16 ? 0 : (M <= 32 ? 1 : 2)][nc == 4 ? 2 : nc - 1][products - 1];
   }
   return names[kind][products - 1];
+}
+
+template <int BM, int BN>
+hipError_t launch_tile_quant(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
+                             const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
+                             const int32_t* eb, int64_t ldb, int16_t* q, int64_t ldq, float* s, int64_t ld_s,
+                             hipStream_t stream) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const dim3 grid((unsigned)tiles), block(kThreads);
+  float* const c = nullptr;
+  if (al && bl)
+    hipLaunchKernelGGL((gemm_comp_kernel<HEAL_F16, BM, BN, true, true, true>), grid, block, 0, stream, M, N, K,
+                       ah, al, ea, lda, bh, bl, eb, ldb, c, (int64_t)0, q, ldq, s, ld_s);
+  else if (al)
+    hipLaunchKernelGGL((gemm_comp_kernel<HEAL_F16, BM, BN, true, false, true>), grid, block, 0, stream, M, N, K,
+                       ah, al, ea, lda, bh, bl, eb, ldb, c, (int64_t)0, q, ldq, s, ld_s);
+  else if (bl)
+    hipLaunchKernelGGL((gemm_comp_kernel<HEAL_F16, BM, BN, false, true, true>), grid, block, 0, stream, M, N, K,
+                       ah, al, ea, lda, bh, bl, eb, ldb, c, (int64_t)0, q, ldq, s, ld_s);
+  else
+    hipLaunchKernelGGL((gemm_comp_kernel<HEAL_F16, BM, BN, false, false, true>), grid, block, 0, stream, M, N,
+                       K, ah, al, ea, lda, bh, bl, eb, ldb, c, (int64_t)0, q, ldq, s, ld_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_comp_quant(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,
+                                  const int32_t* a_exp, int64_t lda, const uint16_t* b_hi, const uint16_t* b_lo,
+                                  const int32_t* b_exp, int64_t ldb, int16_t* q, int64_t ldq, float* s,
+                                  int64_t ld_s, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  // the tile kernels only: a skinny workgroup holds fewer columns than a head
+  switch (choose_tile(M, N)) {
+    case kTile256x256:
+      return launch_tile_quant<256, 256>(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, q, ldq, s, ld_s,
+                                         stream);
+    case kTile256x128:
+      return launch_tile_quant<256, 128>(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, q, ldq, s, ld_s,
+                                         stream);
+    default:
+      return launch_tile_quant<128, 128>(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, q, ldq, s, ld_s,
+                                         stream);
+  }
 }
 
 hipError_t launch_gemm_comp(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,

@@ -21,6 +21,10 @@ hipError_t launch_gemm_comp(int64_t M, int64_t N, int64_t K, const uint16_t* a_h
                             const int32_t* b_exp, int64_t ldb, int part, float* c, int64_t ldc,
                             hipStream_t stream);
 const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products);
+hipError_t launch_gemm_comp_quant(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,
+                                  const int32_t* a_exp, int64_t lda, const uint16_t* b_hi, const uint16_t* b_lo,
+                                  const int32_t* b_exp, int64_t ldb, int16_t* q, int64_t ldq, float* s,
+                                  int64_t ld_s, hipStream_t stream);
 size_t attn_workspace_bytes(const heal_attn_args& a);
 hipError_t launch_attn(const heal_attn_args& a, hipStream_t stream);
 size_t paged_workspace_bytes(const heal_paged_decode_args& a);

@@ -113,6 +113,26 @@ HEAL_API heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void*
                            void* stream);
 
 /*
+ * heal_gemm_comp_quant_i16 -- the compensated GEMM of heal_gemm_comp with the INT16 quantisation of
+ * heal_qkv_quant_i16 applied in its epilogue ([TS 2A Solution]: the attention inputs are stored as INT16), so
+ * a Q/K/V projection writes its INT16 codes and scales straight into a cache without an FP32 round trip.
+ * C (never stored) is split into heads of 128 consecutive columns; for each row i and head h:
+ *   s[i, h] = fl32(max_c |C[i, c]| / 32767),  q[i, c] = clamp(rint(fl32(C[i, c] / s[i, h])), -32767, 32767)
+ *   (q = 0 where s = 0), with C[i, c] the value heal_gemm_comp stores.
+ * For M > 64 the codes and scales equal heal_gemm_comp followed by heal_qkv_quant_i16 (tokens = M,
+ * heads = N / 128) bit for bit.  For M <= 64 heal_gemm_comp uses a skinny kernel whose summation order
+ * differs: both are within the FP32 accumulation bound of the exact sum, and a code may differ by one step.
+ * q is int16 [M, N] (leading dimension ldq, a multiple of 8), scale fp32 [M, N / 128] (leading dimension
+ * ld_s >= N / 128); q may point into a larger cache.  Only part_type HEAL_F16.
+ * Errors: as heal_gemm_comp (q and scale take the place of c), HEAL_ERR_SHAPE (N not a multiple of 128),
+ * HEAL_ERR_STRIDE (ldq < N, ld_s < N / 128), HEAL_ERR_DTYPE (part_type other than HEAL_F16).
+ */
+HEAL_API heal_status heal_gemm_comp_quant_i16(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
+                                     const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
+                                     const int32_t* b_exp, int64_t ldb, int part_type, int16_t* q, int64_t ldq,
+                                     float* scale, int64_t ld_s, void* stream);
+
+/*
  * heal_gemm_comp_variant -- the name of the kernel instantiation heal_gemm_comp launches for an M x N x K
  * problem with `products` (1..3) 16-bit products, e.g. "gemm_comp_kernel 256x128 P2" (static storage;
  * "none" for an empty problem).  For profiling: it lets a caller attribute a profiler's per-kernel times

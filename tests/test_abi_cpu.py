@@ -210,3 +210,23 @@ def test_paged_decode_validation(heal):
     assert call() == 8
     assert call(workspace=FAKE, workspace_bytes=16) == 8
     assert call(batch=0) == 0
+
+
+def test_gemm_quant_validation(heal):
+    lib = heal.load()
+    F16, BF16 = 2, 1
+    args = lambda M=4, N=128, K=8, ah=FAKE, bh=FAKE, q=FAKE, s=FAKE, lda=8, ldb=8, ldq=128, lds=1, part=F16: (
+        M, N, K, P(ah) if ah else None, None, None, lda, P(bh) if bh else None, None, None, ldb, part,
+        P(q) if q else None, ldq, P(s) if s else None, lds, None)
+    assert lib.heal_gemm_comp_quant_i16(*args(N=100, ldq=104)) == 2   # N not a multiple of 128
+    assert lib.heal_gemm_comp_quant_i16(*args(M=-1)) == 2
+    assert lib.heal_gemm_comp_quant_i16(*args(part=BF16)) == 5
+    assert lib.heal_gemm_comp_quant_i16(*args(q=None)) == 1
+    assert lib.heal_gemm_comp_quant_i16(*args(s=None)) == 1
+    assert lib.heal_gemm_comp_quant_i16(*args(ah=None)) == 1
+    assert lib.heal_gemm_comp_quant_i16(*args(ldq=64)) == 3
+    assert lib.heal_gemm_comp_quant_i16(*args(N=256, ldq=256, lds=1)) == 3  # ld_s < N / 128
+    assert lib.heal_gemm_comp_quant_i16(*args(q=MIS)) == 4
+    assert lib.heal_gemm_comp_quant_i16(*args(ldq=132)) == 4
+    assert lib.heal_gemm_comp_quant_i16(*args(s=FAKE + 2)) == 4
+    assert lib.heal_gemm_comp_quant_i16(*args(M=0)) == 0
