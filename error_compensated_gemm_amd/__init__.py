@@ -75,6 +75,10 @@ def load():
     L.heal_split.argtypes = [p, i32, i64, i64, i64, i32, p, p, i64, p, p]
     L.heal_gemm_comp.restype = i32
     L.heal_gemm_comp.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p]
+    L.heal_channel_exponents.restype = i32
+    L.heal_channel_exponents.argtypes = [p, i64, i64, i64, i32, p, p]
+    L.heal_split_scaled.restype = i32
+    L.heal_split_scaled.argtypes = [p, i32, i64, i64, i64, i32, p, p, i64, p, p, i32, p]
     L.heal_gemm_comp_quant_i16.restype = i32
     L.heal_gemm_comp_quant_i16.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p, i64, p]
     L.heal_gemm_comp_variant.restype = ctypes.c_char_p
@@ -95,7 +99,8 @@ def load():
 
 EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp", "heal_gemm_comp_variant",
             "heal_qkv_quant_i16", "heal_attn_workspace_bytes", "heal_attn_dual_fp16",
-            "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged", "heal_gemm_comp_quant_i16")
+            "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged", "heal_gemm_comp_quant_i16",
+            "heal_channel_exponents", "heal_split_scaled")
 
 
 def _check(status: int):
@@ -149,6 +154,48 @@ def heal_split(x, part: str = "f16", prescale: bool = True, residual: bool = Tru
     ex_arg = exps if prescale else None
     _check(L.heal_split(_ptr(x), xt, rows, cols, _ld(x), _PARTS[part], _ptr(hi), _ptr(lo_arg),
                         _ld(hi), _ptr(ex_arg), _stream(x.device)))
+    return hi, lo_arg, ex_arg
+
+
+def heal_channel_exponents(x, threshold_log2: int, col_exps=None):
+    """Outlier-channel exponents of a calibration batch ``x [rows, cols]`` fp32: int32 [cols] with
+    threshold_log2 - ilogb(max_r |x[r, c]|) for the columns whose maximum exceeds 2^threshold_log2, else 0."""
+    import torch
+
+    L = load()
+    rows, cols = x.shape
+    if col_exps is None:
+        col_exps = torch.empty((cols,), dtype=torch.int32, device=x.device)
+    _check(L.heal_channel_exponents(_ptr(x), rows, cols, _ld(x), int(threshold_log2), _ptr(col_exps),
+                                    _stream(x.device)))
+    return col_exps
+
+
+def heal_split_scaled(x, col_exps, col_sign: int, part: str = "f16", prescale: bool = True,
+                      residual: bool = True, hi=None, lo=None, exps=None):
+    """heal_split of x' = x * 2^(col_sign * col_exps[c]) per column (col_sign +1 for activations, -1 for
+    weights).  Returns (hi, lo or None, exps or None) like heal_split."""
+    import torch
+
+    L = load()
+    rows, cols = x.shape
+    if x.dtype == torch.float32:
+        xt = HEAL_F32
+    elif x.dtype == torch.bfloat16:
+        xt = HEAL_BF16
+    else:
+        raise TypeError(f"heal_split_scaled: unsupported dtype {x.dtype}")
+    ld_part = (cols + 7) // 8 * 8
+    if hi is None:
+        hi = torch.empty((rows, ld_part), dtype=torch.int16, device=x.device)[:, :cols]
+    if residual and lo is None:
+        lo = torch.empty((rows, ld_part), dtype=torch.int16, device=x.device)[:, :cols]
+    if prescale and exps is None:
+        exps = torch.empty((rows,), dtype=torch.int32, device=x.device)
+    lo_arg = lo if residual else None
+    ex_arg = exps if prescale else None
+    _check(L.heal_split_scaled(_ptr(x), xt, rows, cols, _ld(x), _PARTS[part], _ptr(hi), _ptr(lo_arg), _ld(hi),
+                               _ptr(ex_arg), _ptr(col_exps), int(col_sign), _stream(x.device)))
     return hi, lo_arg, ex_arg
 
 

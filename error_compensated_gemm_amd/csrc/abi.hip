@@ -61,6 +61,34 @@ heal_status heal_split(const void* x, int x_type, int64_t rows, int64_t cols, in
   }
 }
 
+heal_status heal_channel_exponents(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   int32_t threshold_log2, int32_t* col_exps, void* stream) {
+  if (rows < 0 || cols < 0 || threshold_log2 < -126 || threshold_log2 > 127) return HEAL_ERR_SHAPE;
+  if (cols == 0) return HEAL_OK;
+  if (!col_exps || (rows > 0 && !x)) return HEAL_ERR_NULL;
+  if (ld_x < cols) return HEAL_ERR_STRIDE;
+  if (!aligned4(x) || !aligned16(col_exps)) return HEAL_ERR_ALIGN;
+  return launched(heal::launch_channel_exps(x, rows, cols, ld_x, threshold_log2, col_exps, (hipStream_t)stream));
+}
+
+heal_status heal_split_scaled(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld_x,
+                              int part_type, void* hi, void* lo, int64_t ld_part, int32_t* exps,
+                              const int32_t* col_exps, int32_t col_sign, void* stream) {
+  if (rows < 0 || cols < 0) return HEAL_ERR_SHAPE;
+  if (x_type != HEAL_F32 && x_type != HEAL_BF16) return HEAL_ERR_DTYPE;
+  if (part_type != HEAL_F16 && part_type != HEAL_BF16) return HEAL_ERR_DTYPE;
+  if (col_sign != 1 && col_sign != -1) return HEAL_ERR_SHAPE;
+  if (rows == 0) return HEAL_OK;
+  if (cols > 0 && (!x || !hi || !col_exps)) return HEAL_ERR_NULL;
+  if (ld_x < cols || ld_part < cols) return HEAL_ERR_STRIDE;
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
+  if ((x_type == HEAL_F32 ? (xa & 3u) : (xa & 1u)) || (hi && !aligned16(hi)) || (lo && !aligned16(lo)) ||
+      (exps && !aligned4(exps)) || (col_exps && !aligned16(col_exps)) || (ld_part & 7))
+    return HEAL_ERR_ALIGN;
+  return launched(heal::launch_split_scaled(x, x_type, rows, cols, ld_x, part_type, hi, lo, ld_part, exps, col_exps,
+                                            col_sign, (hipStream_t)stream));
+}
+
 heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
                            const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
                            const int32_t* b_exp, int64_t ldb, int part_type, float* c, int64_t ldc,

@@ -12,6 +12,11 @@ hipError_t launch_split_f32(const float* x, int64_t rows, int64_t cols, int64_t 
                             void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream);
 hipError_t launch_split_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
                              void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream);
+hipError_t launch_split_scaled(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld_x, int part,
+                               void* hi, void* lo, int64_t ld_part, int32_t* exps, const int32_t* col_e,
+                               int col_sign, hipStream_t stream);
+hipError_t launch_channel_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int threshold_log2,
+                               int32_t* col_e, hipStream_t stream);
 hipError_t launch_split_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, void* hi, void* lo,
                             int64_t ld_part, hipStream_t stream);
 hipError_t launch_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim, int64_t ld_x,

@@ -72,18 +72,36 @@ __device__ __forceinline__ float load1(const uint16_t* p) {
 
 // One wavefront per row.  PRESCALE: e = 14 - ilogb(rowmax) (else 0).  RESID: write lo.
 // vec: every row of x starts 16-byte aligned (else every element takes the scalar path).
-template <typename TIn, int PART, bool PRESCALE, bool RESID>
+// COLS: every element is first scaled by its column's power of two, x' = fl32(x * 2^(col_sign * col_e[c]))
+// (exact unless it leaves the normal range), and the row is then split as x'.
+template <typename TIn, int PART, bool PRESCALE, bool RESID, bool COLS = false>
 __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__ x, int64_t rows,
                                                          int64_t cols, int64_t ld_x, int vec,
                                                          uint16_t* __restrict__ hi,
                                                          uint16_t* __restrict__ lo, int64_t ld_part,
-                                                         int32_t* __restrict__ exps) {
+                                                         int32_t* __restrict__ exps,
+                                                         const int32_t* __restrict__ col_e = nullptr,
+                                                         int col_sign = 0) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // the whole wave leaves together
   const TIn* xr = x + row * ld_x;
   const int64_t nvec = vec ? cols >> 3 : 0;
   const int64_t tail0 = nvec << 3;
+  // the column scaling of 8 consecutive values starting at column c0 (col_e is 16-byte aligned)
+  auto colscale8 = [&](float v[8], int64_t c0) {
+    if constexpr (COLS) {
+      const int4 a = *reinterpret_cast<const int4*>(col_e + c0);
+      const int4 b = *reinterpret_cast<const int4*>(col_e + c0 + 4);
+      const int ce[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = __builtin_amdgcn_ldexpf(v[i], col_sign * ce[i]);
+    }
+  };
+  auto colscale1 = [&](float v, int64_t c) {
+    if constexpr (COLS) return __builtin_amdgcn_ldexpf(v, col_sign * col_e[c]);
+    return v;
+  };
 
   int e = 0;
   if constexpr (PRESCALE) {
@@ -92,10 +110,11 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__
     for (int64_t c = lane; c < nvec; c += 64) {
       float v[8];
       load8(xr + (c << 3), v);
+      colscale8(v, c << 3);
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     }
-    for (int64_t c = tail0 + lane; c < cols; c += 64) amax = fmaxf(amax, fabsf(load1(xr + c)));
+    for (int64_t c = tail0 + lane; c < cols; c += 64) amax = fmaxf(amax, fabsf(colscale1(load1(xr + c), c)));
     amax = wave_max(amax);
     e = amax > 0.0f ? 14 - ilogb_pos(amax) : 0;
     if (lane == 0) exps[row] = e;
@@ -107,6 +126,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__
   for (int64_t c = lane; c < nvec; c += 64) {
     float v[8];
     load8(xr + (c << 3), v);
+    colscale8(v, c << 3);
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -128,7 +148,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__
     if constexpr (RESID) *reinterpret_cast<uint4*>(lr + (c << 3)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
   for (int64_t c = tail0 + lane; c < cols; c += 64) {
-    const float xv = load1(xr + c);
+    const float xv = colscale1(load1(xr + c), c);
     const float xs = PRESCALE ? __builtin_amdgcn_ldexpf(xv, e) : xv;
     float hb;
     hr[c] = round16<PART>(xs, &hb);
@@ -227,12 +247,60 @@ __global__ __launch_bounds__(256) void quant_i16_kernel(const float* __restrict_
   }
 }
 
+// Outlier-channel calibration: per column c, m = max_r |x[r, c]| and col_e[c] = T - ilogb(m) where
+// ilogb(m) > T (0 otherwise, and for an all-zero column).  A workgroup owns 64 columns; its 4 wavefronts
+// split the rows (each reads 256 consecutive bytes per row) and meet in LDS.
+__global__ __launch_bounds__(256) void channel_exps_kernel(const float* __restrict__ x, int64_t rows,
+                                                           int64_t cols, int64_t ld_x, int T,
+                                                           int32_t* __restrict__ col_e) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  float m = 0.0f;
+  if (c < cols)
+    for (int64_t r = wave; r < rows; r += 4) m = fmaxf(m, fabsf(x[r * ld_x + c]));
+  red[wave][lane] = m;
+  __syncthreads();
+  if (wave == 0 && c < cols) {
+    m = fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
+    const int il = m > 0.0f ? ilogb_pos(m) : 0;
+    col_e[c] = (m > 0.0f && il > T) ? T - il : 0;
+  }
+}
+
 inline unsigned blocks_for_rows(int64_t rows, int64_t per_block) {
   return (unsigned)((rows + per_block - 1) / per_block);
 }
 
 inline int rows_vectorisable(const void* x, int64_t ld_x, int64_t elem_bytes) {
   return ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && ((ld_x * elem_bytes) & 15) == 0) ? 1 : 0;
+}
+
+template <typename TIn>
+hipError_t launch_split_cols(const TIn* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
+                             void* lo, int64_t ld_part, int32_t* exps, const int32_t* col_e, int col_sign,
+                             hipStream_t stream) {
+  const int vec = rows_vectorisable(x, ld_x, (int64_t)sizeof(TIn));
+  const dim3 grid(blocks_for_rows(rows, 4)), block(256);
+  uint16_t* h = (uint16_t*)hi;
+  uint16_t* l = (uint16_t*)lo;
+  const bool pre = exps != nullptr, res = lo != nullptr;
+#define HEAL_SPLIT_CASE(PART, PRE, RES)                                                                      \
+  if (part == PART && pre == PRE && res == RES) {                                                             \
+    hipLaunchKernelGGL((split_rows_kernel<TIn, PART, PRE, RES, true>), grid, block, 0, stream, x, rows, cols, \
+                       ld_x, vec, h, l, ld_part, exps, col_e, col_sign);                                      \
+    return hipGetLastError();                                                                                 \
+  }
+  HEAL_SPLIT_CASE(HEAL_F16, true, true)
+  HEAL_SPLIT_CASE(HEAL_F16, true, false)
+  HEAL_SPLIT_CASE(HEAL_F16, false, true)
+  HEAL_SPLIT_CASE(HEAL_F16, false, false)
+  HEAL_SPLIT_CASE(HEAL_BF16, true, true)
+  HEAL_SPLIT_CASE(HEAL_BF16, true, false)
+  HEAL_SPLIT_CASE(HEAL_BF16, false, true)
+  HEAL_SPLIT_CASE(HEAL_BF16, false, false)
+#undef HEAL_SPLIT_CASE
+  return hipErrorInvalidValue;
 }
 
 template <typename TIn>
@@ -280,6 +348,29 @@ hipError_t launch_split_f32(const float* x, int64_t rows, int64_t cols, int64_t 
 hipError_t launch_split_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int part,
                              void* hi, void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream) {
   return launch_split_any<uint16_t>(x, rows, cols, ld_x, part, hi, lo, ld_part, exps, stream);
+}
+
+hipError_t launch_split_scaled(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld_x, int part,
+                               void* hi, void* lo, int64_t ld_part, int32_t* exps, const int32_t* col_e,
+                               int col_sign, hipStream_t stream) {
+  if (rows == 0 || cols == 0)  // no column scaling to apply: the exponents of empty rows as heal_split sets them
+    return x_type == HEAL_F32
+               ? launch_split_any<float>((const float*)x, rows, cols, ld_x, part, hi, lo, ld_part, exps, stream)
+               : launch_split_any<uint16_t>((const uint16_t*)x, rows, cols, ld_x, part, hi, lo, ld_part, exps,
+                                            stream);
+  if (x_type == HEAL_F32)
+    return launch_split_cols<float>((const float*)x, rows, cols, ld_x, part, hi, lo, ld_part, exps, col_e,
+                                    col_sign, stream);
+  return launch_split_cols<uint16_t>((const uint16_t*)x, rows, cols, ld_x, part, hi, lo, ld_part, exps, col_e,
+                                     col_sign, stream);
+}
+
+hipError_t launch_channel_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int threshold_log2,
+                               int32_t* col_e, hipStream_t stream) {
+  if (cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(channel_exps_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(256), 0, stream, x, rows, cols,
+                     ld_x, threshold_log2, col_e);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, void* hi, void* lo,

@@ -93,6 +93,29 @@ HEAL_API heal_status heal_split(const void* x, int x_type, int64_t rows, int64_t
                        void* hi, void* lo, int64_t ld_part, int32_t* exps, void* stream);
 
 /*
+ * Calibrated outlier channels -- the "targeted rescaling of rare outlier channels" of [TS 2B Overflow
+ * Handling] as an exact power-of-two scale per input channel (column of the activations X [M, K], column
+ * of the weights W [N, K]): X' = X diag(2^c), W' = W diag(2^-c), so X' W'^T = X W^T exactly while the
+ * large channels no longer set the row prescale of the ordinary values beside them.
+ *
+ * heal_channel_exponents: from a calibration batch x [rows, cols] FP32 (leading dimension ld_x), per column
+ *   m_c = max_r |x[r, c]|  and  col_exps[c] = threshold_log2 - ilogb(m_c) where ilogb(m_c) > threshold_log2,
+ *   else 0 (all-zero columns: 0).  So every column's maximum ends up below 2^(threshold_log2 + 1).
+ *   col_exps is int32 [cols], 16-byte aligned.  Errors: HEAL_ERR_NULL, HEAL_ERR_SHAPE (negative sizes,
+ *   threshold_log2 outside [-126, 127]), HEAL_ERR_STRIDE (ld_x < cols), HEAL_ERR_ALIGN (x not 4-byte aligned,
+ *   col_exps not 16-byte aligned).
+ * heal_split_scaled: heal_split (x_type HEAL_F32 or HEAL_BF16) applied to x'[r, c] = fl32(x[r, c] *
+ *   2^(col_sign * col_exps[c])) (exact unless x' leaves the fp32 normal range); col_sign = +1 for the
+ *   activations, -1 for the weights.  Errors: as heal_split, HEAL_ERR_NULL (col_exps NULL), HEAL_ERR_SHAPE
+ *   (col_sign not +-1), HEAL_ERR_DTYPE (x_type HEAL_I16), HEAL_ERR_ALIGN (col_exps not 16-byte aligned).
+ */
+HEAL_API heal_status heal_channel_exponents(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   int32_t threshold_log2, int32_t* col_exps, void* stream);
+HEAL_API heal_status heal_split_scaled(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld_x,
+                              int part_type, void* hi, void* lo, int64_t ld_part, int32_t* exps,
+                              const int32_t* col_exps, int32_t col_sign, void* stream);
+
+/*
  * heal_gemm_comp -- the error-compensated GEMM of [TS 2B Solution/Mechanism]:
  *   C[i, j] = 2^-(ea_i + eb_j) * sum_k ( ah*bh + [b_lo] ah*bl + [a_lo] al*bh )[i, k, j]
  * with A [M, K] given as parts a_hi / a_lo (leading dimension lda) and B given TRANSPOSED as parts

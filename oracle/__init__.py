@@ -274,3 +274,20 @@ def attn_paged_i16_f64(q, qs, k_pages, ks_pages, v_pages, vs_pages, block_table,
         vs = gather_pages(vs_pages, block_table[b], n, ps)[None]
         out[b] = attn_i16_f64(q[b][None, None], qs[b][None, None], k, ks, v, vs, causal=False, scale=scale)[0, 0]
     return out
+
+
+def channel_exponents(x: np.ndarray, threshold_log2: int) -> np.ndarray:
+    """[TS 2B Overflow Handling] rare outlier channels as exact power-of-two column scales (reading
+    R-chan): m_c = max_r |x[r, c]|; columns with ilogb(m_c) > T get T - ilogb(m_c), the others 0."""
+    x = np.asarray(x, np.float64)
+    m = np.max(np.abs(x), axis=0) if x.shape[0] else np.zeros(x.shape[1])
+    _, e = np.frexp(m)  # m = f 2^e with f in [0.5, 1): ilogb(m) = e - 1
+    il = e - 1
+    return np.where((m > 0) & (il > threshold_log2), threshold_log2 - il, 0).astype(np.int32)
+
+
+def scale_columns(x_values: np.ndarray, col_exps: np.ndarray, sign: int) -> np.ndarray:
+    """x'[r, c] = fl32(x[r, c] 2^(sign col_exps[c])): the product is exact in FP64 and rounded once to FP32
+    (round-to-nearest-even, gradual underflow)."""
+    x = np.asarray(x_values, np.float64)
+    return (x * np.ldexp(1.0, sign * np.asarray(col_exps, np.int64))[None, :]).astype(np.float32)

@@ -230,3 +230,31 @@ def test_gemm_quant_validation(heal):
     assert lib.heal_gemm_comp_quant_i16(*args(ldq=132)) == 4
     assert lib.heal_gemm_comp_quant_i16(*args(s=FAKE + 2)) == 4
     assert lib.heal_gemm_comp_quant_i16(*args(M=0)) == 0
+
+
+def test_channel_validation(heal):
+    lib = heal.load()
+    F32, BF16, F16, I16 = 0, 1, 2, 3
+    ce = lambda x=FAKE, rows=4, cols=8, ld=8, T=8, out=FAKE: lib.heal_channel_exponents(
+        P(x) if x else None, rows, cols, ld, T, P(out) if out else None, None)
+    assert ce(rows=-1) == 2
+    assert ce(T=200) == 2
+    assert ce(out=None) == 1
+    assert ce(x=None) == 1
+    assert ce(ld=4) == 3
+    assert ce(out=FAKE + 4) == 4
+    assert ce(x=FAKE + 2) == 4
+    assert ce(cols=0) == 0
+    sp = lambda x=FAKE, xt=F32, rows=4, cols=8, ldx=8, part=F16, hi=FAKE, lo=FAKE, ldp=8, e=FAKE, c=FAKE, sign=1: (
+        lib.heal_split_scaled(P(x) if x else None, xt, rows, cols, ldx, part, P(hi) if hi else None,
+                              P(lo) if lo else None, ldp, P(e) if e else None, P(c) if c else None, sign, None))
+    assert sp(sign=2) == 2
+    assert sp(xt=I16) == 5
+    assert sp(part=F32) == 5
+    assert sp(c=None) == 1
+    assert sp(hi=None) == 1
+    assert sp(ldx=4) == 3
+    assert sp(c=FAKE + 4) == 4
+    assert sp(hi=MIS) == 4
+    assert sp(ldp=12) == 4
+    assert sp(rows=0) == 0

@@ -141,3 +141,14 @@ def pages_from_contiguous(x: np.ndarray, seq_lens, table: np.ndarray, num_pages:
             j1 = min(int(n), j0 + page_size)
             pool[table[b, j0 // page_size], :j1 - j0] = x[b, j0:j1]
     return pool
+
+
+def massive_channels(M: int, K: int, frac: float = 0.01, big: float = 1e5, small: float = 1e-5, seed: int = 9):
+    """Activations with massive channels: small * N(0, 1) everywhere, except a fixed frac of the K channels
+    that carry +-big * U(0.5, 1) in every row.  Returns (x fp32 [M, K], the outlier channel indices)."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((M, K)) * small).astype(np.float32)
+    idx = np.sort(rng.choice(K, size=max(1, int(round(frac * K))), replace=False))
+    x[:, idx] = (rng.choice([-1.0, 1.0], size=(M, idx.size)) * rng.uniform(0.5, 1.0, (M, idx.size)) * big
+                 ).astype(np.float32)
+    return x, idx
