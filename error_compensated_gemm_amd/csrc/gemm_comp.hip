@@ -668,27 +668,47 @@ hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const uint16_t* ah, cons
 }
 
 // Kernel choice: M <= 64 streams B (skinny kernel); otherwise the largest block tile that still gives
-// every CU a workgroup.
+// every CU a workgroup.  Where A alone has a low part (two A tiles, one B tile per k step), a 128 x 256 tile
+// takes the place of 256 x 128: the same tile count, but each wavefront reads 2 x 2 A and 4 B fragments per
+// 16 MFMAs instead of 4 x 2 A and 2 B, so LDS reads fall from 10 to 8 fragments per 16 MFMAs.
 constexpr int64_t kSkinnyMaxM = 64;
-enum TileKind { kTile256x256 = 0, kTile256x128 = 1, kTile128x128 = 2, kSkinny = 3 };
-TileKind choose_tile(int64_t M, int64_t N) {
+enum TileKind { kTile256x256 = 0, kTile256x128 = 1, kTile128x128 = 2, kSkinny = 3, kTile128x256 = 4 };
+TileKind choose_tile(int64_t M, int64_t N, bool a_lo_only) {
   if (M <= kSkinnyMaxM) return kSkinny;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
+  const int64_t t128t = ((M + 127) / 128) * ((N + 255) / 256);
   if (t256 >= 256) return kTile256x256;
+  if (a_lo_only && t128t >= 256) return kTile128x256;
   if (t128 >= 256) return kTile256x128;
   return kTile128x128;
+}
+
+// The 128 x 256 tile, instantiated for its one use: A with a low part, B without.
+template <int PART, bool QUANT>
+hipError_t launch_tile_128x256(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
+                               const int32_t* ea, int64_t lda, const uint16_t* bh, const int32_t* eb, int64_t ldb,
+                               float* c, int64_t ldc, int16_t* q, int64_t ldq, float* s, int64_t ld_s,
+                               hipStream_t stream) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+  hipLaunchKernelGGL((gemm_comp_kernel<PART, 128, 256, true, false, QUANT>), dim3((unsigned)tiles),
+                     dim3(kThreads), 0, stream, M, N, K, ah, al, ea, lda, bh, (const uint16_t*)nullptr, eb, ldb, c,
+                     ldc, q, ldq, s, ld_s);
+  return hipGetLastError();
 }
 
 template <int PART>
 hipError_t launch_part(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
                        const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
                        const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
-  switch (choose_tile(M, N)) {
+  switch (choose_tile(M, N, al && !bl)) {
     case kSkinny:
       return launch_skinny<PART>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
     case kTile256x256:
       return launch_tile<PART, 256, 256>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    case kTile128x256:
+      return launch_tile_128x256<PART, false>(M, N, K, ah, al, ea, lda, bh, eb, ldb, c, ldc, nullptr, 0, nullptr,
+                                              0, stream);
     case kTile256x128:
       return launch_tile<PART, 256, 128>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
     default:
@@ -706,7 +726,8 @@ const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
       {"gemm_comp_kernel 128x128 P1", "gemm_comp_kernel 128x128 P2", "gemm_comp_kernel 128x128 P3"},
       {"gemm_skinny_kernel P1", "gemm_skinny_kernel P2", "gemm_skinny_kernel P3"}};
   if (M <= 0 || N <= 0 || products < 1 || products > 3) return "none";
-  const TileKind kind = choose_tile(M, N);
+  const TileKind kind = choose_tile(M, N, products == 2);
+  if (kind == kTile128x256) return "gemm_comp_kernel 128x256 P2";
   if (kind == kSkinny) {
     // [rows class][column blocks 1, 2, 4][products]
     static const char* sk[3][3][3] = {
@@ -754,7 +775,10 @@ hipError_t launch_gemm_comp_quant(int64_t M, int64_t N, int64_t K, const uint16_
                                   int64_t ld_s, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   // the tile kernels only: a skinny workgroup holds fewer columns than a head
-  switch (choose_tile(M, N)) {
+  switch (choose_tile(M, N, a_lo && !b_lo)) {
+    case kTile128x256:
+      return launch_tile_128x256<HEAL_F16, true>(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_exp, ldb, nullptr, 0, q,
+                                                 ldq, s, ld_s, stream);
     case kTile256x256:
       return launch_tile_quant<256, 256>(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, q, ldq, s, ld_s,
                                          stream);

@@ -157,8 +157,9 @@ HEAL_API heal_status heal_gemm_comp_quant_i16(int64_t M, int64_t N, int64_t K, c
 
 /*
  * heal_gemm_comp_variant -- the name of the kernel instantiation heal_gemm_comp launches for an M x N x K
- * problem with `products` (1..3) 16-bit products, e.g. "gemm_comp_kernel 256x128 P2" (static storage;
- * "none" for an empty problem).  For profiling: it lets a caller attribute a profiler's per-kernel times
+ * problem with `products` (1..3) 16-bit products, e.g. "gemm_comp_kernel 128x256 P2" (static storage;
+ * "none" for an empty problem).  products = 2 names the case where A has a low part and B has none (an
+ * activation times a 16-bit weight).  For profiling: it lets a caller attribute a profiler's per-kernel times
  * to problem shapes.  Pure host function, no device work.
  */
 HEAL_API const char* heal_gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products);
