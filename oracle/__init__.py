@@ -64,6 +64,7 @@ def lib():
         L.orc_split_f32.argtypes = [p, i64, i64, i64, ctypes.c_int, ctypes.c_int, p, p, i64, p]
         L.orc_split_bf16.argtypes = [p, i64, i64, i64, ctypes.c_int, ctypes.c_int, p, p, i64, p]
         L.orc_split_i16.argtypes = [p, i64, i64, i64, p, p, i64]
+        L.orc_unpack_i16.argtypes = [p, i64, i64, i64, ctypes.c_int, p, p, i64]
         L.orc_quant_i16.argtypes = [p, i64, i64, i64, i64, p, p]
         L.orc_gemm_f64.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
         L.orc_gemm_f64_points.argtypes = [i64, p, i64, p, i64, i64, p, p, p]
@@ -149,6 +150,21 @@ def split_i16(q: np.ndarray):
     hi = np.empty((rows, cols), np.uint16)
     lo = np.empty((rows, cols), np.uint16)
     lib().orc_split_i16(_ptr(q), rows, cols, cols, _ptr(hi), _ptr(lo), cols)
+    return hi, lo
+
+
+DUAL_READINGS = {"byte": 0, "shift10": 1, "float": 2}
+
+
+def unpack_i16(q: np.ndarray, reading: str):
+    """[TS 2A Mechanism] Dual-FP16 unpack under one of three readings of the pair (FP16 bits out):
+    "byte" hi = floor(q / 256), lo = q mod 256; "shift10" hi = floor(q / 1024), lo = q mod 1024;
+    "float" hi = fp16_rn(q), lo = 1024 (q - hi)."""
+    q = _c(q, np.int16)
+    rows, cols = q.shape
+    hi = np.empty((rows, cols), np.uint16)
+    lo = np.empty((rows, cols), np.uint16)
+    lib().orc_unpack_i16(_ptr(q), rows, cols, cols, DUAL_READINGS[reading], _ptr(hi), _ptr(lo), cols)
     return hi, lo
 
 

@@ -28,7 +28,10 @@
  *             ([TS 2A Solution] names only "INT16").
  *   R-dual    Dual-FP16 unpack is the byte split hi = q >> 8 (floor), lo = q & 0xFF, q = 256*hi + lo;
  *             the pages write the pair with a 2^10 shift ([TS 2A Mechanism]); any shift that keeps both
- *             halves integer is exact, and 8 keeps every FP32 partial sum exact at head_dim 128.
+ *             halves integer is exact, and 8 keeps every FP32 partial sum exact at head_dim 128.  Two
+ *             other readings are built as variants: the pages' formula taken as a bit split at 10,
+ *             q = 1024*hi + lo, and as a float-float pair, hi = fp16_rn(q), lo = 2^10 (q - hi), so that
+ *             q = hi + lo / 2^10.
  *   R-attn    attention is graded on the dequantised inputs s*q; causal masking is bottom-right aligned
  *             (key j visible to query i when j <= i + kv_len - q_len); GQA maps query head h to key/value
  *             head h / (n_q_heads / n_kv_heads).
@@ -164,6 +167,35 @@ void orc_split_i16(const int16_t* q, int64_t rows, int64_t cols, int64_t ld, uin
       const int v = q[r * ld + c];
       const int h = (v - (v & 0xFF)) / 256; /* floor(v / 256): v - (v mod 256) is a multiple of 256 */
       const int l = v & 0xFF;
+      hi[r * ld_part + c] = orc_f16_bits((float)h);
+      lo[r * ld_part + c] = orc_f16_bits((float)l);
+    }
+}
+
+/* ------------------------------------------------------------------------------------------------------
+ * Dual-FP16 unpack under the three readings of R-dual ([TS 2A Mechanism]), FP16 bit patterns out:
+ *   reading 0 (byte):     hi = floor(q / 256),  lo = q - 256*hi    (0 <= lo < 256)
+ *   reading 1 (shift-10): hi = floor(q / 1024), lo = q - 1024*hi   (0 <= lo < 1024)
+ *   reading 2 (float):    hi = q rounded to FP16 (nearest, ties to even), lo = 1024 * (q - hi)
+ * Every value written is an integer (times 2^10 for the float lo) of at most 11 significant bits, so
+ * its FP16 encoding is exact; the only rounding is the one that defines the float reading's hi.
+ * ---------------------------------------------------------------------------------------------------- */
+void orc_unpack_i16(const int16_t* q, int64_t rows, int64_t cols, int64_t ld, int reading, uint16_t* hi,
+                    uint16_t* lo, int64_t ld_part) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      const int v = q[r * ld + c];
+      double h, l;
+      if (reading == 0 || reading == 1) {
+        const int base = reading == 0 ? 256 : 1024;
+        const int m = ((v % base) + base) % base; /* v mod base in [0, base) */
+        h = (double)((v - m) / base);              /* exact division: v - m is a multiple of base */
+        l = (double)m;
+      } else {
+        const uint16_t hb = orc_f16_bits((float)v);
+        h = orc_f16_value(hb);
+        l = 1024.0 * ((double)v - h);
+      }
       hi[r * ld_part + c] = orc_f16_bits((float)h);
       lo[r * ld_part + c] = orc_f16_bits((float)l);
     }

@@ -150,3 +150,50 @@ def test_dual_fp16_exhaustive():
     assert np.array_equal(oracle.f16_bits(l.astype(np.float32)), lo[0])
     # exactness of FP32 partial sums over head_dim 128 for each product class (byte split)
     assert 128 * 128 * 128 < 2 ** 24 and 128 * 128 * 255 * 2 < 2 ** 24 and 128 * 255 * 255 < 2 ** 24
+
+
+def test_dual_readings_golden():
+    """Hand-derived pairs of all three readings of the Dual-FP16 pair ([TS 2A Mechanism]), including the
+    ties of the float reading (2049 -> 2048, 2051 -> 2052) and both ends of the INT16 range."""
+    cases = [list(map(int, l.split())) for l in open(os.path.join(GOLDEN, "dual_split_cases.txt"))
+             if l.strip() and not l.startswith("#")]
+    q = np.array([[c[0] for c in cases]], np.int16)
+    for col, reading in ((1, "byte"), (3, "shift10"), (5, "float")):
+        hi, lo = oracle.unpack_i16(q, reading)
+        h = oracle.part_values(hi[0], oracle.F16)
+        l = oracle.part_values(lo[0], oracle.F16)
+        assert np.array_equal(h, [c[col] for c in cases]), reading
+        assert np.array_equal(l, [c[col + 1] for c in cases]), reading
+
+
+def test_dual_readings_exhaustive():
+    """Every INT16 value under each reading: closed forms by integer arithmetic, numpy's own binary16
+    rounding for the float reading, exact reconstruction, and FP16 exactness of every half."""
+    q = np.arange(-32768, 32768, dtype=np.int32).astype(np.int16)
+    qi = q.astype(np.int64)
+    out = {}
+    for reading in ("byte", "shift10", "float"):
+        hi, lo = oracle.unpack_i16(q[None, :], reading)
+        h = oracle.part_values(hi[0], oracle.F16)
+        l = oracle.part_values(lo[0], oracle.F16)
+        assert np.array_equal(oracle.f16_bits(h.astype(np.float32)), hi[0])  # exact in fp16
+        assert np.array_equal(oracle.f16_bits(l.astype(np.float32)), lo[0])
+        out[reading] = (h, l)
+    h, l = out["byte"]
+    assert np.array_equal(h, qi // 256) and np.array_equal(l, qi % 256)
+    assert np.array_equal(256 * h + l, qi)
+    bh, bl = oracle.split_i16(q[None, :])  # the default reading is the byte split
+    assert np.array_equal(oracle.part_values(bh[0], oracle.F16), h)
+    h, l = out["shift10"]
+    assert np.array_equal(h, qi // 1024) and np.array_equal(l, qi % 1024)
+    assert np.all((h >= -32) & (h <= 31)) and np.all((l >= 0) & (l <= 1023))
+    assert np.array_equal(1024 * h + l, qi)
+    h, l = out["float"]
+    assert np.array_equal(h, q.astype(np.float16).astype(np.float64))  # numpy: round to nearest even
+    assert np.array_equal(h + l / 1024.0, qi.astype(np.float64))
+    assert np.all(np.abs(l) <= 16 * 1024)
+    assert np.all(l[np.abs(qi) <= 2048] == 0)
+    # FP32 exactness of the attention's accumulators at head_dim 128 (integer readings): shift-10 hi.hi
+    # partial sums are multiples of 2^20 with |sum hi hi'| <= 128 * 32 * 32 = 2^17; the byte split's are
+    # multiples of 2^16 with |sum| <= 128 * 128 * 128 = 2^21
+    assert 128 * 32 * 32 <= 2 ** 17 and 128 * 128 * 128 <= 2 ** 21
