@@ -411,6 +411,13 @@ def other_rows(heal, workloads, dev):
     rows["a6_prefill_1x4096x32x128_causal"] = {
         "us": round(t * 1e6, 2), "tflops_fp32eq": round(fl / t / 1e12, 2),
         "mfma_frac": round(8 * fl / 2 / t / 1e12 / PEAK_F16_TFLOPS, 4)}
+    # the other readings of the Dual-FP16 pair: shift-10 (4 + 4 products), float-float (3 + 3 products)
+    for reading, prods in (("shift10", 8), ("float", 6)):
+        t = time_fn(lambda: heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None],
+                                                     causal=True, out=out, dual_split=reading), 10)
+        rows[f"a6_prefill_1x4096x32x128_causal_{reading}"] = {
+            "us": round(t * 1e6, 2), "tflops_fp32eq": round(fl / t / 1e12, 2),
+            "mfma_frac": round(prods * fl / 2 / t / 1e12 / PEAK_F16_TFLOPS, 4)}
     del qd, kd, vd, qkv, q, k, v, out
     # a7: decode over an INT16 cache, 64 x 8192 keys, 32 q-heads / 8 kv-heads
     B, L, Hq, Hkv = 64, 8192, 32, 8
@@ -424,6 +431,11 @@ def other_rows(heal, workloads, dev):
     by = 2.0 * B * L * Hkv * 128 * 2 + 2.0 * B * L * Hkv * 4 + B * Hq * 128 * (2 + 4)
     rows["a7_decode_64x8192_gqa32_8"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
                                          "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
+    for reading in ("shift10", "float"):
+        t = time_fn(lambda: heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws,
+                                                     dual_split=reading), 10)
+        rows[f"a7_decode_64x8192_gqa32_8_{reading}"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
+                                                        "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
     # the same cache in 64-key pages of a shuffled pool (paged decode): pages gathered by index, no copy
     # of the keys on the timed path
     ps, npg = 64, L // 64

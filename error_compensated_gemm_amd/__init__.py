@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(HERE, "libheal.so")
 
 HEAL_F32, HEAL_BF16, HEAL_F16, HEAL_I16 = 0, 1, 2, 3
 _PARTS = {"f16": HEAL_F16, "bf16": HEAL_BF16}
+HEAL_DUAL_BYTE, HEAL_DUAL_SHIFT10, HEAL_DUAL_FLOAT = 0, 1, 2
+_DUAL = {"byte": HEAL_DUAL_BYTE, "shift10": HEAL_DUAL_SHIFT10, "float": HEAL_DUAL_FLOAT}
 
 _lib = None
 
@@ -35,7 +37,7 @@ class HealAttnArgs(ctypes.Structure):
         ("q_strides", ctypes.c_int64 * 3), ("kv_strides", ctypes.c_int64 * 3),
         ("qs_strides", ctypes.c_int64 * 3), ("kvs_strides", ctypes.c_int64 * 3),
         ("o_strides", ctypes.c_int64 * 3),
-        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("dual_split", ctypes.c_int32),
         ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -53,7 +55,7 @@ class HealPagedDecodeArgs(ctypes.Structure):
         ("q_strides", ctypes.c_int64 * 2), ("qs_strides", ctypes.c_int64 * 2),
         ("kv_strides", ctypes.c_int64 * 3), ("kvs_strides", ctypes.c_int64 * 3),
         ("o_strides", ctypes.c_int64 * 2), ("bt_stride", ctypes.c_int64),
-        ("softmax_scale", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float), ("dual_split", ctypes.c_int32),
         ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -73,6 +75,8 @@ def load():
     L.heal_abi_version.argtypes = []
     L.heal_split.restype = i32
     L.heal_split.argtypes = [p, i32, i64, i64, i64, i32, p, p, i64, p, p]
+    L.heal_unpack_i16.restype = i32
+    L.heal_unpack_i16.argtypes = [p, i64, i64, i64, i32, p, p, i64, p]
     L.heal_gemm_comp.restype = i32
     L.heal_gemm_comp.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p]
     L.heal_channel_exponents.restype = i32
@@ -100,7 +104,7 @@ def load():
 EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp", "heal_gemm_comp_variant",
             "heal_qkv_quant_i16", "heal_attn_workspace_bytes", "heal_attn_dual_fp16",
             "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged", "heal_gemm_comp_quant_i16",
-            "heal_channel_exponents", "heal_split_scaled")
+            "heal_channel_exponents", "heal_split_scaled", "heal_unpack_i16")
 
 
 def _check(status: int):
@@ -155,6 +159,24 @@ def heal_split(x, part: str = "f16", prescale: bool = True, residual: bool = Tru
     _check(L.heal_split(_ptr(x), xt, rows, cols, _ld(x), _PARTS[part], _ptr(hi), _ptr(lo_arg),
                         _ld(hi), _ptr(ex_arg), _stream(x.device)))
     return hi, lo_arg, ex_arg
+
+
+def heal_unpack_i16(x, dual_split: str = "byte", hi=None, lo=None):
+    """Dual-FP16 unpack of INT16 ``x [rows, cols]`` under the reading ``dual_split`` ("byte", "shift10" or
+    "float"); returns (hi, lo) as int16 tensors holding the FP16 bit patterns."""
+    import torch
+
+    if x.dtype != torch.int16:
+        raise TypeError("heal_unpack_i16: x must be int16")
+    rows, cols = x.shape
+    ld_part = (cols + 7) // 8 * 8
+    if hi is None:
+        hi = torch.empty((rows, ld_part), dtype=torch.int16, device=x.device)[:, :cols]
+    if lo is None:
+        lo = torch.empty((rows, ld_part), dtype=torch.int16, device=x.device)[:, :cols]
+    _check(load().heal_unpack_i16(_ptr(x), rows, cols, _ld(x), _DUAL[dual_split], _ptr(hi), _ptr(lo), _ld(hi),
+                                  _stream(x.device)))
+    return hi, lo
 
 
 def heal_channel_exponents(x, threshold_log2: int, col_exps=None):
@@ -270,7 +292,7 @@ def heal_qkv_quant_i16(x, q=None, scale=None):
 
 # ----------------------------------------------------------------------------------------- heal_attn_dual_fp16
 def make_attn_args(q, q_scale, k, k_scale, v, v_scale, out, causal: bool = True,
-                   softmax_scale: float | None = None, workspace=None) -> HealAttnArgs:
+                   softmax_scale: float | None = None, workspace=None, dual_split: str = "byte") -> HealAttnArgs:
     """Fill heal_attn_args from torch tensors q [B, Lq, Hq, D], k/v [B, Lkv, Hkv, D] (int16), scales
     [B, L, H] (fp32) and out [B, Lq, Hq, D] (fp32).  k and v must share strides, as must their scales."""
     B, Lq, Hq, D = q.shape
@@ -291,6 +313,7 @@ def make_attn_args(q, q_scale, k, k_scale, v, v_scale, out, causal: bool = True,
     a.o_strides[:] = list(out.stride()[:3])
     a.causal = 1 if causal else 0
     a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.dual_split = _DUAL[dual_split]
     a.out = out.data_ptr()
     if workspace is not None:
         a.workspace = workspace.data_ptr()
@@ -303,15 +326,16 @@ def heal_attn_workspace_bytes(args: HealAttnArgs) -> int:
 
 
 def heal_attn_dual_fp16(q, q_scale, k, k_scale, v, v_scale, causal: bool = True,
-                        softmax_scale: float | None = None, out=None, workspace=None):
+                        softmax_scale: float | None = None, out=None, workspace=None, dual_split: str = "byte"):
     """Attention over INT16 Q/K/V with Dual-FP16 products and FP32 softmax; returns out [B, Lq, Hq, D] fp32.
-    A workspace of heal_attn_workspace_bytes() is allocated with torch when none is given."""
+    ``dual_split`` selects the reading of the pair ("byte", "shift10" or "float").  A workspace of
+    heal_attn_workspace_bytes() is allocated with torch when none is given."""
     import torch
 
     L = load()
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    args = make_attn_args(q, q_scale, k, k_scale, v, v_scale, out, causal, softmax_scale, workspace)
+    args = make_attn_args(q, q_scale, k, k_scale, v, v_scale, out, causal, softmax_scale, workspace, dual_split)
     need = heal_attn_workspace_bytes(args)
     if need and workspace is None:
         workspace = torch.empty((need + 255) // 256 * 256, dtype=torch.uint8, device=q.device)
@@ -322,7 +346,8 @@ def heal_attn_dual_fp16(q, q_scale, k, k_scale, v, v_scale, causal: bool = True,
 
 
 def make_paged_args(q, q_scale, k_pages, k_scale, v_pages, v_scale, block_table, seq_lens, max_kv_len: int,
-                    out, softmax_scale: float | None = None, workspace=None) -> HealPagedDecodeArgs:
+                    out, softmax_scale: float | None = None, workspace=None,
+                    dual_split: str = "byte") -> HealPagedDecodeArgs:
     """Fill heal_paged_decode_args from torch tensors: q [B, Hq, D] int16, q_scale [B, Hq] fp32, k/v pages
     [P, page_size, Hkv, D] int16, their scales [P, page_size, Hkv] fp32, block_table [B, max_pages] int32,
     seq_lens [B] int32 and out [B, Hq, D] fp32.  k and v pages (and their scales) must share strides."""
@@ -347,6 +372,7 @@ def make_paged_args(q, q_scale, k_pages, k_scale, v_pages, v_scale, block_table,
     a.o_strides[:] = list(out.stride()[:2])
     a.bt_stride = block_table.stride(0)
     a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.dual_split = _DUAL[dual_split]
     a.out = out.data_ptr()
     if workspace is not None:
         a.workspace = workspace.data_ptr()
@@ -359,7 +385,8 @@ def heal_attn_paged_workspace_bytes(args: HealPagedDecodeArgs) -> int:
 
 
 def heal_attn_decode_paged(q, q_scale, k_pages, k_scale, v_pages, v_scale, block_table, seq_lens,
-                           max_kv_len: int, softmax_scale: float | None = None, out=None, workspace=None):
+                           max_kv_len: int, softmax_scale: float | None = None, out=None, workspace=None,
+                           dual_split: str = "byte"):
     """Decode attention (one query token per sequence) over a paged INT16 KV cache; returns out [B, Hq, D]
     fp32.  A workspace of heal_attn_paged_workspace_bytes() is allocated with torch when none is given."""
     import torch
@@ -368,7 +395,7 @@ def heal_attn_decode_paged(q, q_scale, k_pages, k_scale, v_pages, v_scale, block
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     args = make_paged_args(q, q_scale, k_pages, k_scale, v_pages, v_scale, block_table, seq_lens, max_kv_len,
-                           out, softmax_scale, workspace)
+                           out, softmax_scale, workspace, dual_split)
     need = heal_attn_paged_workspace_bytes(args)
     if need and workspace is None:
         workspace = torch.empty((need + 255) // 256 * 256, dtype=torch.uint8, device=q.device)

@@ -57,8 +57,26 @@ heal_status heal_split(const void* x, int x_type, int64_t rows, int64_t cols, in
       return launched(heal::launch_split_bf16((const uint16_t*)x, rows, cols, ld_x, part_type, hi, lo,
                                               ld_part, exps, s));
     default:
-      return launched(heal::launch_split_i16((const int16_t*)x, rows, cols, ld_x, hi, lo, ld_part, s));
+      return launched(heal::launch_unpack_i16((const int16_t*)x, rows, cols, ld_x, HEAL_DUAL_BYTE, hi, lo, ld_part,
+                                              s));
   }
+}
+
+static bool valid_dual_split(int d) {
+  return d == HEAL_DUAL_BYTE || d == HEAL_DUAL_SHIFT10 || d == HEAL_DUAL_FLOAT;
+}
+
+heal_status heal_unpack_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int dual_split, void* hi,
+                            void* lo, int64_t ld_part, void* stream) {
+  if (rows < 0 || cols < 0) return HEAL_ERR_SHAPE;
+  if (!valid_dual_split(dual_split)) return HEAL_ERR_DTYPE;
+  if (rows == 0 || cols == 0) return HEAL_OK;
+  if (!x || !hi || !lo) return HEAL_ERR_NULL;
+  if (ld_x < cols || ld_part < cols) return HEAL_ERR_STRIDE;
+  if ((reinterpret_cast<uintptr_t>(x) & 1u) || !aligned16(hi) || !aligned16(lo) || (ld_part & 7))
+    return HEAL_ERR_ALIGN;
+  return launched(
+      heal::launch_unpack_i16(x, rows, cols, ld_x, dual_split, hi, lo, ld_part, (hipStream_t)stream));
 }
 
 heal_status heal_channel_exponents(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -153,6 +171,7 @@ size_t heal_attn_workspace_bytes(const heal_attn_args* a) {
 
 heal_status heal_attn_dual_fp16(const heal_attn_args* a, void* stream) {
   if (!a) return HEAL_ERR_NULL;
+  if (!valid_dual_split(a->dual_split)) return HEAL_ERR_DTYPE;
   if (a->batch < 0 || a->q_len < 0 || a->kv_len < 0 || a->n_q_heads < 0 || a->n_kv_heads < 0 ||
       a->head_dim < 0)
     return HEAL_ERR_SHAPE;
@@ -188,6 +207,7 @@ size_t heal_attn_paged_workspace_bytes(const heal_paged_decode_args* a) {
 
 heal_status heal_attn_decode_paged(const heal_paged_decode_args* a, void* stream) {
   if (!a) return HEAL_ERR_NULL;
+  if (!valid_dual_split(a->dual_split)) return HEAL_ERR_DTYPE;
   if (a->batch < 0 || a->n_q_heads < 0 || a->n_kv_heads < 0 || a->head_dim < 0 || a->page_size < 0 ||
       a->num_pages < 0 || a->max_pages_per_seq < 0 || a->max_kv_len < 0)
     return HEAL_ERR_SHAPE;

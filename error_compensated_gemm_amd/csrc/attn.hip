@@ -6,10 +6,14 @@
 // LLM Inference: Achieving Reproducible Inference for Mission-Critical Tasks with HEAL", Technical Summary.
 //
 // Arithmetic (identical in both kernels):
-//   * unpack  q = 256 * (q >> 8) + (q & 0xFF):  H = fp16(q & ~0xFF) (multiple of 256, |H| <= 32768) and
-//     L = fp16(q & 0xFF) (0..255), both exact, H + L = q.
-//   * S_int = q_i . k_j as two FP32 accumulators: Hq.Hk (every partial sum is a multiple of 2^16 below
-//     2^37: exact) and Hq.Lk + Lq.Hk + Lq.Lk (about 2^-7 of the first); S_int = their FP32 sum.
+//   * unpack (default, the byte split)  q = 256 * (q >> 8) + (q & 0xFF):  H = fp16(q & ~0xFF) (multiple of
+//     256, |H| <= 32768) and L = fp16(q & 0xFF) (0..255), both exact, H + L = q.  Two other exact readings
+//     of the pair are selectable: the shift-10 split H = 1024 * (q >> 10), L = q & 0x3FF, and the
+//     float-float pair H = fp16_rn(q), L = q - H.
+//   * S_int = q_i . k_j as two FP32 accumulators: Hq.Hk (byte split: every partial sum is a multiple of
+//     2^16 below 2^37, exact; shift-10: multiples of 2^20 below 2^37, exact) and Hq.Lk + Lq.Hk + Lq.Lk
+//     (about 2^-7 of the first); S_int = their FP32 sum.  The float-float pair drops Lq.Lk and Lv.P~l
+//     (3 + 3 products), and its Hq.Hk sum rounds: about 2^-24 of sum |Hq Hk| per logit.
 //   * t_ij = S_int * s_k,j * (s_q,i * softmax_scale * log2 e), carried as an FP32 pair (hi + FMA-captured
 //     rounding error) so that t - max keeps its precision for logits of any size; online softmax in
 //     base 2, FP32 running maximum and sum.
@@ -55,26 +59,53 @@ __device__ __forceinline__ uint32_t pack2(_Float16 a, _Float16 b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Dual-FP16 unpack of 8 INT16 values (one 16-byte chunk): H = fp16(q & ~0xFF) = 256 * (q >> 8) and
-// L = fp16(q & 0xFF), two values per 32-bit word with packed FP16 arithmetic, exact by construction:
-//   L: the FP16 pattern 0x5C00 | (l << 2) is 256 + l (exponent 2^8, l in the top 8 mantissa bits), minus 256.
-//   H: with b = the signed high byte, 0x6400 | (b ^ 0x80) is 1024 + b + 128; minus 1152 gives b, times 256
-//      gives H (|H| <= 2^15).  Every intermediate is an integer below 2^11, so no step rounds.
+// Dual-FP16 unpack of 8 INT16 values (one 16-byte chunk) into FP16 halves H + L, two values per 32-bit
+// word.  The halves are scaled so that every product of two operands lands in the same accumulators:
+//   HEAL_DUAL_BYTE     H = 256 * (q >> 8), L = q & 0xFF;  H + L = q, both exact.  Packed FP16 arithmetic:
+//     L: the FP16 pattern 0x5C00 | (l << 2) is 256 + l (exponent 2^8, l in the top 8 mantissa bits), minus 256.
+//     H: with b = the signed high byte, 0x6400 | (b ^ 0x80) is 1024 + b + 128; minus 1152 gives b, times 256
+//        gives H (|H| <= 2^15).  Every intermediate is an integer below 2^11, so no step rounds.
+//   HEAL_DUAL_SHIFT10  H = 1024 * (q >> 10), L = q & 0x3FF;  H + L = q, both exact.
+//     L: 0x6400 | l is 1024 + l (ulp 1 in [1024, 2048)), minus 1024.
+//     H: with b = q >> 10 in [-32, 31] (the top 6 bits), 0x6400 | (f ^ 0x20) for the 6-bit field f is
+//        1024 + b + 32; minus 1056 gives b, times 1024 gives H.
+//   HEAL_DUAL_FLOAT    H = fp16_rn(q), L = q - H (an integer, |L| <= 16): the float-float pair, exact.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <int SPLIT>
 __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t& h, uint32_t& l) {
-  const f16x2 lo = __builtin_bit_cast(f16x2, ((w & 0x00FF00FFu) << 2) | 0x5C005C00u);
-  const f16x2 hb = __builtin_bit_cast(f16x2, ((w >> 8) & 0x00FF00FFu) ^ 0x64806480u);
-  const f16x2 c256 = {(_Float16)256.0f, (_Float16)256.0f};
-  const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
-  l = __builtin_bit_cast(uint32_t, lo - c256);
-  h = __builtin_bit_cast(uint32_t, (hb - c1152) * c256);
+  if constexpr (SPLIT == HEAL_DUAL_BYTE) {
+    const f16x2 lo = __builtin_bit_cast(f16x2, ((w & 0x00FF00FFu) << 2) | 0x5C005C00u);
+    const f16x2 hb = __builtin_bit_cast(f16x2, ((w >> 8) & 0x00FF00FFu) ^ 0x64806480u);
+    const f16x2 c256 = {(_Float16)256.0f, (_Float16)256.0f};
+    const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+    l = __builtin_bit_cast(uint32_t, lo - c256);
+    h = __builtin_bit_cast(uint32_t, (hb - c1152) * c256);
+  } else if constexpr (SPLIT == HEAL_DUAL_SHIFT10) {
+    const f16x2 lo = __builtin_bit_cast(f16x2, (w & 0x03FF03FFu) | 0x64006400u);
+    const f16x2 hb = __builtin_bit_cast(f16x2, ((w >> 10) & 0x003F003Fu) ^ 0x64206420u);
+    const f16x2 c1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const f16x2 c1056 = {(_Float16)1056.0f, (_Float16)1056.0f};
+    l = __builtin_bit_cast(uint32_t, lo - c1024);
+    h = __builtin_bit_cast(uint32_t, (hb - c1056) * c1024);
+  } else {
+    const float f0 = (float)(int16_t)(w & 0xFFFFu), f1 = (float)(int16_t)(w >> 16);
+    const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;  // round to nearest even
+    const _Float16 l0 = (_Float16)(f0 - (float)h0), l1 = (_Float16)(f1 - (float)h1);  // exact residuals
+    h = pack2(h0, h1);
+    l = pack2(l0, l1);
+  }
 }
+template <int SPLIT>
 __device__ __forceinline__ void unpack8(const uint4& raw, uint4& H, uint4& L) {
-  unpack_word(raw.x, H.x, L.x);
-  unpack_word(raw.y, H.y, L.y);
-  unpack_word(raw.z, H.z, L.z);
-  unpack_word(raw.w, H.w, L.w);
+  unpack_word<SPLIT>(raw.x, H.x, L.x);
+  unpack_word<SPLIT>(raw.y, H.y, L.y);
+  unpack_word<SPLIT>(raw.z, H.z, L.z);
+  unpack_word<SPLIT>(raw.w, H.w, L.w);
 }
+// The float-float pair drops L.L (|L| <= 16 beside |H| up to 2^15: the product is below 2^-22 of H.H);
+// the integer readings need all four products for an exact q.k.
+template <int SPLIT>
+constexpr bool kLoLo = SPLIT != HEAL_DUAL_FLOAT;
 
 __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
@@ -91,10 +122,13 @@ __device__ __forceinline__ int ilogb_pos(float x) { return __builtin_amdgcn_frex
 // costs 2^-24 |t|, which for logits of magnitude 10^3 moves exp2(t - m) by ~1e-4; carrying the product's
 // rounding error (FMA) keeps t - m accurate to ~2^-24 |t - m| instead.
 // S_int = shh + srest is first rounded with its error kept: s_hi + s_lo == shh + srest exactly.  Fast2Sum
-// suffices here although |srest| may exceed |shh|: shh sums products of two multiples of 256, so it is a
-// multiple of 2^16, while |srest| < 2^31 makes ulp(srest) <= 2^8; an addend that is a multiple of the
-// other's ulp makes the error term exact in either order.  t_hi is then the correctly rounded logit and
-// |t_lo| <= ~2^-23 |t_hi| whatever cancellation happens.
+// suffices here although |srest| may exceed |shh|.  Byte split: shh sums products of two multiples of 256,
+// so it is a multiple of 2^16, while |srest| < 2^31 makes ulp(srest) <= 2^8.  Shift-10 split: shh is a
+// multiple of 2^20 and |srest| < 2^34, ulp(srest) <= 2^10.  An addend that is a multiple of the other's ulp
+// makes the error term exact in either order.  t_hi is then the correctly rounded logit and
+// |t_lo| <= ~2^-23 |t_hi| whatever cancellation happens.  Float-float split: shh (a sum of 22-bit products
+// at different exponents) has already been rounded by its FP32 accumulator; Fast2Sum is exact whenever
+// |shh| >= |srest|, the usual case since |srest| is about 2^-11 |shh|.
 __device__ __forceinline__ void logit2(float shh, float srest, float sk, float cq, float& t_hi, float& t_lo) {
   const float s_hi = shh + srest;
   const float s_lo = srest - (s_hi - shh);
@@ -214,6 +248,7 @@ struct AttnParams {
   int page_shift;
 };
 
+template <int SPLIT>
 __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) {
   __shared__ PfRaw r0;
   __shared__ PfRaw r1;
@@ -279,10 +314,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
   // ---- unpack this thread's chunks of a landed tile into the Dual-FP16 planes ----
   auto unpack = [&](const PfRaw& R, PfPlanes& P) {
     uint4 hi, lo;
-    unpack8(R.k[tid], hi, lo);
+    unpack8<SPLIT>(R.k[tid], hi, lo);
     P.kh[kv_pos(ckey, cchunk)] = hi;
     P.kl[kv_pos(ckey, cchunk)] = lo;
-    unpack8(R.v[tid], hi, lo);
+    unpack8<SPLIT>(R.v[tid], hi, lo);
     P.vh[vt_pos<VT_PREFILL>(ckey, cchunk)] = hi;
     P.vl[vt_pos<VT_PREFILL>(ckey, cchunk)] = lo;
     if (wave == 0) {
@@ -299,7 +334,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
   const int16_t* qrow = a.q + b * a.q_st[0] + qi_c * a.q_st[1] + h * a.q_st[2];
   uint4 QH[8], QL[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) unpack8(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half), QH[ks], QL[ks]);
+  for (int ks = 0; ks < 8; ++ks)
+    unpack8<SPLIT>(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half), QH[ks], QL[ks]);
   const float cq = a.qs[b * a.qs_st[0] + qi_c * a.qs_st[1] + h * a.qs_st[2]] * a.scale_log2;
   // queries of this wave: [q0 + 32 wave, q0 + 32 wave + 31]; key j visible to query i iff j <= i + off
   const int64_t wq_first = q0 + 32 * wave, wq_last = wq_first + 31;
@@ -329,7 +365,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
       shh = mfma32(KH, QH[ks], shh);
       srest = mfma32(KH, QL[ks], srest);
       srest = mfma32(KL, QH[ks], srest);
-      srest = mfma32(KL, QL[ks], srest);
+      if constexpr (kLoLo<SPLIT>) srest = mfma32(KL, QL[ks], srest);
     }
     // ---- scores of this lane's query for its 16 keys: key = 8 (r/4) + 4 half + r%4.  Keys past the end
     //      or above this query's causal limit are hidden: tile key kk is visible iff kk < lim, so the lane's
@@ -412,7 +448,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
         O[dt] = mfma32(VH, PH, O[dt]);
         O[dt] = mfma32(VL, PH, O[dt]);
         O[dt] = mfma32(VH, PL, O[dt]);
-        O[dt] = mfma32(VL, PL, O[dt]);
+        if constexpr (kLoLo<SPLIT>) O[dt] = mfma32(VL, PL, O[dt]);
       }
     }
   };
@@ -483,7 +519,7 @@ size_t decode_workspace(int64_t B, int64_t Hq, int64_t Lkv) {
 
 // PAGED: the keys of each sequence are in pages of a shared pool (AttnParams::bt / lens) and every sequence
 // has its own length; otherwise one contiguous run of a.Lkv keys per (batch, kv head).
-template <bool PAGED>
+template <bool PAGED, int SPLIT>
 __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_decode_kernel(
     AttnParams a, float* __restrict__ ws, int nsplit) {
   // two stages per wavefront, each stage its own object (the compiler can tell the stage being read
@@ -527,7 +563,7 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int ks = 0; ks < 4; ++ks) {
       uint4 raw = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * grp);
       if (!qvalid) raw = make_uint4(0u, 0u, 0u, 0u);
-      unpack8(raw, QH[ks], QL[ks]);
+      unpack8<SPLIT>(raw, QH[ks], QL[ks]);
     }
   }
   const float cq = qvalid ? a.qs[b * a.qs_st[0] + hq * a.qs_st[2]] * a.scale_log2 : 0.0f;
@@ -617,11 +653,11 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         uint4 KH, KL;
-        unpack8(kraw[mt][ks], KH, KL);
+        unpack8<SPLIT>(kraw[mt][ks], KH, KL);
         shh[mt] = mfma16(KH, QH[ks], shh[mt]);
         srest[mt] = mfma16(KH, QL[ks], srest[mt]);
         srest[mt] = mfma16(KL, QH[ks], srest[mt]);
-        srest[mt] = mfma16(KL, QL[ks], srest[mt]);
+        if constexpr (kLoLo<SPLIT>) srest[mt] = mfma16(KL, QL[ks], srest[mt]);
       }
     }
     float skr[2][4] = {{skq[0].x, skq[0].y, skq[0].z, skq[0].w}, {skq[1].x, skq[1].y, skq[1].z, skq[1].w}};
@@ -696,11 +732,11 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       uint4 VH, VL;
-      unpack8(join_v4i16(vtr[dt][0], vtr[dt][1]), VH, VL);
+      unpack8<SPLIT>(join_v4i16(vtr[dt][0], vtr[dt][1]), VH, VL);
       O[dt] = mfma16(VH, PH, O[dt]);
       O[dt] = mfma16(VL, PH, O[dt]);
       O[dt] = mfma16(VH, PL, O[dt]);
-      O[dt] = mfma16(VL, PL, O[dt]);
+      if constexpr (kLoLo<SPLIT>) O[dt] = mfma16(VL, PL, O[dt]);
     }
   };
 
@@ -868,15 +904,28 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
   if (use_decode(x)) {
     const int nsplit = (int)((x.kv_len + DC_CHUNK - 1) / DC_CHUNK);
     float* ws = reinterpret_cast<float*>(x.workspace);
-    hipLaunchKernelGGL(attn_decode_kernel<false>, dim3((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads)),
-                       dim3(DC_THREADS), 0, stream, p, ws, nsplit);
+    const dim3 grid((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads));
+    if (x.dual_split == HEAL_DUAL_SHIFT10)
+      hipLaunchKernelGGL((attn_decode_kernel<false, HEAL_DUAL_SHIFT10>), grid, dim3(DC_THREADS), 0, stream, p, ws,
+                         nsplit);
+    else if (x.dual_split == HEAL_DUAL_FLOAT)
+      hipLaunchKernelGGL((attn_decode_kernel<false, HEAL_DUAL_FLOAT>), grid, dim3(DC_THREADS), 0, stream, p, ws,
+                         nsplit);
+    else
+      hipLaunchKernelGGL((attn_decode_kernel<false, HEAL_DUAL_BYTE>), grid, dim3(DC_THREADS), 0, stream, p, ws,
+                         nsplit);
     hipLaunchKernelGGL(attn_decode_merge_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream,
                        p, (const float*)ws, nsplit);
     return hipGetLastError();
   }
   const unsigned ntq = (unsigned)((x.q_len + PF_BQ - 1) / PF_BQ);
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)(x.batch * x.n_q_heads), ntq), dim3(PF_THREADS), 0,
-                     stream, p);
+  const dim3 grid((unsigned)(x.batch * x.n_q_heads), ntq);
+  if (x.dual_split == HEAL_DUAL_SHIFT10)
+    hipLaunchKernelGGL(attn_prefill_kernel<HEAL_DUAL_SHIFT10>, grid, dim3(PF_THREADS), 0, stream, p);
+  else if (x.dual_split == HEAL_DUAL_FLOAT)
+    hipLaunchKernelGGL(attn_prefill_kernel<HEAL_DUAL_FLOAT>, grid, dim3(PF_THREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_prefill_kernel<HEAL_DUAL_BYTE>, grid, dim3(PF_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -894,8 +943,16 @@ hipError_t launch_attn_paged(const heal_paged_decode_args& x, hipStream_t stream
   // the grid covers max_kv_len; splits past a sequence's own length write empty partials
   const int nsplit = (int)((x.max_kv_len + DC_CHUNK - 1) / DC_CHUNK);
   float* ws = reinterpret_cast<float*>(x.workspace);
-  hipLaunchKernelGGL(attn_decode_kernel<true>, dim3((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads)),
-                     dim3(DC_THREADS), 0, stream, p, ws, nsplit);
+  const dim3 grid((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads));
+  if (x.dual_split == HEAL_DUAL_SHIFT10)
+    hipLaunchKernelGGL((attn_decode_kernel<true, HEAL_DUAL_SHIFT10>), grid, dim3(DC_THREADS), 0, stream, p, ws,
+                       nsplit);
+  else if (x.dual_split == HEAL_DUAL_FLOAT)
+    hipLaunchKernelGGL((attn_decode_kernel<true, HEAL_DUAL_FLOAT>), grid, dim3(DC_THREADS), 0, stream, p, ws,
+                       nsplit);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<true, HEAL_DUAL_BYTE>), grid, dim3(DC_THREADS), 0, stream, p, ws,
+                       nsplit);
   hipLaunchKernelGGL(attn_decode_merge_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream, p,
                      (const float*)ws, nsplit);
   return hipGetLastError();

@@ -17,8 +17,8 @@ hipError_t launch_split_scaled(const void* x, int x_type, int64_t rows, int64_t 
                                int col_sign, hipStream_t stream);
 hipError_t launch_channel_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int threshold_log2,
                                int32_t* col_e, hipStream_t stream);
-hipError_t launch_split_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, void* hi, void* lo,
-                            int64_t ld_part, hipStream_t stream);
+hipError_t launch_unpack_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int dual_split, void* hi,
+                             void* lo, int64_t ld_part, hipStream_t stream);
 hipError_t launch_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim, int64_t ld_x,
                             int16_t* q, int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream);
 hipError_t launch_gemm_comp(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,

@@ -159,11 +159,32 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__
   }
 }
 
-// Dual-FP16 byte split: hi = q >> 8 (arithmetic shift = floor), lo = q & 0xFF; both exact in FP16.
-__global__ __launch_bounds__(256) void split_i16_kernel(const int16_t* __restrict__ x, int64_t rows,
-                                                        int64_t cols, int64_t ld_x, int vec,
-                                                        uint16_t* __restrict__ hi,
-                                                        uint16_t* __restrict__ lo, int64_t ld_part) {
+// Dual-FP16 pair of one INT16 value under each reading; every value is an integer (or an integer times
+// 2^10) of at most 11 significant bits, so each conversion to FP16 is exact except the one that defines the
+// float-float hi (round to nearest even).
+//   byte:     hi = q >> 8 (arithmetic shift = floor), lo = q & 0xFF
+//   shift-10: hi = q >> 10, lo = q & 0x3FF
+//   float:    hi = fp16_rn(q), lo = 2^10 (q - hi)  (q - hi is an integer of magnitude <= 16)
+template <int SPLIT>
+__device__ __forceinline__ void dual_pair(int q, _Float16& h, _Float16& l) {
+  if constexpr (SPLIT == HEAL_DUAL_BYTE) {
+    h = (_Float16)(float)(q >> 8);
+    l = (_Float16)(float)(q & 0xFF);
+  } else if constexpr (SPLIT == HEAL_DUAL_SHIFT10) {
+    h = (_Float16)(float)(q >> 10);
+    l = (_Float16)(float)(q & 0x3FF);
+  } else {
+    const float f = (float)q;
+    h = (_Float16)f;
+    l = (_Float16)(1024.0f * (f - (float)h));
+  }
+}
+
+template <int SPLIT>
+__global__ __launch_bounds__(256) void unpack_i16_kernel(const int16_t* __restrict__ x, int64_t rows,
+                                                         int64_t cols, int64_t ld_x, int vec,
+                                                         uint16_t* __restrict__ hi,
+                                                         uint16_t* __restrict__ lo, int64_t ld_part) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -177,10 +198,9 @@ __global__ __launch_bounds__(256) void split_i16_kernel(const int16_t* __restric
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int q0 = (int)(int16_t)(w[i] & 0xFFFFu);
-      const int q1 = (int)(int16_t)(w[i] >> 16);
-      const _Float16 h0 = (_Float16)(float)(q0 >> 8), h1 = (_Float16)(float)(q1 >> 8);
-      const _Float16 l0 = (_Float16)(float)(q0 & 0xFF), l1 = (_Float16)(float)(q1 & 0xFF);
+      _Float16 h0, l0, h1, l1;
+      dual_pair<SPLIT>((int)(int16_t)(w[i] & 0xFFFFu), h0, l0);
+      dual_pair<SPLIT>((int)(int16_t)(w[i] >> 16), h1, l1);
       hw[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
       lw[i] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
     }
@@ -188,9 +208,10 @@ __global__ __launch_bounds__(256) void split_i16_kernel(const int16_t* __restric
     *reinterpret_cast<uint4*>(lr + (c << 3)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
   for (int64_t c = (nvec << 3) + lane; c < cols; c += 64) {
-    const int q = xr[c];
-    hr[c] = __builtin_bit_cast(uint16_t, (_Float16)(float)(q >> 8));
-    lr[c] = __builtin_bit_cast(uint16_t, (_Float16)(float)(q & 0xFF));
+    _Float16 h, l;
+    dual_pair<SPLIT>(xr[c], h, l);
+    hr[c] = __builtin_bit_cast(uint16_t, h);
+    lr[c] = __builtin_bit_cast(uint16_t, l);
   }
 }
 
@@ -373,11 +394,20 @@ hipError_t launch_channel_exps(const float* x, int64_t rows, int64_t cols, int64
   return hipGetLastError();
 }
 
-hipError_t launch_split_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, void* hi, void* lo,
-                            int64_t ld_part, hipStream_t stream) {
+hipError_t launch_unpack_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int dual_split, void* hi,
+                             void* lo, int64_t ld_part, hipStream_t stream) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  hipLaunchKernelGGL(split_i16_kernel, dim3(blocks_for_rows(rows, 4)), dim3(256), 0, stream, x, rows, cols,
-                     ld_x, rows_vectorisable(x, ld_x, 2), (uint16_t*)hi, (uint16_t*)lo, ld_part);
+  const dim3 grid(blocks_for_rows(rows, 4)), block(256);
+  const int vec = rows_vectorisable(x, ld_x, 2);
+  if (dual_split == HEAL_DUAL_SHIFT10)
+    hipLaunchKernelGGL(unpack_i16_kernel<HEAL_DUAL_SHIFT10>, grid, block, 0, stream, x, rows, cols, ld_x, vec,
+                       (uint16_t*)hi, (uint16_t*)lo, ld_part);
+  else if (dual_split == HEAL_DUAL_FLOAT)
+    hipLaunchKernelGGL(unpack_i16_kernel<HEAL_DUAL_FLOAT>, grid, block, 0, stream, x, rows, cols, ld_x, vec,
+                       (uint16_t*)hi, (uint16_t*)lo, ld_part);
+  else
+    hipLaunchKernelGGL(unpack_i16_kernel<HEAL_DUAL_BYTE>, grid, block, 0, stream, x, rows, cols, ld_x, vec,
+                       (uint16_t*)hi, (uint16_t*)lo, ld_part);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define HEAL_ABI_VERSION 2
+#define HEAL_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define HEAL_API __attribute__((visibility("default")))
@@ -60,6 +60,16 @@ typedef enum {
 } heal_status;
 
 typedef enum { HEAL_F32 = 0, HEAL_BF16 = 1, HEAL_F16 = 2, HEAL_I16 = 3 } heal_dtype;
+
+/*
+ * Readings of the Dual-FP16 pair of an INT16 value q ([TS 2A Mechanism] writes the pair as
+ * X_hi + X_lo / 2^10 without fixing how the bits are divided).  Each is exact: q is recovered from the
+ * two FP16 values without rounding.
+ *   HEAL_DUAL_BYTE     hi = q >> 8 (floor), lo = q & 0xFF;           q = 256 hi + lo.  The default.
+ *   HEAL_DUAL_SHIFT10  hi = q >> 10 (floor), lo = q & 0x3FF;         q = 1024 hi + lo.
+ *   HEAL_DUAL_FLOAT    hi = fp16_rn(q), lo = 2^10 (q - hi);           q = hi + lo / 2^10 (|lo| <= 2^14).
+ */
+typedef enum { HEAL_DUAL_BYTE = 0, HEAL_DUAL_SHIFT10 = 1, HEAL_DUAL_FLOAT = 2 } heal_dual_split;
 
 /* Human-readable name of a status code (static storage; never NULL). */
 HEAL_API const char* heal_status_str(int status);
@@ -82,6 +92,7 @@ HEAL_API int heal_abi_version(void);
  * x_type = HEAL_I16 (x is int16 [rows, cols]): the byte split hi = x >> 8 (floor), lo = x & 0xFF, written
  *   as FP16 values with x = 256*hi + lo exactly.  part_type must be HEAL_F16, lo must be non-NULL and
  *   exps must be NULL.
+ * (heal_unpack_i16 below offers the other readings of the pair.)
  * hi and lo are [rows, cols] 16-bit, leading dimension ld_part.  Rows are independent; hi/lo must not
  * overlap x.  Alignment: x needs only its element alignment and any ld_x >= cols (rows that start on a
  * 16-byte boundary are read with 16-byte loads, others element by element); hi and lo must be 16-byte
@@ -91,6 +102,16 @@ HEAL_API int heal_abi_version(void);
  */
 HEAL_API heal_status heal_split(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld_x, int part_type,
                        void* hi, void* lo, int64_t ld_part, int32_t* exps, void* stream);
+
+/*
+ * heal_unpack_i16 -- the Dual-FP16 unpack of [TS 2A Mechanism] under any of the three readings of
+ * heal_dual_split: x is int16 [rows, cols] (leading dimension ld_x); hi and lo receive the FP16 bit
+ * patterns of the reading's two values, [rows, cols] with leading dimension ld_part.  HEAL_DUAL_BYTE gives
+ * the same output as heal_split with x_type HEAL_I16.  Alignment and errors as heal_split (x_type HEAL_I16),
+ * plus HEAL_ERR_DTYPE for a dual_split code outside heal_dual_split.
+ */
+HEAL_API heal_status heal_unpack_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int dual_split,
+                            void* hi, void* lo, int64_t ld_part, void* stream);
 
 /*
  * Calibrated outlier channels -- the "targeted rescaling of rare outlier channels" of [TS 2B Overflow
@@ -209,6 +230,7 @@ typedef struct {
   int64_t o_strides[3];
   int32_t causal;
   float softmax_scale;
+  int32_t dual_split; /* heal_dual_split; 0 (a zero-initialised struct) is the byte split */
   float* out;
   void* workspace;
   size_t workspace_bytes;
@@ -224,11 +246,13 @@ HEAL_API size_t heal_attn_workspace_bytes(const heal_attn_args* args);
  * Each INT16 operand is unpacked in registers into FP16 halves (hi = q >> 8, lo = q & 0xFF), QK^T is the
  * sum of the four 16-bit products of the halves, and PV is formed from P * s_v (renormalised by an exact
  * power of two and split into FP16 hi + lo) against the halves of V: 4 + 4 16-bit matrix products,
- * FP32 accumulation, FP32 output.  q_len = 1 takes the decode path (split over the keys, partial results
+ * FP32 accumulation, FP32 output.  args->dual_split selects the reading of the pair: HEAL_DUAL_SHIFT10
+ * (also 4 + 4 products, q.k still exact) or HEAL_DUAL_FLOAT (3 + 3 products: the lo.lo terms are dropped,
+ * and the FP32 sum of the hi.hi products rounds, about 2^-24 of sum |hi hi| per logit).  q_len = 1 takes the decode path (split over the keys, partial results
  * merged in a fixed order); q_len > 1 the prefill path.
  * Errors: HEAL_ERR_NULL, HEAL_ERR_SHAPE (sizes, n_q_heads % n_kv_heads != 0), HEAL_ERR_STRIDE,
  * HEAL_ERR_ALIGN (q/k/v/out 16-byte aligned, strides multiples of 8), HEAL_ERR_UNSUPPORTED
- * (head_dim != 128), HEAL_ERR_WORKSPACE.
+ * (head_dim != 128), HEAL_ERR_WORKSPACE, HEAL_ERR_DTYPE (dual_split outside heal_dual_split).
  */
 HEAL_API heal_status heal_attn_dual_fp16(const heal_attn_args* args, void* stream);
 
@@ -258,7 +282,7 @@ HEAL_API heal_status heal_attn_dual_fp16(const heal_attn_args* args, void* strea
  * Errors: HEAL_ERR_NULL, HEAL_ERR_SHAPE (sizes, n_q_heads % n_kv_heads != 0, max_pages_per_seq *
  * page_size < max_kv_len), HEAL_ERR_STRIDE, HEAL_ERR_ALIGN (q/pages/out 16-byte aligned, q/kv/o strides
  * multiples of 8), HEAL_ERR_UNSUPPORTED (head_dim, page_size, n_q_heads / n_kv_heads > 16),
- * HEAL_ERR_WORKSPACE.
+ * HEAL_ERR_WORKSPACE, HEAL_ERR_DTYPE (dual_split outside heal_dual_split).
  */
 typedef struct {
   int64_t batch, n_q_heads, n_kv_heads, head_dim;
@@ -278,6 +302,7 @@ typedef struct {
   int64_t o_strides[2];
   int64_t bt_stride;
   float softmax_scale; /* 0 selects 1/sqrt(head_dim) */
+  int32_t dual_split;  /* heal_dual_split, as in heal_attn_args */
   float* out;
   void* workspace;
   size_t workspace_bytes;

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(heal):
 
 def test_version_and_status_strings(heal):
     lib = heal.load()
-    assert lib.heal_abi_version() == 2
+    assert lib.heal_abi_version() == 3
     for s in range(9):
         assert lib.heal_status_str(s).decode().startswith("HEAL")
     assert b"unknown" in lib.heal_status_str(99)
@@ -81,6 +81,20 @@ def test_split_validation(heal):
     assert lib.heal_split(P(FAKE), I16, 4, 8, 8, F16, P(FAKE), P(FAKE), 8, P(FAKE), None) == 5  # I16 + exps
     assert lib.heal_split(P(FAKE), I16, 4, 8, 8, F16, P(FAKE), None, 8, None, None) == 1      # I16 needs lo
     assert lib.heal_split(None, F32, 0, 8, 8, F16, None, None, 8, None, None) == 0            # empty: OK
+
+
+def test_unpack_validation(heal):
+    lib = heal.load()
+    un = lib.heal_unpack_i16
+    assert un(None, 4, 8, 8, 0, P(FAKE), P(FAKE), 8, None) == 1       # NULL x
+    assert un(P(FAKE), 4, 8, 8, 0, P(FAKE), None, 8, None) == 1       # NULL lo
+    assert un(P(FAKE), 4, -8, 8, 0, P(FAKE), P(FAKE), 8, None) == 2   # shape
+    assert un(P(FAKE), 4, 8, 8, 3, P(FAKE), P(FAKE), 8, None) == 5    # unknown reading
+    assert un(P(FAKE), 4, 8, 4, 1, P(FAKE), P(FAKE), 8, None) == 3    # ld_x < cols
+    assert un(P(FAKE + 1), 4, 8, 8, 2, P(FAKE), P(FAKE), 8, None) == 4  # x not int16-aligned
+    assert un(P(FAKE), 4, 8, 8, 2, P(MIS), P(FAKE), 8, None) == 4     # hi misaligned
+    assert un(P(FAKE), 4, 8, 8, 2, P(FAKE), P(FAKE), 12, None) == 4   # ld_part % 8
+    assert un(P(FAKE), 0, 8, 8, 2, P(FAKE), P(FAKE), 8, None) == 0    # empty: no launch
 
 
 def test_gemm_validation(heal):
@@ -142,6 +156,7 @@ def test_attn_validation(heal):
     assert call(k=0) == 1
     assert call(out=MIS) == 4
     assert call(softmax_scale=-1.0) == 2
+    assert call(dual_split=3) == 5 and call(dual_split=-1) == 5  # not a reading of the Dual-FP16 pair
     a = _attn_args(heal)
     a.q_strides[1] = 100  # not a multiple of 8
     assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 4
@@ -197,6 +212,7 @@ def test_paged_decode_validation(heal):
     assert call(k_pages=0) == 1
     assert call(bt_stride=3) == 3
     assert call(softmax_scale=float("inf")) == 2
+    assert call(dual_split=7) == 5
     assert call(v_pages=MIS) == 4
     assert call(block_table=FAKE + 2) == 4
     a = _paged_args(heal)
