@@ -66,14 +66,14 @@ def source_sha256(path):
 
 def kernel_symbol(variant):
     """Template symbol of a GEMM variant name, as rocprofv3 prints it ("gemm_comp_kernel 256x128 P2" ->
-    "gemm_comp_kernel<2, 256, 128, true, false, false>": FP16 parts, block tile, a_lo used, b_lo used, no
-    fused quantisation)."""
+    "gemm_comp_kernel<2, 256, 128, true, false, false, false>": FP16 parts, block tile, a_lo used, b_lo
+    used, no fused quantisation, A given as parts)."""
     parts = variant.split()
     if len(parts) != 3 or parts[0] != "gemm_comp_kernel":
         return None
     bm, bn = parts[1].split("x")
     p = int(parts[2][1:])
-    return f"gemm_comp_kernel<2, {bm}, {bn}, {str(p >= 2).lower()}, {str(p >= 3).lower()}, false>"
+    return f"gemm_comp_kernel<2, {bm}, {bn}, {str(p >= 2).lower()}, {str(p >= 3).lower()}, false, false>"
 
 
 def stored_traffic(variant):
@@ -482,6 +482,34 @@ def other_rows(heal, workloads, dev):
         "us": round(t_f * 1e6, 2), "unfused_us": round(t_u * 1e6, 2), "tflops_fp32eq": round(fl / t_f / 1e12, 1),
         "kernel": heal.heal_gemm_comp_variant(2048, 6144, 4096, 2)}
     del X, Wq, ah, al, ea, bh, eb, qf, sf, c, qu, su
+    # split in the GEMM prologue: the three Llama-3-8B projections at M = 2048 and at M = 16, FP32
+    # activations split inside the GEMM (row exponents + heal_gemm_comp_f32a) against the split pass + the
+    # GEMM on its parts
+    for M in (2048, 16):
+        ops = []
+        for K, N in ((4096, 4096), (4096, 14336), (14336, 4096)):
+            X = dev(workloads.llama_activations(M, K, seed=8))
+            W = dev(workloads.llama_weights_bf16(N, K, seed=8).view(np.int16)).view(torch.bfloat16)
+            bh, _, eb = heal.heal_split(W, residual=False)
+            ah, al, ea = heal.heal_split(X)
+            c = heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
+            ops.append((X, bh, eb, ah, al, ea, c, heal.heal_row_exponents(X)))
+        def split_then_gemm():
+            for X, bh, eb, ah, al, ea, c, _ in ops:
+                heal.heal_split(X, hi=ah, lo=al, exps=ea)
+                heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
+        def split_in_prologue():
+            for X, bh, eb, _, _, _, c, e2 in ops:
+                heal.heal_row_exponents(X, exps=e2)
+                heal.heal_gemm_comp_f32a(X, e2, bh, None, eb, c=c)
+        t_f = t_u = float("inf")
+        for _ in range(3):
+            t_f = min(t_f, time_fn(split_in_prologue, 10))
+            t_u = min(t_u, time_fn(split_then_gemm, 10))
+        rows[f"split_in_prologue_{M}_llama3_8b_3_shapes"] = {"us": round(t_f * 1e6, 2),
+                                                             "split_then_gemm_us": round(t_u * 1e6, 2)}
+        del ops, X, W, bh, eb, ah, al, ea, c
+    torch.cuda.empty_cache()
     # config 5a: 8192^3 FP32 x FP32, rows scaled by 10^U(-3,3), P = 3
     A, Bt = workloads.gemm_rowscaled(8192, 8192, 8192, seed=4)
     ah, al, ea = heal.heal_split(dev(A))

@@ -75,6 +75,10 @@ def load():
     L.heal_abi_version.argtypes = []
     L.heal_split.restype = i32
     L.heal_split.argtypes = [p, i32, i64, i64, i64, i32, p, p, i64, p, p]
+    L.heal_row_exponents.restype = i32
+    L.heal_row_exponents.argtypes = [p, i64, i64, i64, p, p]
+    L.heal_gemm_comp_f32a.restype = i32
+    L.heal_gemm_comp_f32a.argtypes = [i64, i64, i64, p, i64, p, p, p, p, i64, p, i64, p]
     L.heal_unpack_i16.restype = i32
     L.heal_unpack_i16.argtypes = [p, i64, i64, i64, i32, p, p, i64, p]
     L.heal_gemm_comp.restype = i32
@@ -104,7 +108,8 @@ def load():
 EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp", "heal_gemm_comp_variant",
             "heal_qkv_quant_i16", "heal_attn_workspace_bytes", "heal_attn_dual_fp16",
             "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged", "heal_gemm_comp_quant_i16",
-            "heal_channel_exponents", "heal_split_scaled", "heal_unpack_i16")
+            "heal_channel_exponents", "heal_split_scaled", "heal_unpack_i16", "heal_row_exponents",
+            "heal_gemm_comp_f32a")
 
 
 def _check(status: int):
@@ -239,6 +244,34 @@ def heal_gemm_comp(a_hi, a_lo, a_exp, b_hi, b_lo, b_exp, part: str = "f16", c=No
         raise ValueError("b_lo must match b_hi's shape and strides")
     _check(L.heal_gemm_comp(M, N, K, _ptr(a_hi), _ptr(a_lo), _ptr(a_exp), _ld(a_hi), _ptr(b_hi), _ptr(b_lo),
                             _ptr(b_exp), _ld(b_hi), _PARTS[part], _ptr(c), _ld(c), _stream(a_hi.device)))
+    return c
+
+
+def heal_row_exponents(x, exps=None):
+    """Row exponents e = 14 - ilogb(max |x[r, :]|) of FP32 ``x [rows, cols]`` (those heal_split writes)."""
+    import torch
+
+    rows, cols = x.shape
+    if exps is None:
+        exps = torch.empty((rows,), dtype=torch.int32, device=x.device)
+    _check(load().heal_row_exponents(_ptr(x), rows, cols, _ld(x), _ptr(exps), _stream(x.device)))
+    return exps
+
+
+def heal_gemm_comp_f32a(a, a_exp, b_hi, b_lo, b_exp, c=None):
+    """Compensated GEMM with FP32 ``a [M, K]`` split inside the kernel (row exponents ``a_exp`` from
+    heal_row_exponents) against FP16 parts of B^T ``[N, K]``; returns C [M, N] fp32, bit for bit what
+    heal_split + heal_gemm_comp give."""
+    import torch
+
+    M, K = a.shape
+    N = b_hi.shape[0]
+    if c is None:
+        c = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.float32, device=a.device)[:, :N]
+    if b_lo is not None and (b_lo.shape != b_hi.shape or b_lo.stride() != b_hi.stride()):
+        raise ValueError("b_lo must match b_hi's shape and strides")
+    _check(load().heal_gemm_comp_f32a(M, N, K, _ptr(a), _ld(a), _ptr(a_exp), _ptr(b_hi), _ptr(b_lo), _ptr(b_exp),
+                                      _ld(b_hi), _ptr(c), _ld(c), _stream(a.device)))
     return c
 
 

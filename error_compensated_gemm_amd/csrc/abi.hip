@@ -126,6 +126,31 @@ heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, co
                                          c, ldc, (hipStream_t)stream));
 }
 
+heal_status heal_row_exponents(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t* exps,
+                               void* stream) {
+  if (rows < 0 || cols < 0) return HEAL_ERR_SHAPE;
+  if (rows == 0) return HEAL_OK;
+  if (!exps || (cols > 0 && !x)) return HEAL_ERR_NULL;
+  if (ld_x < cols) return HEAL_ERR_STRIDE;
+  if ((x && !aligned4(x)) || !aligned4(exps)) return HEAL_ERR_ALIGN;
+  return launched(heal::launch_row_exps(x, rows, cols, ld_x, exps, (hipStream_t)stream));
+}
+
+heal_status heal_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda, const int32_t* a_exp,
+                                const void* b_hi, const void* b_lo, const int32_t* b_exp, int64_t ldb, float* c,
+                                int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return HEAL_ERR_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
+  if (M == 0 || N == 0) return HEAL_OK;
+  if (!c || !a_exp || (K > 0 && (!a || !b_hi))) return HEAL_ERR_NULL;
+  if (lda < K || ldb < K || ldc < N) return HEAL_ERR_STRIDE;
+  if ((a && !aligned16(a)) || (b_hi && !aligned16(b_hi)) || (b_lo && !aligned16(b_lo)) || !aligned16(c) ||
+      !aligned4(a_exp) || (b_exp && !aligned4(b_exp)) || (lda & 3) || (ldb & 7) || (ldc & 3))
+    return HEAL_ERR_ALIGN;
+  return launched(heal::launch_gemm_comp_f32a(M, N, K, a, lda, a_exp, (const uint16_t*)b_hi, (const uint16_t*)b_lo,
+                                              b_exp, ldb, c, ldc, (hipStream_t)stream));
+}
+
 heal_status heal_gemm_comp_quant_i16(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
                                      const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
                                      const int32_t* b_exp, int64_t ldb, int part_type, int16_t* q, int64_t ldq,

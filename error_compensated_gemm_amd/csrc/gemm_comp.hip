@@ -70,6 +70,30 @@ __device__ __forceinline__ uint4 mask_chunk(uint4 v, int64_t valid) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// The FP16 split of 8 consecutive FP32 values of one row of A (bits in x0, x1) after the row's power-of-two
+// prescale, in the same operations as the standalone split ([TS 2B Mechanism, Overflow Handling]):
+// xs = fl32(x * 2^e), hi = fp16_rn(xs), lo = fp16_rn(xs - hi), the subtraction exact in FP32.  So a GEMM
+// that splits A on the way to its MFMAs multiplies exactly the parts the split pass would have written.
+struct Split8 {
+  uint4 hi, lo;
+};
+__device__ __forceinline__ uint32_t split2(uint32_t a, uint32_t b, int e, uint32_t& lo) {
+  const float xa = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, a), e);
+  const float xb = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, b), e);
+  const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
+  const _Float16 la = (_Float16)(xa - (float)ha), lb = (_Float16)(xb - (float)hb);
+  lo = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ Split8 split8(uint4 x0, uint4 x1, int e) {
+  Split8 r;
+  r.hi.x = split2(x0.x, x0.y, e, r.lo.x);
+  r.hi.y = split2(x0.z, x0.w, e, r.lo.y);
+  r.hi.z = split2(x1.x, x1.y, e, r.lo.z);
+  r.hi.w = split2(x1.z, x1.w, e, r.lo.w);
+  return r;
+}
+
 // maximum over the 32 lanes of each half-wavefront, with DPP and one swizzle (no LDS traffic): quad
 // swaps (lane ^ 1, lane ^ 2), mirrors within 8 and within 16 lanes, then lane ^ 16
 __device__ __forceinline__ float halfwave_max32(float m) {
@@ -105,13 +129,17 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_wave_base)
 // QUANT: instead of storing C, quantise each (row, 128-column head) of it to INT16 exactly as
 // heal_qkv_quant_i16 does (s = fl32(max |c| / 32767), q = clamp(rint(fl32(c / s)), +-32767)) and store the
 // codes in Qo [M, N] and the scales in So [M, N / 128].
-template <int PART, int BM, int BN, bool ALO, bool BLO, bool QUANT = false>
+// AF32: A arrives as FP32 rows (af, leading dimension lda in floats) with its row exponents ea; a stage
+// holds A as one FP32 plane (the bytes of the hi and lo planes together, chunk c of row r at
+// r * 8 + (c ^ (r & 7))), and each wavefront splits its A fragments in registers as it reads them.
+template <int PART, int BM, int BN, bool ALO, bool BLO, bool QUANT = false, bool AF32 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_comp_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
     const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
     const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
     int64_t ldc, int16_t* __restrict__ Qo = nullptr, int64_t ldq = 0, float* __restrict__ So = nullptr,
-    int64_t ld_s = 0) {
+    int64_t ld_s = 0, const float* __restrict__ af = nullptr) {
+  static_assert(!AF32 || (ALO && PART == HEAL_F16 && !QUANT), "FP32 A: FP16 parts, both A parts, plain C");
   constexpr int NA = ALO ? 2 : 1, NB = BLO ? 2 : 1;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_PER_T = BM * kCPR / kThreads, B_PER_T = BN * kCPR / kThreads;
@@ -162,14 +190,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint16_t* a_src[A_PER_T];
   const uint16_t* al_src[A_PER_T];
   int a_col[A_PER_T];
+  if constexpr (!AF32) {
 #pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int p = tid + kThreads * i, r = p / kCPR, c = (p % kCPR) ^ swz(r);
-    int64_t gr = m0 + r;
-    if (gr > M - 1) gr = M - 1;  // rows past M only feed outputs that are never stored
-    a_col[i] = 8 * c;
-    a_src[i] = ah + gr * lda + 8 * c;
-    al_src[i] = ALO ? al + gr * lda + 8 * c : nullptr;
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int p = tid + kThreads * i, r = p / kCPR, c = (p % kCPR) ^ swz(r);
+      int64_t gr = m0 + r;
+      if (gr > M - 1) gr = M - 1;  // rows past M only feed outputs that are never stored
+      a_col[i] = 8 * c;
+      a_src[i] = ah + gr * lda + 8 * c;
+      al_src[i] = ALO ? al + gr * lda + 8 * c : nullptr;
+    }
+  }
+  // FP32 A: position p = tid + 256 i of the plane holds row p / 8, chunk (p % 8) ^ (row & 7) of 4 floats
+  constexpr int AF_PER_T = AF32 ? 2 * A_PER_T : 1;
+  const float* af_src[AF_PER_T];
+  int af_col[AF_PER_T];
+  if constexpr (AF32) {
+#pragma unroll
+    for (int i = 0; i < AF_PER_T; ++i) {
+      const int p = tid + kThreads * i, r = p >> 3, c = (p & 7) ^ (r & 7);
+      int64_t gr = m0 + r;
+      if (gr > M - 1) gr = M - 1;
+      af_col[i] = 4 * c;
+      af_src[i] = af + gr * lda + 4 * c;
+    }
   }
   const uint16_t* b_src[B_PER_T];
   const uint16_t* bl_src[B_PER_T];
@@ -185,11 +229,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   // full K tiles: direct-to-LDS
   auto dma_stage = [&](uint4* s, int64_t k0) {
+    if constexpr (AF32) {
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      uint4* dst = s + kThreads * i + 64 * wave;
-      dma16(a_src[i] + k0, dst);
-      if constexpr (ALO) dma16(al_src[i] + k0, dst + APLANE);
+      for (int i = 0; i < AF_PER_T; ++i)
+        dma16(reinterpret_cast<const uint16_t*>(af_src[i] + k0), s + kThreads * i + 64 * wave);
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) {
+        uint4* dst = s + kThreads * i + 64 * wave;
+        dma16(a_src[i] + k0, dst);
+        if constexpr (ALO) dma16(al_src[i] + k0, dst + APLANE);
+      }
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
@@ -201,14 +251,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // the partial last K tile: through registers, zeroing the columns at or past K
   const int64_t klast = ((K + 7) / 8 - 1) * 8;
   auto tail_stage = [&](uint4* s, int64_t k0) {
+    if constexpr (AF32) {  // element by element: an FP32 row need not extend past K
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int64_t k = k0 + a_col[i];
-      const int64_t kc = k < klast ? k : klast;
-      s[kThreads * i + tid] = mask_chunk(*reinterpret_cast<const uint4*>(a_src[i] - a_col[i] + kc), K - k);
-      if constexpr (ALO)
-        s[APLANE + kThreads * i + tid] =
-            mask_chunk(*reinterpret_cast<const uint4*>(al_src[i] - a_col[i] + kc), K - k);
+      for (int i = 0; i < AF_PER_T; ++i) {
+        const float* row = af_src[i] - af_col[i];
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t k = k0 + af_col[i] + j;
+          const float v = row[k < K ? k : K - 1];
+          w[j] = k < K ? __builtin_bit_cast(uint32_t, v) : 0u;
+        }
+        s[kThreads * i + tid] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) {
+        const int64_t k = k0 + a_col[i];
+        const int64_t kc = k < klast ? k : klast;
+        s[kThreads * i + tid] = mask_chunk(*reinterpret_cast<const uint4*>(a_src[i] - a_col[i] + kc), K - k);
+        if constexpr (ALO)
+          s[APLANE + kThreads * i + tid] =
+              mask_chunk(*reinterpret_cast<const uint4*>(al_src[i] - a_col[i] + kc), K - k);
+      }
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
@@ -252,8 +317,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * WM + i * 32 + frow;
+      if constexpr (AF32) {
+        const int c0 = 4 * ks + 2 * fhalf, sw = r & 7;
+        const Split8 sp = split8(s[r * 8 + (c0 ^ sw)], s[r * 8 + ((c0 + 1) ^ sw)], exps_s[r]);
+        F.a[0][i] = sp.hi;
+        F.a[1][i] = sp.lo;
+      } else {
 #pragma unroll
-      for (int p = 0; p < NA; ++p) F.a[p][i] = s[p * APLANE + r * kCPR + (c ^ swz(r))];
+        for (int p = 0; p < NA; ++p) F.a[p][i] = s[p * APLANE + r * kCPR + (c ^ swz(r))];
+      }
     }
   };
   auto mma = [&](const Frag& F) {
@@ -463,12 +535,16 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f3
 
 constexpr int kSkWaves = 8;
 
-template <int PART, int MT, int NC, bool ALO, bool BLO>
+// AF32: A arrives as FP32 rows (af, leading dimension lda in floats) with row exponents ea; a lane's 8
+// values of a K step are held as raw FP32 bits (the registers the hi and lo chunks would take) and split
+// just before the MFMAs, so the prefetch never waits on them.
+template <int PART, int MT, int NC, bool ALO, bool BLO, bool AF32 = false>
 __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
     const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
     const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
-    int64_t ldc) {
+    int64_t ldc, const float* __restrict__ af = nullptr) {
+  static_assert(!AF32 || (ALO && PART == HEAL_F16), "FP32 A: FP16 parts, both A parts");
   __shared__ float red[kSkWaves][MT * NC][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cl = lane & 15, kg = lane >> 4;
@@ -484,12 +560,19 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   }
   const uint16_t* arow[MT];
   const uint16_t* alrow[MT];
+  const float* afrow[MT];
+  int ea_l[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     int64_t m = 16 * mt + cl;
     if (m > M - 1) m = M - 1;
-    arow[mt] = ah + m * lda;
-    alrow[mt] = ALO ? al + m * lda : nullptr;
+    if constexpr (AF32) {
+      afrow[mt] = af + m * lda;
+      ea_l[mt] = ea[m];
+    } else {
+      arow[mt] = ah + m * lda;
+      alrow[mt] = ALO ? al + m * lda : nullptr;
+    }
   }
   const int64_t nsteps = (K + 31) / 32, nfull = K / 32;
   const int64_t klast = ((K + 7) / 8 - 1) * 8;
@@ -499,8 +582,20 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc) acc[mt][nc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma1 = [&](const uint4 (&a)[MT], const uint4 (&a2)[ALO ? MT : 1], const uint4 (&b)[NC],
+  auto mma1 = [&](const uint4 (&a_in)[MT], const uint4 (&a2_in)[ALO ? MT : 1], const uint4 (&b)[NC],
                   const uint4 (&b2)[BLO ? NC : 1]) {
+    uint4 a[MT], a2[ALO ? MT : 1];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (AF32) {
+        const Split8 sp = split8(a_in[mt], a2_in[mt], ea_l[mt]);  // raw FP32 bits -> hi, lo
+        a[mt] = sp.hi;
+        a2[mt] = sp.lo;
+      } else {
+        a[mt] = a_in[mt];
+        if constexpr (ALO) a2[mt] = a2_in[mt];
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -509,6 +604,24 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
         if constexpr (BLO) acc[mt][nc] = mfma16<PART>(a[mt], b2[nc], acc[mt][nc]);
         if constexpr (ALO) acc[mt][nc] = mfma16<PART>(a2[mt], b[nc], acc[mt][nc]);
       }
+  };
+  // FP32 A: the 8 values of row afrow[mt] from column k, as raw bits (all in bounds for a full step)
+  struct Raw8 {
+    uint4 x0, x1;
+  };
+  auto load_af = [&](int mt, int64_t k) -> Raw8 {
+    return Raw8{*reinterpret_cast<const uint4*>(afrow[mt] + k), *reinterpret_cast<const uint4*>(afrow[mt] + k + 4)};
+  };
+  // the same for the partial last step, the columns at or past K cleared (and never read)
+  auto load_af_tail = [&](int mt, int64_t k) -> Raw8 {
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t kk = k + j;
+      const float v = afrow[mt][kk < K ? kk : K - 1];
+      w[j] = kk < K ? __builtin_bit_cast(uint32_t, v) : 0u;
+    }
+    return Raw8{make_uint4(w[0], w[1], w[2], w[3]), make_uint4(w[4], w[5], w[6], w[7])};
   };
   // one K step with the columns at or past K cleared (the partial last step; padding past K may hold any
   // bits, even NaN patterns, so both operands are cleared)
@@ -522,8 +635,14 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      a[mt] = mask_chunk(load_chunk(arow[mt], k, klast), K - k);
-      if constexpr (ALO) a2[mt] = mask_chunk(load_chunk(alrow[mt], k, klast), K - k);
+      if constexpr (AF32) {
+        const Raw8 r = load_af_tail(mt, k);
+        a[mt] = r.x0;
+        a2[mt] = r.x1;
+      } else {
+        a[mt] = mask_chunk(load_chunk(arow[mt], k, klast), K - k);
+        if constexpr (ALO) a2[mt] = mask_chunk(load_chunk(alrow[mt], k, klast), K - k);
+      }
     }
     mma1(a, a2, b, b2);
   };
@@ -547,8 +666,14 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        g.a[u][mt] = load_chunk(arow[mt], k, klast);
-        if constexpr (ALO) g.a2[u][mt] = load_chunk(alrow[mt], k, klast);
+        if constexpr (AF32) {
+          const Raw8 r = load_af(mt, k);
+          g.a[u][mt] = r.x0;
+          g.a2[u][mt] = r.x1;
+        } else {
+          g.a[u][mt] = load_chunk(arow[mt], k, klast);
+          if constexpr (ALO) g.a2[u][mt] = load_chunk(alrow[mt], k, klast);
+        }
       }
     }
   };
@@ -788,6 +913,80 @@ hipError_t launch_gemm_comp_quant(int64_t M, int64_t N, int64_t K, const uint16_
     default:
       return launch_tile_quant<128, 128>(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, q, ldq, s, ld_s,
                                          stream);
+  }
+}
+
+namespace {
+
+// FP32 A split in the GEMM: the same kernel choice as launch_gemm_comp (with both A parts), so both paths
+// run the same MFMAs in the same accumulation order on the same operand bits.  (Every tile kernel sums an
+// element over the same 16-wide k steps, with the same products per step in the same order, so the block
+// tile does not change the result: the three-product 256 x 256 case, whose registers the in-register
+// split does not fit, runs on 256 x 128 tiles with identical output.)
+template <int MT, int NC>
+hipError_t launch_skinny_f32a_nc(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,
+                                 const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
+                                 int64_t ldc, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + 16 * NC - 1) / (16 * NC))), block(64 * kSkWaves);
+  const uint16_t* const none = nullptr;
+  if (bl)
+    hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, true, true>), grid, block, 0, stream, M, N, K,
+                       none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, false, true>), grid, block, 0, stream, M, N,
+                       K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny_f32a(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,
+                              const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
+                              int64_t ldc, hipStream_t stream) {
+  const int nc = skinny_nc(M, N);
+  if (M <= 16) {
+    if (nc >= 4) return launch_skinny_f32a_nc<1, 4>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    if (nc == 2) return launch_skinny_f32a_nc<1, 2>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    return launch_skinny_f32a_nc<1, 1>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  }
+  if (M <= 32) {
+    if (nc >= 2) return launch_skinny_f32a_nc<2, 2>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    return launch_skinny_f32a_nc<2, 1>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  }
+  return launch_skinny_f32a_nc<4, 1>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+}
+
+template <int BM, int BN, bool BLO>
+hipError_t launch_tile_f32a(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,
+                            const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
+                            int64_t ldc, hipStream_t stream) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const uint16_t* const none = nullptr;
+  hipLaunchKernelGGL((gemm_comp_kernel<HEAL_F16, BM, BN, true, BLO, false, true>), dim3((unsigned)tiles),
+                     dim3(kThreads), 0, stream, M, N, K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc,
+                     (int16_t*)nullptr, (int64_t)0, (float*)nullptr, (int64_t)0, af);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda, const int32_t* a_exp,
+                                 const uint16_t* b_hi, const uint16_t* b_lo, const int32_t* b_exp, int64_t ldb,
+                                 float* c, int64_t ldc, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const bool blo = b_lo != nullptr;
+  switch (choose_tile(M, N, !blo)) {
+    case kSkinny:
+      return launch_skinny_f32a(M, N, K, a, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
+    case kTile256x256:
+      return blo ? launch_tile_f32a<256, 128, true>(M, N, K, a, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream)
+                 : launch_tile_f32a<256, 256, false>(M, N, K, a, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
+    case kTile128x256:  // chosen only when B has no low part
+      return launch_tile_f32a<128, 256, false>(M, N, K, a, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
+    case kTile256x128:
+      return blo ? launch_tile_f32a<256, 128, true>(M, N, K, a, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream)
+                 : launch_tile_f32a<256, 128, false>(M, N, K, a, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
+    default:
+      return blo ? launch_tile_f32a<128, 128, true>(M, N, K, a, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream)
+                 : launch_tile_f32a<128, 128, false>(M, N, K, a, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
   }
 }
 

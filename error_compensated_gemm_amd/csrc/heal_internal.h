@@ -15,6 +15,8 @@ hipError_t launch_split_bf16(const uint16_t* x, int64_t rows, int64_t cols, int6
 hipError_t launch_split_scaled(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld_x, int part,
                                void* hi, void* lo, int64_t ld_part, int32_t* exps, const int32_t* col_e,
                                int col_sign, hipStream_t stream);
+hipError_t launch_row_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t* exps,
+                           hipStream_t stream);
 hipError_t launch_channel_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int threshold_log2,
                                int32_t* col_e, hipStream_t stream);
 hipError_t launch_unpack_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int dual_split, void* hi,
@@ -30,6 +32,9 @@ hipError_t launch_gemm_comp_quant(int64_t M, int64_t N, int64_t K, const uint16_
                                   const int32_t* a_exp, int64_t lda, const uint16_t* b_hi, const uint16_t* b_lo,
                                   const int32_t* b_exp, int64_t ldb, int16_t* q, int64_t ldq, float* s,
                                   int64_t ld_s, hipStream_t stream);
+hipError_t launch_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda, const int32_t* a_exp,
+                                 const uint16_t* b_hi, const uint16_t* b_lo, const int32_t* b_exp, int64_t ldb,
+                                 float* c, int64_t ldc, hipStream_t stream);
 size_t attn_workspace_bytes(const heal_attn_args& a);
 hipError_t launch_attn(const heal_attn_args& a, hipStream_t stream);
 size_t paged_workspace_bytes(const heal_paged_decode_args& a);

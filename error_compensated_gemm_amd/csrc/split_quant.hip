@@ -74,7 +74,8 @@ __device__ __forceinline__ float load1(const uint16_t* p) {
 // vec: every row of x starts 16-byte aligned (else every element takes the scalar path).
 // COLS: every element is first scaled by its column's power of two, x' = fl32(x * 2^(col_sign * col_e[c]))
 // (exact unless it leaves the normal range), and the row is then split as x'.
-template <typename TIn, int PART, bool PRESCALE, bool RESID, bool COLS = false>
+// PARTS = false: only the row exponents are written (for a GEMM that splits its operand itself).
+template <typename TIn, int PART, bool PRESCALE, bool RESID, bool COLS = false, bool PARTS = true>
 __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__ x, int64_t rows,
                                                          int64_t cols, int64_t ld_x, int vec,
                                                          uint16_t* __restrict__ hi,
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__
     e = amax > 0.0f ? 14 - ilogb_pos(amax) : 0;
     if (lane == 0) exps[row] = e;
   }
+  if constexpr (!PARTS) return;
 
   uint16_t* hr = hi + row * ld_part;
   uint16_t* lr = RESID ? lo + row * ld_part : nullptr;
@@ -364,6 +366,15 @@ hipError_t launch_split_any(const TIn* x, int64_t rows, int64_t cols, int64_t ld
 hipError_t launch_split_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
                             void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream) {
   return launch_split_any<float>(x, rows, cols, ld_x, part, hi, lo, ld_part, exps, stream);
+}
+
+hipError_t launch_row_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t* exps,
+                           hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((split_rows_kernel<float, kPartF16, true, false, false, false>), dim3(blocks_for_rows(rows, 4)),
+                     dim3(256), 0, stream, x, rows, cols, ld_x, rows_vectorisable(x, ld_x, 4), (uint16_t*)nullptr,
+                     (uint16_t*)nullptr, (int64_t)0, exps);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int part,

@@ -157,6 +157,34 @@ HEAL_API heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void*
                            void* stream);
 
 /*
+ * Split in the GEMM's prologue ([TS 2B Mechanism]: A's primary 16-bit value and residual are formed where
+ * they are multiplied, so the 16-bit parts of A never travel through memory).  heal_row_exponents followed
+ * by heal_gemm_comp_f32a computes what heal_split (FP32 x, HEAL_F16 parts, prescale, residual) followed by
+ * heal_gemm_comp computes, bit for bit, reading A once in each call instead of writing and re-reading its
+ * parts.
+ *
+ * heal_row_exponents: exps[r] = 14 - ilogb(max_c |x[r, c]|) (0 for an all-zero or empty row): the
+ *   exponents heal_split writes.  x FP32 [rows, cols] with leading dimension ld_x (4-byte alignment only);
+ *   exps int32 [rows], 4-byte aligned.
+ *   Errors: HEAL_ERR_NULL (exps NULL, or x NULL with cols > 0), HEAL_ERR_SHAPE, HEAL_ERR_STRIDE
+ *   (ld_x < cols), HEAL_ERR_ALIGN.
+ * heal_gemm_comp_f32a: heal_gemm_comp with A given as FP32 a [M, K] (leading dimension lda, in floats) and
+ *   its row exponents a_exp (required): each A value is split as heal_split splits it, xs = fl32(a * 2^e),
+ *   hi = fp16_rn(xs), lo = fp16_rn(xs - hi), inside the kernel.  B as in heal_gemm_comp with FP16 parts
+ *   (b_lo NULL: P = 2 products, else 3).  With the exponents of heal_row_exponents every |xs| < 2^15;
+ *   other exponents are accepted, with the parts heal_split would form from them.  a must be 16-byte
+ *   aligned and lda a multiple of 4; a row needs to hold only its K values (the last partial step of K is
+ *   read element by element).
+ *   Errors: HEAL_ERR_NULL (c or a_exp NULL with M*N > 0; a or b_hi NULL with M*N*K > 0), HEAL_ERR_SHAPE,
+ *   HEAL_ERR_STRIDE (lda, ldb < K or ldc < N), HEAL_ERR_ALIGN.
+ */
+HEAL_API heal_status heal_row_exponents(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t* exps,
+                               void* stream);
+HEAL_API heal_status heal_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda,
+                                const int32_t* a_exp, const void* b_hi, const void* b_lo, const int32_t* b_exp,
+                                int64_t ldb, float* c, int64_t ldc, void* stream);
+
+/*
  * heal_gemm_comp_quant_i16 -- the compensated GEMM of heal_gemm_comp with the INT16 quantisation of
  * heal_qkv_quant_i16 applied in its epilogue ([TS 2A Solution]: the attention inputs are stored as INT16), so
  * a Q/K/V projection writes its INT16 codes and scales straight into a cache without an FP32 round trip.

@@ -97,6 +97,30 @@ def test_unpack_validation(heal):
     assert un(P(FAKE), 0, 8, 8, 2, P(FAKE), P(FAKE), 8, None) == 0    # empty: no launch
 
 
+def test_row_exponents_and_f32a_validation(heal):
+    lib = heal.load()
+    rx = lib.heal_row_exponents
+    assert rx(P(FAKE), 4, 8, 8, None, None) == 1          # NULL exps
+    assert rx(None, 4, 8, 8, P(FAKE), None) == 1          # NULL x with columns
+    assert rx(P(FAKE), -1, 8, 8, P(FAKE), None) == 2
+    assert rx(P(FAKE), 4, 8, 7, P(FAKE), None) == 3       # ld_x < cols
+    assert rx(P(FAKE + 2), 4, 8, 8, P(FAKE), None) == 4   # x not 4-byte aligned
+    assert rx(P(FAKE), 0, 8, 8, None, None) == 0          # no rows: nothing to do
+    g = lib.heal_gemm_comp_f32a
+    ok = dict(M=64, N=32, K=100, a=P(FAKE), lda=100, ae=P(FAKE), bh=P(FAKE), bl=None, be=None, ldb=104,
+              c=P(FAKE), ldc=32)
+    call = lambda **kw: g(*[{**ok, **kw}[k] for k in ("M", "N", "K", "a", "lda", "ae", "bh", "bl", "be", "ldb",
+                                                       "c", "ldc")], None)
+    assert call(K=-1) == 2
+    assert call(ae=None) == 1                             # the row exponents are required
+    assert call(a=None) == 1 and call(c=None) == 1 and call(bh=None) == 1
+    assert call(lda=96) == 3 and call(ldb=96) == 3 and call(ldc=16) == 3
+    assert call(a=P(FAKE + 4)) == 4                       # a not 16-byte aligned
+    assert call(lda=102) == 4                             # lda not a multiple of 4
+    assert call(ldb=100) == 4                             # ldb not a multiple of 8
+    assert call(M=0) == 0
+
+
 def test_gemm_validation(heal):
     lib = heal.load()
     F16, F32 = 2, 0

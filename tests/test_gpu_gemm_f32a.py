@@ -1,0 +1,102 @@
+"""GPU parity of the GEMM that splits its FP32 A operand in the prologue (heal_row_exponents +
+heal_gemm_comp_f32a, [TS 2B Mechanism]).
+
+Bar: the row exponents equal heal_split's bit for bit; C equals heal_split + heal_gemm_comp bit for bit
+(the same parts, MFMAs and accumulation order) on every kernel kind (skinny with 1, 2 and 4 column
+blocks, 128 x 128, 128 x 256, 256 x 128 and 256 x 256 tiles, 2 and 3 products) with ragged M, N and K,
+including K not a multiple of 4; and against the oracle: normwise <= 2e-6 to the FP64 definition and
+every element within the FP32-accumulation bound of the exact sum of the same products."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import banner, bits, dev, host, normwise
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-6
+
+
+def _a_dev(A):
+    """FP32 A on the device with a leading dimension rounded up to 4 floats, as a [M, K] view"""
+    M, K = A.shape
+    t = torch.zeros((M, (K + 3) // 4 * 4), dtype=torch.float32, device="cuda")
+    t[:, :K] = dev(A)
+    return t[:, :K]
+
+
+def _both(heal, A, Bt, b_residual):
+    a = _a_dev(A)
+    bh, bl, eb = heal.heal_split(dev(Bt), residual=b_residual)
+    ah, al, ea = heal.heal_split(a)
+    c_ref = heal.heal_gemm_comp(ah, al, ea, bh, bl, eb)
+    e2 = heal.heal_row_exponents(a)
+    c = heal.heal_gemm_comp_f32a(a, e2, bh, bl, eb)
+    torch.cuda.synchronize()
+    assert torch.equal(e2, ea)
+    return host(c), host(c_ref), (ah, al, ea, bh, bl, eb)
+
+
+@pytest.mark.parametrize("M,N,K,P", [
+    (1, 300, 77, 2), (16, 7300, 130, 2), (30, 7300, 301, 3), (64, 1000, 1001, 2), (5, 14350, 64, 3),   # skinny
+    (100, 300, 1003, 2), (129, 257, 999, 3),                                                            # 128 x 128
+    (2048, 4096, 258, 2),                                                                               # 128 x 256
+    (2048, 4096, 130, 3),                                                                               # 256 x 128
+    (2048, 14336, 97, 2), (2048, 14336, 66, 3)])                                                        # 256 x 256
+def test_fused_equals_split_then_gemm(heal, M, N, K, P):
+    banner(f"gemm f32a {M}x{N}x{K} P={P}: {heal.heal_gemm_comp_variant(M, N, K, P)}")
+    A, Bt = workloads.gemm_rowscaled(M, N, K, seed=7)
+    c, c_ref, _ = _both(heal, A, Bt, b_residual=(P == 3))
+    assert np.array_equal(c.view(np.uint32), c_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 1001), (16, 1000, 777)])
+def test_fused_vs_oracle(heal, M, N, K):
+    banner(f"gemm f32a vs oracle {M}x{N}x{K} P=3")
+    A, Bt = workloads.gemm_uniform(M, N, K, seed=3)
+    c, _, parts = _both(heal, A, Bt, b_residual=True)
+    ah, al, ea, bh, bl, eb = [bits(p) if p.dtype == torch.int16 else host(p) for p in parts]
+    Ce, G = oracle.gemm_emul(ah, al, ea, bh, bl, eb)
+    assert np.all(np.abs(c.astype(np.float64) - Ce) <= (3 * K + 2) * 2.0 ** -24 * G)
+    err = normwise(c, oracle.gemm_f64(A, Bt))
+    print(f"[f32a] {M}x{N}x{K} normwise {err:.3e}")
+    assert err <= TOL
+
+
+def test_row_exponents_special_rows(heal):
+    banner("row exponents: zero row, subnormal maximum, empty rows")
+    x = np.random.default_rng(1).standard_normal((6, 37)).astype(np.float32)
+    x[1] = 0
+    x[2] = np.float32(1e-40)  # subnormal maximum
+    x[3, 5] = np.float32(3e38)
+    xd = dev(x)
+    e = heal.heal_row_exponents(xd)
+    _, _, es = heal.heal_split(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(e, es)
+    assert host(e)[1] == 0
+    e0 = heal.heal_row_exponents(xd[:, :0])
+    torch.cuda.synchronize()
+    assert np.all(host(e0) == 0)
+
+
+@pytest.mark.parametrize("M", [16, 2048])
+@pytest.mark.parametrize("K,N", [(4096, 4096), (14336, 4096)])
+def test_llama_linear_fused(heal, M, K, N):
+    banner(f"gemm f32a llama M={M} K={K} N={N}")
+    X = workloads.llama_activations(M, K, seed=1)
+    W = workloads.llama_weights_bf16(N, K, seed=1)
+    bh, _, eb = heal.heal_split(dev(W.view(np.int16)).view(torch.bfloat16), residual=False)
+    a = _a_dev(X)
+    ah, al, ea = heal.heal_split(a)
+    c_ref = heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
+    c = heal.heal_gemm_comp_f32a(a, heal.heal_row_exponents(a), bh, None, eb)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int32), c_ref.view(torch.int32))
+    rng = np.random.default_rng(M + K)
+    ii, jj = rng.integers(0, M, 256), rng.integers(0, N, 256)
+    ref = oracle.gemm_f64_points(X.astype(np.float64), oracle.part_values(W, oracle.BF16), ii, jj)
+    err = normwise(host(c)[ii, jj], ref)
+    print(f"[f32a] llama M={M} K={K} N={N} sampled normwise {err:.3e}")
+    assert err <= TOL
