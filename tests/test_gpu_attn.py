@@ -89,7 +89,8 @@ def test_decode_matches_last_prefill_row(heal):
     assert normwise(dec, full[:, -1:]) <= 2 * TOL
 
 
-@pytest.mark.parametrize("B,L,Hq,Hkv", [(3, 1000, 32, 8), (1, 1, 4, 4), (2, 4097, 16, 1), (1, 33, 8, 8)])
+@pytest.mark.parametrize("B,L,Hq,Hkv", [(3, 1000, 32, 8), (1, 1, 4, 4), (2, 4097, 16, 1), (1, 33, 8, 8),
+                                        (2, 700, 32, 1)])  # 32 query heads per kv head: the prefill kernel
 def test_decode_small(heal, B, L, Hq, Hkv):
     banner(f"decode B={B} L={L} Hq={Hq} Hkv={Hkv}")
     q, qs = workloads.int16_cache_host(B, 1, Hq, 128, seed=31)

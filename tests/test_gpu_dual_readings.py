@@ -65,7 +65,7 @@ def test_prefill(heal, reading, B, Lq, Lkv, Hq, Hkv, causal):
 
 
 @pytest.mark.parametrize("reading", READINGS)
-@pytest.mark.parametrize("B,L,Hq,Hkv", [(3, 1000, 32, 8), (1, 1, 4, 4), (2, 4097, 16, 1)])
+@pytest.mark.parametrize("B,L,Hq,Hkv", [(3, 1000, 32, 8), (1, 1, 4, 4), (2, 4097, 16, 1), (1, 300, 24, 1)])
 def test_decode(heal, reading, B, L, Hq, Hkv):
     banner(f"decode reading {reading} B={B} L={L} Hq={Hq} Hkv={Hkv}")
     q, qs = workloads.int16_cache_host(B, 1, Hq, 128, seed=31)
