@@ -458,6 +458,16 @@ def other_rows(heal, workloads, dev):
                                                     workspace=pws), 10)
     rows["a7p_paged_decode_64x8192_page64"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
                                                "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
+    # the same pool laid out head-major within each page ([P, Hkv, 64, D], passed through the strides): a
+    # head's 64 keys are one contiguous 16 KB run
+    def head_major(p):
+        return p.transpose(1, 2).contiguous().transpose(1, 2)
+    kp, ksp = head_major(kp), head_major(ksp)
+    vp, vsp = head_major(vp), head_major(vsp)
+    t = time_fn(lambda: heal.heal_attn_decode_paged(q1, qs1, kp, ksp, vp, vsp, tab, lens, L, out=o1,
+                                                    workspace=pws), 10)
+    rows["a7p_paged_decode_64x8192_page64_head_major"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
+                                                          "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
     del kp, ksp, vp, vsp, tab, lens, q, qs, out, ws, q1, qs1, o1, pws
     torch.cuda.empty_cache()
     # quantise-on-append: the Llama-3-8B QKV projection (2048 tokens x 4096 -> 6144 = 48 heads of 128, bf16
