@@ -1,0 +1,261 @@
+"""Model-level check of the HEAL path: a random-initialised Llama-style decoder stack run three ways,
+  * HEAL: every projection is heal_split + heal_gemm_comp (FP32 activations, bf16 weights exact in FP16,
+    P = 2), Q/K/V are INT16-quantised into the KV cache by heal_qkv_quant_i16, attention is
+    heal_attn_dual_fp16 (prefill, then one decode step per token); the other block steps are the FP32 glue
+    kernels of libheal_glue.so;
+  * plain bf16: bf16 values between every op and in the KV cache, each op's arithmetic in FP32 on those values
+    and its result rounded to bf16 (the kernel-boundary truncation the HEAL pages name as the source of
+    irreproducibility);
+  * FP64: ``oracle.stack``.
+The FP64 model decodes greedily; the two 16-bit paths are then fed its tokens (teacher forcing) and their
+argmax compared with its argmax at every step, and each also decodes on its own to find its first divergence.
+Reported: per-step argmax agreement, first divergence, final-hidden normwise error against FP64.
+
+Run as a script for the full-size stack (32 layers, d 4096, 32/8 heads, FFN 14336, vocab 128256, 512-token
+prompt, 64 steps; it needs ~100 GB of host memory for the FP64 weights):
+    python tests/llama_stack.py --full
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import error_compensated_gemm_amd as heal  # noqa: E402
+from oracle import stack as ostack  # noqa: E402
+
+FULL = dict(layers=32, d=4096, hq=32, hkv=8, f=14336, vocab=128256, prompt=512, steps=64)
+SMALL = dict(layers=2, d=1024, hq=8, hkv=2, f=3584, vocab=4096, prompt=64, steps=8)
+EPS, THETA = 1e-5, 5e5
+
+
+def glue():
+    L = ctypes.CDLL(os.path.join(ROOT, "error_compensated_gemm_amd", "libheal_glue.so"))
+    p, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    for name, args in (("glue_embed", [p, p, i64, i64, p, p]), ("glue_rmsnorm", [p, i64, i64, f32, p, p]),
+                       ("glue_rope", [p, i64, i64, i64, i64, p, p]), ("glue_swiglu", [p, p, i64, p, p]),
+                       ("glue_add", [p, p, i64, p]), ("glue_argmax", [p, i64, p, p])):
+        getattr(L, name).argtypes = args
+        getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _s():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_weights(cfg: dict, seed: int) -> dict:
+    """bf16 N(0, 0.02) weights on the device, drawn with torch's Philox generator from ``seed``."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    d, hq, hkv, f, V = cfg["d"], cfg["hq"], cfg["hkv"], cfg["f"], cfg["vocab"]
+
+    def draw(r, c):
+        return (torch.randn((r, c), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    w = {"emb": draw(V, d), "head": draw(V, d)}
+    for l in range(cfg["layers"]):
+        w[f"{l}.wq"], w[f"{l}.wk"], w[f"{l}.wv"] = draw(hq * 128, d), draw(hkv * 128, d), draw(hkv * 128, d)
+        w[f"{l}.wo"] = draw(d, hq * 128)
+        w[f"{l}.wg"], w[f"{l}.wu"], w[f"{l}.wd"] = draw(f, d), draw(f, d), draw(d, f)
+    return w
+
+
+def rope_table(positions: int) -> torch.Tensor:
+    """cos and sin of pos * theta^(-i / 64), in FP64 rounded once to FP32, as [positions, 64, 2]."""
+    i = np.arange(64, dtype=np.float64)
+    ang = np.arange(positions, dtype=np.float64)[:, None] * np.power(THETA, -i / 64.0)[None, :]
+    return torch.from_numpy(np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)).cuda()
+
+
+class HealPath:
+    def __init__(self, w: dict, cfg: dict, G):
+        self.cfg, self.G = cfg, G
+        d, hq, hkv = cfg["d"], cfg["hq"], cfg["hkv"]
+        self.parts = {}
+        for l in range(cfg["layers"]):
+            self.parts[f"{l}.wqkv"] = heal.heal_split(torch.cat([w[f"{l}.wq"], w[f"{l}.wk"], w[f"{l}.wv"]]),
+                                                      residual=False)[0::2]
+            for n in ("wo", "wg", "wu", "wd"):
+                self.parts[f"{l}.{n}"] = heal.heal_split(w[f"{l}.{n}"], residual=False)[0::2]
+        self.parts["head"] = heal.heal_split(w["head"], residual=False)[0::2]
+        self.emb = w["emb"]
+        Lmax = cfg["prompt"] + cfg["steps"]
+        self.cs = rope_table(Lmax)
+        self.kc = [torch.zeros((Lmax, hkv, 128), dtype=torch.int16, device="cuda") for _ in range(cfg["layers"])]
+        self.vc = [torch.zeros((Lmax, hkv, 128), dtype=torch.int16, device="cuda") for _ in range(cfg["layers"])]
+        self.ks = [torch.zeros((Lmax, hkv), dtype=torch.float32, device="cuda") for _ in range(cfg["layers"])]
+        self.vs = [torch.zeros((Lmax, hkv), dtype=torch.float32, device="cuda") for _ in range(cfg["layers"])]
+
+    def linear(self, x, name):
+        ah, al, ea = heal.heal_split(x)
+        bh, eb = self.parts[name]
+        return heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
+
+    def norm(self, x):
+        y = torch.empty_like(x)
+        assert self.G.glue_rmsnorm(_p(x), x.shape[0], x.shape[1], EPS, _p(y), _s()) == 0
+        return y
+
+    def forward(self, ids: np.ndarray, pos0: int):
+        cfg, G = self.cfg, self.G
+        T, d, hq, hkv = len(ids), cfg["d"], cfg["hq"], cfg["hkv"]
+        idt = torch.from_numpy(np.asarray(ids, np.int32)).cuda()
+        x = torch.empty((T, d), dtype=torch.float32, device="cuda")
+        assert G.glue_embed(_p(self.emb), _p(idt), T, d, _p(x), _s()) == 0
+        for l in range(cfg["layers"]):
+            qkv = self.linear(self.norm(x), f"{l}.wqkv")  # [T, (hq + 2 hkv) 128]
+            ld = qkv.stride(0)
+            assert G.glue_rope(_p(qkv), T, hq, ld, pos0, _p(self.cs), _s()) == 0
+            kv = qkv[:, hq * 128:]
+            assert G.glue_rope(_p(kv), T, hkv, ld, pos0, _p(self.cs), _s()) == 0
+            q, qs = heal.heal_qkv_quant_i16(qkv[:, :hq * 128].view(T, hq, 128))
+            heal.heal_qkv_quant_i16(kv[:, :hkv * 128].view(T, hkv, 128), q=self.kc[l][pos0:pos0 + T],
+                                    scale=self.ks[l][pos0:pos0 + T])
+            heal.heal_qkv_quant_i16(kv[:, hkv * 128:].view(T, hkv, 128), q=self.vc[l][pos0:pos0 + T],
+                                    scale=self.vs[l][pos0:pos0 + T])
+            n = pos0 + T
+            a = heal.heal_attn_dual_fp16(q[None], qs[None], self.kc[l][None, :n], self.ks[l][None, :n],
+                                         self.vc[l][None, :n], self.vs[l][None, :n], causal=True)
+            o = self.linear(a.view(T, hq * 128), f"{l}.wo")
+            assert G.glue_add(_p(x), _p(o), x.numel(), _s()) == 0
+            h = self.norm(x)
+            gte, up = self.linear(h, f"{l}.wg"), self.linear(h, f"{l}.wu")
+            act = torch.empty_like(gte)
+            assert G.glue_swiglu(_p(gte), _p(up), gte.numel(), _p(act), _s()) == 0
+            dn = self.linear(act, f"{l}.wd")
+            assert G.glue_add(_p(x), _p(dn), x.numel(), _s()) == 0
+        hn = self.norm(x[-1:].contiguous())
+        logits = self.linear(hn, "head")
+        am = torch.empty((1,), dtype=torch.int32, device="cuda")
+        assert G.glue_argmax(_p(logits), logits.numel(), _p(am), _s()) == 0
+        return hn[0], logits[0], am
+
+
+class Bf16Path:
+    """bf16 values between ops and in the cache; each op computes in FP32 on them and rounds its result."""
+
+    def __init__(self, w: dict, cfg: dict):
+        self.cfg = cfg
+        self.wt = {k: v.float().t().contiguous() for k, v in w.items() if k not in ("emb",)}
+        self.emb = w["emb"]
+        Lmax = cfg["prompt"] + cfg["steps"]
+        ang = torch.from_numpy(np.arange(Lmax, dtype=np.float64)[:, None]
+                               * np.power(THETA, -np.arange(64, dtype=np.float64) / 64.0)[None, :])
+        self.cos, self.sin = ang.cos().float().cuda(), ang.sin().float().cuda()
+        self.k = [None] * cfg["layers"]
+        self.v = [None] * cfg["layers"]
+
+    @staticmethod
+    def r(x):
+        return x.to(torch.bfloat16).float()
+
+    def norm(self, x):
+        return self.r(x * torch.rsqrt((x * x).mean(-1, keepdim=True) + EPS))
+
+    def rope(self, x, pos0):  # x [T, H, 128]
+        T = x.shape[0]
+        c, s = self.cos[pos0:pos0 + T, None, :], self.sin[pos0:pos0 + T, None, :]
+        a, b = x[..., :64], x[..., 64:]
+        return self.r(torch.cat([a * c - b * s, b * c + a * s], -1))
+
+    def forward(self, ids: np.ndarray, pos0: int):
+        cfg = self.cfg
+        T, hq, hkv = len(ids), cfg["hq"], cfg["hkv"]
+        g = hq // hkv
+        x = self.emb[torch.from_numpy(np.asarray(ids, np.int64)).cuda()].float()
+        for l in range(cfg["layers"]):
+            h = self.norm(x)
+            q = self.rope(self.r(h @ self.wt[f"{l}.wq"]).view(T, hq, 128), pos0)
+            k = self.rope(self.r(h @ self.wt[f"{l}.wk"]).view(T, hkv, 128), pos0)
+            v = self.r(h @ self.wt[f"{l}.wv"]).view(T, hkv, 128)
+            self.k[l] = k if pos0 == 0 else torch.cat([self.k[l], k])
+            self.v[l] = v if pos0 == 0 else torch.cat([self.v[l], v])
+            K, V = self.k[l], self.v[l]
+            L = K.shape[0]
+            qh = q.view(T, hkv, g, 128).permute(1, 2, 0, 3).contiguous()          # [hkv, g, T, 128]
+            s = torch.matmul(qh, K.permute(1, 2, 0).contiguous()[:, None]) / np.sqrt(128.0)  # [hkv, g, T, L]
+            mask = torch.arange(L, device="cuda")[None, :] > (pos0 + torch.arange(T, device="cuda"))[:, None]
+            s = s.masked_fill(mask, float("-inf"))
+            p = torch.softmax(s, -1)
+            o = torch.matmul(self.r(p), V.permute(1, 0, 2).contiguous()[:, None])  # [hkv, g, T, 128]
+            a = self.r(o.permute(2, 0, 1, 3).reshape(T, hq * 128))
+            x = self.r(x + self.r(a @ self.wt[f"{l}.wo"]))
+            h = self.norm(x)
+            gte, up = self.r(h @ self.wt[f"{l}.wg"]), self.r(h @ self.wt[f"{l}.wu"])
+            act = self.r(gte / (1.0 + torch.exp(-gte)) * up)
+            x = self.r(x + self.r(act @ self.wt[f"{l}.wd"]))
+        hn = self.norm(x[-1:])
+        logits = (hn @ self.wt["head"])[0]
+        return hn[0], logits, torch.argmax(logits)
+
+
+def _nw(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def run(cfg: dict, seed: int = 0, log=print) -> dict:
+    t0 = time.time()
+    w = make_weights(cfg, seed)
+    host = {k: v.view(torch.int16).cpu().numpy().view(np.uint16) for k, v in w.items()}
+    prompt = np.random.default_rng(seed).integers(0, cfg["vocab"], cfg["prompt"])
+    log(f"[stack] weights ready ({time.time() - t0:.0f} s)")
+    ref = ostack.Stack(host, cfg["layers"], cfg["hq"], cfg["hkv"], EPS, THETA, cfg["prompt"] + cfg["steps"])
+    hid, lg = ref.forward(prompt, 0)
+    toks, hids, gaps = [], [], []
+    for s in range(cfg["steps"]):
+        if s:
+            hid, lg = ref.forward([toks[-1]], cfg["prompt"] + s - 1)
+        top2 = np.sort(lg)[-2:]
+        toks.append(int(np.argmax(lg)))
+        hids.append(hid)
+        gaps.append(float(top2[1] - top2[0]))
+        log(f"[stack] fp64 step {s}: token {toks[-1]} (top-2 gap {gaps[-1]:.3e}, {time.time() - t0:.0f} s)")
+    del ref
+    G = glue()
+    out = {"config": cfg, "seed": seed, "fp64_tokens": toks, "fp64_top2_gap_min": min(gaps)}
+    for name, make in (("heal", lambda: HealPath(w, cfg, G)), ("bf16", lambda: Bf16Path(w, cfg))):
+        path = make()
+        agree, errs = [], []
+        for mode in ("teacher_forced", "free"):
+            h, logits, am = path.forward(prompt, 0)
+            tok = int(am.item())
+            first_div = None
+            for s in range(cfg["steps"]):
+                if s:
+                    feed = toks[s - 1] if mode == "teacher_forced" else tok
+                    h, logits, am = path.forward([feed], cfg["prompt"] + s - 1)
+                    tok = int(am.item())
+                if mode == "teacher_forced":
+                    agree.append(tok == toks[s])
+                    errs.append(_nw(h.double().cpu().numpy(), hids[s]))
+                elif first_div is None and tok != toks[s]:
+                    first_div = s
+            if mode == "free":
+                out[name] = {"teacher_forced_agreement": sum(agree) / len(agree),
+                             "disagreeing_steps": [s for s, a in enumerate(agree) if not a],
+                             "free_running_first_divergence": first_div,
+                             "final_hidden_normwise_err_max": max(errs),
+                             "final_hidden_normwise_err_mean": float(np.mean(errs))}
+        log(f"[stack] {name}: {json.dumps(out[name])} ({time.time() - t0:.0f} s)")
+        del path
+        torch.cuda.empty_cache()
+    return out
+
+
+if __name__ == "__main__":
+    cfg = FULL if "--full" in sys.argv else SMALL
+    res = run(cfg, log=lambda m: print(m, flush=True))
+    print(json.dumps(res), flush=True)
