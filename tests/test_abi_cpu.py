@@ -36,6 +36,19 @@ def test_library_exports_every_declared_symbol(heal):
     assert all(s.startswith("heal_") for s in exported)
 
 
+def test_glue_library_exports_every_declared_symbol():
+    """the decoder-block glue of the model-level check (include/heal_glue.h, libheal_glue.so)"""
+    txt = open(os.path.join(ROOT, "include", "heal_glue.h")).read()
+    names = sorted(set(re.findall(r"GLUE_API\s+int\s+(glue_\w+)\s*\(", txt)))
+    assert len(names) == 6
+    lib_path = os.path.join(ROOT, "error_compensated_gemm_amd", "libheal_glue.so")
+    lib = ctypes.CDLL(lib_path)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True, text=True).stdout
+    assert set(names) == set(re.findall(r" T (glue_\w+)$", out, re.M))
+
+
 def test_version_and_status_strings(heal):
     lib = heal.load()
     assert lib.heal_abi_version() == 3
