@@ -9,7 +9,8 @@
   * FP64: ``oracle.stack``.
 The FP64 model decodes greedily; the two 16-bit paths are then fed its tokens (teacher forcing) and their
 argmax compared with its argmax at every step, and each also decodes on its own to find its first divergence.
-Reported: per-step argmax agreement, first divergence, final-hidden normwise error against FP64.
+Reported: per-step argmax agreement, first divergence, final-hidden normwise error against FP64, and the
+median time of one decode step (informational; the bf16 path is plain torch, not an inference engine).
 
 Run as a script for the full-size stack (32 layers, d 4096, 32/8 heads, FFN 14336, vocab 128256, 512-token
 prompt, 64 steps; it needs ~100 GB of host memory for the FP64 weights):
@@ -110,9 +111,12 @@ class HealPath:
         return y
 
     def forward(self, ids: np.ndarray, pos0: int):
+        return self.forward_dev(torch.from_numpy(np.asarray(ids, np.int32)).cuda(), pos0)
+
+    def forward_dev(self, idt: torch.Tensor, pos0: int):
+        """forward() on token ids already in device memory (so that a decode step can be captured)"""
         cfg, G = self.cfg, self.G
-        T, d, hq, hkv = len(ids), cfg["d"], cfg["hq"], cfg["hkv"]
-        idt = torch.from_numpy(np.asarray(ids, np.int32)).cuda()
+        T, d, hq, hkv = idt.numel(), cfg["d"], cfg["hq"], cfg["hkv"]
         x = torch.empty((T, d), dtype=torch.float32, device="cuda")
         assert G.glue_embed(_p(self.emb), _p(idt), T, d, _p(x), _s()) == 0
         for l in range(cfg["layers"]):
@@ -202,6 +206,31 @@ class Bf16Path:
         return hn[0], logits, torch.argmax(logits)
 
 
+def graph_step_ms(path: HealPath, tok: int, pos: int, reps: int = 20) -> float:
+    """GPU time of one decode step of the HEAL path, captured once as a HIP graph and replayed (it rewrites the
+    same cache slot with the same values every time)."""
+    ids = torch.tensor([tok], dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path.forward_dev(ids, pos)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path.forward_dev(ids, pos)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def _nw(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
@@ -228,7 +257,8 @@ def run(cfg: dict, seed: int = 0, log=print) -> dict:
     out = {"config": cfg, "seed": seed, "fp64_tokens": toks, "fp64_top2_gap_min": min(gaps)}
     for name, make in (("heal", lambda: HealPath(w, cfg, G)), ("bf16", lambda: Bf16Path(w, cfg))):
         path = make()
-        agree, errs = [], []
+        agree, errs, step_ms = [], [], []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for mode in ("teacher_forced", "free"):
             h, logits, am = path.forward(prompt, 0)
             tok = int(am.item())
@@ -236,8 +266,11 @@ def run(cfg: dict, seed: int = 0, log=print) -> dict:
             for s in range(cfg["steps"]):
                 if s:
                     feed = toks[s - 1] if mode == "teacher_forced" else tok
+                    e0.record()
                     h, logits, am = path.forward([feed], cfg["prompt"] + s - 1)
+                    e1.record()
                     tok = int(am.item())
+                    step_ms.append(e0.elapsed_time(e1))
                 if mode == "teacher_forced":
                     agree.append(tok == toks[s])
                     errs.append(_nw(h.double().cpu().numpy(), hids[s]))
@@ -248,7 +281,10 @@ def run(cfg: dict, seed: int = 0, log=print) -> dict:
                              "disagreeing_steps": [s for s, a in enumerate(agree) if not a],
                              "free_running_first_divergence": first_div,
                              "final_hidden_normwise_err_max": max(errs),
-                             "final_hidden_normwise_err_mean": float(np.mean(errs))}
+                             "final_hidden_normwise_err_mean": float(np.mean(errs)),
+                             "decode_step_ms_median": float(np.median(step_ms))}
+                if name == "heal":
+                    out[name]["decode_step_ms_hip_graph"] = graph_step_ms(path, toks[-1], cfg["prompt"] + cfg["steps"] - 1)
         log(f"[stack] {name}: {json.dumps(out[name])} ({time.time() - t0:.0f} s)")
         del path
         torch.cuda.empty_cache()
