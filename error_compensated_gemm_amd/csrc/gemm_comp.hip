@@ -9,17 +9,21 @@
 // [TS] = gist.science explainer "Demystifying Numerical Instability in LLM Inference: Achieving
 // Reproducible Inference for Mission-Critical Tasks with HEAL", Technical Summary.
 //
-// Kernel shape (tiled GEMM, both operands K-contiguous, "TN"):
-//   * 256 threads = 4 wavefronts in a 2 x 2 arrangement; a wave owns a (BM/2) x (BN/2) block of C held as
-//     32 x 32 MFMA accumulators (256 x 256 block tile: 16 accumulators = 256 accumulation registers).
+// Kernel shapes (both operands K-contiguous, "TN"):
+//   * tile kernel (M > 64): 256 threads = 4 wavefronts in a 2 x 2 arrangement; a wave owns a (BM/2) x (BN/2)
+//     block of C held as 32 x 32 MFMA accumulators (256 x 256 block tile: 16 accumulators = 256 accumulation
+//     registers).  Block tiles 256 x 256, 128 x 256 (only A has a low part), 256 x 128 and 128 x 128.
 //   * BK = 32 per stage; the A parts (hi, lo) and B parts (hi, lo) of a stage sit in LDS as 16-byte chunks
 //     with an XOR swizzle on the chunk index so that the 32 rows a fragment read touches fall in distinct
-//     bank groups; two stages double-buffer the LDS, so one barrier per stage suffices.
-//   * the next stage's global loads are issued before the current stage's MFMAs and written to LDS after
-//     them, so HBM/L2 latency hides behind the matrix work.
+//     bank groups.  Full K tiles arrive by direct global -> LDS transfers into three stages where they fit
+//     (two otherwise): the step for tile k issues tile k + 2's transfers, multiplies tile k, and waits only
+//     for tile k + 1's, so two stages of MFMAs cover each transfer.  The partial last K tile goes through
+//     registers with the columns past K zeroed.
 //   * the block -> tile mapping first gives each of the 8 XCDs (workgroups are dealt to XCDs round-robin)
 //     a contiguous range of tiles, then walks that range in groups of 4 tile rows, so concurrently
 //     running tiles of one XCD share A and B panels in that XCD's L2.
+//   * skinny kernel (M <= 64): 8 wavefronts per 16 NC output columns split K, stream B from memory through
+//     registers with v_mfma_f32_16x16x32, and meet in a fixed-order LDS reduction.
 #include "heal_internal.h"
 
 namespace heal {
