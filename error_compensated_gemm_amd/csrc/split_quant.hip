@@ -1,14 +1,18 @@
 // split_quant.hip -- the HBM-bound passes of the HEAL hot path on gfx950:
 //   * the split of an FP32 / bf16 matrix into a 16-bit primary value and a 16-bit residual, with an exact
 //     power-of-two row prescale ([TS 2B Mechanism, Overflow Handling]);
-//   * the Dual-FP16 byte split of an INT16 matrix ([TS 2A Mechanism]);
+//   * the same split's row exponents alone, for a GEMM that splits its FP32 operand itself;
+//   * the outlier-channel calibration (per-column exponents) and the column-scaled split ([TS 2B Overflow
+//     Handling]);
+//   * the Dual-FP16 unpack of an INT16 matrix under the byte, shift-10 or float-float reading ([TS 2A
+//     Mechanism]);
 //   * the INT16 quantisation of Q/K/V per (token, head) ([TS 2A Solution]).
 // [TS] = gist.science explainer "Demystifying Numerical Instability in LLM Inference: Achieving
 // Reproducible Inference for Mission-Critical Tasks with HEAL", Technical Summary.
 //
 // Layout of the work: one 64-lane wavefront per matrix row (split) or one 32-lane half-wave per
 // (token, head) row (quantise), 16-byte vector loads and stores, the row maximum reduced with cross-lane
-// shuffles, no LDS and no atomics.  Each pass reads every input byte once from HBM (the split's second
+// shuffles, no atomics (only the column calibration meets its wavefronts in LDS).  Each pass reads every input byte once from HBM (the split's second
 // read of a row hits the cache it was just read into) and writes every output byte once.
 #include "heal_internal.h"
 
