@@ -10,7 +10,10 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-heal_status launched(hipError_t e) { return e == hipSuccess ? HEAL_OK : HEAL_ERR_LAUNCH; }
+// the launchers answer hipErrorInvalidConfiguration, before any runtime call, for a grid beyond HIP's limits
+heal_status launched(hipError_t e) {
+  return e == hipSuccess ? HEAL_OK : (e == hipErrorInvalidConfiguration ? HEAL_ERR_UNSUPPORTED : HEAL_ERR_LAUNCH);
+}
 
 }  // namespace
 
@@ -112,7 +115,7 @@ heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, co
                            const int32_t* b_exp, int64_t ldb, int part_type, float* c, int64_t ldc,
                            void* stream) {
   if (M < 0 || N < 0 || K < 0) return HEAL_ERR_SHAPE;
-  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
   if (part_type != HEAL_F16 && part_type != HEAL_BF16) return HEAL_ERR_DTYPE;
   if (M == 0 || N == 0) return HEAL_OK;
   if (!c || (K > 0 && (!a_hi || !b_hi))) return HEAL_ERR_NULL;
@@ -140,7 +143,7 @@ heal_status heal_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a,
                                 const void* b_hi, const void* b_lo, const int32_t* b_exp, int64_t ldb, float* c,
                                 int64_t ldc, void* stream) {
   if (M < 0 || N < 0 || K < 0) return HEAL_ERR_SHAPE;
-  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
   if (M == 0 || N == 0) return HEAL_OK;
   if (!c || !a_exp || (K > 0 && (!a || !b_hi))) return HEAL_ERR_NULL;
   if (lda < K || ldb < K || ldc < N) return HEAL_ERR_STRIDE;
@@ -156,7 +159,7 @@ heal_status heal_gemm_comp_quant_i16(int64_t M, int64_t N, int64_t K, const void
                                      const int32_t* b_exp, int64_t ldb, int part_type, int16_t* q, int64_t ldq,
                                      float* scale, int64_t ld_s, void* stream) {
   if (M < 0 || N < 0 || K < 0) return HEAL_ERR_SHAPE;
-  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
   if (N % 128 != 0) return HEAL_ERR_SHAPE;
   if (part_type != HEAL_F16) return HEAL_ERR_DTYPE;
   if (M == 0 || N == 0) return HEAL_OK;
@@ -182,7 +185,8 @@ heal_status heal_qkv_quant_i16(const float* x, int64_t tokens, int64_t heads, in
   if (head_dim % 4 != 0 || head_dim > 1024) return HEAL_ERR_UNSUPPORTED;
   if (tokens == 0 || heads == 0 || head_dim == 0) return HEAL_OK;
   if (!x || !q || !scale) return HEAL_ERR_NULL;
-  if (ld_x < heads * head_dim || ld_q < heads * head_dim || ld_s < heads) return HEAL_ERR_STRIDE;
+  if (ld_x < heal::mul_sat(heads, head_dim) || ld_q < heal::mul_sat(heads, head_dim) || ld_s < heads)
+    return HEAL_ERR_STRIDE;
   if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u) || !aligned4(scale) || (ld_x & 3) || (ld_q & 3))
     return HEAL_ERR_ALIGN;
   return launched(heal::launch_quant_i16(x, tokens, heads, head_dim, ld_x, q, ld_q, scale, ld_s,

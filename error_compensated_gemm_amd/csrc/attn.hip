@@ -514,7 +514,8 @@ struct DcStage {
 
 size_t decode_workspace(int64_t B, int64_t Hq, int64_t Lkv) {
   const int64_t nsplit = (Lkv + DC_CHUNK - 1) / DC_CHUNK;
-  return (size_t)(B * Hq * (nsplit > 0 ? nsplit : 1) * DC_PART) * sizeof(float);
+  // saturates rather than wraps: an impossible size is refused, never under-sized
+  return (size_t)mul_sat(mul_sat(mul_sat(B, Hq), nsplit > 0 ? nsplit : 1), DC_PART * (int64_t)sizeof(float));
 }
 
 // PAGED: the keys of each sequence are in pages of a shared pool (AttnParams::bt / lens) and every sequence
@@ -897,12 +898,17 @@ size_t attn_workspace_bytes(const heal_attn_args& x) {
 hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
   const AttnParams p = make_params(x);
   if (x.kv_len == 0) {
+    if (!grid_fits(mul_sat(mul_sat(x.batch, x.q_len), x.n_q_heads), D)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)(x.batch * x.q_len * x.n_q_heads)), dim3(D), 0, stream,
                        p);
     return hipGetLastError();
   }
   if (use_decode(x)) {
-    const int nsplit = (int)((x.kv_len + DC_CHUNK - 1) / DC_CHUNK);
+    const int64_t nsplit64 = (x.kv_len + DC_CHUNK - 1) / DC_CHUNK;
+    if (!grid_fits(nsplit64, DC_THREADS) || !grid_fits(mul_sat(x.batch, x.n_kv_heads), 1) ||
+        !grid_fits(mul_sat(x.batch, x.n_q_heads), D))
+      return hipErrorInvalidConfiguration;
+    const int nsplit = (int)nsplit64;
     float* ws = reinterpret_cast<float*>(x.workspace);
     const dim3 grid((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads));
     if (x.dual_split == HEAL_DUAL_SHIFT10)
@@ -918,6 +924,8 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
                        p, (const float*)ws, nsplit);
     return hipGetLastError();
   }
+  if (!grid_fits(mul_sat(x.batch, x.n_q_heads), PF_THREADS) || !grid_fits((x.q_len + PF_BQ - 1) / PF_BQ, 1))
+    return hipErrorInvalidConfiguration;
   const unsigned ntq = (unsigned)((x.q_len + PF_BQ - 1) / PF_BQ);
   const dim3 grid((unsigned)(x.batch * x.n_q_heads), ntq);
   if (x.dual_split == HEAL_DUAL_SHIFT10)
@@ -937,11 +945,16 @@ size_t paged_workspace_bytes(const heal_paged_decode_args& x) {
 hipError_t launch_attn_paged(const heal_paged_decode_args& x, hipStream_t stream) {
   const AttnParams p = make_params_paged(x);
   if (x.max_kv_len == 0) {
+    if (!grid_fits(mul_sat(x.batch, x.n_q_heads), D)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream, p);
     return hipGetLastError();
   }
   // the grid covers max_kv_len; splits past a sequence's own length write empty partials
-  const int nsplit = (int)((x.max_kv_len + DC_CHUNK - 1) / DC_CHUNK);
+  const int64_t nsplit64 = (x.max_kv_len + DC_CHUNK - 1) / DC_CHUNK;
+  if (!grid_fits(nsplit64, DC_THREADS) || !grid_fits(mul_sat(x.batch, x.n_kv_heads), 1) ||
+      !grid_fits(mul_sat(x.batch, x.n_q_heads), D))
+    return hipErrorInvalidConfiguration;
+  const int nsplit = (int)nsplit64;
   float* ws = reinterpret_cast<float*>(x.workspace);
   const dim3 grid((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads));
   if (x.dual_split == HEAL_DUAL_SHIFT10)

@@ -742,6 +742,7 @@ template <int PART, int MT, int NC>
 hipError_t launch_skinny_nc(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
                             const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
                             const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
+  if (!grid_fits((N + 16 * NC - 1) / (16 * NC), 64 * kSkWaves)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((N + 16 * NC - 1) / (16 * NC))), block(64 * kSkWaves);
   if (al && bl)
     hipLaunchKernelGGL((gemm_skinny_kernel<PART, MT, NC, true, true>), grid, block, 0, stream, M, N, K, ah, al,
@@ -780,6 +781,7 @@ hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const uint16_t* ah, cons
                        const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
                        const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (!grid_fits(tiles, kThreads)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)tiles), block(kThreads);
   if (al && bl)
     hipLaunchKernelGGL((gemm_comp_kernel<PART, BM, BN, true, true>), grid, block, 0, stream, M, N, K, ah, al,
@@ -820,6 +822,7 @@ hipError_t launch_tile_128x256(int64_t M, int64_t N, int64_t K, const uint16_t* 
                                float* c, int64_t ldc, int16_t* q, int64_t ldq, float* s, int64_t ld_s,
                                hipStream_t stream) {
   const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+  if (!grid_fits(tiles, kThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((gemm_comp_kernel<PART, 128, 256, true, false, QUANT>), dim3((unsigned)tiles),
                      dim3(kThreads), 0, stream, M, N, K, ah, al, ea, lda, bh, (const uint16_t*)nullptr, eb, ldb, c,
                      ldc, q, ldq, s, ld_s);
@@ -881,6 +884,7 @@ hipError_t launch_tile_quant(int64_t M, int64_t N, int64_t K, const uint16_t* ah
                              const int32_t* eb, int64_t ldb, int16_t* q, int64_t ldq, float* s, int64_t ld_s,
                              hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (!grid_fits(tiles, kThreads)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)tiles), block(kThreads);
   float* const c = nullptr;
   if (al && bl)
@@ -931,6 +935,7 @@ template <int MT, int NC>
 hipError_t launch_skinny_f32a_nc(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,
                                  const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
                                  int64_t ldc, hipStream_t stream) {
+  if (!grid_fits((N + 16 * NC - 1) / (16 * NC), 64 * kSkWaves)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((N + 16 * NC - 1) / (16 * NC))), block(64 * kSkWaves);
   const uint16_t* const none = nullptr;
   if (bl)
@@ -963,6 +968,7 @@ hipError_t launch_tile_f32a(int64_t M, int64_t N, int64_t K, const float* af, co
                             const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
                             int64_t ldc, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (!grid_fits(tiles, kThreads)) return hipErrorInvalidConfiguration;
   const uint16_t* const none = nullptr;
   hipLaunchKernelGGL((gemm_comp_kernel<HEAL_F16, BM, BN, true, BLO, false, true>), dim3((unsigned)tiles),
                      dim3(kThreads), 0, stream, M, N, K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc,

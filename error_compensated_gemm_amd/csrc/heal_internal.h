@@ -7,6 +7,18 @@
 
 namespace heal {
 
+// HIP runs fewer than 2^32 work-items per grid dimension.  Every launcher checks its grid with this before
+// any runtime call and answers hipErrorInvalidConfiguration, which the C ABI reports as
+// HEAL_ERR_UNSUPPORTED; a 64-bit block count is never truncated into a smaller grid.
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks <= ((((int64_t)1) << 32) - 1) / threads;
+}
+// a * b for non-negative sizes, saturating at INT64_MAX instead of wrapping
+inline int64_t mul_sat(int64_t a, int64_t b) {
+  if (a <= 0 || b <= 0) return 0;
+  return a > INT64_MAX / b ? INT64_MAX : a * b;
+}
+
 // Launchers (host side).  Each enqueues its kernels on `stream` and returns hipGetLastError().
 hipError_t launch_split_f32(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
                             void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream);

@@ -307,6 +307,7 @@ template <typename TIn>
 hipError_t launch_split_cols(const TIn* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
                              void* lo, int64_t ld_part, int32_t* exps, const int32_t* col_e, int col_sign,
                              hipStream_t stream) {
+  if (!grid_fits((rows + 3) / 4, 256)) return hipErrorInvalidConfiguration;
   const int vec = rows_vectorisable(x, ld_x, (int64_t)sizeof(TIn));
   const dim3 grid(blocks_for_rows(rows, 4)), block(256);
   uint16_t* h = (uint16_t*)hi;
@@ -333,6 +334,7 @@ hipError_t launch_split_cols(const TIn* x, int64_t rows, int64_t cols, int64_t l
 template <typename TIn>
 hipError_t launch_split_any(const TIn* x, int64_t rows, int64_t cols, int64_t ld_x, int part, void* hi,
                             void* lo, int64_t ld_part, int32_t* exps, hipStream_t stream) {
+  if (!grid_fits((rows + 3) / 4, 256)) return hipErrorInvalidConfiguration;
   const int vec = rows_vectorisable(x, ld_x, (int64_t)sizeof(TIn));
   if (rows == 0 || cols == 0) {
     // an empty row still has a defined exponent (0); set it with a one-wave launch of the kernel
@@ -375,6 +377,7 @@ hipError_t launch_split_f32(const float* x, int64_t rows, int64_t cols, int64_t 
 hipError_t launch_row_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t* exps,
                            hipStream_t stream) {
   if (rows == 0) return hipSuccess;
+  if (!grid_fits((rows + 3) / 4, 256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((split_rows_kernel<float, kPartF16, true, false, false, false>), dim3(blocks_for_rows(rows, 4)),
                      dim3(256), 0, stream, x, rows, cols, ld_x, rows_vectorisable(x, ld_x, 4), (uint16_t*)nullptr,
                      (uint16_t*)nullptr, (int64_t)0, exps);
@@ -404,6 +407,7 @@ hipError_t launch_split_scaled(const void* x, int x_type, int64_t rows, int64_t 
 hipError_t launch_channel_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int threshold_log2,
                                int32_t* col_e, hipStream_t stream) {
   if (cols == 0) return hipSuccess;
+  if (!grid_fits((cols + 63) / 64, 256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(channel_exps_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(256), 0, stream, x, rows, cols,
                      ld_x, threshold_log2, col_e);
   return hipGetLastError();
@@ -412,6 +416,7 @@ hipError_t launch_channel_exps(const float* x, int64_t rows, int64_t cols, int64
 hipError_t launch_unpack_i16(const int16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int dual_split, void* hi,
                              void* lo, int64_t ld_part, hipStream_t stream) {
   if (rows == 0 || cols == 0) return hipSuccess;
+  if (!grid_fits((rows + 3) / 4, 256)) return hipErrorInvalidConfiguration;
   const dim3 grid(blocks_for_rows(rows, 4)), block(256);
   const int vec = rows_vectorisable(x, ld_x, 2);
   if (dual_split == HEAL_DUAL_SHIFT10)
@@ -428,8 +433,9 @@ hipError_t launch_unpack_i16(const int16_t* x, int64_t rows, int64_t cols, int64
 
 hipError_t launch_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim, int64_t ld_x,
                             int16_t* q, int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream) {
-  const int64_t rows = tokens * heads;
+  const int64_t rows = mul_sat(tokens, heads);
   if (rows == 0) return hipSuccess;
+  if (!grid_fits((rows + 7) / 8, 256)) return hipErrorInvalidConfiguration;
   const dim3 grid(blocks_for_rows(rows, 8)), block(256);
   const int nv = (int)((head_dim + 127) / 128);
   switch (nv) {

@@ -54,7 +54,8 @@ typedef enum {
   HEAL_ERR_STRIDE = 3,      /* a leading dimension / stride is smaller than the row it must hold */
   HEAL_ERR_ALIGN = 4,       /* pointer not 16-byte aligned, or leading dimension not a multiple of 8 */
   HEAL_ERR_DTYPE = 5,       /* a dtype code that the call does not accept */
-  HEAL_ERR_UNSUPPORTED = 6, /* a valid request this library does not implement (e.g. head_dim != 128) */
+  HEAL_ERR_UNSUPPORTED = 6, /* a valid request this library does not implement (e.g. head_dim != 128), or
+                               one whose launch grid would exceed HIP's 2^32 work-items per dimension */
   HEAL_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
   HEAL_ERR_WORKSPACE = 8    /* workspace missing or smaller than heal_attn_workspace_bytes() */
 } heal_status;
@@ -148,8 +149,8 @@ HEAL_API heal_status heal_split_scaled(const void* x, int x_type, int64_t rows, 
  * accumulator scaled by the exact power of two is the only rounding at the kernel boundary.
  * Each part buffer holds its rows x ld elements (the padding columns K .. ld-1 may hold anything; they are
  * read as whole 16-byte chunks and never contribute).  K = 0 writes zeros.
- * Errors: HEAL_ERR_NULL (a_hi, b_hi or c NULL with M*N > 0), HEAL_ERR_SHAPE,
- * HEAL_ERR_STRIDE (lda, ldb < K or ldc < N), HEAL_ERR_ALIGN, HEAL_ERR_DTYPE.
+ * Errors: HEAL_ERR_NULL (a_hi, b_hi or c NULL with M*N > 0), HEAL_ERR_SHAPE (a negative size, or M, N or
+ * K above 2^31), HEAL_ERR_STRIDE (lda, ldb < K or ldc < N), HEAL_ERR_ALIGN, HEAL_ERR_DTYPE.
  */
 HEAL_API heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
                            const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,

@@ -209,6 +209,36 @@ def test_attn_validation(heal):
     assert call(batch=0) == 0
 
 
+def test_grid_limits_refused_before_launch(heal):
+    """Shapes whose launch grid would pass HIP's 2^32 work-items per dimension are refused with
+    HEAL_ERR_UNSUPPORTED before any runtime call (a truncated grid would silently skip rows); sizes
+    whose workspace product overflows 64 bits saturate instead of wrapping to a small number."""
+    lib = heal.load()
+    F32, F16 = 0, 2
+    # split of 2^26 rows: 2^24 workgroups of 256 work-items
+    assert lib.heal_split(P(FAKE), F32, 1 << 26, 1, 1, F16, P(FAKE), None, 8, None, None) == 6
+    assert lib.heal_unpack_i16(P(FAKE), 1 << 26, 8, 8, 0, P(FAKE), P(FAKE), 8, None) == 6
+    assert lib.heal_row_exponents(P(FAKE), 1 << 26, 1, 1, P(FAKE), None) == 6
+    # quantiser over 2^33 (token, head) rows
+    assert lib.heal_qkv_quant_i16(P(FAKE), 1 << 30, 8, 128, 1024, P(FAKE), 1024, P(FAKE), 8, None) == 6
+    # GEMM: K above 2^31 is a shape error; a skinny GEMM 2^31 columns wide has too many workgroups
+    big = (1 << 31) + 8
+    assert lib.heal_gemm_comp(4, 4, big, P(FAKE), None, None, big, P(FAKE), None, None, big, F16, P(FAKE), 4,
+                              None) == 2
+    assert lib.heal_gemm_comp(16, 1 << 31, 8, P(FAKE), None, None, 8, P(FAKE), None, None, 8, F16, P(FAKE),
+                              1 << 31, None) == 6
+    # attention: 2^30 (batch, head) prefill workgroups; 2^33 (batch, kv-head) decode rows
+    a = _attn_args(heal, batch=1 << 20, n_q_heads=1 << 10, n_kv_heads=1 << 10)
+    assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 6
+    a = _attn_args(heal, batch=1 << 24, n_q_heads=1 << 9, n_kv_heads=1 << 9, q_len=1, kv_len=5000)
+    need = lib.heal_attn_workspace_bytes(ctypes.byref(a))
+    assert need == (1 << 24) * (1 << 9) * 3 * (4 + 128) * 4
+    a.workspace, a.workspace_bytes = FAKE, need
+    assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 6
+    a = _attn_args(heal, batch=1 << 40, n_q_heads=1 << 30, n_kv_heads=1 << 30, q_len=1, kv_len=1)
+    assert lib.heal_attn_workspace_bytes(ctypes.byref(a)) == (1 << 63) - 1
+
+
 def test_gemm_variant_names(heal):
     assert heal.heal_gemm_comp_variant(0, 5, 5, 2) == "none"
     assert heal.heal_gemm_comp_variant(8192, 8192, 8192, 3).startswith("gemm_comp_kernel")
