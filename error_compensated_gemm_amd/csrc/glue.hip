@@ -100,24 +100,30 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : 7; }
 
+// fewer than 2^32 work-items per grid dimension, checked before the launch (6 otherwise)
+bool fits(int64_t blocks, int64_t threads) { return blocks <= ((((int64_t)1) << 32) - 1) / threads; }
+
 }  // namespace
 
 extern "C" {
 
 int glue_embed(const uint16_t* emb, const int32_t* ids, int64_t T, int64_t d, float* out, void* stream) {
   if (T <= 0 || d <= 0) return 0;
+  if (!fits(T, 256)) return 6;
   hipLaunchKernelGGL(embed_kernel, dim3((unsigned)T), dim3(256), 0, (hipStream_t)stream, emb, ids, d, out);
   return status(hipGetLastError());
 }
 
 int glue_rmsnorm(const float* x, int64_t T, int64_t d, float eps, float* y, void* stream) {
   if (T <= 0 || d <= 0) return 0;
+  if (!fits(T, 256)) return 6;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)T), dim3(256), 0, (hipStream_t)stream, x, d, eps, y);
   return status(hipGetLastError());
 }
 
 int glue_rope(float* x, int64_t T, int64_t H, int64_t ld_t, int64_t pos0, const float* cs, void* stream) {
   if (T <= 0 || H <= 0) return 0;
+  if (!fits(T, 64) || !fits(H, 1)) return 6;
   hipLaunchKernelGGL(rope_kernel, dim3((unsigned)T, (unsigned)H), dim3(64), 0, (hipStream_t)stream, x, T, H, ld_t,
                      pos0, cs);
   return status(hipGetLastError());
@@ -125,6 +131,7 @@ int glue_rope(float* x, int64_t T, int64_t H, int64_t ld_t, int64_t pos0, const 
 
 int glue_swiglu(const float* g, const float* u, int64_t n, float* out, void* stream) {
   if (n <= 0) return 0;
+  if (!fits((n + 255) / 256, 256)) return 6;
   hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, g, u, n,
                      out);
   return status(hipGetLastError());
@@ -132,12 +139,14 @@ int glue_swiglu(const float* g, const float* u, int64_t n, float* out, void* str
 
 int glue_add(float* x, const float* y, int64_t n, void* stream) {
   if (n <= 0) return 0;
+  if (!fits((n + 255) / 256, 256)) return 6;
   hipLaunchKernelGGL(add_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, x, y, n);
   return status(hipGetLastError());
 }
 
 int glue_argmax(const float* x, int64_t n, int32_t* out, void* stream) {
   if (n <= 0) return 0;
+  if (n > INT32_MAX) return 6;  // the index is returned as int32
   hipLaunchKernelGGL(argmax_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, x, n, out);
   return status(hipGetLastError());
 }

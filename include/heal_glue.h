@@ -5,8 +5,9 @@
  * the HEAL boundary of heal.h; built into libheal_glue.so.
  *
  * All pointers are device memory owned by the caller; all arithmetic is FP32 with fixed-order reductions;
- * each call enqueues on `stream` (a hipStream_t, NULL = the default stream) and returns 0, or 7 when the HIP
- * runtime refused the launch.  Sizes <= 0 do nothing.
+ * each call enqueues on `stream` (a hipStream_t, NULL = the default stream) and returns 0, 6 when a size
+ * would need a launch grid beyond HIP's 2^32 work-items per dimension (or, for argmax, n above INT32_MAX),
+ * checked before any runtime call, or 7 when the HIP runtime refused the launch.  Sizes <= 0 do nothing.
  */
 #ifndef HEAL_GLUE_H
 #define HEAL_GLUE_H

@@ -49,6 +49,23 @@ def test_glue_library_exports_every_declared_symbol():
     assert set(names) == set(re.findall(r" T (glue_\w+)$", out, re.M))
 
 
+def test_glue_grid_limits_refused_before_launch():
+    """glue calls whose grid would pass 2^32 work-items per dimension return 6 before any runtime call"""
+    lib = ctypes.CDLL(os.path.join(ROOT, "error_compensated_gemm_amd", "libheal_glue.so"))
+    for f in (lib.glue_embed, lib.glue_rmsnorm, lib.glue_rope, lib.glue_swiglu, lib.glue_add, lib.glue_argmax):
+        f.restype = ctypes.c_int
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    fake = vp(FAKE)
+    assert lib.glue_embed(fake, fake, i64(1 << 24), i64(128), fake, None) == 6
+    assert lib.glue_rmsnorm(fake, i64(1 << 24), i64(128), ctypes.c_float(1e-5), fake, None) == 6
+    assert lib.glue_rope(fake, i64(1 << 26), i64(1), i64(128), i64(0), fake, None) == 6
+    assert lib.glue_rope(fake, i64(1), i64(1 << 32), i64(128), i64(0), fake, None) == 6
+    assert lib.glue_swiglu(fake, fake, i64(1 << 32), fake, None) == 6
+    assert lib.glue_add(fake, fake, i64(1 << 32), None) == 6
+    assert lib.glue_argmax(fake, i64(1 << 31), fake, None) == 6
+    assert lib.glue_add(fake, fake, i64(0), None) == 0  # empty: nothing to do
+
+
 def test_version_and_status_strings(heal):
     lib = heal.load()
     assert lib.heal_abi_version() == 3
