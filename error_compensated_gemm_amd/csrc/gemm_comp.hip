@@ -729,10 +729,12 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
 
 // Column blocks per skinny workgroup.  Each workgroup re-reads A (M x K) from L2, so more columns per
 // workgroup save that traffic, but fewer workgroups keep fewer loads in flight.  Measured on MI355X at
-// K = 4096 / 14336 (M = 1, 16, 32): N = 4096 runs best with 1 block (256 workgroups), N = 14336 with 4
-// blocks for M <= 16 (224 workgroups: M = 16 36 -> 28 us) and 2 for M <= 32.
+// K = 4096 / 14336 (M = 1 .. 64; weights rotated through four copies, so read from HBM): N = 4096 runs
+// best with 1 block (256 workgroups); N = 14336 with 2 blocks for M <= 4 (448 workgroups: M = 1 32.1 ->
+// 30.0 us) and 4 above (224 workgroups: M = 16 44.1 -> 38.5 us, M = 32 59.9 -> 45.6 us, M = 64 149.3 ->
+// 62.2 us).
 int skinny_nc(int64_t M, int64_t N) {
-  const int64_t cap = M <= 16 ? 4 : (M <= 32 ? 2 : 1);
+  const int64_t cap = M <= 4 ? 2 : 4;
   int64_t nc = 1;
   while (nc < cap && N / (16 * 2 * nc) >= 224) nc *= 2;
   return (int)nc;
@@ -770,9 +772,12 @@ hipError_t launch_skinny(int64_t M, int64_t N, int64_t K, const uint16_t* ah, co
     return launch_skinny_nc<PART, 1, 1>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
   }
   if (M <= 32) {
-    if (nc >= 2) return launch_skinny_nc<PART, 2, 2>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    if (nc >= 4) return launch_skinny_nc<PART, 2, 4>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    if (nc == 2) return launch_skinny_nc<PART, 2, 2>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
     return launch_skinny_nc<PART, 2, 1>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
   }
+  if (nc >= 4) return launch_skinny_nc<PART, 4, 4>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  if (nc == 2) return launch_skinny_nc<PART, 4, 2>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
   return launch_skinny_nc<PART, 4, 1>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
 }
 
@@ -868,10 +873,10 @@ const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
          {"gemm_skinny_kernel M<=16 NC4 P1", "gemm_skinny_kernel M<=16 NC4 P2", "gemm_skinny_kernel M<=16 NC4 P3"}},
         {{"gemm_skinny_kernel M<=32 NC1 P1", "gemm_skinny_kernel M<=32 NC1 P2", "gemm_skinny_kernel M<=32 NC1 P3"},
          {"gemm_skinny_kernel M<=32 NC2 P1", "gemm_skinny_kernel M<=32 NC2 P2", "gemm_skinny_kernel M<=32 NC2 P3"},
-         {"none", "none", "none"}},
+         {"gemm_skinny_kernel M<=32 NC4 P1", "gemm_skinny_kernel M<=32 NC4 P2", "gemm_skinny_kernel M<=32 NC4 P3"}},
         {{"gemm_skinny_kernel M<=64 NC1 P1", "gemm_skinny_kernel M<=64 NC1 P2", "gemm_skinny_kernel M<=64 NC1 P3"},
-         {"none", "none", "none"},
-         {"none", "none", "none"}}};
+         {"gemm_skinny_kernel M<=64 NC2 P1", "gemm_skinny_kernel M<=64 NC2 P2", "gemm_skinny_kernel M<=64 NC2 P3"},
+         {"gemm_skinny_kernel M<=64 NC4 P1", "gemm_skinny_kernel M<=64 NC4 P2", "gemm_skinny_kernel M<=64 NC4 P3"}}};
     const int nc = skinny_nc(M, N);
     return sk[M <= 16 ? 0 : (M <= 32 ? 1 : 2)][nc == 4 ? 2 : nc - 1][products - 1];
   }
@@ -931,19 +936,26 @@ namespace {
 // element over the same 16-wide k steps, with the same products per step in the same order, so the block
 // tile does not change the result: the three-product 256 x 256 case, whose registers the in-register
 // split does not fit, runs on 256 x 128 tiles with identical output.)
-template <int MT, int NC>
+// BLO: whether this (MT, NC) is instantiated with B's low part; the wide 64-row ones are not (their
+// registers would spill), and the dispatcher sends three-product calls at M > 32 to NC = 1.
+template <int MT, int NC, bool BLO = true>
 hipError_t launch_skinny_f32a_nc(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,
                                  const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
                                  int64_t ldc, hipStream_t stream) {
   if (!grid_fits((N + 16 * NC - 1) / (16 * NC), 64 * kSkWaves)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((N + 16 * NC - 1) / (16 * NC))), block(64 * kSkWaves);
   const uint16_t* const none = nullptr;
-  if (bl)
-    hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, true, true>), grid, block, 0, stream, M, N, K,
-                       none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
-  else
-    hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, false, true>), grid, block, 0, stream, M, N,
-                       K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
+  if constexpr (BLO) {
+    if (bl) {
+      hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, true, true>), grid, block, 0, stream, M, N,
+                         K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
+      return hipGetLastError();
+    }
+  } else if (bl) {
+    return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, false, true>), grid, block, 0, stream, M, N, K,
+                     none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
   return hipGetLastError();
 }
 
@@ -957,9 +969,13 @@ hipError_t launch_skinny_f32a(int64_t M, int64_t N, int64_t K, const float* af, 
     return launch_skinny_f32a_nc<1, 1>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
   }
   if (M <= 32) {
-    if (nc >= 2) return launch_skinny_f32a_nc<2, 2>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    if (nc >= 4) return launch_skinny_f32a_nc<2, 4>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+    if (nc == 2) return launch_skinny_f32a_nc<2, 2>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
     return launch_skinny_f32a_nc<2, 1>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
   }
+  // three products at 64 rows: NC = 1 (the wider ones spill; every NC gives the same sums)
+  if (nc >= 4 && !bl) return launch_skinny_f32a_nc<4, 4, false>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
+  if (nc == 2 && !bl) return launch_skinny_f32a_nc<4, 2, false>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
   return launch_skinny_f32a_nc<4, 1>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
 }
 

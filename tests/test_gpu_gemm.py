@@ -41,7 +41,9 @@ def _bound_check(C, parts, K):
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (1, 1, 1), (7, 5, 3), (300, 200, 100), (129, 257, 1000),
                                    (64, 640, 4104), (513, 96, 33), (20, 70, 999), (48, 33, 64), (65, 300, 130),
                                    # skinny workgroups of 2 and 4 column blocks with ragged N and K
-                                   (3, 7201, 130), (16, 14350, 77), (30, 7300, 300)])
+                                   (3, 7201, 130), (16, 14350, 77), (30, 7300, 300),
+                                   # 32- and 64-row skinny workgroups with 2 and 4 column blocks
+                                   (30, 14390, 70), (50, 7300, 130), (64, 14390, 77)])
 def test_uniform_p3(heal, M, N, K):
     banner(f"gemm uniform P=3 {M}x{N}x{K}")
     A, Bt = workloads.gemm_uniform(M, N, K, seed=0)

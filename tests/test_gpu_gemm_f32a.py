@@ -40,6 +40,8 @@ def _both(heal, A, Bt, b_residual):
 
 @pytest.mark.parametrize("M,N,K,P", [
     (1, 300, 77, 2), (16, 7300, 130, 2), (30, 7300, 301, 3), (64, 1000, 1001, 2), (5, 14350, 64, 3),   # skinny
+    (30, 14390, 70, 2), (30, 14390, 70, 3), (50, 7300, 130, 2), (64, 14390, 77, 2),                     # NC 2, 4
+    (64, 14390, 77, 3),                           # three products at 64 rows: NC 1 against split + GEMM's NC 4
     (100, 300, 1003, 2), (129, 257, 999, 3),                                                            # 128 x 128
     (2048, 4096, 258, 2),                                                                               # 128 x 256
     (2048, 4096, 130, 3),                                                                               # 256 x 128
