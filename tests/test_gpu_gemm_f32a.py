@@ -83,9 +83,10 @@ def test_row_exponents_special_rows(heal):
     assert np.all(host(e0) == 0)
 
 
-@pytest.mark.parametrize("M", [16, 2048])
-@pytest.mark.parametrize("K,N", [(4096, 4096), (14336, 4096)])
+@pytest.mark.parametrize("M", [1, 16, 2048])
+@pytest.mark.parametrize("K,N", workloads.LLAMA3_8B_KN)
 def test_llama_linear_fused(heal, M, K, N):
+    """every Llama-3-8B projection at the bench's sizes (its decode-sized shapes run this entry point)"""
     banner(f"gemm f32a llama M={M} K={K} N={N}")
     X = workloads.llama_activations(M, K, seed=1)
     W = workloads.llama_weights_bf16(N, K, seed=1)
