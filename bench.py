@@ -66,14 +66,14 @@ def source_sha256(path):
 
 def kernel_symbol(variant):
     """Template symbol of a GEMM variant name, as rocprofv3 prints it ("gemm_comp_kernel 256x128 P2" ->
-    "gemm_comp_kernel<2, 256, 128, true, false, false, false>": FP16 parts, block tile, a_lo used, b_lo
-    used, no fused quantisation, A given as parts)."""
+    "gemm_comp_kernel<2, 256, 128, true, false, false, false, false>": FP16 parts, block tile, a_lo used, b_lo
+    used, no fused quantisation, A given as parts, K not split)."""
     parts = variant.split()
     if len(parts) != 3 or parts[0] != "gemm_comp_kernel":
         return None
     bm, bn = parts[1].split("x")
     p = int(parts[2][1:])
-    return f"gemm_comp_kernel<2, {bm}, {bn}, {str(p >= 2).lower()}, {str(p >= 3).lower()}, false, false>"
+    return f"gemm_comp_kernel<2, {bm}, {bn}, {str(p >= 2).lower()}, {str(p >= 3).lower()}, false, false, false>"
 
 
 def stored_traffic(variant):
@@ -556,6 +556,39 @@ def other_rows(heal, workloads, dev):
     rows["hipblaslt_fp16_equal_mfma_work_2048_llama3_8b_3_shapes"] = {
         "us": round(t_blas * 1e6, 2), "compensated_gemm_us": round(t_ours * 1e6, 2),
         "compensated_over_hipblaslt_time": round(t_ours / t_blas, 3), "per_shape_ours_hipblaslt_us": pairs}
+    torch.cuda.empty_cache()
+    # medium M (decode batches, short prefills): heal_gemm_comp_splitk, which cuts K across workgroups where the
+    # plain launch leaves CUs idle, against heal_gemm_comp, on the three Llama projections; the weights rotate
+    # through four copies so they stream from HBM, best of 3 in turn
+    per = {}
+    t_plain = t_split = 0.0
+    for K, N in ((4096, 4096), (4096, 14336), (14336, 4096)):
+        W = dev(workloads.llama_weights_bf16(N, K, seed=10).view(np.int16)).view(torch.bfloat16)
+        bh, _, eb = heal.heal_split(W, residual=False)
+        copies = [bh] + [bh.clone() for _ in range(3)]
+        for M in (64, 128, 512):
+            ah, al, ea = heal.heal_split(dev(workloads.llama_activations(M, K, seed=10)))
+            c = heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
+            need = heal.heal_gemm_comp_workspace_bytes(M, N, K, 2)
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+            def rotate(fn):
+                def run():
+                    for b_ in copies:
+                        fn(b_)
+                return run
+            plain = rotate(lambda b_: heal.heal_gemm_comp(ah, al, ea, b_, None, eb, c=c))
+            split = rotate(lambda b_: heal.heal_gemm_comp_splitk(ah, al, ea, b_, None, eb, c=c, workspace=ws))
+            p_best = s_best = float("inf")
+            for _ in range(3):
+                p_best = min(p_best, time_fn(plain, 5) / 4)
+                s_best = min(s_best, time_fn(split, 5) / 4)
+            t_plain += p_best
+            t_split += s_best
+            per[f"{M}x{K}x{N}"] = {"slices": heal.heal_gemm_comp_splitk_slices(M, N, K, 2),
+                                   "splitk_us": round(s_best * 1e6, 1), "plain_us": round(p_best * 1e6, 1)}
+        del W, bh, eb, copies, ah, al, ea, c, ws
+    rows["gemm_splitk_medium_m_llama3_8b"] = {"us": round(t_split * 1e6, 1), "plain_us": round(t_plain * 1e6, 1),
+                                              "per_shape": per}
     torch.cuda.empty_cache()
     # config 5a: 8192^3 FP32 x FP32, rows scaled by 10^U(-3,3), P = 3
     A, Bt = workloads.gemm_rowscaled(8192, 8192, 8192, seed=4)

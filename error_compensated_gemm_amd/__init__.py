@@ -91,6 +91,12 @@ def load():
     L.heal_gemm_comp_quant_i16.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p, i64, p]
     L.heal_gemm_comp_variant.restype = ctypes.c_char_p
     L.heal_gemm_comp_variant.argtypes = [i64, i64, i64, i32]
+    L.heal_gemm_comp_splitk.restype = i32
+    L.heal_gemm_comp_splitk.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, i64, i32, p, i64, p, ctypes.c_size_t, p]
+    L.heal_gemm_comp_workspace_bytes.restype = ctypes.c_size_t
+    L.heal_gemm_comp_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    L.heal_gemm_comp_splitk_slices.restype = i32
+    L.heal_gemm_comp_splitk_slices.argtypes = [i64, i64, i64, i32]
     L.heal_qkv_quant_i16.restype = i32
     L.heal_qkv_quant_i16.argtypes = [p, i64, i64, i64, i64, p, i64, p, i64, p]
     L.heal_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -109,7 +115,8 @@ EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp
             "heal_qkv_quant_i16", "heal_attn_workspace_bytes", "heal_attn_dual_fp16",
             "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged", "heal_gemm_comp_quant_i16",
             "heal_channel_exponents", "heal_split_scaled", "heal_unpack_i16", "heal_row_exponents",
-            "heal_gemm_comp_f32a")
+            "heal_gemm_comp_f32a", "heal_gemm_comp_splitk", "heal_gemm_comp_workspace_bytes",
+            "heal_gemm_comp_splitk_slices")
 
 
 def _check(status: int):
@@ -244,6 +251,49 @@ def heal_gemm_comp(a_hi, a_lo, a_exp, b_hi, b_lo, b_exp, part: str = "f16", c=No
         raise ValueError("b_lo must match b_hi's shape and strides")
     _check(L.heal_gemm_comp(M, N, K, _ptr(a_hi), _ptr(a_lo), _ptr(a_exp), _ld(a_hi), _ptr(b_hi), _ptr(b_lo),
                             _ptr(b_exp), _ld(b_hi), _PARTS[part], _ptr(c), _ld(c), _stream(a_hi.device)))
+    return c
+
+
+def heal_gemm_comp_workspace_bytes(M: int, N: int, K: int, products: int) -> int:
+    """Workspace bytes heal_gemm_comp_splitk needs (0 when it does not split K)."""
+    return int(load().heal_gemm_comp_workspace_bytes(M, N, K, products))
+
+
+def heal_gemm_comp_splitk_slices(M: int, N: int, K: int, products: int) -> int:
+    """K slices heal_gemm_comp_splitk uses (1: no split, the call is heal_gemm_comp)."""
+    return int(load().heal_gemm_comp_splitk_slices(M, N, K, products))
+
+
+def heal_gemm_comp_splitk(a_hi, a_lo, a_exp, b_hi, b_lo, b_exp, part: str = "f16", c=None, workspace=None):
+    """heal_gemm_comp with K split across workgroups where its own launch would leave CUs idle (partials added
+    in slice order).  A workspace of heal_gemm_comp_workspace_bytes() is allocated with torch when none is
+    given."""
+    import torch
+
+    L = load()
+    M, K = a_hi.shape
+    N = b_hi.shape[0]
+    if c is None:
+        ldc = (N + 3) // 4 * 4
+        c = torch.empty((M, ldc), dtype=torch.float32, device=a_hi.device)[:, :N]
+    if a_lo is not None and (a_lo.shape != a_hi.shape or a_lo.stride() != a_hi.stride()):
+        raise ValueError("a_lo must match a_hi's shape and strides")
+    if b_lo is not None and (b_lo.shape != b_hi.shape or b_lo.stride() != b_hi.stride()):
+        raise ValueError("b_lo must match b_hi's shape and strides")
+    products = 1 + (a_lo is not None) + (b_lo is not None)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is None:
+        # products = 2 is sized as A's low part; B's low part alone plans like three products: cover both
+        need = heal_gemm_comp_workspace_bytes(M, N, K, products)
+        if products == 2:
+            need = max(need, heal_gemm_comp_workspace_bytes(M, N, K, 3))
+        if need:
+            workspace = torch.empty((need + 255) // 256 * 256, dtype=torch.uint8, device=a_hi.device)
+    if workspace is not None:
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check(L.heal_gemm_comp_splitk(M, N, K, _ptr(a_hi), _ptr(a_lo), _ptr(a_exp), _ld(a_hi), _ptr(b_hi), _ptr(b_lo),
+                                   _ptr(b_exp), _ld(b_hi), _PARTS[part], _ptr(c), _ld(c), ws_ptr, ws_bytes,
+                                   _stream(a_hi.device)))
     return c
 
 

@@ -178,6 +178,41 @@ const char* heal_gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products
   return heal::gemm_comp_variant(M, N, K, products);
 }
 
+static bool gemm_sizes_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 0 && N >= 0 && K >= 0 && M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31 && K <= (int64_t)1 << 31;
+}
+
+size_t heal_gemm_comp_workspace_bytes(int64_t M, int64_t N, int64_t K, int products) {
+  if (!gemm_sizes_ok(M, N, K) || products < 1 || products > 3) return 0;
+  return heal::gemm_comp_workspace(M, N, K, products >= 2, products == 3);
+}
+
+int heal_gemm_comp_splitk_slices(int64_t M, int64_t N, int64_t K, int products) {
+  if (!gemm_sizes_ok(M, N, K) || products < 1 || products > 3) return 1;
+  return heal::gemm_comp_slices(M, N, K, products >= 2, products == 3);
+}
+
+heal_status heal_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
+                                  const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
+                                  const int32_t* b_exp, int64_t ldb, int part_type, float* c, int64_t ldc,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gemm_sizes_ok(M, N, K)) return HEAL_ERR_SHAPE;
+  if (part_type != HEAL_F16 && part_type != HEAL_BF16) return HEAL_ERR_DTYPE;
+  if (M == 0 || N == 0) return HEAL_OK;
+  if (!c || (K > 0 && (!a_hi || !b_hi))) return HEAL_ERR_NULL;
+  if (lda < K || ldb < K || ldc < N) return HEAL_ERR_STRIDE;
+  if ((a_hi && !aligned16(a_hi)) || (a_lo && !aligned16(a_lo)) || (b_hi && !aligned16(b_hi)) ||
+      (b_lo && !aligned16(b_lo)) || !aligned16(c) || (a_exp && !aligned4(a_exp)) ||
+      (b_exp && !aligned4(b_exp)) || (lda & 7) || (ldb & 7) || (ldc & 3))
+    return HEAL_ERR_ALIGN;
+  const size_t need = heal::gemm_comp_workspace(M, N, K, a_lo != nullptr, b_lo != nullptr);
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return HEAL_ERR_WORKSPACE;
+  return launched(heal::launch_gemm_comp_splitk(M, N, K, (const uint16_t*)a_hi, (const uint16_t*)a_lo, a_exp, lda,
+                                                (const uint16_t*)b_hi, (const uint16_t*)b_lo, b_exp, ldb, part_type,
+                                                c, ldc, workspace, (hipStream_t)stream));
+}
+
 heal_status heal_qkv_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim,
                                int64_t ld_x, int16_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                                void* stream) {

@@ -136,14 +136,29 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_wave_base)
 // AF32: A arrives as FP32 rows (af, leading dimension lda in floats) with its row exponents ea; a stage
 // holds A as one FP32 plane (the bytes of the hi and lo planes together, chunk c of row r at
 // r * 8 + (c ^ (r & 7))), and each wavefront splits its A fragments in registers as it reads them.
-template <int PART, int BM, int BN, bool ALO, bool BLO, bool QUANT = false, bool AF32 = false>
+// SPLITK: this workgroup multiplies slice blockIdx.y of K ([y * kslice, (y + 1) * kslice) of the parts) and
+// writes its FP32 sums unscaled into slice y of the partials C ([gridDim.y][M][ldc]); splitk_reduce_kernel adds
+// the slices in order and applies the exponents.
+template <int PART, int BM, int BN, bool ALO, bool BLO, bool QUANT = false, bool AF32 = false, bool SPLITK = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_comp_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
     const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
     const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
     int64_t ldc, int16_t* __restrict__ Qo = nullptr, int64_t ldq = 0, float* __restrict__ So = nullptr,
-    int64_t ld_s = 0, const float* __restrict__ af = nullptr) {
+    int64_t ld_s = 0, const float* __restrict__ af = nullptr, int64_t kslice = 0) {
   static_assert(!AF32 || (ALO && PART == HEAL_F16 && !QUANT), "FP32 A: FP16 parts, both A parts, plain C");
+  static_assert(!SPLITK || (!AF32 && !QUANT), "split K: 16-bit parts, FP32 partials");
+  if constexpr (SPLITK) {
+    const int64_t k0 = (int64_t)blockIdx.y * kslice;
+    K = K - k0 < kslice ? K - k0 : kslice;
+    ah += k0;
+    bh += k0;
+    if constexpr (ALO) al += k0;
+    if constexpr (BLO) bl += k0;
+    C += (int64_t)blockIdx.y * M * ldc;
+    ea = nullptr;
+    eb = nullptr;
+  }
   constexpr int NA = ALO ? 2 : 1, NB = BLO ? 2 : 1;
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_PER_T = BM * kCPR / kThreads, B_PER_T = BN * kCPR / kThreads;
@@ -542,13 +557,26 @@ constexpr int kSkWaves = 8;
 // AF32: A arrives as FP32 rows (af, leading dimension lda in floats) with row exponents ea; a lane's 8
 // values of a K step are held as raw FP32 bits (the registers the hi and lo chunks would take) and split
 // just before the MFMAs, so the prefetch never waits on them.
-template <int PART, int MT, int NC, bool ALO, bool BLO, bool AF32 = false>
+// SPLITK: as for gemm_comp_kernel, slice blockIdx.y of K into slice blockIdx.y of the unscaled partials C.
+template <int PART, int MT, int NC, bool ALO, bool BLO, bool AF32 = false, bool SPLITK = false>
 __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
     const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
     const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
-    int64_t ldc, const float* __restrict__ af = nullptr) {
+    int64_t ldc, const float* __restrict__ af = nullptr, int64_t kslice = 0) {
   static_assert(!AF32 || (ALO && PART == HEAL_F16), "FP32 A: FP16 parts, both A parts");
+  static_assert(!SPLITK || !AF32, "split K: 16-bit parts");
+  if constexpr (SPLITK) {
+    const int64_t k0 = (int64_t)blockIdx.y * kslice;
+    K = K - k0 < kslice ? K - k0 : kslice;
+    ah += k0;
+    bh += k0;
+    if constexpr (ALO) al += k0;
+    if constexpr (BLO) bl += k0;
+    C += (int64_t)blockIdx.y * M * ldc;
+    ea = nullptr;
+    eb = nullptr;
+  }
   __shared__ float red[kSkWaves][MT * NC][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cl = lane & 15, kg = lane >> 4;
@@ -1024,6 +1052,156 @@ hipError_t launch_gemm_comp(int64_t M, int64_t N, int64_t K, const uint16_t* a_h
   if (part == HEAL_F16)
     return launch_part<HEAL_F16>(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
   return launch_part<HEAL_BF16>(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
+}
+
+
+// ============================================================================ split K through a workspace
+// When heal_gemm_comp's own launch would leave CUs without work (at most 128 tiles of 128 x 128, or a skinny
+// GEMM of 17..64 rows whose every workgroup re-reads all of A), K is cut into S slices: each workgroup
+// multiplies one slice of one tile into an FP32 partial, and a second kernel adds the S partials of an
+// output in slice order (0, 1, ..., S - 1) and applies the exponents once.  Every slice keeps its products
+// in one FP32 accumulator, so the result has the same error bound as the unsplit GEMM and is the same bits on
+// every run; it differs from heal_gemm_comp's bits only by the grouping of the FP32 additions.
+namespace {
+
+constexpr int64_t kSplitTileMinK = 1024;   // K per slice, at least, for the tile kernel
+constexpr int64_t kSplitSkinnyMinK = 512;  // and for the skinny kernel
+
+struct SplitPlan {
+  bool split;      // false: heal_gemm_comp's own launch
+  bool skinny;     // skinny kernel (four column blocks) or 128 x 128 tiles
+  int64_t S;       // slices
+  int64_t kslice;  // K per slice (a multiple of 64; the last slice takes the rest)
+  int64_t ldw;     // row stride of a partial (N rounded up to 4 floats)
+};
+
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo) {
+  SplitPlan p{false, false, 1, K, 0};
+  if (M <= 0 || N <= 0 || K <= 0) return p;
+  const TileKind kind = choose_tile(M, N, a_lo && !b_lo);
+  int64_t wgs, target, min_k;
+  if (kind == kSkinny) {
+    // split only where every workgroup's re-read of A (M x K x 4 bytes) is over twice its share of B
+    // (16 NC columns x K x 2 bytes): the unsplit launch's column blocks already serve the rest
+    if (M <= 16 * (int64_t)skinny_nc(M, N)) return p;
+    wgs = (N + 63) / 64;
+    target = 512;
+    min_k = kSplitSkinnyMinK;
+  } else if (kind == kTile128x128) {
+    wgs = ((M + 127) / 128) * ((N + 127) / 128);
+    target = 256;
+    min_k = kSplitTileMinK;
+  } else {
+    return p;  // at least one full round of tiles already
+  }
+  int64_t S = target / wgs;  // at most one round: a partial second round costs more than the split gains
+  if (S > K / min_k) S = K / min_k;
+  if (S > 16) S = 16;
+  if (S < 2) return p;
+  const int64_t ks = ((K + S - 1) / S + 63) / 64 * 64;
+  p.split = true;
+  p.skinny = kind == kSkinny;
+  p.kslice = ks;
+  p.S = (K + ks - 1) / ks;
+  p.ldw = (N + 3) / 4 * 4;
+  return p;
+}
+
+// C[i, j] = 2^-(ea_i + eb_j) * (((w_0 + w_1) + w_2) + ... + w_{S-1})[i, j]; one thread per 4 columns
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int S, int64_t M, int64_t N,
+                                                            int64_t ldw, const int32_t* __restrict__ ea,
+                                                            const int32_t* __restrict__ eb, float* __restrict__ C,
+                                                            int64_t ldc) {
+  const int64_t nq = ldw >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * nq) return;
+  const int64_t i = idx / nq, j0 = (idx - i * nq) * 4;
+  const float* p = ws + i * ldw + j0;  // columns N .. ldw - 1 of a partial are never written and never stored
+  const int64_t slice = M * ldw;
+  float4 acc = *reinterpret_cast<const float4*>(p);
+  for (int s = 1; s < S; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(p + s * slice);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const int e = ea ? ea[i] : 0;
+  const float r[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t j = j0 + t;
+    if (j < N) C[i * ldc + j] = __builtin_amdgcn_ldexpf(r[t], -(e + (eb ? eb[j] : 0)));
+  }
+}
+
+template <int PART, bool ALO, bool BLO>
+void launch_split_kernel(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const uint16_t* ah,
+                         const uint16_t* al, int64_t lda, const uint16_t* bh, const uint16_t* bl, int64_t ldb,
+                         float* ws, hipStream_t stream) {
+  const int32_t* const none = nullptr;
+  if (p.skinny) {
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)p.S), block(64 * kSkWaves);
+    if (M <= 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<PART, 2, 4, ALO, BLO, false, true>), grid, block, 0, stream, M, N, K,
+                         ah, al, none, lda, bh, bl, none, ldb, ws, p.ldw, (const float*)nullptr, p.kslice);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<PART, 4, 4, ALO, BLO, false, true>), grid, block, 0, stream, M, N, K,
+                         ah, al, none, lda, bh, bl, none, ldb, ws, p.ldw, (const float*)nullptr, p.kslice);
+  } else {
+    const dim3 grid((unsigned)(((M + 127) / 128) * ((N + 127) / 128)), (unsigned)p.S), block(kThreads);
+    hipLaunchKernelGGL((gemm_comp_kernel<PART, 128, 128, ALO, BLO, false, false, true>), grid, block, 0, stream, M,
+                       N, K, ah, al, none, lda, bh, bl, none, ldb, ws, p.ldw, (int16_t*)nullptr, (int64_t)0,
+                       (float*)nullptr, (int64_t)0, (const float*)nullptr, p.kslice);
+  }
+}
+
+template <int PART>
+void launch_split_part(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
+                       int64_t lda, const uint16_t* bh, const uint16_t* bl, int64_t ldb, float* ws,
+                       hipStream_t stream) {
+  if (al && bl)
+    launch_split_kernel<PART, true, true>(p, M, N, K, ah, al, lda, bh, bl, ldb, ws, stream);
+  else if (al)
+    launch_split_kernel<PART, true, false>(p, M, N, K, ah, al, lda, bh, bl, ldb, ws, stream);
+  else if (bl)
+    launch_split_kernel<PART, false, true>(p, M, N, K, ah, al, lda, bh, bl, ldb, ws, stream);
+  else
+    launch_split_kernel<PART, false, false>(p, M, N, K, ah, al, lda, bh, bl, ldb, ws, stream);
+}
+
+}  // namespace
+
+size_t gemm_comp_workspace(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo) {
+  const SplitPlan p = plan_split(M, N, K, a_lo, b_lo);
+  return p.split ? (size_t)mul_sat(mul_sat(p.S, M), p.ldw * (int64_t)sizeof(float)) : 0;
+}
+
+int gemm_comp_slices(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo) {
+  return (int)plan_split(M, N, K, a_lo, b_lo).S;
+}
+
+hipError_t launch_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,
+                                   const int32_t* a_exp, int64_t lda, const uint16_t* b_hi, const uint16_t* b_lo,
+                                   const int32_t* b_exp, int64_t ldb, int part, float* c, int64_t ldc, void* workspace,
+                                   hipStream_t stream) {
+  const SplitPlan p = plan_split(M, N, K, a_lo != nullptr, b_lo != nullptr);
+  if (!p.split)
+    return launch_gemm_comp(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, part, c, ldc, stream);
+  const int64_t gemm_blocks = p.skinny ? (N + 63) / 64 : ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t red_blocks = (M * (p.ldw / 4) + 255) / 256;
+  if (!grid_fits(gemm_blocks, p.skinny ? 64 * kSkWaves : kThreads) || !grid_fits(red_blocks, 256))
+    return hipErrorInvalidConfiguration;
+  float* ws = reinterpret_cast<float*>(workspace);
+  if (part == HEAL_F16)
+    launch_split_part<HEAL_F16>(p, M, N, K, a_hi, a_lo, lda, b_hi, b_lo, ldb, ws, stream);
+  else
+    launch_split_part<HEAL_BF16>(p, M, N, K, a_hi, a_lo, lda, b_hi, b_lo, ldb, ws, stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)red_blocks), dim3(256), 0, stream, (const float*)ws,
+                     (int)p.S, M, N, p.ldw, a_exp, b_exp, c, ldc);
+  return hipGetLastError();
 }
 
 }  // namespace heal

@@ -47,6 +47,12 @@ hipError_t launch_gemm_comp_quant(int64_t M, int64_t N, int64_t K, const uint16_
 hipError_t launch_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda, const int32_t* a_exp,
                                  const uint16_t* b_hi, const uint16_t* b_lo, const int32_t* b_exp, int64_t ldb,
                                  float* c, int64_t ldc, hipStream_t stream);
+size_t gemm_comp_workspace(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo);
+int gemm_comp_slices(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo);
+hipError_t launch_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,
+                                   const int32_t* a_exp, int64_t lda, const uint16_t* b_hi, const uint16_t* b_lo,
+                                   const int32_t* b_exp, int64_t ldb, int part, float* c, int64_t ldc, void* workspace,
+                                   hipStream_t stream);
 size_t attn_workspace_bytes(const heal_attn_args& a);
 hipError_t launch_attn(const heal_attn_args& a, hipStream_t stream);
 size_t paged_workspace_bytes(const heal_paged_decode_args& a);

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define HEAL_ABI_VERSION 3
+#define HEAL_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define HEAL_API __attribute__((visibility("default")))
@@ -213,6 +213,35 @@ HEAL_API heal_status heal_gemm_comp_quant_i16(int64_t M, int64_t N, int64_t K, c
  * to problem shapes.  Pure host function, no device work.
  */
 HEAL_API const char* heal_gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products);
+
+/*
+ * heal_gemm_comp_splitk -- the error-compensated GEMM of [TS 2B Solution/Mechanism], the operation and
+ * arguments of heal_gemm_comp, for problems whose own launch would leave compute units idle: M x N of at
+ * most 128 tiles of 128 x 128 (M > 64), or 17..64 rows where every workgroup would re-read more of A than
+ * twice its share of B.  There K is cut into S slices (2..16, each a multiple of
+ * 64 but the last); each slice's products go into one FP32 accumulator as in heal_gemm_comp, the S FP32
+ * partials of an output are added in slice order (0, 1, ..., S-1), and the exponents are applied once, so the
+ * result keeps the FP32-accumulation error bound of the exact sum and is the same bits on every run.  It
+ * differs from heal_gemm_comp's bits only by the grouping of those additions.  When no split helps (S = 1)
+ * the call is heal_gemm_comp itself, bit for bit, and needs no workspace.
+ * workspace: device memory of at least heal_gemm_comp_workspace_bytes(M, N, K, P) bytes, 256-byte aligned,
+ * owned by the caller, with P = 1 + (a_lo != NULL) + (b_lo != NULL); its contents on entry do not matter and
+ * are scratch afterwards.  Calls that share a workspace must not overlap.
+ * Errors: as heal_gemm_comp, and HEAL_ERR_WORKSPACE (workspace needed but NULL, too small or misaligned).
+ */
+HEAL_API heal_status heal_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const void* a_hi, const void* a_lo,
+                                  const int32_t* a_exp, int64_t lda, const void* b_hi, const void* b_lo,
+                                  const int32_t* b_exp, int64_t ldb, int part_type, float* c, int64_t ldc,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * heal_gemm_comp_workspace_bytes -- the workspace heal_gemm_comp_splitk needs for an M x N x K problem with
+ * `products` (1..3) 16-bit products (products = 2: A has a low part, B none, as in heal_gemm_comp_variant);
+ * 0 when it does not split.  heal_gemm_comp_splitk_slices -- its slice count S (1 = no split).  Pure host
+ * functions; sizes out of range give 0 bytes and 1 slice.
+ */
+HEAL_API size_t heal_gemm_comp_workspace_bytes(int64_t M, int64_t N, int64_t K, int products);
+HEAL_API int heal_gemm_comp_splitk_slices(int64_t M, int64_t N, int64_t K, int products);
 
 /*
  * heal_qkv_quant_i16 -- INT16 quantisation of Q, K or V per (token, head) ([TS 2A Solution]; [ABS]):

@@ -68,7 +68,7 @@ def test_glue_grid_limits_refused_before_launch():
 
 def test_version_and_status_strings(heal):
     lib = heal.load()
-    assert lib.heal_abi_version() == 3
+    assert lib.heal_abi_version() == 4
     for s in range(9):
         assert lib.heal_status_str(s).decode().startswith("HEAL")
     assert b"unknown" in lib.heal_status_str(99)
@@ -254,6 +254,39 @@ def test_grid_limits_refused_before_launch(heal):
     assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 6
     a = _attn_args(heal, batch=1 << 40, n_q_heads=1 << 30, n_kv_heads=1 << 30, q_len=1, kv_len=1)
     assert lib.heal_attn_workspace_bytes(ctypes.byref(a)) == (1 << 63) - 1
+
+
+def test_splitk_validation_and_plan(heal):
+    """heal_gemm_comp_splitk: heal_gemm_comp's checks, then the workspace (needed only where K is split)"""
+    lib = heal.load()
+    F16, F32 = 2, 0
+    # 128 x 4096 x 14336 with A's low part splits K (32 tiles of 128 x 128); 2048 x 4096 x 4096 does not
+    assert heal.heal_gemm_comp_splitk_slices(128, 4096, 14336, 2) == 8
+    need = heal.heal_gemm_comp_workspace_bytes(128, 4096, 14336, 2)
+    assert need == 8 * 128 * 4096 * 4
+    assert heal.heal_gemm_comp_workspace_bytes(2048, 4096, 4096, 2) == 0
+    assert heal.heal_gemm_comp_splitk_slices(2048, 4096, 4096, 2) == 1
+    assert heal.heal_gemm_comp_splitk_slices(16, 4096, 14336, 2) == 1      # 16-row skinny: no split
+    assert heal.heal_gemm_comp_splitk_slices(64, 4096, 14336, 2) == 8      # 64-row skinny: split
+    assert heal.heal_gemm_comp_workspace_bytes(-1, 4, 4, 2) == 0 and heal.heal_gemm_comp_splitk_slices(4, 4, 4, 0) == 1
+    # K per slice at least 1024 for tiles: 256 x 4096 x 1500 stays whole
+    assert heal.heal_gemm_comp_splitk_slices(256, 4096, 1500, 2) == 1
+
+    def call(M=128, N=4096, K=14336, ah=FAKE, al=FAKE, bh=FAKE, c=FAKE, lda=14336, ldb=14336, ldc=4096, part=F16,
+             ws=FAKE, ws_bytes=need):
+        return lib.heal_gemm_comp_splitk(M, N, K, P(ah) if ah else None, P(al) if al else None, None, lda,
+                                         P(bh) if bh else None, None, None, ldb, part, P(c) if c else None, ldc,
+                                         P(ws) if ws else None, ws_bytes, None)
+    assert call(M=-1) == 2
+    assert call(K=(1 << 31) + 8, lda=(1 << 31) + 8, ldb=(1 << 31) + 8) == 2
+    assert call(part=F32) == 5
+    assert call(ah=None) == 1 and call(c=None) == 1
+    assert call(lda=100) == 3 and call(ldc=100) == 3
+    assert call(ah=MIS) == 4 and call(ldc=4098) == 4
+    assert call(ws=None) == 8                       # workspace needed, none given
+    assert call(ws_bytes=need - 4) == 8             # too small
+    assert call(ws=FAKE + 16) == 8                  # not 256-byte aligned
+    assert call(M=0) == 0                           # empty: nothing to do
 
 
 def test_gemm_variant_names(heal):
