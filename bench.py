@@ -49,6 +49,11 @@ def parse():
                     help="only print the HBM traffic summary of the rocprofv3 --pmc runs under DIR "
                          "(fetch/, write/, copy_fetch/, copy_write/)")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (MiB)")
+    ap.add_argument("--only", choices=("prefill", "decode"),
+                    help="only run 5 launches of that attention kernel on its workload (for counter runs)")
+    ap.add_argument("--summarize-attn", metavar="DIR",
+                    help="only print the counter summary of the attention runs under DIR (decode_fetch/, "
+                         "decode_write/, copy_fetch/, copy_write/, prefill_sq/)")
     return ap.parse_args()
 
 
@@ -158,6 +163,122 @@ def summarize_pmc(d, copy_mib):
     print(TRAFFIC_TAG + json.dumps(rec))
 
 
+def attn_decode_bytes(B=64, L=8192, Hq=32, Hkv=8, D=128):
+    """algorithmic bytes of one decode call: K and V (INT16), their scales, q (INT16 + scale) and O (FP32)"""
+    return 2.0 * B * L * Hkv * D * 2 + 2.0 * B * L * Hkv * 4 + B * Hq * D * (2 + 4)
+
+
+def only_attention(heal, workloads, which):
+    """5 launches of the a6 prefill (1 x 4096 x 32 x 128, causal) or the a7 decode (64 x 8192 keys, 32 / 8
+    heads) on the bench's own inputs, nothing else: the program the attention counter runs profile."""
+    import numpy as np
+    import torch
+
+    heal.load()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    if which == "prefill":
+        Q, K, V = workloads.qkv_fp32(1, 4096, 32, 128, seed=2)
+        (q, qs), (k, ks), (v, vs) = (heal.heal_qkv_quant_i16(dev(t[0])) for t in (Q, K, V))
+        args = (q[None], qs[None], k[None], ks[None], v[None], vs[None])
+        out = heal.heal_attn_dual_fp16(*args, causal=True)
+        for _ in range(4):
+            heal.heal_attn_dual_fp16(*args, causal=True, out=out)
+    else:
+        B, L, Hq, Hkv = 64, 8192, 32, 8
+        k, ks = workloads.int16_cache_device(B, L, Hkv, 128, seed=3)
+        v, vs = workloads.int16_cache_device(B, L, Hkv, 128, seed=4)
+        q, qs = [dev(a) for a in workloads.int16_cache_host(B, 1, Hq, 128, seed=5)]
+        out = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device="cuda")
+        ws = torch.empty(heal.heal_attn_workspace_bytes(heal.make_attn_args(q, qs, k, ks, v, vs, out, True)),
+                         dtype=torch.uint8, device="cuda")
+        for _ in range(5):
+            heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"{which}: 5 launches done", flush=True)
+
+
+def summarize_attn(d, copy_mib):
+    """Markdown summary of the attention counter runs: decode HBM bytes (FETCH_SIZE / WRITE_SIZE scaled by a
+    plain copy, as for the GEMM) and the prefill's matrix / vector occupancy (SQ counters, per SIMD)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def read(sub):
+        vals = defaultdict(lambda: defaultdict(list))
+        for f in glob.glob(os.path.join(d, sub, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    def trace(sub):
+        durs = defaultdict(list)
+        for f in glob.glob(os.path.join(d, sub, "*kernel_trace.csv")):
+            for r in csv.DictReader(open(f)):
+                durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+        return durs
+
+    mean = lambda v: sum(v) / len(v)
+    short = lambda n: n.replace("void ", "").replace("heal::(anonymous namespace)::", "").split("(")[0]
+    cf, cw = read("copy_fetch"), read("copy_write")
+    copy = lambda v: max((k for k in v if "copyBuffer" in k), key=lambda k: len(v[k]["FETCH_SIZE"] or
+                                                                                 v[k]["WRITE_SIZE"]))
+    nbytes = copy_mib * (1 << 20)
+    ff = nbytes / (mean(cf[copy(cf)]["FETCH_SIZE"]) * 1024)
+    fw = nbytes / (mean(cw[copy(cw)]["WRITE_SIZE"]) * 1024)
+    fetch, write = read("decode_fetch"), read("decode_write")
+    print("# Attention kernels: decode HBM traffic and prefill matrix / vector occupancy (bench.py workloads)\n")
+    print("Commands (from the repository root on one MI355X, ROCm 7.2; D = gpurun_out/attn):\n")
+    print("```")
+    print("cd /tmp && export TMPDIR=/tmp")
+    for c, sub, prog in (("FETCH_SIZE", "decode_fetch", "--only decode"), ("WRITE_SIZE", "decode_write", "--only decode"),
+                         ("FETCH_SIZE", "copy_fetch", f"--copy-calibration {copy_mib}"),
+                         ("WRITE_SIZE", "copy_write", f"--copy-calibration {copy_mib}")):
+        print(f"timeout -s KILL 60 rocprofv3 --pmc {c} --output-format csv -d $D/{sub} -o pmc -- "
+              f"python3 /root/repo/bench.py {prog}")
+    print(f"timeout -s KILL 60 rocprofv3 --pmc {' '.join(PREFILL_SQ)} --kernel-trace --output-format csv "
+          "-d $D/prefill_sq -o pmc -- python3 /root/repo/bench.py --only prefill")
+    print(f"python3 /root/repo/bench.py --summarize-attn $D --copy-mib {copy_mib}")
+    print("```\n")
+    algo = attn_decode_bytes()
+    print(f"Decode (64 x 8192 keys, 32 query / 8 key-value heads): algorithmic {algo / 1e9:.3f} GB per call "
+          f"(K and V INT16, their scales, q and O).  Counter scale from a plain {copy_mib} MiB copy: FETCH_SIZE x "
+          f"{ff:.3f}, WRITE_SIZE x {fw:.3f}.\n")
+    print("| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | bytes per launch | / algorithmic |")
+    print("|---|---|---|---|---|---|")
+    for name in sorted(fetch):
+        if "attn_decode" not in name:
+            continue
+        fk = mean(fetch[name]["FETCH_SIZE"])
+        wk = mean(write[name]["WRITE_SIZE"]) if name in write else float("nan")
+        tb = fk * 1024 * ff + wk * 1024 * fw
+        ratio = f"{tb / algo:.3f}" if "merge" not in name else "-"
+        print(f"| `{short(name)}` | {len(fetch[name]['FETCH_SIZE'])} | {fk:.1f} | {wk:.1f} | {tb / 1e9:.4f} GB | "
+              f"{ratio} |")
+    sq, durs = read("prefill_sq"), trace("prefill_sq")
+    print("\nPrefill (1 x 4096 x 32 x 128, causal, byte reading): counters summed over the chip, per launch; per-SIMD "
+          "figures divide by 1024 SIMDs; the clock is GRBM_GUI_ACTIVE over 8 XCDs and the launch's duration under "
+          "the counter run.\n")
+    print("| kernel | launches | duration (us) | clock (GHz) | cycles / SIMD | MFMA busy / SIMD | VALU-MFMA "
+          "co-issue / SIMD | VALU instructions (non-MFMA) / SIMD |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name in sorted(sq):
+        if "attn_prefill" not in name:
+            continue
+        c = {k: mean(v) for k, v in sq[name].items()}
+        dur = mean(durs[name]) if durs.get(name) else float("nan")
+        clk = c["GRBM_GUI_ACTIVE"] / 8 / dur / 1e9
+        print(f"| `{short(name)}` | {len(sq[name]['GRBM_GUI_ACTIVE'])} | {dur * 1e6:.1f} | {clk:.2f} | "
+              f"{dur * clk * 1e9:.3g} | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024:.3g} | "
+              f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / 1024:.3g} | {(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / 1024:.3g} |")
+    print("\nSQ_VALU_MFMA_BUSY_CYCLES counts 32 cycles per v_mfma_f32_32x32x16_f16; a non-MFMA VALU instruction of "
+          "a 64-wide wavefront takes 4 cycles on a 16-lane SIMD.")
+
+
+PREFILL_SQ = ("GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES",
+              "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_BUSY_CYCLES")
+
+
 class Timer:
     """HIP events on the current (launch) stream."""
 
@@ -204,6 +325,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.copy_mib)
         return
+    if args.summarize_attn:
+        summarize_attn(args.summarize_attn, args.copy_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -219,6 +343,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.only:
+        only_attention(heal, workloads, args.only)
         return
     heal.load()
     torch.cuda.set_device(0)
@@ -439,7 +566,7 @@ def other_rows(heal, workloads, dev):
     args = heal.make_attn_args(q, qs, k, ks, v, vs, out, True)
     ws = torch.empty(heal.heal_attn_workspace_bytes(args), dtype=torch.uint8, device="cuda")
     t = time_fn(lambda: heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws), 10)
-    by = 2.0 * B * L * Hkv * 128 * 2 + 2.0 * B * L * Hkv * 4 + B * Hq * 128 * (2 + 4)
+    by = attn_decode_bytes(B, L, Hq, Hkv)
     rows["a7_decode_64x8192_gqa32_8"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
                                          "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
     for reading in ("shift10", "float"):
