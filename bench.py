@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the per-step measurements of the other rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of each M=2048 shape in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="rows of each M=2048 shape in the CPU sample (2048: every output, about 10 s of FP64 work)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (scale run for the HBM byte counters)")
     ap.add_argument("--summarize-pmc", metavar="DIR",
