@@ -142,7 +142,7 @@ def summarize_pmc(d, copy_mib):
     rec = {"source_sha256": source_sha256(GEMM_SRC), "fetch_factor": round(ff, 4), "write_factor": round(fw, 4),
            "copy_mib": copy_mib, "kernels": kernels}
     print("# HBM traffic of the compensated-GEMM kernels: bench.py (Llama-3-8B linear shapes)\n")
-    print("Commands (from the repository root on one MI355X, ROCm 7.2; D = gpurun_out/traffic):\n")
+    print("Commands (from the repository root on one MI355X, ROCm 7.2; D = an output directory):\n")
     print("```")
     print("cd /tmp && export TMPDIR=/tmp")
     for c, sub, prog in (("FETCH_SIZE", "fetch", "--steps 2 --warmup 1 --no-cpu --no-rows"),
@@ -229,7 +229,7 @@ def summarize_attn(d, copy_mib):
     fw = nbytes / (mean(cw[copy(cw)]["WRITE_SIZE"]) * 1024)
     fetch, write = read("decode_fetch"), read("decode_write")
     print("# Attention kernels: decode HBM traffic and prefill matrix / vector occupancy (bench.py workloads)\n")
-    print("Commands (from the repository root on one MI355X, ROCm 7.2; D = gpurun_out/attn):\n")
+    print("Commands (from the repository root on one MI355X, ROCm 7.2; D = an output directory):\n")
     print("```")
     print("cd /tmp && export TMPDIR=/tmp")
     for c, sub, prog in (("FETCH_SIZE", "decode_fetch", "--only decode"), ("WRITE_SIZE", "decode_write", "--only decode"),
