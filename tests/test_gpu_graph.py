@@ -59,3 +59,48 @@ def test_hot_path_graph_replays_equal_eager(heal):
         for w, t in zip(want, (ah, al, ea, c, q, s, out)):
             assert torch.equal(w.view(torch.uint8) if w.dtype == torch.float32 else w,
                                t.view(torch.uint8) if t.dtype == torch.float32 else t), f"replay {rep}"
+
+
+def test_splitk_and_fp32a_graph_replays_equal_eager(heal):
+    """the split-K GEMM (caller workspace, clobbered with NaN between replays: its contents on entry do not
+    matter) and the FP32-A path (row exponents + split in the GEMM) under capture"""
+    banner("graph capture: split-K gemm + row exponents + FP32-A gemm, 4 replays")
+    M, K, N = 128, 4096, 1024
+    X = dev(workloads.llama_activations(M, K, seed=7))
+    W = dev(workloads.llama_weights_bf16(N, K, seed=7).view(np.int16)).view(torch.bfloat16)
+    bh, _, eb = heal.heal_split(W, residual=False)
+    ah, al, ea = heal.heal_split(X)
+    assert heal.heal_gemm_comp_splitk_slices(M, N, K, 2) >= 2
+    ws = torch.empty(heal.heal_gemm_comp_workspace_bytes(M, N, K, 2), dtype=torch.uint8, device="cuda")
+    c1 = heal.heal_gemm_comp_splitk(ah, al, ea, bh, None, eb, workspace=ws)
+    e2 = heal.heal_row_exponents(X)
+    c2 = heal.heal_gemm_comp_f32a(X, e2, bh, None, eb)
+
+    def path():
+        heal.heal_gemm_comp_splitk(ah, al, ea, bh, None, eb, c=c1, workspace=ws)
+        heal.heal_row_exponents(X, exps=e2)
+        heal.heal_gemm_comp_f32a(X, e2, bh, None, eb, c=c2)
+
+    path()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (c1, e2, c2)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        c1.fill_(float("nan"))
+        c2.fill_(float("nan"))
+        e2.fill_(-99)
+        ws.view(torch.float32).fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for w, t in zip(want, (c1, e2, c2)):
+            assert torch.equal(w.view(torch.uint8), t.view(torch.uint8)), f"replay {rep}"
