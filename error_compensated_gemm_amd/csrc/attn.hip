@@ -16,7 +16,8 @@
 //     (3 + 3 products), and its Hq.Hk sum rounds: about 2^-24 of sum |Hq Hk| per logit.
 //   * t_ij = S_int * s_k,j * (s_q,i * softmax_scale * log2 e), carried as an FP32 pair (hi + FMA-captured
 //     rounding error) so that t - max keeps its precision for logits of any size; online softmax in
-//     base 2, FP32 running maximum and sum.
+//     base 2, FP32 running maximum and sum.  Prefill keeps u_ij = S_int * s_k,j as the pair and its maximum
+//     in the same units, and multiplies only the difference by the query's factor: t - m = cq (u - m_u).
 //   * P~ = p * (s_v,j * 2^E) with E = 14 - ilogb(max_j s_v,j) over the keys a workgroup reads, so P~ < 2^15
 //     and its FP16 split P~ = P~h + P~l (P~l = fp16(P~ - P~h), exact residual) keeps 22 bits;
 //     O += P~h.H + P~h.L + P~l.H + P~l.L (4 products, one FP32 accumulator); O = acc * 2^-E / l.
@@ -136,6 +137,16 @@ __device__ __forceinline__ void logit2(float shh, float srest, float sk, float c
   const float c_lo = __builtin_fmaf(sk, cq, -c_hi);
   t_hi = s_hi * c_hi;
   t_lo = __builtin_fmaf(s_hi, c_hi, -t_hi) + __builtin_fmaf(s_lo, c_hi, s_hi * c_lo);
+}
+
+// Prefill's form of the same pair: u = S_int * s_k as u_hi + u_lo (the query's factor cq is applied later, to
+// the difference u - max, so t - m = cq ((u_hi - m_hi) + (u_lo - m_lo)) keeps ~2^-24 |t - m| for logits of
+// any size with fewer operations per score than forming t itself).
+__device__ __forceinline__ void score2(float shh, float srest, float sk, float& u_hi, float& u_lo) {
+  const float s_hi = shh + srest;
+  const float s_lo = srest - (s_hi - shh);
+  u_hi = s_hi * sk;
+  u_lo = __builtin_fmaf(s_lo, sk, __builtin_fmaf(s_hi, sk, -u_hi));
 }
 
 // 2^x by the hardware instruction (about 1 ulp; results below 2^-126 flush to 0).  Softmax weights are
@@ -336,7 +347,9 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
     unpack8<SPLIT>(*reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half), QH[ks], QL[ks]);
-  const float cq = a.qs[b * a.qs_st[0] + qi_c * a.qs_st[1] + h * a.qs_st[2]] * a.scale_log2;
+  // the query's factor of every logit; at least the smallest normal float, so that a zero scale (a query of
+  // zeros: every logit 0) never meets an infinity in cq * (u - m)
+  const float cq = fmaxf(a.qs[b * a.qs_st[0] + qi_c * a.qs_st[1] + h * a.qs_st[2]] * a.scale_log2, 1.17549435e-38f);
   // queries of this wave: [q0 + 32 wave, q0 + 32 wave + 31]; key j visible to query i iff j <= i + off
   const int64_t wq_first = q0 + 32 * wave, wq_last = wq_first + 31;
 
@@ -374,6 +387,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
     int64_t lim = a.Lkv - kb;
     if (a.causal && qi + off + 1 - kb < lim) lim = qi + off + 1 - kb;
     const int lim2 = (int)(lim < 0 ? 0 : (lim > PF_BKV ? PF_BKV : lim)) - 4 * half;
+    // u = S_int * s_k per key (logit / cq), as a pair; hidden keys get u = -inf
     float tv[16], tl[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -382,7 +396,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
-        logit2(shh[r], srest[r], skv[i], cq, tv[r], tl[r]);
+        score2(shh[r], srest[r], skv[i], tv[r], tl[r]);
         tv[r] = 8 * g + i >= lim2 ? -INFINITY : tv[r];
       }
     }
@@ -399,9 +413,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
     //      PF_TAU, and then for the whole wavefront at once, so most tiles skip rescaling O.  Otherwise
     //      every p <= 2^PF_TAU, which the P~ scale 2^E leaves room for.  The first visible tile always
     //      moves it (m_run = -inf), so a key that is alone at the maximum still gets p = 1 exactly. ----
-    const bool grow = tmax > m_run + PF_TAU;
+    // (in logit units: cq > 0 turns the u-space difference into t - m; NaN when both are -inf: no growth)
+    const bool grow = ((tmax - m_run) + (tmax_lo - m_run_lo)) * cq > PF_TAU;
     if (__ballot(grow)) {  // wave-uniform
-      const float alpha = grow ? exp2_raw((m_run - tmax) + (m_run_lo - tmax_lo)) : 1.0f;  // 0 from -inf
+      const float alpha = grow ? exp2_raw(cq * ((m_run - tmax) + (m_run_lo - tmax_lo))) : 1.0f;  // 0 from -inf
       m_run = grow ? tmax : m_run;
       m_run_lo = grow ? tmax_lo : m_run_lo;
       l_run *= alpha;
@@ -421,8 +436,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
         const int r = 4 * g + i;
-        const float p0 = exp2_raw((tv[r] - m_use) + (tl[r] - m_use_lo));
-        const float p1 = exp2_raw((tv[r + 1] - m_use) + (tl[r + 1] - m_use_lo));
+        const float p0 = exp2_raw(cq * ((tv[r] - m_use) + (tl[r] - m_use_lo)));
+        const float p1 = exp2_raw(cq * ((tv[r + 1] - m_use) + (tl[r + 1] - m_use_lo)));
         psum += p0 + p1;
         _Float16 h0, l0, h1, l1;
         split_p(p0 * svv[i], h0, l0);
