@@ -33,8 +33,9 @@
 // Causal workgroups are dispatched longest first.
 //
 // Decode (q_len = 1): HBM-streaming, split over the keys.  A workgroup of 4 wavefronts owns one
-// (batch, kv-head) and a chunk of 2048 keys; the G = n_q/n_kv query heads of the group are the 16 columns
-// of v_mfma_f32_16x16x32_f16 (G <= 16).  Each wavefront streams its 512 keys in steps of 32: K straight
+// (batch, kv-head) and a chunk of 4 kpw keys; the G = n_q/n_kv query heads of the group are the 16 columns
+// of v_mfma_f32_16x16x32_f16 (G <= 16).  Each wavefront streams its kpw keys in steps of 32 (kpw = 512, or
+// less when a short cache or a small batch would leave most CUs idle: see decode_kpw): K straight
 // into MFMA operand registers, V and the scales through two private LDS stages filled by direct-to-LDS
 // transfers, so the next step's 16 KB are in flight while the current step is multiplied (66 KB of LDS
 // per workgroup: two workgroups, eight wavefronts, per CU); the V^T operand comes straight from the
@@ -513,8 +514,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 // ============================================================================================= decode
 constexpr int DC_WAVES = 4;
 constexpr int DC_THREADS = 64 * DC_WAVES;
-constexpr int DC_KPW = 512;                   // keys per wavefront
-constexpr int DC_CHUNK = DC_KPW * DC_WAVES;   // keys per workgroup
+constexpr int DC_KPW = 512;                   // keys per wavefront, at most
 constexpr int DC_SUB = 32;                    // keys per step
 constexpr int DC_PART = 4 + D;                // floats per partial: m_hi, m_lo, l, (pad), O[128]
 constexpr int DC_NDMA = 17;                   // direct-to-LDS transfers per lane per step
@@ -527,8 +527,20 @@ struct DcStage {
   float sc[2 * DC_SUB];
 };
 
-size_t decode_workspace(int64_t B, int64_t Hq, int64_t Lkv) {
-  const int64_t nsplit = (Lkv + DC_CHUNK - 1) / DC_CHUNK;
+// Keys per wavefront: 512, halved (down to one 32-key step) while the grid would hold fewer than 512
+// workgroups, the number two per CU makes resident.  With 512 keys a workgroup runs 16 dependent steps, so
+// a grid of a few dozen workgroups (one sequence of a few hundred keys) is bound by that chain's latency,
+// not by HBM; shorter runs spread the same keys over more workgroups at the price of more partials for the
+// merge.  Every wavefront range stays kpw-aligned, a power of two from 32 to 512.
+int decode_kpw(int64_t B, int64_t Hkv, int64_t Lkv) {
+  int kpw = DC_KPW;
+  while (kpw > DC_SUB && mul_sat(mul_sat(B, Hkv), (Lkv + 4 * kpw - 1) / (4 * kpw)) < 512) kpw >>= 1;
+  return kpw;
+}
+
+size_t decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lkv) {
+  const int64_t chunk = (int64_t)DC_WAVES * decode_kpw(B, Hkv, Lkv);
+  const int64_t nsplit = (Lkv + chunk - 1) / chunk;
   // saturates rather than wraps: an impossible size is refused, never under-sized
   return (size_t)mul_sat(mul_sat(mul_sat(B, Hq), nsplit > 0 ? nsplit : 1), DC_PART * (int64_t)sizeof(float));
 }
@@ -537,7 +549,7 @@ size_t decode_workspace(int64_t B, int64_t Hq, int64_t Lkv) {
 // has its own length; otherwise one contiguous run of a.Lkv keys per (batch, kv head).
 template <bool PAGED, int SPLIT>
 __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_decode_kernel(
-    AttnParams a, float* __restrict__ ws, int nsplit) {
+    AttnParams a, float* __restrict__ ws, int nsplit, int kpw) {
   // two stages per wavefront, each stage its own object (the compiler can tell the stage being read
   // from the one being filled); after the key loop the same bytes hold the wavefront partials
   __shared__ DcStage st0[DC_WAVES];
@@ -557,11 +569,11 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     const int64_t len = a.lens[b];
     L = len < 0 ? 0 : (len > a.Lkv ? a.Lkv : len);
   }
-  const int64_t c0 = (int64_t)split * DC_CHUNK;
-  int64_t c1 = c0 + DC_CHUNK;
+  const int64_t c0 = (int64_t)split * DC_WAVES * kpw;
+  int64_t c1 = c0 + DC_WAVES * kpw;
   if (c1 > L) c1 = L;
-  const int64_t w0 = c0 + (int64_t)wave * DC_KPW;
-  int64_t w1 = w0 + DC_KPW;
+  const int64_t w0 = c0 + (int64_t)wave * kpw;
+  int64_t w1 = w0 + kpw;
   if (w1 > c1) w1 = c1;
 
   // contiguous: the (batch, kv head) runs; paged: the kv head's offset inside a page
@@ -588,8 +600,8 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   // scales direct-to-LDS (position p = 64 i + l holds key p / 16 in the VT_DECODE layout)
   //  A step's keys past this wavefront's range are clamped to its last key (read, never used).  Paged: the
   //  page size is a power of two >= 32 and steps start at multiples of 32, so after that clamp every key of
-  //  a step lies in the page of its first (clamped) key.  The wavefront's range (512 keys, 512-aligned)
-  //  spans at most 16 pages, whose ids lane l holds from the start (pid_lane); a step takes its page id from
+  //  a step lies in the page of its first (clamped) key.  The wavefront's range (kpw <= 512 keys,
+  //  kpw-aligned, kpw a power of two) spans at most 16 pages, whose ids lane l holds from the start (pid_lane); a step takes its page id from
   //  the lane of its page, so no table read waits in front of the step's loads.
   const int64_t kvs1 = a.kv_st[1], ss1 = a.kvs_st[1];
   const int64_t jmax = w1 - 1;
@@ -907,7 +919,7 @@ __global__ void zero_rows_kernel(AttnParams a) {
 
 size_t attn_workspace_bytes(const heal_attn_args& x) {
   if (!use_decode(x) || x.batch <= 0 || x.n_q_heads <= 0) return 0;
-  return decode_workspace(x.batch, x.n_q_heads, x.kv_len);
+  return decode_workspace(x.batch, x.n_q_heads, x.n_kv_heads, x.kv_len);
 }
 
 hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
@@ -919,7 +931,8 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
     return hipGetLastError();
   }
   if (use_decode(x)) {
-    const int64_t nsplit64 = (x.kv_len + DC_CHUNK - 1) / DC_CHUNK;
+    const int kpw = decode_kpw(x.batch, x.n_kv_heads, x.kv_len);
+    const int64_t nsplit64 = (x.kv_len + DC_WAVES * kpw - 1) / (DC_WAVES * kpw);
     if (!grid_fits(nsplit64, DC_THREADS) || !grid_fits(mul_sat(x.batch, x.n_kv_heads), 1) ||
         !grid_fits(mul_sat(x.batch, x.n_q_heads), D))
       return hipErrorInvalidConfiguration;
@@ -928,13 +941,13 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
     const dim3 grid((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads));
     if (x.dual_split == HEAL_DUAL_SHIFT10)
       hipLaunchKernelGGL((attn_decode_kernel<false, HEAL_DUAL_SHIFT10>), grid, dim3(DC_THREADS), 0, stream, p, ws,
-                         nsplit);
+                         nsplit, kpw);
     else if (x.dual_split == HEAL_DUAL_FLOAT)
       hipLaunchKernelGGL((attn_decode_kernel<false, HEAL_DUAL_FLOAT>), grid, dim3(DC_THREADS), 0, stream, p, ws,
-                         nsplit);
+                         nsplit, kpw);
     else
       hipLaunchKernelGGL((attn_decode_kernel<false, HEAL_DUAL_BYTE>), grid, dim3(DC_THREADS), 0, stream, p, ws,
-                         nsplit);
+                         nsplit, kpw);
     hipLaunchKernelGGL(attn_decode_merge_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream,
                        p, (const float*)ws, nsplit);
     return hipGetLastError();
@@ -954,7 +967,7 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
 
 size_t paged_workspace_bytes(const heal_paged_decode_args& x) {
   if (x.batch <= 0 || x.n_q_heads <= 0) return 0;
-  return decode_workspace(x.batch, x.n_q_heads, x.max_kv_len);
+  return decode_workspace(x.batch, x.n_q_heads, x.n_kv_heads, x.max_kv_len);
 }
 
 hipError_t launch_attn_paged(const heal_paged_decode_args& x, hipStream_t stream) {
@@ -965,7 +978,8 @@ hipError_t launch_attn_paged(const heal_paged_decode_args& x, hipStream_t stream
     return hipGetLastError();
   }
   // the grid covers max_kv_len; splits past a sequence's own length write empty partials
-  const int64_t nsplit64 = (x.max_kv_len + DC_CHUNK - 1) / DC_CHUNK;
+  const int kpw = decode_kpw(x.batch, x.n_kv_heads, x.max_kv_len);
+  const int64_t nsplit64 = (x.max_kv_len + DC_WAVES * kpw - 1) / (DC_WAVES * kpw);
   if (!grid_fits(nsplit64, DC_THREADS) || !grid_fits(mul_sat(x.batch, x.n_kv_heads), 1) ||
       !grid_fits(mul_sat(x.batch, x.n_q_heads), D))
     return hipErrorInvalidConfiguration;
@@ -974,13 +988,13 @@ hipError_t launch_attn_paged(const heal_paged_decode_args& x, hipStream_t stream
   const dim3 grid((unsigned)nsplit, (unsigned)(x.batch * x.n_kv_heads));
   if (x.dual_split == HEAL_DUAL_SHIFT10)
     hipLaunchKernelGGL((attn_decode_kernel<true, HEAL_DUAL_SHIFT10>), grid, dim3(DC_THREADS), 0, stream, p, ws,
-                       nsplit);
+                       nsplit, kpw);
   else if (x.dual_split == HEAL_DUAL_FLOAT)
     hipLaunchKernelGGL((attn_decode_kernel<true, HEAL_DUAL_FLOAT>), grid, dim3(DC_THREADS), 0, stream, p, ws,
-                       nsplit);
+                       nsplit, kpw);
   else
     hipLaunchKernelGGL((attn_decode_kernel<true, HEAL_DUAL_BYTE>), grid, dim3(DC_THREADS), 0, stream, p, ws,
-                       nsplit);
+                       nsplit, kpw);
   hipLaunchKernelGGL(attn_decode_merge_kernel, dim3((unsigned)(x.batch * x.n_q_heads)), dim3(D), 0, stream, p,
                      (const float*)ws, nsplit);
   return hipGetLastError();

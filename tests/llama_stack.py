@@ -1,6 +1,7 @@
 """Model-level check of the HEAL path: a random-initialised Llama-style decoder stack run three ways,
-  * HEAL: every projection is heal_split + heal_gemm_comp (FP32 activations, bf16 weights exact in FP16,
-    P = 2), Q/K/V are INT16-quantised into the KV cache by heal_qkv_quant_i16, attention is
+  * HEAL: every projection is the compensated GEMM (FP32 activations, bf16 weights exact in FP16, P = 2;
+    heal_split + heal_gemm_comp, or heal_gemm_comp_f32a for up to 64 rows, which gives the same bits), Q/K/V
+    are INT16-quantised into the KV cache by heal_qkv_quant_i16 (one launch for all three), attention is
     heal_attn_dual_fp16 (prefill, then one decode step per token); the other block steps are the FP32 glue
     kernels of libheal_glue.so;
   * plain bf16: bf16 values between every op and in the KV cache, each op's arithmetic in FP32 on those values
@@ -89,20 +90,27 @@ class HealPath:
         for l in range(cfg["layers"]):
             self.parts[f"{l}.wqkv"] = heal.heal_split(torch.cat([w[f"{l}.wq"], w[f"{l}.wk"], w[f"{l}.wv"]]),
                                                       residual=False)[0::2]
-            for n in ("wo", "wg", "wu", "wd"):
+            self.parts[f"{l}.wgu"] = heal.heal_split(torch.cat([w[f"{l}.wg"], w[f"{l}.wu"]]), residual=False)[0::2]
+            for n in ("wo", "wd"):
                 self.parts[f"{l}.{n}"] = heal.heal_split(w[f"{l}.{n}"], residual=False)[0::2]
         self.parts["head"] = heal.heal_split(w["head"], residual=False)[0::2]
         self.emb = w["emb"]
         Lmax = cfg["prompt"] + cfg["steps"]
         self.cs = rope_table(Lmax)
-        self.kc = [torch.zeros((Lmax, hkv, 128), dtype=torch.int16, device="cuda") for _ in range(cfg["layers"])]
-        self.vc = [torch.zeros((Lmax, hkv, 128), dtype=torch.int16, device="cuda") for _ in range(cfg["layers"])]
-        self.ks = [torch.zeros((Lmax, hkv), dtype=torch.float32, device="cuda") for _ in range(cfg["layers"])]
-        self.vs = [torch.zeros((Lmax, hkv), dtype=torch.float32, device="cuda") for _ in range(cfg["layers"])]
+        # per layer, the INT16 Q, K and V heads of every position side by side ([Lmax, hq + 2 hkv, 128]) and
+        # their scales, so that one quantiser launch fills all three; attention reads K and V as strided views
+        H = hq + 2 * hkv
+        self.qkv = [torch.zeros((Lmax, H, 128), dtype=torch.int16, device="cuda") for _ in range(cfg["layers"])]
+        self.qkvs = [torch.zeros((Lmax, H), dtype=torch.float32, device="cuda") for _ in range(cfg["layers"])]
 
-    def linear(self, x, name):
-        ah, al, ea = heal.heal_split(x)
+    def linear(self, x, name, rows=slice(None)):
+        """x W^T for the FP16 parts of ``name`` (``rows`` selects a block of W's rows).  Up to 64 rows of x are
+        split inside the GEMM's prologue (the same bits as heal_split + heal_gemm_comp, one launch fewer)."""
         bh, eb = self.parts[name]
+        bh, eb = bh[rows], eb[rows]
+        if x.shape[0] <= 64:
+            return heal.heal_gemm_comp_f32a(x, heal.heal_row_exponents(x), bh, None, eb)
+        ah, al, ea = heal.heal_split(x)
         return heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
 
     def norm(self, x):
@@ -119,26 +127,26 @@ class HealPath:
         T, d, hq, hkv = idt.numel(), cfg["d"], cfg["hq"], cfg["hkv"]
         x = torch.empty((T, d), dtype=torch.float32, device="cuda")
         assert G.glue_embed(_p(self.emb), _p(idt), T, d, _p(x), _s()) == 0
+        H, F = hq + 2 * hkv, cfg["f"]
         for l in range(cfg["layers"]):
             qkv = self.linear(self.norm(x), f"{l}.wqkv")  # [T, (hq + 2 hkv) 128]
-            ld = qkv.stride(0)
-            assert G.glue_rope(_p(qkv), T, hq, ld, pos0, _p(self.cs), _s()) == 0
-            kv = qkv[:, hq * 128:]
-            assert G.glue_rope(_p(kv), T, hkv, ld, pos0, _p(self.cs), _s()) == 0
-            q, qs = heal.heal_qkv_quant_i16(qkv[:, :hq * 128].view(T, hq, 128))
-            heal.heal_qkv_quant_i16(kv[:, :hkv * 128].view(T, hkv, 128), q=self.kc[l][pos0:pos0 + T],
-                                    scale=self.ks[l][pos0:pos0 + T])
-            heal.heal_qkv_quant_i16(kv[:, hkv * 128:].view(T, hkv, 128), q=self.vc[l][pos0:pos0 + T],
-                                    scale=self.vs[l][pos0:pos0 + T])
+            assert G.glue_rope(_p(qkv), T, hq + hkv, qkv.stride(0), pos0, _p(self.cs), _s()) == 0  # Q and K heads
+            c, cs = self.qkv[l], self.qkvs[l]
+            heal.heal_qkv_quant_i16(qkv.view(T, H, 128), q=c[pos0:pos0 + T], scale=cs[pos0:pos0 + T])
             n = pos0 + T
-            a = heal.heal_attn_dual_fp16(q[None], qs[None], self.kc[l][None, :n], self.ks[l][None, :n],
-                                         self.vc[l][None, :n], self.vs[l][None, :n], causal=True)
+            kh, vh = slice(hq, hq + hkv), slice(hq + hkv, H)
+            a = heal.heal_attn_dual_fp16(c[None, pos0:n, :hq], cs[None, pos0:n, :hq], c[None, :n, kh],
+                                         cs[None, :n, kh], c[None, :n, vh], cs[None, :n, vh], causal=True)
             o = self.linear(a.view(T, hq * 128), f"{l}.wo")
             assert G.glue_add(_p(x), _p(o), x.numel(), _s()) == 0
             h = self.norm(x)
-            gte, up = self.linear(h, f"{l}.wg"), self.linear(h, f"{l}.wu")
-            act = torch.empty_like(gte)
-            assert G.glue_swiglu(_p(gte), _p(up), gte.numel(), _p(act), _s()) == 0
+            if T == 1:  # gate and up in one GEMM: the two halves of its one output row are each contiguous
+                gu = self.linear(h, f"{l}.wgu")
+                gte, up = gu[:, :F], gu[:, F:]
+            else:
+                gte, up = self.linear(h, f"{l}.wgu", slice(0, F)), self.linear(h, f"{l}.wgu", slice(F, 2 * F))
+            act = torch.empty((T, F), dtype=torch.float32, device="cuda")
+            assert G.glue_swiglu(_p(gte), _p(up), T * F, _p(act), _s()) == 0
             dn = self.linear(act, f"{l}.wd")
             assert G.glue_add(_p(x), _p(dn), x.numel(), _s()) == 0
         hn = self.norm(x[-1:].contiguous())
@@ -291,7 +299,55 @@ def run(cfg: dict, seed: int = 0, log=print) -> dict:
     return out
 
 
+def summarize_trace(d: str, steps: int = 20) -> None:
+    """Markdown breakdown of the replayed HEAL decode steps in a rocprofv3 kernel trace of this script.  Every
+    HEAL forward ends with the glue argmax kernel and the graph replays are the last HEAL forwards, so the last
+    ``steps`` argmax-terminated runs of dispatches are the timed replays."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    short = lambda n: n.replace("void ", "").replace("(anonymous namespace)::", "").replace("heal::", "").split("(")[0]
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short(r["Kernel_Name"])))
+    rows.sort()
+    ends = [i for i, r in enumerate(rows) if r[2] == "argmax_kernel"]
+    assert len(ends) > steps, f"{len(ends)} HEAL forwards in the trace"
+    per = defaultdict(lambda: [0, 0])  # name -> [launches, ns] over the replays
+    wall = busy = launches = 0
+    for k in range(len(ends) - steps, len(ends)):
+        seg = rows[ends[k - 1] + 1:ends[k] + 1]
+        wall += seg[-1][1] - seg[0][0]
+        for t0, t1, n in seg:
+            busy += t1 - t0
+            per[n][0] += 1
+            per[n][1] += t1 - t0
+        launches += len(seg)
+    print("# Decode step of the HEAL decoder stack (32 layers, d 4096, 32/8 heads, FFN 14336, vocabulary 128256), "
+          "replayed as a HIP graph: per-kernel time\n")
+    print("Command (from the repository root on one MI355X, ROCm 7.2; D = an output directory):\n")
+    print("```")
+    print("cd /tmp && export TMPDIR=/tmp")
+    print("rocprofv3 --kernel-trace --output-format csv -d $D -o run -- python3 /root/repo/tests/llama_stack.py --full")
+    print("python3 /root/repo/tests/llama_stack.py --summarize-trace $D")
+    print("```\n")
+    print(f"Over the last {steps} replays (context 575 tokens), per step: {launches / steps:.0f} kernel launches, "
+          f"{wall / steps / 1e3:.1f} us from the first kernel's start to the last one's end, of which "
+          f"{busy / steps / 1e3:.1f} us inside kernels and {(wall - busy) / steps / 1e3:.1f} us between them "
+          f"({(wall - busy) / launches / 1e3:.2f} us per launch).  Timestamps are the tracer's; the untraced "
+          "replay time is printed by the script itself.\n")
+    print("| kernel | launches per step | us per launch | us per step | share of kernel time |")
+    print("|---|---|---|---|---|")
+    for n, (c, ns) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        print(f"| `{n}` | {c / steps:.0f} | {ns / c / 1e3:.2f} | {ns / steps / 1e3:.1f} | {ns / busy:.1%} |")
+
+
 if __name__ == "__main__":
+    if "--summarize-trace" in sys.argv:
+        summarize_trace(sys.argv[sys.argv.index("--summarize-trace") + 1])
+        sys.exit(0)
     cfg = FULL if "--full" in sys.argv else SMALL
     res = run(cfg, log=lambda m: print(m, flush=True))
     print(json.dumps(res), flush=True)

@@ -103,6 +103,31 @@ def test_decode_small(heal, B, L, Hq, Hkv):
     assert err <= TOL
 
 
+# The decode plan: 512 keys per wavefront, halved (down to 32) while the grid would hold fewer than 512
+# workgroups; the workspace holds one partial per (batch, query head, chunk of 4 wavefronts' keys), so its
+# size shows the plan taken.  Each case has a ragged last chunk.
+@pytest.mark.parametrize("B,L,Hq,Hkv,kpw", [(64, 2500, 32, 8, 512), (24, 3000, 32, 8, 256),
+                                            (16, 3000, 32, 8, 128), (4, 5000, 32, 8, 64), (1, 575, 32, 8, 32)])
+def test_decode_plans(heal, B, L, Hq, Hkv, kpw):
+    banner(f"decode plan B={B} L={L} Hq={Hq} Hkv={Hkv}, {kpw} keys per wavefront")
+    q, qs = workloads.int16_cache_host(B, 1, Hq, 128, seed=34)
+    k, ks = workloads.int16_cache_host(B, L, Hkv, 128, seed=35)
+    v, vs = workloads.int16_cache_host(B, L, Hkv, 128, seed=36)
+    args = [dev(t) for t in (q, qs, k, ks, v, vs)]
+    out = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device="cuda")
+    need = heal.heal_attn_workspace_bytes(heal.make_attn_args(*args, out))
+    assert need == B * Hq * -(-L // (4 * kpw)) * (4 + 128) * 4
+    o1 = heal.heal_attn_dual_fp16(*args, causal=True)
+    o2 = heal.heal_attn_dual_fp16(*args, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    sel = sorted({0, B // 2, B - 1})
+    ref = oracle.attn_i16_f64(q[sel], qs[sel], k[sel], ks[sel], v[sel], vs[sel], causal=True)
+    err = normwise(host(o1)[sel], ref)
+    print(f"[attn] decode plan {B},{L} kpw {kpw} normwise {err:.3e}")
+    assert err <= TOL
+
+
 def test_prefill_config_sampled_and_deterministic(heal):
     banner("prefill 1x4096x32x128 causal, sampled rows")
     B, L, H = 1, 4096, 32
