@@ -65,9 +65,15 @@ TRAFFIC_TAG = "traffic-json: "
 
 
 def source_sha256(path):
+    """SHA-256 of a C++ source with its comments and whitespace removed, so that the stored counters stay valid
+    across comment edits and go stale with any change to the code itself."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(path) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256("".join(src.split()).encode()).hexdigest()
 
 
 def kernel_symbol(variant):

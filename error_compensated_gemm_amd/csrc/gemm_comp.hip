@@ -1,7 +1,8 @@
 // gemm_comp.hip -- the error-compensated GEMM of HEAL on gfx950 matrix cores.
 //
-// [TS 2B Mechanism]: an FP32 operand is decomposed into a primary 16-bit value and a residual, and the
-// 16-bit products are summed so that the truncation error of the primary part is captured.  Here
+// [TS 2B Mechanism]: an FP32 operand becomes a 16-bit leading part plus a 16-bit remainder (what the leading
+// part could not hold), and the 16-bit products are summed so that the leading part's rounding error is
+// recovered.  Here
 //   C[i, j] = 2^-(ea_i + eb_j) * sum_k ( ah*bh + ah*bl + al*bh )
 // with every product formed by v_mfma_f32_32x32x16_{f16,bf16} from the SAME LDS-staged tiles and summed
 // into ONE FP32 accumulator; the only rounding at the kernel boundary is the FP32 store of the scaled

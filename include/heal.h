@@ -2,7 +2,7 @@
  * heal.h -- C ABI of the HEAL hot path on AMD Instinct MI355X (gfx950).
  *
  * HEAL gets near-FP32 results out of 16-bit matrix units and keeps the attention inputs at 16 bits:
- *   - an FP32 operand is split into a primary 16-bit value and a residual, and the 16-bit products are
+ *   - an FP32 operand is split into a 16-bit leading part and a 16-bit remainder, and the 16-bit products are
  *     summed into one FP32 accumulator (the "algebraic error compensation" GEMM);
  *   - Q, K and V are stored as INT16, and each INT16 value is unpacked into two exactly representable
  *     FP16 halves ("Dual-FP16") for the QK^T and PV products, with FP32 softmax.

@@ -293,8 +293,9 @@ def attn_paged_i16_f64(q, qs, k_pages, ks_pages, v_pages, vs_pages, block_table,
 
 
 def channel_exponents(x: np.ndarray, threshold_log2: int) -> np.ndarray:
-    """[TS 2B Overflow Handling] rare outlier channels as exact power-of-two column scales (reading
-    R-chan): m_c = max_r |x[r, c]|; columns with ilogb(m_c) > T get T - ilogb(m_c), the others 0."""
+    """[TS 2B Overflow Handling] read as exact power-of-two scales of the few outlier columns only (the pages
+    give no rule; this one is the plainest): m_c = max_r |x[r, c]|; columns with ilogb(m_c) > T get
+    T - ilogb(m_c), the others 0."""
     x = np.asarray(x, np.float64)
     m = np.max(np.abs(x), axis=0) if x.shape[0] else np.zeros(x.shape[1])
     _, e = np.frexp(m)  # m = f 2^e with f in [0.5, 1): ilogb(m) = e - 1

@@ -19,13 +19,13 @@
  *
  * Readings adopted where the pages are silent (each is listed with its reason in the design notes):
  *   R-split   16-bit parts are FP16 after an exact power-of-two prescale per row, e = 14 - ilogb(max|x|),
- *             so the row maximum lands in [2^14, 2^15).  The "targeted rescaling" of [TS 2B Overflow
+ *             so the row maximum lands in [2^14, 2^15).  The outlier rescaling of [TS 2B Overflow
  *             Handling] read as an always-on, exact per-row scale.
  *   R-prod    the compensated product sums hi*hi + hi*lo + lo*hi (lo*lo dropped) when both operands are
- *             split, hi*hi + lo*hi when only the activations are ([TS 2B Mechanism]: "two" products).
+ *             split, hi*hi + lo*hi when only the activations are ([TS 2B Mechanism] names two products).
  *   R-quant   symmetric INT16 per (token, head): s = fl32(max|x| / 32767), q = clamp(rint(fl32(x / s)),
  *             -32767, 32767); s = 0 (an all-zero row, or max|x| so small that s underflows) gives q = 0
- *             ([TS 2A Solution] names only "INT16").
+ *             ([TS 2A Solution] names INT16 and no scheme).
  *   R-dual    Dual-FP16 unpack is the byte split hi = q >> 8 (floor), lo = q & 0xFF, q = 256*hi + lo;
  *             the pages write the pair with a 2^10 shift ([TS 2A Mechanism]); any shift that keeps both
  *             halves integer is exact, and 8 keeps every FP32 partial sum exact at head_dim 128.  Two
@@ -112,9 +112,9 @@ static double part_value(uint16_t b, int part) {
 }
 
 /* ------------------------------------------------------------------------------------------------------
- * Split of an FP32 (or bf16-valued) matrix into a primary 16-bit value and a residual: [TS 2B Mechanism]
- * ("decomposed into a primary 16-bit value and a residual error term"), with the exact power-of-two row
- * prescale of R-split standing for [TS 2B Overflow Handling].
+ * Split of an FP32 (or bf16-valued) matrix into a 16-bit leading part and the 16-bit remainder of what that
+ * part could not hold: [TS 2B Mechanism], with an exact power-of-two row prescale standing for
+ * [TS 2B Overflow Handling].
  *
  *   e_r = 14 - ilogb(max_c |x_rc|)   (0 when the row is all zero, or when prescale == 0)
  *   x'  = fl32(x * 2^e_r)

@@ -1,6 +1,6 @@
 """Pins of the oracle's split (the compensated GEMM's operand decomposition) and of the Dual-FP16 unpack.
 
-Split: [TS 2B Mechanism] "primary 16-bit value and a residual error term", with the exact power-of-two
+Split: [TS 2B Mechanism], a 16-bit leading part plus the 16-bit remainder it leaves, with the exact power-of-two
 row prescale standing for [TS 2B Overflow Handling].  Dual-FP16: [TS 2A Mechanism].  ([TS] is the
 gist.science explainer "Demystifying Numerical Instability in LLM Inference ... with HEAL", Technical
 Summary.)  Pins: hand-derived cases (tests/golden), invariants that hold for every input (property
