@@ -548,6 +548,14 @@ def other_rows(heal, workloads, dev):
     t = time_fn(quant_all, 20)
     nel = 3 * qd.numel()
     rows["a4_quant_3x4096x32x128"] = {"us": round(t * 1e6, 2), "gbs": round(nel * (4 + 2 + 4 / 128) / t / 1e9, 1)}
+    # the same values with each token's Q, K and V heads side by side ([4096, 96, 128], as a fused QKV
+    # projection writes them): one launch, the same codes and scales
+    fused = torch.cat([qd, kd, vd], dim=1)
+    fq, fs = heal.heal_qkv_quant_i16(fused)
+    t = time_fn(lambda: heal.heal_qkv_quant_i16(fused, q=fq, scale=fs), 20)
+    rows["a4_quant_fused_qkv_4096x96x128"] = {"us": round(t * 1e6, 2),
+                                              "gbs": round(nel * (4 + 2 + 4 / 128) / t / 1e9, 1)}
+    del fused, fq, fs
     (q, qs), (k, ks), (v, vs) = qkv
     out = heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None], causal=True)
     t = time_fn(lambda: heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None],

@@ -34,6 +34,17 @@ __device__ __forceinline__ float halfwave_max(float v) {
 
 // ilogb of a positive finite float (subnormals included): v_frexp_exp gives e with x = m * 2^e,
 // m in [0.5, 1).
+// Nontemporal (streaming) stores for outputs that this kernel never reads back.  On the INT16 quantiser they
+// took one launch over 4096 tokens x 96 heads x 128 from 69 to 60 us, the plain device-copy rate; the same
+// hint on the loads gained nothing and, combined with it, lost the gain.
+__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 t;
+  t.x = v.x;
+  t.y = v.y;
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+}
+
 __device__ __forceinline__ int ilogb_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
 
 // round-to-nearest-even into the 16-bit part type; returns the bit pattern and the value back in fp32
@@ -269,7 +280,7 @@ __global__ __launch_bounds__(256) void quant_i16_kernel(const float* __restrict_
         }
         packed[j] = (uint32_t)(uint16_t)o[0] | ((uint32_t)(uint16_t)o[1] << 16);
       }
-      *reinterpret_cast<uint2*>(qr + d) = make_uint2(packed[0], packed[1]);
+      store_nt(reinterpret_cast<uint2*>(qr + d), make_uint2(packed[0], packed[1]));
     }
   }
 }

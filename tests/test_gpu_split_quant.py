@@ -67,7 +67,8 @@ def test_split_i16_exhaustive(heal):
 
 
 @pytest.mark.parametrize("T,H,D", [(256, 1, 128), (300, 8, 128), (4096, 32, 128), (33, 3, 64), (7, 2, 256),
-                                   (5, 1, 1024), (9, 4, 4)])
+                                   (5, 1, 1024), (9, 4, 4),
+                                   (4096, 96, 128)])  # Q, K and V heads of a token side by side, one launch
 def test_quant_bit_exact(heal, T, H, D):
     banner(f"quant {T}x{H}x{D}")
     x, _, _ = workloads.qkv_fp32(1, T, H, D, seed=T + H + D)
