@@ -381,23 +381,27 @@ def main():
     torch.cuda.synchronize()
     # decode-sized M takes the entry point that splits A in the GEMM's prologue (the same bits as split +
     # GEMM, without the parts' round trip through HBM); prefill-sized M splits in its own pass
+    # (one-row activations also leave the row exponent to the GEMM: a launch fewer, the same bits)
     fused = lambda M: M <= 64
+    derived = lambda M: M == 1
     variants = {(M, K, N): heal.heal_gemm_comp_variant(M, N, K, 2) + (" FP32-A" if fused(M) else "")
-                for (M, K, N) in shapes}
+                + (", exponent in the kernel" if derived(M) else "") for (M, K, N) in shapes}
 
     timer = Timer()
 
     def step(record):
         for (M, K, N, x, ah, al, ea, c) in bufs:
             bh, eb = weights[(K, N)]
-            if fused(M):
+            if derived(M):
+                pass
+            elif fused(M):
                 heal.heal_row_exponents(x, exps=ea)
             else:
                 heal.heal_split(x, hi=ah, lo=al, exps=ea)
             if record:
                 e0 = timer.start()
             if fused(M):
-                heal.heal_gemm_comp_f32a(x, ea, bh, None, eb, c=c)
+                heal.heal_gemm_comp_f32a(x, None if derived(M) else ea, bh, None, eb, c=c)
             else:
                 heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
             if record:
@@ -465,7 +469,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "llama3_8b_linear: split(fp32 X) + compensated GEMM, P=2, 9 shapes (M <= 64: the split "
-                        "in the GEMM's prologue)",
+                        "in the GEMM's prologue; M = 1: the row exponent there too)",
             "shapes_MKN": [list(s) for s in shapes],
             "activations": "fp32 N(0,1), 1% channels x50",
             "weights": "bf16 N(0,0.02), pre-split to fp16 once",

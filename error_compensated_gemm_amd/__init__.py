@@ -310,8 +310,8 @@ def heal_row_exponents(x, exps=None):
 
 def heal_gemm_comp_f32a(a, a_exp, b_hi, b_lo, b_exp, c=None):
     """Compensated GEMM with FP32 ``a [M, K]`` split inside the kernel (row exponents ``a_exp`` from
-    heal_row_exponents) against FP16 parts of B^T ``[N, K]``; returns C [M, N] fp32, bit for bit what
-    heal_split + heal_gemm_comp give."""
+    heal_row_exponents, or None for M <= 16: the kernel derives the same ones) against FP16 parts of B^T
+    ``[N, K]``; returns C [M, N] fp32, bit for bit what heal_split + heal_gemm_comp give."""
     import torch
 
     M, K = a.shape

@@ -145,10 +145,10 @@ heal_status heal_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a,
   if (M < 0 || N < 0 || K < 0) return HEAL_ERR_SHAPE;
   if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31) return HEAL_ERR_SHAPE;
   if (M == 0 || N == 0) return HEAL_OK;
-  if (!c || !a_exp || (K > 0 && (!a || !b_hi))) return HEAL_ERR_NULL;
+  if (!c || (!a_exp && M > 16) || (K > 0 && (!a || !b_hi))) return HEAL_ERR_NULL;
   if (lda < K || ldb < K || ldc < N) return HEAL_ERR_STRIDE;
   if ((a && !aligned16(a)) || (b_hi && !aligned16(b_hi)) || (b_lo && !aligned16(b_lo)) || !aligned16(c) ||
-      !aligned4(a_exp) || (b_exp && !aligned4(b_exp)) || (lda & 3) || (ldb & 7) || (ldc & 3))
+      (a_exp && !aligned4(a_exp)) || (b_exp && !aligned4(b_exp)) || (lda & 3) || (ldb & 7) || (ldc & 3))
     return HEAL_ERR_ALIGN;
   return launched(heal::launch_gemm_comp_f32a(M, N, K, a, lda, a_exp, (const uint16_t*)b_hi, (const uint16_t*)b_lo,
                                               b_exp, ldb, c, ldc, (hipStream_t)stream));

@@ -559,7 +559,8 @@ constexpr int kSkWaves = 8;
 // values of a K step are held as raw FP32 bits (the registers the hi and lo chunks would take) and split
 // just before the MFMAs, so the prefetch never waits on them.
 // SPLITK: as for gemm_comp_kernel, slice blockIdx.y of K into slice blockIdx.y of the unscaled partials C.
-template <int PART, int MT, int NC, bool ALO, bool BLO, bool AF32 = false, bool SPLITK = false>
+// AEXP (FP32 A, at most 16 rows): A's row exponents are derived in the kernel instead of read from ea.
+template <int PART, int MT, int NC, bool ALO, bool BLO, bool AF32 = false, bool SPLITK = false, bool AEXP = false>
 __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
     const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
@@ -582,6 +583,36 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cl = lane & 15, kg = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16 * NC;
+  // AEXP: e = 14 - ilogb(max_k |a[m, k]|) for each row (0 for a row without a nonzero value), the value
+  // heal_row_exponents writes (a maximum is exact in any order).  The 512 threads stride over each row in
+  // float4 chunks and the wavefront maxima meet in LDS.  Every workgroup reads all of A for this once more
+  // (16 KB per row at K = 4096, from L2), in place of a launch of its own before the GEMM.
+  __shared__ float amax_s[AEXP ? kSkWaves : 1][16];
+  __shared__ int aexp_s[AEXP ? 16 : 1];
+  if constexpr (AEXP) {
+    static_assert(AF32 && MT == 1 && !SPLITK, "derived row exponents: FP32 A, at most 16 rows");
+    const int64_t nch = K >> 2;
+    for (int r = 0; r < M; ++r) {
+      const float* xr = af + r * lda;
+      float m = 0.0f;
+      for (int64_t j = threadIdx.x; j < nch; j += 64 * kSkWaves) {
+        const float4 v = *reinterpret_cast<const float4*>(xr + 4 * j);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      }
+      for (int64_t k = 4 * nch + threadIdx.x; k < K; k += 64 * kSkWaves) m = fmaxf(m, fabsf(xr[k]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (lane == 0) amax_s[wave][r] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x < M) {
+      float m = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kSkWaves; ++w) m = fmaxf(m, amax_s[w][threadIdx.x]);
+      aexp_s[threadIdx.x] = m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;  // 14 - ilogb(m)
+    }
+    __syncthreads();
+  }
   const uint16_t* brow[NC];
   const uint16_t* blrow[NC];
 #pragma unroll
@@ -601,7 +632,10 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     if (m > M - 1) m = M - 1;
     if constexpr (AF32) {
       afrow[mt] = af + m * lda;
-      ea_l[mt] = ea[m];
+      if constexpr (AEXP)
+        ea_l[mt] = aexp_s[m];
+      else
+        ea_l[mt] = ea[m];
     } else {
       arow[mt] = ah + m * lda;
       alrow[mt] = ALO ? al + m * lda : nullptr;
@@ -750,7 +784,11 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     for (int w = 0; w < kSkWaves; ++w) s += red[w][blk][i][l];
     const int64_t row = 16 * mt + 4 * (l >> 4) + i, col = n0 + 16 * nc + (l & 15);
     if (row < M && col < N) {
-      const int e = (ea ? ea[row] : 0) + (eb ? eb[col] : 0);
+      int e = eb ? eb[col] : 0;
+      if constexpr (AEXP)
+        e += aexp_s[row];
+      else
+        e += ea ? ea[row] : 0;
       C[row * ldc + col] = __builtin_amdgcn_ldexpf(s, -e);
     }
   }
@@ -974,6 +1012,24 @@ hipError_t launch_skinny_f32a_nc(int64_t M, int64_t N, int64_t K, const float* a
   if (!grid_fits((N + 16 * NC - 1) / (16 * NC), 64 * kSkWaves)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((N + 16 * NC - 1) / (16 * NC))), block(64 * kSkWaves);
   const uint16_t* const none = nullptr;
+  if (!ea) {  // row exponents derived in the kernel: at most 16 rows
+    if constexpr (MT == 1) {
+      if constexpr (BLO) {
+        if (bl) {
+          hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, 1, NC, true, true, true, false, true>), grid, block, 0,
+                             stream, M, N, K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af, (int64_t)0);
+          return hipGetLastError();
+        }
+      } else if (bl) {
+        return hipErrorInvalidValue;
+      }
+      hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, 1, NC, true, false, true, false, true>), grid, block, 0,
+                         stream, M, N, K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af, (int64_t)0);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if constexpr (BLO) {
     if (bl) {
       hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, true, true>), grid, block, 0, stream, M, N,
@@ -1027,6 +1083,7 @@ hipError_t launch_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a
                                  const uint16_t* b_hi, const uint16_t* b_lo, const int32_t* b_exp, int64_t ldb,
                                  float* c, int64_t ldc, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (!a_exp && M > 16) return hipErrorInvalidValue;  // derived exponents: the skinny kernel, at most 16 rows
   const bool blo = b_lo != nullptr;
   switch (choose_tile(M, N, !blo)) {
     case kSkinny:

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define HEAL_ABI_VERSION 4
+#define HEAL_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define HEAL_API __attribute__((visibility("default")))
@@ -170,13 +170,16 @@ HEAL_API heal_status heal_gemm_comp(int64_t M, int64_t N, int64_t K, const void*
  *   Errors: HEAL_ERR_NULL (exps NULL, or x NULL with cols > 0), HEAL_ERR_SHAPE, HEAL_ERR_STRIDE
  *   (ld_x < cols), HEAL_ERR_ALIGN.
  * heal_gemm_comp_f32a: heal_gemm_comp with A given as FP32 a [M, K] (leading dimension lda, in floats) and
- *   its row exponents a_exp (required): each A value is split as heal_split splits it, xs = fl32(a * 2^e),
+ *   its row exponents a_exp: each A value is split as heal_split splits it, xs = fl32(a * 2^e),
  *   hi = fp16_rn(xs), lo = fp16_rn(xs - hi), inside the kernel.  B as in heal_gemm_comp with FP16 parts
  *   (b_lo NULL: P = 2 products, else 3).  With the exponents of heal_row_exponents every |xs| < 2^15;
  *   other exponents are accepted, with the parts heal_split would form from them.  a must be 16-byte
  *   aligned and lda a multiple of 4; a row needs to hold only its K values (the last partial step of K is
- *   read element by element).
- *   Errors: HEAL_ERR_NULL (c or a_exp NULL with M*N > 0; a or b_hi NULL with M*N*K > 0), HEAL_ERR_SHAPE,
+ *   read element by element).  For M <= 16, a_exp may be NULL: the kernel then derives the exponents of
+ *   heal_row_exponents itself (the same values, so the same C bits), saving that launch at the cost of one
+ *   more read of A per workgroup from L2 (cheap for a few rows; at 16 rows and K = 14336 it is 0.9 MB).
+ *   Errors: HEAL_ERR_NULL (c NULL with M*N > 0; a_exp NULL with M > 16 and M*N > 0; a or b_hi NULL with
+ *   M*N*K > 0), HEAL_ERR_SHAPE,
  *   HEAL_ERR_STRIDE (lda, ldb < K or ldc < N), HEAL_ERR_ALIGN.
  */
 HEAL_API heal_status heal_row_exponents(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t* exps,

@@ -105,9 +105,12 @@ class HealPath:
 
     def linear(self, x, name, rows=slice(None)):
         """x W^T for the FP16 parts of ``name`` (``rows`` selects a block of W's rows).  Up to 64 rows of x are
-        split inside the GEMM's prologue (the same bits as heal_split + heal_gemm_comp, one launch fewer)."""
+        split inside the GEMM's prologue (the same bits as heal_split + heal_gemm_comp, one launch fewer), and one
+        row also has its exponent derived there."""
         bh, eb = self.parts[name]
         bh, eb = bh[rows], eb[rows]
+        if x.shape[0] == 1:  # the GEMM derives the row exponent itself: one launch
+            return heal.heal_gemm_comp_f32a(x, None, bh, None, eb)
         if x.shape[0] <= 64:
             return heal.heal_gemm_comp_f32a(x, heal.heal_row_exponents(x), bh, None, eb)
         ah, al, ea = heal.heal_split(x)

@@ -68,7 +68,7 @@ def test_glue_grid_limits_refused_before_launch():
 
 def test_version_and_status_strings(heal):
     lib = heal.load()
-    assert lib.heal_abi_version() == 4
+    assert lib.heal_abi_version() == 5
     for s in range(9):
         assert lib.heal_status_str(s).decode().startswith("HEAL")
     assert b"unknown" in lib.heal_status_str(99)
@@ -142,7 +142,9 @@ def test_row_exponents_and_f32a_validation(heal):
     call = lambda **kw: g(*[{**ok, **kw}[k] for k in ("M", "N", "K", "a", "lda", "ae", "bh", "bl", "be", "ldb",
                                                        "c", "ldc")], None)
     assert call(K=-1) == 2
-    assert call(ae=None) == 1                             # the row exponents are required
+    assert call(ae=None) == 1                             # the row exponents are required above 16 rows
+    assert call(M=17, ae=None) == 1
+    assert call(M=16, ae=None, a=P(FAKE + 4)) == 4        # 16 rows may omit them; the other checks still apply
     assert call(a=None) == 1 and call(c=None) == 1 and call(bh=None) == 1
     assert call(lda=96) == 3 and call(ldb=96) == 3 and call(ldc=16) == 3
     assert call(a=P(FAKE + 4)) == 4                       # a not 16-byte aligned

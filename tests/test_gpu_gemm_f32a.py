@@ -103,3 +103,33 @@ def test_llama_linear_fused(heal, M, K, N):
     err = normwise(host(c)[ii, jj], ref)
     print(f"[f32a] llama M={M} K={K} N={N} sampled normwise {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("M,N,K,P", [(1, 300, 77, 2), (1, 14336, 4096, 2), (1, 4096, 14336, 2), (3, 700, 1001, 3),
+                                     (16, 4096, 4096, 2), (16, 14350, 130, 3), (5, 300, 3, 2), (4, 7300, 64, 2)])
+def test_derived_row_exponents(heal, M, N, K, P):
+    """a_exp = None (at most 16 rows): the kernel derives the row exponents itself, so C is bit for bit what the
+    exponents of heal_row_exponents give.  Rows with no nonzero value, a subnormal maximum and a value near
+    1e30 are included, and the padding past K holds 1e30, which would change an exponent if it were read."""
+    banner(f"gemm f32a derived exponents {M}x{N}x{K} P={P}")
+    A, Bt = workloads.gemm_rowscaled(M, N, K, seed=11)
+    if M >= 3:
+        A[0] = 0.0
+        A[1] = np.float32(1e-40) * np.sign(A[1] + 0.5)
+        A[2, K // 2] = np.float32(1e30)
+    t = torch.full((M, (K + 3) // 4 * 4 + 4), 1e30, dtype=torch.float32, device="cuda")
+    t[:, :K] = dev(A)
+    a = t[:, :K]
+    bh, bl, eb = heal.heal_split(dev(Bt), residual=(P == 3))
+    c_given = heal.heal_gemm_comp_f32a(a, heal.heal_row_exponents(a), bh, bl, eb)
+    c_derived = heal.heal_gemm_comp_f32a(a, None, bh, bl, eb)
+    torch.cuda.synchronize()
+    assert torch.equal(c_derived.view(torch.int32), c_given.view(torch.int32))
+    assert bool(torch.isfinite(c_derived).all())
+
+
+def test_derived_row_exponents_refused_above_16_rows(heal):
+    a = torch.zeros((17, 64), dtype=torch.float32, device="cuda")
+    bh, _, eb = heal.heal_split(torch.ones((32, 64), dtype=torch.float32, device="cuda"), residual=False)
+    with pytest.raises(RuntimeError):
+        heal.heal_gemm_comp_f32a(a, None, bh, None, eb)
