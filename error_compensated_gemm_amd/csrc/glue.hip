@@ -42,6 +42,28 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   for (int64_t c = threadIdx.x; c < d; c += 256) y[t * d + c] = xr[c] * inv;
 }
 
+// x += r, then y = rmsnorm(x) as rmsnorm_kernel forms it: each thread adds and squares the columns it later
+// scales, so the values and the order of every sum are those of add_kernel followed by rmsnorm_kernel
+__global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x, const float* __restrict__ r,
+                                                          int64_t d, float eps, float* __restrict__ y) {
+  __shared__ float part[4];
+  const int64_t t = blockIdx.x;
+  float* xr = x + t * d;
+  const float* rr = r + t * d;
+  float s = 0.0f;
+  for (int64_t c = threadIdx.x; c < d; c += 256) {
+    const float v = xr[c] + rr[c];
+    xr[c] = v;
+    s = fmaf(v, v, s);
+  }
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int64_t c = threadIdx.x; c < d; c += 256) y[t * d + c] = xr[c] * inv;
+}
+
 // rotary embedding on heads of 128 (pairs (i, i + 64)), in place; cs holds cos and sin per (position, i) as
 // [positions][64][2], computed by the caller
 __global__ void rope_kernel(float* __restrict__ x, int64_t T, int64_t H, int64_t ld_t, int64_t pos0,
@@ -118,6 +140,13 @@ int glue_rmsnorm(const float* x, int64_t T, int64_t d, float eps, float* y, void
   if (T <= 0 || d <= 0) return 0;
   if (!fits(T, 256)) return 6;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)T), dim3(256), 0, (hipStream_t)stream, x, d, eps, y);
+  return status(hipGetLastError());
+}
+
+int glue_add_rmsnorm(float* x, const float* r, int64_t T, int64_t d, float eps, float* y, void* stream) {
+  if (T <= 0 || d <= 0) return 0;
+  if (!fits(T, 256)) return 6;
+  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)T), dim3(256), 0, (hipStream_t)stream, x, r, d, eps, y);
   return status(hipGetLastError());
 }
 

@@ -28,6 +28,8 @@ extern "C" {
 GLUE_API int glue_embed(const uint16_t* emb, const int32_t* ids, int64_t T, int64_t d, float* out, void* stream);
 /* y[t, :] = x[t, :] / sqrt(mean_c x[t, c]^2 + eps)  (unit weight; x, y [T, d], may alias) */
 GLUE_API int glue_rmsnorm(const float* x, int64_t T, int64_t d, float eps, float* y, void* stream);
+/* x[T, d] += r[T, d] in place, then y = rmsnorm(x) (the bits of glue_add followed by glue_rmsnorm), one launch */
+GLUE_API int glue_add_rmsnorm(float* x, const float* r, int64_t T, int64_t d, float eps, float* y, void* stream);
 /* rotary embedding in place on H heads of 128 per token (row stride ld_t floats): for i < 64, the pair
  * (v[i], v[i + 64]) of the token at position pos0 + t is rotated by the angle whose cosine and sine are
  * cs[((pos0 + t) * 64 + i) * 2 + {0, 1}] */

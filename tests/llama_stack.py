@@ -44,6 +44,7 @@ def glue():
     L = ctypes.CDLL(os.path.join(ROOT, "error_compensated_gemm_amd", "libheal_glue.so"))
     p, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
     for name, args in (("glue_embed", [p, p, i64, i64, p, p]), ("glue_rmsnorm", [p, i64, i64, f32, p, p]),
+                       ("glue_add_rmsnorm", [p, p, i64, i64, f32, p, p]),
                        ("glue_rope", [p, i64, i64, i64, i64, p, p]), ("glue_swiglu", [p, p, i64, p, p]),
                        ("glue_add", [p, p, i64, p]), ("glue_argmax", [p, i64, p, p])):
         getattr(L, name).argtypes = args
@@ -116,6 +117,12 @@ class HealPath:
         ah, al, ea = heal.heal_split(x)
         return heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
 
+    def add_norm(self, x, r):
+        """x += r, then rmsnorm(x), in one launch"""
+        y = torch.empty_like(x)
+        assert self.G.glue_add_rmsnorm(_p(x), _p(r), x.shape[0], x.shape[1], EPS, _p(y), _s()) == 0
+        return y
+
     def norm(self, x):
         y = torch.empty_like(x)
         assert self.G.glue_rmsnorm(_p(x), x.shape[0], x.shape[1], EPS, _p(y), _s()) == 0
@@ -131,8 +138,9 @@ class HealPath:
         x = torch.empty((T, d), dtype=torch.float32, device="cuda")
         assert G.glue_embed(_p(self.emb), _p(idt), T, d, _p(x), _s()) == 0
         H, F = hq + 2 * hkv, cfg["f"]
+        h = self.norm(x)
         for l in range(cfg["layers"]):
-            qkv = self.linear(self.norm(x), f"{l}.wqkv")  # [T, (hq + 2 hkv) 128]
+            qkv = self.linear(h, f"{l}.wqkv")  # [T, (hq + 2 hkv) 128]
             assert G.glue_rope(_p(qkv), T, hq + hkv, qkv.stride(0), pos0, _p(self.cs), _s()) == 0  # Q and K heads
             c, cs = self.qkv[l], self.qkvs[l]
             heal.heal_qkv_quant_i16(qkv.view(T, H, 128), q=c[pos0:pos0 + T], scale=cs[pos0:pos0 + T])
@@ -141,8 +149,7 @@ class HealPath:
             a = heal.heal_attn_dual_fp16(c[None, pos0:n, :hq], cs[None, pos0:n, :hq], c[None, :n, kh],
                                          cs[None, :n, kh], c[None, :n, vh], cs[None, :n, vh], causal=True)
             o = self.linear(a.view(T, hq * 128), f"{l}.wo")
-            assert G.glue_add(_p(x), _p(o), x.numel(), _s()) == 0
-            h = self.norm(x)
+            h = self.add_norm(x, o)  # the residual add and the FFN's norm
             if T == 1:  # gate and up in one GEMM: the two halves of its one output row are each contiguous
                 gu = self.linear(h, f"{l}.wgu")
                 gte, up = gu[:, :F], gu[:, F:]
@@ -151,7 +158,10 @@ class HealPath:
             act = torch.empty((T, F), dtype=torch.float32, device="cuda")
             assert G.glue_swiglu(_p(gte), _p(up), T * F, _p(act), _s()) == 0
             dn = self.linear(act, f"{l}.wd")
-            assert G.glue_add(_p(x), _p(dn), x.numel(), _s()) == 0
+            if l + 1 < cfg["layers"]:
+                h = self.add_norm(x, dn)  # the residual add and the next layer's attention norm
+            else:
+                assert G.glue_add(_p(x), _p(dn), x.numel(), _s()) == 0
         hn = self.norm(x[-1:].contiguous())
         logits = self.linear(hn, "head")
         am = torch.empty((1,), dtype=torch.int32, device="cuda")

@@ -40,7 +40,7 @@ def test_glue_library_exports_every_declared_symbol():
     """the decoder-block glue of the model-level check (include/heal_glue.h, libheal_glue.so)"""
     txt = open(os.path.join(ROOT, "include", "heal_glue.h")).read()
     names = sorted(set(re.findall(r"GLUE_API\s+int\s+(glue_\w+)\s*\(", txt)))
-    assert len(names) == 6
+    assert len(names) == 7
     lib_path = os.path.join(ROOT, "error_compensated_gemm_amd", "libheal_glue.so")
     lib = ctypes.CDLL(lib_path)
     for n in names:
@@ -52,12 +52,14 @@ def test_glue_library_exports_every_declared_symbol():
 def test_glue_grid_limits_refused_before_launch():
     """glue calls whose grid would pass 2^32 work-items per dimension return 6 before any runtime call"""
     lib = ctypes.CDLL(os.path.join(ROOT, "error_compensated_gemm_amd", "libheal_glue.so"))
-    for f in (lib.glue_embed, lib.glue_rmsnorm, lib.glue_rope, lib.glue_swiglu, lib.glue_add, lib.glue_argmax):
+    for f in (lib.glue_embed, lib.glue_rmsnorm, lib.glue_rope, lib.glue_swiglu, lib.glue_add, lib.glue_argmax,
+              lib.glue_add_rmsnorm):
         f.restype = ctypes.c_int
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     fake = vp(FAKE)
     assert lib.glue_embed(fake, fake, i64(1 << 24), i64(128), fake, None) == 6
     assert lib.glue_rmsnorm(fake, i64(1 << 24), i64(128), ctypes.c_float(1e-5), fake, None) == 6
+    assert lib.glue_add_rmsnorm(fake, fake, i64(1 << 24), i64(128), ctypes.c_float(1e-5), fake, None) == 6
     assert lib.glue_rope(fake, i64(1 << 26), i64(1), i64(128), i64(0), fake, None) == 6
     assert lib.glue_rope(fake, i64(1), i64(1 << 32), i64(128), i64(0), fake, None) == 6
     assert lib.glue_swiglu(fake, fake, i64(1 << 32), fake, None) == 6
