@@ -272,15 +272,29 @@ void orc_gemm_f64_points(int64_t K, const double* A, int64_t lda, const double* 
 void orc_gemm_emul(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
                    const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
                    const int32_t* eb, int64_t ldb, int part, double* C, double* G, int64_t ldc) {
+  /* the values of the parts, decoded once (an absent lo part is 0) */
+  double* xa = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? 2 * M * K : 1));
+  double* ya = (double*)malloc(sizeof(double) * (size_t)(N * K > 0 ? 2 * N * K : 1));
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t k = 0; k < K; ++k) {
+      xa[2 * (i * K + k)] = part_value(ah[i * lda + k], part);
+      xa[2 * (i * K + k) + 1] = al ? part_value(al[i * lda + k], part) : 0.0;
+    }
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < N; ++j)
+    for (int64_t k = 0; k < K; ++k) {
+      ya[2 * (j * K + k)] = part_value(bh[j * ldb + k], part);
+      ya[2 * (j * K + k) + 1] = bl ? part_value(bl[j * ldb + k], part) : 0.0;
+    }
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < M; ++i)
     for (int64_t j = 0; j < N; ++j) {
+      const double* x = xa + 2 * i * K;
+      const double* y = ya + 2 * j * K;
       double acc = 0.0, mag = 0.0;
       for (int64_t k = 0; k < K; ++k) {
-        const double xh = part_value(ah[i * lda + k], part);
-        const double xl = al ? part_value(al[i * lda + k], part) : 0.0;
-        const double yh = part_value(bh[j * ldb + k], part);
-        const double yl = bl ? part_value(bl[j * ldb + k], part) : 0.0;
+        const double xh = x[2 * k], xl = x[2 * k + 1], yh = y[2 * k], yl = y[2 * k + 1];
         acc += xh * yh + xh * yl + xl * yh;
         mag += fabs(xh * yh) + fabs(xh * yl) + fabs(xl * yh);
       }
@@ -288,6 +302,8 @@ void orc_gemm_emul(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const ui
       C[i * ldc + j] = ldexp(acc, -e);
       if (G) G[i * ldc + j] = ldexp(mag, -e);
     }
+  free(xa);
+  free(ya);
 }
 
 /* ------------------------------------------------------------------------------------------------------
