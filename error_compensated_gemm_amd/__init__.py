@@ -103,6 +103,8 @@ def load():
     L.heal_attn_workspace_bytes.argtypes = [ctypes.POINTER(HealAttnArgs)]
     L.heal_attn_dual_fp16.restype = i32
     L.heal_attn_dual_fp16.argtypes = [ctypes.POINTER(HealAttnArgs), p]
+    L.heal_attn_dual_fp16_noalloc.restype = i32
+    L.heal_attn_dual_fp16_noalloc.argtypes = [ctypes.POINTER(HealAttnArgs), p]
     L.heal_attn_paged_workspace_bytes.restype = ctypes.c_size_t
     L.heal_attn_paged_workspace_bytes.argtypes = [ctypes.POINTER(HealPagedDecodeArgs)]
     L.heal_attn_decode_paged.restype = i32
@@ -116,7 +118,8 @@ EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp
             "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged", "heal_gemm_comp_quant_i16",
             "heal_channel_exponents", "heal_split_scaled", "heal_unpack_i16", "heal_row_exponents",
             "heal_gemm_comp_f32a", "heal_gemm_comp_splitk", "heal_gemm_comp_workspace_bytes",
-            "heal_gemm_comp_splitk_slices")
+            "heal_gemm_comp_splitk_slices", "heal_attn_dual_fp16_noalloc")
+HEAL_ATTN_NOALLOC_MAX_WORKSPACE = 8 << 20
 
 
 def _check(status: int):
@@ -425,6 +428,15 @@ def heal_attn_dual_fp16(q, q_scale, k, k_scale, v, v_scale, causal: bool = True,
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = workspace.numel()
     _check(L.heal_attn_dual_fp16(ctypes.byref(args), _stream(q.device)))
+    return out
+
+
+def heal_attn_dual_fp16_noalloc(q, q_scale, k, k_scale, v, v_scale, out, causal: bool = True,
+                                softmax_scale: float | None = None, dual_split: str = "byte"):
+    """heal_attn_dual_fp16 into the caller's ``out`` without any workspace: the library keeps the decode
+    partials in its own device scratch (calls that overlap on one GPU race on it)."""
+    args = make_attn_args(q, q_scale, k, k_scale, v, v_scale, out, causal, softmax_scale, None, dual_split)
+    _check(load().heal_attn_dual_fp16_noalloc(ctypes.byref(args), _stream(q.device)))
     return out
 
 

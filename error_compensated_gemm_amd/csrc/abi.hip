@@ -233,7 +233,14 @@ size_t heal_attn_workspace_bytes(const heal_attn_args* a) {
   return heal::attn_workspace_bytes(*a);
 }
 
-heal_status heal_attn_dual_fp16(const heal_attn_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The argument checks of heal_attn_dual_fp16 other than the workspace.  HEAL_OK with *empty set means a
+// valid problem with nothing to compute.
+heal_status check_attn(const heal_attn_args* a, bool* empty) {
+  *empty = false;
   if (!a) return HEAL_ERR_NULL;
   if (!valid_dual_split(a->dual_split)) return HEAL_ERR_DTYPE;
   if (a->batch < 0 || a->q_len < 0 || a->kv_len < 0 || a->n_q_heads < 0 || a->n_kv_heads < 0 ||
@@ -241,7 +248,10 @@ heal_status heal_attn_dual_fp16(const heal_attn_args* a, void* stream) {
     return HEAL_ERR_SHAPE;
   if (a->head_dim != 128) return HEAL_ERR_UNSUPPORTED;
   if (a->n_kv_heads == 0 || a->n_q_heads % a->n_kv_heads != 0) return HEAL_ERR_SHAPE;
-  if (a->batch == 0 || a->q_len == 0 || a->n_q_heads == 0) return HEAL_OK;
+  if (a->batch == 0 || a->q_len == 0 || a->n_q_heads == 0) {
+    *empty = true;
+    return HEAL_OK;
+  }
   if (!a->q || !a->q_scale || !a->out) return HEAL_ERR_NULL;
   if (a->kv_len > 0 && (!a->k || !a->v || !a->k_scale || !a->v_scale)) return HEAL_ERR_NULL;
   if (!(a->softmax_scale >= 0.0f) || isinf(a->softmax_scale)) return HEAL_ERR_SHAPE;
@@ -258,10 +268,29 @@ heal_status heal_attn_dual_fp16(const heal_attn_args* a, void* stream) {
   if (!aligned16(a->q) || !aligned16(a->out) || (a->k && !aligned16(a->k)) || (a->v && !aligned16(a->v)) ||
       !aligned4(a->q_scale) || (a->k_scale && !aligned4(a->k_scale)) || (a->v_scale && !aligned4(a->v_scale)))
     return HEAL_ERR_ALIGN;
+  return HEAL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+heal_status heal_attn_dual_fp16(const heal_attn_args* a, void* stream) {
+  bool empty = false;
+  const heal_status st = check_attn(a, &empty);
+  if (st != HEAL_OK || empty) return st;
   const size_t need = heal::attn_workspace_bytes(*a);
   if (need > 0 && (!a->workspace || a->workspace_bytes < need || (reinterpret_cast<uintptr_t>(a->workspace) & 255u)))
     return HEAL_ERR_WORKSPACE;
   return launched(heal::launch_attn(*a, (hipStream_t)stream));
+}
+
+heal_status heal_attn_dual_fp16_noalloc(const heal_attn_args* a, void* stream) {
+  bool empty = false;
+  const heal_status st = check_attn(a, &empty);
+  if (st != HEAL_OK || empty) return st;
+  if (heal::attn_workspace_bytes(*a) > HEAL_ATTN_NOALLOC_MAX_WORKSPACE) return HEAL_ERR_WORKSPACE;
+  return launched(heal::launch_attn_noalloc(*a, (hipStream_t)stream));
 }
 
 size_t heal_attn_paged_workspace_bytes(const heal_paged_decode_args* a) {

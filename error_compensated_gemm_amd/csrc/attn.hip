@@ -46,6 +46,8 @@
 // each (batch, head) in a fixed order.  No atomics: results are bitwise reproducible.
 #include <math.h>
 
+#include <mutex>
+
 #include "heal_internal.h"
 
 namespace heal {
@@ -963,6 +965,61 @@ hipError_t launch_attn(const heal_attn_args& x, hipStream_t stream) {
   else
     hipLaunchKernelGGL(attn_prefill_kernel<HEAL_DUAL_BYTE>, grid, dim3(PF_THREADS), 0, stream, p);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------ decode without a caller workspace
+// The partials of heal_attn_dual_fp16_noalloc live in this array: one copy per GPU, allocated by the runtime
+// with the code object and kept until the process ends.  In host code `scratch` names a host-side stand-in,
+// never the device memory: its device address is looked up once per device (with that device current) and
+// only that address is ever passed to a kernel.
+static __device__ __align__(256) float scratch[HEAL_ATTN_NOALLOC_MAX_WORKSPACE / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// the device address of `scratch` on the device that runs `stream`
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_noalloc(const heal_attn_args& x, hipStream_t stream) {
+  heal_attn_args y = x;
+  y.workspace = nullptr;
+  y.workspace_bytes = 0;
+  if (attn_workspace_bytes(x) > 0) {
+    void* p = nullptr;
+    const hipError_t e = scratch_address(stream, &p);
+    if (e != hipSuccess) return e;
+    y.workspace = p;
+    y.workspace_bytes = HEAL_ATTN_NOALLOC_MAX_WORKSPACE;
+  }
+  return launch_attn(y, stream);
 }
 
 size_t paged_workspace_bytes(const heal_paged_decode_args& x) {

@@ -55,6 +55,9 @@ hipError_t launch_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const uint16
                                    hipStream_t stream);
 size_t attn_workspace_bytes(const heal_attn_args& a);
 hipError_t launch_attn(const heal_attn_args& a, hipStream_t stream);
+// launch_attn with the decode partials in the library's own device scratch (HEAL_ATTN_NOALLOC_MAX_WORKSPACE
+// bytes per device); the caller has checked that attn_workspace_bytes(a) fits
+hipError_t launch_attn_noalloc(const heal_attn_args& a, hipStream_t stream);
 size_t paged_workspace_bytes(const heal_paged_decode_args& a);
 hipError_t launch_attn_paged(const heal_paged_decode_args& a, hipStream_t stream);
 

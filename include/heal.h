@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define HEAL_ABI_VERSION 5
+#define HEAL_ABI_VERSION 6
 
 #if defined(__GNUC__) || defined(__clang__)
 #define HEAL_API __attribute__((visibility("default")))
@@ -316,6 +316,23 @@ HEAL_API size_t heal_attn_workspace_bytes(const heal_attn_args* args);
  * (head_dim != 128), HEAL_ERR_WORKSPACE, HEAL_ERR_DTYPE (dual_split outside heal_dual_split).
  */
 HEAL_API heal_status heal_attn_dual_fp16(const heal_attn_args* args, void* stream);
+
+/*
+ * heal_attn_dual_fp16_noalloc -- heal_attn_dual_fp16 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same operation, the
+ * same kernels and the same output bits, with the decode partials kept in a scratch array the library
+ * holds in device memory (one per GPU it runs on, HEAL_ATTN_NOALLOC_MAX_WORKSPACE bytes, kept until the
+ * process ends) instead of a caller workspace.  args->workspace and args->workspace_bytes are ignored.
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library routine.  Its first call on a
+ * device looks up that device's scratch address once.  Every call on one GPU shares that GPU's scratch, so
+ * calls that may overlap on one GPU (several streams, several host threads) race and must be ordered by
+ * the caller.  The scratch needs no clearing: the decode kernels write every partial they later read.
+ * Errors: as heal_attn_dual_fp16; HEAL_ERR_WORKSPACE when heal_attn_workspace_bytes(args) exceeds
+ * HEAL_ATTN_NOALLOC_MAX_WORKSPACE (checked on the host before any device call); HEAL_ERR_LAUNCH when the
+ * runtime cannot give the scratch address.
+ */
+#define HEAL_ATTN_NOALLOC_MAX_WORKSPACE ((size_t)8 << 20)
+HEAL_API heal_status heal_attn_dual_fp16_noalloc(const heal_attn_args* args, void* stream);
 
 /*
  * Paged, variable-length INT16 KV cache for decode (one query token per sequence): the attention of

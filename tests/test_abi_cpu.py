@@ -70,7 +70,7 @@ def test_glue_grid_limits_refused_before_launch():
 
 def test_version_and_status_strings(heal):
     lib = heal.load()
-    assert lib.heal_abi_version() == 5
+    assert lib.heal_abi_version() == 6
     for s in range(9):
         assert lib.heal_status_str(s).decode().startswith("HEAL")
     assert b"unknown" in lib.heal_status_str(99)
@@ -228,6 +228,24 @@ def test_attn_validation(heal):
     a = _attn_args(heal, q_len=1, kv_len=5000, workspace=FAKE, workspace_bytes=16)
     assert lib.heal_attn_dual_fp16(ctypes.byref(a), None) == 8
     assert call(batch=0) == 0
+
+
+def test_attn_noalloc_validation(heal):
+    """heal_attn_dual_fp16_noalloc applies heal_attn_dual_fp16's checks and refuses, on the host before any
+    device call, a decode whose partials would not fit the library's fixed scratch."""
+    lib = heal.load()
+    call = lambda **kw: lib.heal_attn_dual_fp16_noalloc(ctypes.byref(_attn_args(heal, **kw)), None)
+    assert lib.heal_attn_dual_fp16_noalloc(None, None) == 1
+    assert call(head_dim=64) == 6
+    assert call(n_q_heads=3, n_kv_heads=2) == 2
+    assert call(out=MIS) == 4
+    assert call(dual_split=3) == 5
+    assert call(batch=0) == 0
+    # 64 x 20000 keys, 32 / 8 heads: 64 * 32 * 10 partials of 528 bytes, over the 8 MiB scratch
+    big = dict(batch=64, q_len=1, kv_len=20000, n_q_heads=32, n_kv_heads=8)
+    a = _attn_args(heal, **big)
+    assert lib.heal_attn_workspace_bytes(ctypes.byref(a)) > heal.HEAL_ATTN_NOALLOC_MAX_WORKSPACE
+    assert lib.heal_attn_dual_fp16_noalloc(ctypes.byref(a), None) == 8
 
 
 def test_grid_limits_refused_before_launch(heal):
