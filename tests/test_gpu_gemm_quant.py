@@ -25,7 +25,8 @@ def _parts(heal, M, N, K, P, seed=0):
 
 @pytest.mark.parametrize("M,N,K,P", [
     (2048, 8192, 256, 3),   # 256 x 256 tiles: a head is one wavefront's 128 columns
-    (2048, 4096, 512, 2),   # 256 x 128 tiles: a head spans two wavefronts (row maxima meet in LDS)
+    (2048, 4096, 512, 2),   # 128 x 256 tiles: a head is one wavefront's 128 columns
+    (2048, 4096, 512, 3),   # 256 x 128 tiles: a head spans two wavefronts (row maxima meet in LDS)
     (300, 384, 200, 3),     # 128 x 128 tiles, ragged M
     (129, 256, 1000, 2),
 ])

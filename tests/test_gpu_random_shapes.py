@@ -1,5 +1,6 @@
 """Parity over seeded random shapes, beyond the hand-picked ones: compensated GEMMs with P = 1, 2, 3 and
-ragged M, N, K (every kernel kind: skinny and all four tiles), and attention with random batch, lengths, GQA
+ragged M, N, K (the skinny kernel and the 128 x 128 tile kernel: these shapes stay below the tile counts at
+which the 256-wide tiles are chosen, which test_gpu_gemm_tiles.py checks element by element), and attention with random batch, lengths, GQA
 ratios, causal or not.  Bars as elsewhere: GEMM every element within the FP32-accumulation bound of the exact
 sum of its products and normwise <= 2e-6 to the FP64 definition when the residuals are kept; attention
 normwise <= 2e-6 to the FP64 attention on the dequantised inputs."""
