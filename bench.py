@@ -1,24 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the HEAL hot path on one MI355X.
 
-Headline (one JSON line on stdout): FP32-equivalent TFLOP/s of the error-compensated GEMM on the
-Llama-3-8B projection shapes -- M in {1, 16, 2048} tokens x (K, N) in {(4096, 4096), (4096, 14336),
-(14336, 4096)} -- with FP32 activations N(0, 1) carrying 1 % outlier channels x50 and bf16 weights N(0, 0.02)
-(exact in FP16 after the per-row power-of-two prescale, so P = 2 products).  One step = for each of the
-9 shapes: heal_split of the activations (FP32 -> FP16 hi + lo + row exponents) and heal_gemm_comp.  The
-weights are split once at load time, outside the timed region.  Inputs are synthetic, seeded, resident in
-HBM before timing starts.
+Headline (one JSON line on stdout): FP32-equivalent TFLOP/s of the error-compensated GEMM C = A B at
+8192 x 8192 x 8192 with both operands FP32 (N(0, 1), every row of A and every k-row of B scaled by
+10^U(-3, 3)).  One step is the whole operation: heal_split of A and of B^T (FP32 -> FP16 hi + lo + row
+exponents) and heal_gemm_comp with the three 16-bit products (hi hi + hi lo + lo hi) in one FP32
+accumulator.  Inputs are synthetic and seeded, resident in HBM before timing starts, and rotate through
+--rotate copies of (A, B^T) (3 copies: 1.6 GB, beyond the 256 MB memory-side cache).
 
-Also reported in the same line:
-  * "roofline" -- the dominant kernel of the step (the GEMM instantiation with the most time), its
-    16-bit MFMA work per launch (P x 2MNK) over its average launch duration, measured with HIP events on
-    the launch stream inside the timed region, against the 2516.6 TFLOP/s dense FP16 peak;
-  * "cpu_baseline" -- the FP64 CPU oracle on a bounded row sample of the same 9 shapes (all host threads),
-    and the GPU's error against it on those rows;
-  * "rows" -- the other hot-path steps, timed after the headline loop: the activation split, the INT16
-    quantiser, Dual-FP16 prefill (1 x 4096 x 32 heads x 128, causal), decode (64 x 8192 keys, GQA 32/8),
-    the same decode over a paged cache (64-key pages, shuffled pool), the QKV projection with the INT16
-    quantisation fused into the GEMM (against GEMM + quantiser) and the 8192^3 FP32 x FP32 GEMM (P = 3).
+Also in the same line:
+  * "roofline" -- the GEMM kernel of the step (its dominant kernel): 16-bit MFMA work per launch
+    (3 x 2MNK) over its average launch duration (HIP events on the launch stream inside the timed region),
+    against the 2516.6 TFLOP/s dense FP16 peak; "traffic" from committed rocprofv3 counters;
+  * "cpu_baseline" -- the plain-C FP64 oracle on a row sample of the same GEMM (all host threads), and the
+    GPU's error against it on those rows, with the plain-bf16 and bf16 x 3 contrast GEMMs on the same rows;
+  * "rows" -- the other hot-path steps and configurations, each timed on its own workload: the 256^3
+    correctness configuration, the Llama-3-8B linear layers (weights rotated through three copies), the
+    activation split, the INT16 quantiser, Dual-FP16 prefill (1 x 4096 x 32 heads x 128, causal) and decode
+    (64 x 8192 keys, GQA 32/8) with their own roofline and oracle legs, the paged decode, the fused variants,
+    the vendor GEMM at equal matrix work and the split-K GEMM at medium M.
 """
 from __future__ import annotations
 
@@ -33,6 +33,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6  # MI355X dense FP16/BF16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "error_compensated_gemm_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_TAG = "traffic-json: "
 
 
 def parse():
@@ -40,33 +43,34 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-rows", action="store_true", help="skip the per-step measurements of the other rows")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
-                    help="rows of each M=2048 shape in the CPU sample (2048: every output, about 10 s of FP64 work)")
+    ap.add_argument("--rotate", type=int, default=3, help="copies of the inputs the timed steps rotate through")
+    ap.add_argument("--no-rows", action="store_true", help="skip the measurements of the other rows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
+    ap.add_argument("--cpu-rows", type=int, default=3072,
+                    help="rows of the 8192^3 output the FP64 oracle recomputes (3072: about 10 s on 16 threads)")
+    ap.add_argument("--only", choices=("gemm8192", "llama", "split", "quant", "prefill", "decode"),
+                    help="only run a few launches of that workload (the program a counter run profiles)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (scale run for the HBM byte counters)")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="only print the HBM traffic summary of the rocprofv3 --pmc runs under DIR "
                          "(fetch/, write/, copy_fetch/, copy_write/)")
+    ap.add_argument("--title", default="", help="title of the --summarize-pmc summary")
+    ap.add_argument("--program", default="", help="the bench.py arguments the --summarize-pmc runs profiled")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (MiB)")
-    ap.add_argument("--only", choices=("prefill", "decode"),
-                    help="only run 5 launches of that attention kernel on its workload (for counter runs)")
-    ap.add_argument("--summarize-attn", metavar="DIR",
-                    help="only print the counter summary of the attention runs under DIR (decode_fetch/, "
-                         "decode_write/, copy_fetch/, copy_write/, prefill_sq/)")
     return ap.parse_args()
 
 
 # ------------------------------------------------------------------ HBM traffic from stored counters
-GEMM_SRC = os.path.join(ROOT, "error_compensated_gemm_amd", "csrc", "gemm_comp.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_comp_llama3_8b_hbm_traffic.md")
-TRAFFIC_TAG = "traffic-json: "
+KERNEL_SOURCES = (("gemm_comp_kernel", "gemm_comp.hip"), ("gemm_skinny_kernel", "gemm_comp.hip"),
+                  ("splitk_reduce_kernel", "gemm_comp.hip"), ("split_rows_kernel", "split_quant.hip"),
+                  ("quant_i16_kernel", "split_quant.hip"), ("unpack_i16_kernel", "split_quant.hip"),
+                  ("attn_", "attn.hip"))
 
 
 def source_sha256(path):
-    """SHA-256 of a C++ source with its comments and whitespace removed, so that the stored counters stay valid
-    across comment edits and go stale with any change to the code itself."""
+    """SHA-256 of a C++ source with its comments and whitespace removed, so that stored counters stay valid across
+    comment edits and go stale with any change to the code itself."""
     import hashlib
     import re
     with open(path) as f:
@@ -76,7 +80,21 @@ def source_sha256(path):
     return hashlib.sha256("".join(src.split()).encode()).hexdigest()
 
 
-def kernel_symbol(variant):
+def kernel_source(sym):
+    for prefix, src in KERNEL_SOURCES:
+        if sym.startswith(prefix):
+            return src
+    return None
+
+
+def short_symbol(name):
+    """'void heal::(anonymous namespace)::gemm_comp_kernel<2, 256, ...>(long, ...)' -> 'gemm_comp_kernel<2, 256, ...>'"""
+    n = name.replace("void ", "")
+    head = n.split("(")[0] if "<" not in n.split("(")[0] else n[:n.index(">") + 1]
+    return head.split("::")[-1].strip()
+
+
+def gemm_symbol(variant):
     """Template symbol of a GEMM variant name, as rocprofv3 prints it ("gemm_comp_kernel 256x128 P2" ->
     "gemm_comp_kernel<2, 256, 128, true, false, false, false, false>": FP16 parts, block tile, a_lo used, b_lo
     used, no fused quantisation, A given as parts, K not split)."""
@@ -88,18 +106,25 @@ def kernel_symbol(variant):
     return f"gemm_comp_kernel<2, {bm}, {bn}, {str(p >= 2).lower()}, {str(p >= 3).lower()}, false, false, false>"
 
 
-def stored_traffic(variant):
-    """HBM bytes per launch of `variant` from the committed counter summary, or None when there is none or
-    the GEMM source changed since the counters were taken."""
-    sym = kernel_symbol(variant)
-    if sym is None or not os.path.exists(TRAFFIC_FILE):
+def stored_traffic(sym):
+    """HBM bytes per launch of kernel `sym` from the committed counter summaries under profiles/, or None when
+    there is none or the kernel's source changed since the counters were taken."""
+    import glob
+    if sym is None:
         return None
-    with open(TRAFFIC_FILE) as f:
-        rec = next((json.loads(l[len(TRAFFIC_TAG):]) for l in f if l.startswith(TRAFFIC_TAG)), None)
-    if rec is None or rec.get("source_sha256") != source_sha256(GEMM_SRC):
+    src = kernel_source(sym)
+    if src is None:
         return None
-    k = rec.get("kernels", {}).get(sym)
-    return None if k is None else k["traffic_bytes_per_launch"]
+    sha = source_sha256(os.path.join(CSRC, src))
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        for line in open(f):
+            if not line.startswith(TRAFFIC_TAG):
+                continue
+            rec = json.loads(line[len(TRAFFIC_TAG):])
+            k = rec.get("kernels", {}).get(sym)
+            if k is not None and k.get("source_sha256") == sha:
+                return {"bytes_per_launch": k["traffic_bytes_per_launch"], "profile": os.path.basename(f)}
+    return None
 
 
 def copy_calibration(mib):
@@ -113,16 +138,16 @@ def copy_calibration(mib):
     print(f"copy calibration: 5 copies of {mib} MiB done", flush=True)
 
 
-def summarize_pmc(d, copy_mib):
-    """Markdown summary of FETCH_SIZE / WRITE_SIZE (KiB per dispatch) for every GEMM kernel of a bench run,
-    each scaled by the ratio of known bytes to the counter's reading for a plain copy of copy_mib MiB."""
+def summarize_pmc(d, copy_mib, title, program):
+    """Markdown summary of FETCH_SIZE / WRITE_SIZE (KiB per dispatch) for every HEAL kernel of a profiled run,
+    each scaled by the ratio of known bytes to the counter's reading for a plain device copy of copy_mib MiB."""
     import csv
     import glob
     from collections import defaultdict
 
     def read(sub):
         vals = defaultdict(list)
-        for f in glob.glob(os.path.join(d, sub, "*counter_collection.csv")):
+        for f in glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         return vals
@@ -133,161 +158,46 @@ def summarize_pmc(d, copy_mib):
     cfk = sum(cf[copy_name(cf)]) / len(cf[copy_name(cf)])
     cwk = sum(cw[copy_name(cw)]) / len(cw[copy_name(cw)])
     ff, fw = nbytes / (cfk * 1024), nbytes / (cwk * 1024)
-    kernels = {}
-    rows = []
+    kernels, rows = {}, []
     for name in sorted(fetch):
-        if "gemm_comp_kernel<" not in name and "gemm_skinny_kernel<" not in name:
+        sym = short_symbol(name)
+        src = kernel_source(sym)
+        if src is None:
             continue
-        sym = name[name.index("gemm_"):].split(">")[0] + ">"
         fk = sum(fetch[name]) / len(fetch[name])
         wk = sum(write[name]) / len(write[name]) if name in write else float("nan")
         tb = fk * 1024 * ff + wk * 1024 * fw
         kernels[sym] = {"dispatches": len(fetch[name]), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
-                        "traffic_bytes_per_launch": round(tb)}
+                        "traffic_bytes_per_launch": round(tb), "source": src,
+                        "source_sha256": source_sha256(os.path.join(CSRC, src))}
         rows.append(f"| `{sym}` | {len(fetch[name])} | {fk:.1f} | {wk:.1f} | {tb / 1e6:.2f} |")
-    rec = {"source_sha256": source_sha256(GEMM_SRC), "fetch_factor": round(ff, 4), "write_factor": round(fw, 4),
-           "copy_mib": copy_mib, "kernels": kernels}
-    print("# HBM traffic of the compensated-GEMM kernels: bench.py (Llama-3-8B linear shapes)\n")
+    rec = {"fetch_factor": round(ff, 4), "write_factor": round(fw, 4), "copy_mib": copy_mib, "kernels": kernels}
+    print(f"# HBM traffic per launch: {title}\n")
     print("Commands (from the repository root on one MI355X, ROCm 7.2; D = an output directory):\n")
     print("```")
     print("cd /tmp && export TMPDIR=/tmp")
-    for c, sub, prog in (("FETCH_SIZE", "fetch", "--steps 2 --warmup 1 --no-cpu --no-rows"),
-                         ("WRITE_SIZE", "write", "--steps 2 --warmup 1 --no-cpu --no-rows"),
+    for c, sub, prog in (("FETCH_SIZE", "fetch", program), ("WRITE_SIZE", "write", program),
                          ("FETCH_SIZE", "copy_fetch", f"--copy-calibration {copy_mib}"),
                          ("WRITE_SIZE", "copy_write", f"--copy-calibration {copy_mib}")):
         print(f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $D/{sub} -o pmc -- "
               f"python3 /root/repo/bench.py {prog}")
-    print(f"python3 /root/repo/bench.py --summarize-pmc $D --copy-mib {copy_mib}")
+    print(f"python3 /root/repo/bench.py --summarize-pmc $D --copy-mib {copy_mib} --title '{title}' "
+          f"--program '{program}'")
     print("```\n")
     print(f"Scale: a plain device copy of {copy_mib} MiB reads {cfk:.0f} KiB by FETCH_SIZE and writes {cwk:.0f} KiB "
           f"by WRITE_SIZE per dispatch, so FETCH_SIZE x {ff:.3f} and WRITE_SIZE x {fw:.3f} give bytes.  The "
-          "counters see traffic below the L2 (to the memory-side cache and HBM).\n")
+          "counters see traffic below the L2 (to the memory-side cache and HBM), so memory-side-cache hits count.\n")
     print("| kernel | dispatches | FETCH_SIZE (KiB/launch) | WRITE_SIZE (KiB/launch) | traffic (MB/launch) |")
     print("|---|---|---|---|---|")
     print("\n".join(rows))
-    print("\nbench.py reads the record below and reports the traffic of its dominant kernel only while "
-          "gemm_comp.hip still has this SHA-256.\n")
+    print("\nbench.py reads the record below and reports a kernel's traffic only while its source file still has "
+          "the SHA-256 stored with it (comments and whitespace ignored).\n")
     print(TRAFFIC_TAG + json.dumps(rec))
 
 
-def attn_decode_bytes(B=64, L=8192, Hq=32, Hkv=8, D=128):
-    """algorithmic bytes of one decode call: K and V (INT16), their scales, q (INT16 + scale) and O (FP32)"""
-    return 2.0 * B * L * Hkv * D * 2 + 2.0 * B * L * Hkv * 4 + B * Hq * D * (2 + 4)
-
-
-def only_attention(heal, workloads, which):
-    """5 launches of the a6 prefill (1 x 4096 x 32 x 128, causal) or the a7 decode (64 x 8192 keys, 32 / 8
-    heads) on the bench's own inputs, nothing else: the program the attention counter runs profile."""
-    import numpy as np
-    import torch
-
-    heal.load()
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
-    if which == "prefill":
-        Q, K, V = workloads.qkv_fp32(1, 4096, 32, 128, seed=2)
-        (q, qs), (k, ks), (v, vs) = (heal.heal_qkv_quant_i16(dev(t[0])) for t in (Q, K, V))
-        args = (q[None], qs[None], k[None], ks[None], v[None], vs[None])
-        out = heal.heal_attn_dual_fp16(*args, causal=True)
-        for _ in range(4):
-            heal.heal_attn_dual_fp16(*args, causal=True, out=out)
-    else:
-        B, L, Hq, Hkv = 64, 8192, 32, 8
-        k, ks = workloads.int16_cache_device(B, L, Hkv, 128, seed=3)
-        v, vs = workloads.int16_cache_device(B, L, Hkv, 128, seed=4)
-        q, qs = [dev(a) for a in workloads.int16_cache_host(B, 1, Hq, 128, seed=5)]
-        out = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device="cuda")
-        ws = torch.empty(heal.heal_attn_workspace_bytes(heal.make_attn_args(q, qs, k, ks, v, vs, out, True)),
-                         dtype=torch.uint8, device="cuda")
-        for _ in range(5):
-            heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    print(f"{which}: 5 launches done", flush=True)
-
-
-def summarize_attn(d, copy_mib):
-    """Markdown summary of the attention counter runs: decode HBM bytes (FETCH_SIZE / WRITE_SIZE scaled by a
-    plain copy, as for the GEMM) and the prefill's matrix / vector occupancy (SQ counters, per SIMD)."""
-    import csv
-    import glob
-    from collections import defaultdict
-
-    def read(sub):
-        vals = defaultdict(lambda: defaultdict(list))
-        for f in glob.glob(os.path.join(d, sub, "*counter_collection.csv")):
-            for r in csv.DictReader(open(f)):
-                vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
-        return vals
-
-    def trace(sub):
-        durs = defaultdict(list)
-        for f in glob.glob(os.path.join(d, sub, "*kernel_trace.csv")):
-            for r in csv.DictReader(open(f)):
-                durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
-        return durs
-
-    mean = lambda v: sum(v) / len(v)
-    short = lambda n: n.replace("void ", "").replace("heal::(anonymous namespace)::", "").split("(")[0]
-    cf, cw = read("copy_fetch"), read("copy_write")
-    copy = lambda v: max((k for k in v if "copyBuffer" in k), key=lambda k: len(v[k]["FETCH_SIZE"] or
-                                                                                 v[k]["WRITE_SIZE"]))
-    nbytes = copy_mib * (1 << 20)
-    ff = nbytes / (mean(cf[copy(cf)]["FETCH_SIZE"]) * 1024)
-    fw = nbytes / (mean(cw[copy(cw)]["WRITE_SIZE"]) * 1024)
-    fetch, write = read("decode_fetch"), read("decode_write")
-    print("# Attention kernels: decode HBM traffic and prefill matrix / vector occupancy (bench.py workloads)\n")
-    print("Commands (from the repository root on one MI355X, ROCm 7.2; D = an output directory):\n")
-    print("```")
-    print("cd /tmp && export TMPDIR=/tmp")
-    for c, sub, prog in (("FETCH_SIZE", "decode_fetch", "--only decode"), ("WRITE_SIZE", "decode_write", "--only decode"),
-                         ("FETCH_SIZE", "copy_fetch", f"--copy-calibration {copy_mib}"),
-                         ("WRITE_SIZE", "copy_write", f"--copy-calibration {copy_mib}")):
-        print(f"timeout -s KILL 60 rocprofv3 --pmc {c} --output-format csv -d $D/{sub} -o pmc -- "
-              f"python3 /root/repo/bench.py {prog}")
-    print(f"timeout -s KILL 60 rocprofv3 --pmc {' '.join(PREFILL_SQ)} --kernel-trace --output-format csv "
-          "-d $D/prefill_sq -o pmc -- python3 /root/repo/bench.py --only prefill")
-    print(f"python3 /root/repo/bench.py --summarize-attn $D --copy-mib {copy_mib}")
-    print("```\n")
-    algo = attn_decode_bytes()
-    print(f"Decode (64 x 8192 keys, 32 query / 8 key-value heads): algorithmic {algo / 1e9:.3f} GB per call "
-          f"(K and V INT16, their scales, q and O).  Counter scale from a plain {copy_mib} MiB copy: FETCH_SIZE x "
-          f"{ff:.3f}, WRITE_SIZE x {fw:.3f}.\n")
-    print("| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | bytes per launch | / algorithmic |")
-    print("|---|---|---|---|---|---|")
-    for name in sorted(fetch):
-        if "attn_decode" not in name:
-            continue
-        fk = mean(fetch[name]["FETCH_SIZE"])
-        wk = mean(write[name]["WRITE_SIZE"]) if name in write else float("nan")
-        tb = fk * 1024 * ff + wk * 1024 * fw
-        ratio = f"{tb / algo:.3f}" if "merge" not in name else "-"
-        print(f"| `{short(name)}` | {len(fetch[name]['FETCH_SIZE'])} | {fk:.1f} | {wk:.1f} | {tb / 1e9:.4f} GB | "
-              f"{ratio} |")
-    sq, durs = read("prefill_sq"), trace("prefill_sq")
-    print("\nPrefill (1 x 4096 x 32 x 128, causal, byte reading): counters summed over the chip, per launch; per-SIMD "
-          "figures divide by 1024 SIMDs; the clock is GRBM_GUI_ACTIVE over 8 XCDs and the launch's duration under "
-          "the counter run.\n")
-    print("| kernel | launches | duration (us) | clock (GHz) | cycles / SIMD | MFMA busy / SIMD | VALU-MFMA "
-          "co-issue / SIMD | VALU instructions (non-MFMA) / SIMD |")
-    print("|---|---|---|---|---|---|---|---|")
-    for name in sorted(sq):
-        if "attn_prefill" not in name:
-            continue
-        c = {k: mean(v) for k, v in sq[name].items()}
-        dur = mean(durs[name]) if durs.get(name) else float("nan")
-        clk = c["GRBM_GUI_ACTIVE"] / 8 / dur / 1e9
-        print(f"| `{short(name)}` | {len(sq[name]['GRBM_GUI_ACTIVE'])} | {dur * 1e6:.1f} | {clk:.2f} | "
-              f"{dur * clk * 1e9:.3g} | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024:.3g} | "
-              f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / 1024:.3g} | {(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / 1024:.3g} |")
-    print("\nSQ_VALU_MFMA_BUSY_CYCLES counts 32 cycles per v_mfma_f32_32x32x16_f16; a non-MFMA VALU instruction of "
-          "a 64-wide wavefront takes 4 cycles on a 16-lane SIMD.")
-
-
-PREFILL_SQ = ("GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES",
-              "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_BUSY_CYCLES")
-
-
+# ------------------------------------------------------------------------------------------------- timing
 class Timer:
-    """HIP events on the current (launch) stream."""
+    """HIP events on the current (launch) stream, one pair per launch."""
 
     def __init__(self):
         import torch
@@ -327,79 +237,288 @@ def time_fn(fn, reps, warm=2):
     return a.elapsed_time(b) * 1e-3 / reps
 
 
-def main():
-    args = parse()
-    if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, args.copy_mib)
-        return
-    if args.summarize_attn:
-        summarize_attn(args.summarize_attn, args.copy_mib)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the hot path shards without communication and multi-GPU runs are not part of it",
-              file=sys.stderr)
-        sys.exit(2)
+def log(msg):
+    """progress on stderr (the JSON line is the only output on stdout)"""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    import numpy as np
+
+def host_threads():
+    import ctypes
+    try:
+        return int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+    except OSError:
+        return os.cpu_count()
+
+
+def attn_decode_bytes(B=64, L=8192, Hq=32, Hkv=8, D=128):
+    """algorithmic bytes of one decode call: K and V (INT16), their scales, q (INT16 + scale) and O (FP32)"""
+    return 2.0 * B * L * Hkv * D * 2 + 2.0 * B * L * Hkv * 4 + B * Hq * D * (2 + 4)
+
+
+def bf16_round(x):
+    """x (float64 numpy) rounded to bf16 (torch's RNE cast), returned as float32"""
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+import numpy as np  # noqa: E402  (numpy is needed by the helpers above and below)
+
+
+def bf16_attention_rows(qd, kd, vd, rows, causal, scale):
+    """Plain-bf16 attention (the contrast): Q, K, V and the probabilities P rounded to bf16 at the op
+    boundaries, products accumulated in FP32, FP32 softmax; computed on the host for the listed (b, i, h) rows.
+    qd [B, Lq, Hq, D], kd / vd [B, Lkv, Hkv, D] float64 dequantised values."""
+    B, Lq, Hq, D = qd.shape
+    Lkv, Hkv = kd.shape[1], kd.shape[2]
+    g = Hq // Hkv
+    out = np.empty((len(rows), D), np.float64)
+    for r, (b, i, h) in enumerate(rows):
+        jmax = min(Lkv - 1, i + (Lkv - Lq)) if causal else Lkv - 1
+        q = bf16_round(qd[b, i, h])
+        k = bf16_round(kd[b, :jmax + 1, h // g])
+        v = bf16_round(vd[b, :jmax + 1, h // g])
+        s = (k @ q).astype(np.float32) * np.float32(scale)
+        p = np.exp(s - s.max()).astype(np.float32)
+        p = p / p.sum(dtype=np.float32)
+        out[r] = (bf16_round(p) @ v).astype(np.float32)
+    return out
+
+
+def row_err(got, ref):
+    """(normwise over the rows, worst single row normwise)"""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nw = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    den = np.linalg.norm(ref, axis=-1)
+    wr = float(np.max(np.linalg.norm(got - ref, axis=-1) / np.where(den > 0, den, 1.0)))
+    return nw, wr
+
+
+# --------------------------------------------------------------------------------------- headline: 8192^3
+def gemm8192_inputs(heal, workloads, rotate):
+    import torch
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    host0 = workloads.gemm_rowscaled(8192, 8192, 8192, seed=4)
+    copies = [(dev(host0[0]), dev(host0[1]))]
+    for i in range(1, rotate):
+        A, Bt = workloads.gemm_rowscaled(8192, 8192, 8192, seed=4 + i)
+        copies.append((dev(A), dev(Bt)))
+        del A, Bt
+    ah, al, ea = heal.heal_split(copies[0][0])
+    bh, bl, eb = heal.heal_split(copies[0][1])
+    c = heal.heal_gemm_comp(ah, al, ea, bh, bl, eb)
+    torch.cuda.synchronize()
+    return host0, copies, (ah, al, ea, bh, bl, eb, c)
+
+
+def headline(args, heal, workloads):
     import torch
 
-    import error_compensated_gemm_amd as heal
-    import workloads
+    M = N = K = 8192
+    host0, copies, (ah, al, ea, bh, bl, eb, c) = gemm8192_inputs(heal, workloads, args.rotate)
+    timer = Timer()
 
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.only:
-        only_attention(heal, workloads, args.only)
-        return
-    heal.load()
-    torch.cuda.set_device(0)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    def step(i, record):
+        A, Bt = copies[i % len(copies)]
+        e = timer.start() if record else None
+        heal.heal_split(A, hi=ah, lo=al, exps=ea)
+        if record:
+            timer.stop("split_a", e)
+            e = timer.start()
+        heal.heal_split(Bt, hi=bh, lo=bl, exps=eb)
+        if record:
+            timer.stop("split_b", e)
+            e = timer.start()
+        heal.heal_gemm_comp(ah, al, ea, bh, bl, eb, c=c)
+        if record:
+            timer.stop("gemm", e)
 
-    # ---------------------------------------------------------------- set-up (untimed): weights split once
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i, True)
+    t1.record()
+    torch.cuda.synchronize()
+    total_s = t0.elapsed_time(t1) * 1e-3
+    step_s = total_s / args.steps
+    flop = 2.0 * M * N * K
+    durs = {k: sum(v) / len(v) for k, v in timer.durations().items()}
+    kernel = heal.heal_gemm_comp_variant(M, N, K, 3)
+    sym = gemm_symbol(kernel)
+    achieved = 3 * flop / durs["gemm"] / 1e12
+    tr = stored_traffic(sym)
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None if tr is None else tr["bytes_per_launch"],
+        "traffic_profile": None if tr is None else tr["profile"],
+        "kernel": kernel, "symbol": sym, "avg_launch_us": round(durs["gemm"] * 1e6, 2), "launches_per_step": 1,
+        "work_per_launch": "3 x 2MNK = 3.299e12 16-bit MFMA flop (three products per FP32-equivalent product)",
+    }
+    split_bytes = 8.0 * M * K  # read 4 B, write 2 + 2 B per element
+    parts = {
+        "split_a_us": round(durs["split_a"] * 1e6, 1), "split_b_us": round(durs["split_b"] * 1e6, 1),
+        "split_gbs": round(split_bytes / ((durs["split_a"] + durs["split_b"]) / 2) / 1e9, 1),
+        "split_symbol": "split_rows_kernel<float, true, false, false>",
+        "gemm_us": round(durs["gemm"] * 1e6, 1),
+        "gemm_tflops_fp32eq": round(flop / durs["gemm"] / 1e12, 1),
+    }
+    st = stored_traffic(parts["split_symbol"])
+    parts["split_traffic"] = None if st is None else st["bytes_per_launch"]
+    result = {
+        "metric": "FP32-equiv TFLOP/s of compensated GEMM + % of MFMA roofline; max rel err vs FP64",
+        "value": round(flop / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gemm_fp32_8192x8192x8192_p3: heal_split(A) + heal_split(B^T) + heal_gemm_comp, 3 products",
+            "M": M, "N": N, "K": K, "products": 3,
+            "inputs": "fp32 N(0,1), rows of A and k-rows of B scaled by 10^U(-3,3), seeds 4..",
+            "rotation": f"{len(copies)} copies of (A, B^T), {len(copies) * 2 * M * K * 4 / 1e9:.2f} GB",
+            "flop_per_step_fp32eq": flop,
+        },
+        "roofline": roofline,
+        "step_parts": parts,
+    }
+    # one more step on the first copy: the output the CPU legs compare
+    step(0, False)
+    torch.cuda.synchronize()
+    return result, host0, (ah, al, ea, bh, bl, eb, c), copies[0]
+
+
+def cpu_baseline_gemm8192(args, heal, host0, bufs, first):
+    """The FP64 oracle on the first --cpu-rows rows of the 8192^3 product (all host threads), timed; the GPU's
+    error on those rows; and the contrast GEMMs (plain bf16, and bf16 hi + lo with three products) on them."""
+    import torch
+
+    import oracle
+
+    A, Bt = host0
+    rows = max(1, min(args.cpu_rows, A.shape[0]))
+    Ad = A[:rows].astype(np.float64)
+    Bd = Bt.astype(np.float64)
+    t = time.perf_counter()
+    C = oracle.gemm_f64(Ad, Bd)
+    t_cpu = time.perf_counter() - t
+    flops = 2.0 * rows * Bt.shape[0] * A.shape[1]
+    ah, al, ea, bh, bl, eb, c = bufs
+    G = c[:rows].cpu().numpy().astype(np.float64)
+    absab = np.abs(Ad) @ np.abs(Bd).T  # library FP64 matmul, only for the componentwise denominator
+    nw, wr = row_err(G, C)
+    comp = float(np.max(np.abs(G - C) / absab))
+    # contrast: bf16 parts, no prescale: one product (plain bf16) and three products
+    Ag, Bg = first
+    ah2, al2, _ = heal.heal_split(Ag, part="bf16", prescale=False, hi=ah, lo=al)
+    bh2, bl2, _ = heal.heal_split(Bg, part="bf16", prescale=False, hi=bh, lo=bl)
+    c1 = heal.heal_gemm_comp(ah2, None, None, bh2, None, None, part="bf16")
+    e1 = row_err(c1[:rows].cpu().numpy(), C)[0]
+    del c1
+    c3 = heal.heal_gemm_comp(ah2, al2, None, bh2, bl2, None, part="bf16")
+    e3 = row_err(c3[:rows].cpu().numpy(), C)[0]
+    del c3
+    torch.cuda.synchronize()
+    return {
+        "value": round(flops / t_cpu / 1e12, 5), "unit": "TFLOP/s", "cores": host_threads(), "kind": "oracle",
+        "sample": f"plain-C FP64 GEMM of the first {rows} rows of A (seed 4) times B, "
+                  f"{flops:.3e} flop in {t_cpu:.1f} s",
+        "gpu_err_vs_fp64_on_sample": {"normwise": nw, "worst_row_normwise": wr, "componentwise_max": comp},
+        "contrast_err_vs_fp64_on_sample": {"plain_bf16_one_product": e1, "bf16_hi_lo_three_products": e3},
+    }
+
+
+# --------------------------------------------------------------------------------------------- other rows
+def row_config1(heal, workloads, dev, with_cpu):
+    """256^3 FP32 x FP32 (U[-1, 1]), three products, and the INT16 quantisation of one 256 x 128 K tile: the
+    correctness configuration, timed as launch latency (one step = split A + split B + GEMM)."""
+    import torch
+
+    A, Bt = workloads.gemm_uniform(256, 256, 256, seed=0)
+    a, b = dev(A), dev(Bt)
+    ah, al, ea = heal.heal_split(a)
+    bh, bl, eb = heal.heal_split(b)
+    c = heal.heal_gemm_comp(ah, al, ea, bh, bl, eb)
+
+    def step():
+        heal.heal_split(a, hi=ah, lo=al, exps=ea)
+        heal.heal_split(b, hi=bh, lo=bl, exps=eb)
+        heal.heal_gemm_comp(ah, al, ea, bh, bl, eb, c=c)
+    t = time_fn(step, 200, warm=10)
+    Q, Kt, V = workloads.qkv_fp32(1, 256, 1, 128, seed=0)
+    kd = dev(Kt[0])
+    q, s = heal.heal_qkv_quant_i16(kd)
+    tq = time_fn(lambda: heal.heal_qkv_quant_i16(kd, q=q, scale=s), 200, warm=10)
+    torch.cuda.synchronize()
+    row = {"us_per_step": round(t * 1e6, 2), "tflops_fp32eq": round(2 * 256.0 ** 3 / t / 1e12, 3),
+           "quant_256x128_us": round(tq * 1e6, 2),
+           "bound": "launch latency (3 launches per step)"}
+    if with_cpu:
+        row["cpu_baseline"] = cpu_baseline_config1(A, Bt, c, Kt[0], q, s)
+    return row
+
+
+def cpu_baseline_config1(A, Bt, c, kt, q, s):
+    import oracle
+
+    t = time.perf_counter()
+    C = oracle.gemm_f64(A, Bt)
+    t_cpu = time.perf_counter() - t
+    qo, so = oracle.quant_i16(kt)
+    return {"value": round(2 * 256.0 ** 3 / t_cpu / 1e12, 5), "unit": "TFLOP/s", "cores": host_threads(),
+            "kind": "oracle", "sample": "the whole 256^3 product",
+            "gpu_err_vs_fp64": {"normwise": row_err(c.cpu().numpy(), C)[0]},
+            "quant_bit_exact": bool(np.array_equal(q.cpu().numpy(), qo) and
+                                    np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32)))}
+
+
+def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10):
+    """Llama-3-8B projection shapes: split + compensated GEMM, P = 2 (bf16 weights exact in FP16 after the row
+    prescale), M in {1, 16, 2048}; the weights rotate through `rotate` copies (805 MB for 3), so the skinny
+    shapes stream them from HBM."""
+    import torch
+
     shapes = [(M, K, N) for M in workloads.LLAMA3_8B_M for (K, N) in workloads.LLAMA3_8B_KN]
-    weights = {}
-    host_w = {}
+    weights, host_w = {}, {}
     for (K, N) in workloads.LLAMA3_8B_KN:
         W = workloads.llama_weights_bf16(N, K, seed=1)
         host_w[(K, N)] = W
-        wt = dev(W.view(np.int16)).view(torch.bfloat16)
-        bh, _, eb = heal.heal_split(wt, residual=False)
-        weights[(K, N)] = (bh, eb)
-        del wt
-    bufs = []
-    host_x = {}
+        bh, _, eb = heal.heal_split(dev(W.view(np.int16)).view(torch.bfloat16), residual=False)
+        weights[(K, N)] = ([bh] + [bh.clone() for _ in range(rotate - 1)], eb)
+    bufs, host_x = [], {}
     for (M, K, N) in shapes:
         X = workloads.llama_activations(M, K, seed=1)
         host_x[(M, K)] = X
         x = dev(X)
         ah, al, ea = heal.heal_split(x)
-        c = heal.heal_gemm_comp(ah, al, ea, *weights[(K, N)][:1], None, weights[(K, N)][1])
+        c = heal.heal_gemm_comp(ah, al, ea, weights[(K, N)][0][0], None, weights[(K, N)][1])
         bufs.append((M, K, N, x, ah, al, ea, c))
     torch.cuda.synchronize()
-    # decode-sized M takes the entry point that splits A in the GEMM's prologue (the same bits as split +
-    # GEMM, without the parts' round trip through HBM); prefill-sized M splits in its own pass
-    # (one-row activations also leave the row exponent to the GEMM: a launch fewer, the same bits)
-    fused = lambda M: M <= 64
-    derived = lambda M: M == 1
+    fused = lambda M: M <= 64      # the split in the GEMM's prologue (same bits as split + GEMM)
+    derived = lambda M: M == 1     # and the row exponent there too
     variants = {(M, K, N): heal.heal_gemm_comp_variant(M, N, K, 2) + (" FP32-A" if fused(M) else "")
                 + (", exponent in the kernel" if derived(M) else "") for (M, K, N) in shapes}
-
     timer = Timer()
 
-    def step(record):
+    def step(i, record):
         for (M, K, N, x, ah, al, ea, c) in bufs:
-            bh, eb = weights[(K, N)]
+            copies, eb = weights[(K, N)]
+            bh = copies[i % len(copies)]
             if derived(M):
                 pass
             elif fused(M):
                 heal.heal_row_exponents(x, exps=ea)
             else:
                 heal.heal_split(x, hi=ah, lo=al, exps=ea)
-            if record:
-                e0 = timer.start()
+            e0 = timer.start() if record else None
             if fused(M):
                 heal.heal_gemm_comp_f32a(x, None if derived(M) else ea, bh, None, eb, c=c)
             else:
@@ -407,33 +526,26 @@ def main():
             if record:
                 timer.stop((M, K, N), e0)
 
-    for _ in range(args.warmup):
-        step(False)
+    for i in range(3):
+        step(i, False)
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(args.steps):
-        step(True)
+    for i in range(steps):
+        step(i, True)
     t1.record()
     torch.cuda.synchronize()
-    total_s = t0.elapsed_time(t1) * 1e-3
-    ms_per_step = total_s / args.steps * 1e3
+    step_s = t0.elapsed_time(t1) * 1e-3 / steps
     flops_step = sum(2.0 * M * N * K for (M, K, N) in shapes)
-    value = flops_step / (total_s / args.steps) / 1e12
-
     durs = timer.durations()
-    per_shape = {}
-    by_variant = {}
+    per_shape, by_variant = {}, {}
     for (M, K, N) in shapes:
         d = durs[(M, K, N)]
         avg = sum(d) / len(d)
-        per_shape[f"{M}x{K}x{N}"] = {
-            "us": round(avg * 1e6, 2),
-            "tflops_fp32eq": round(2.0 * M * N * K / avg / 1e12, 2),
-            "hbm_gbs": round((2.0 * N * K + 8.0 * M * K + 4.0 * M * N) / avg / 1e9, 1),
-            "kernel": variants[(M, K, N)],
-        }
+        gbs = (2.0 * N * K + 4.0 * M * K + 4.0 * M * N) / avg / 1e9
+        per_shape[f"{M}x{K}x{N}"] = {"us": round(avg * 1e6, 2), "tflops_fp32eq": round(2.0 * M * N * K / avg / 1e12, 2),
+                                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                                     "kernel": variants[(M, K, N)]}
         v = by_variant.setdefault(variants[(M, K, N)], {"time": 0.0, "launches": 0, "mfma_flop": 0.0})
         v["time"] += sum(d)
         v["launches"] += len(d)
@@ -441,142 +553,148 @@ def main():
     dom_name, dom = max(by_variant.items(), key=lambda kv: kv[1]["time"])
     avg_dur = dom["time"] / dom["launches"]
     achieved = dom["mfma_flop"] / dom["launches"] / avg_dur / 1e12
-    roofline = {
-        "bound": "mfma",
-        "achieved": round(achieved, 1),
-        "peak": PEAK_F16_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-        "traffic": stored_traffic(dom_name),
-        "kernel": dom_name,
-        "avg_launch_us": round(avg_dur * 1e6, 2),
-        "launches_per_step": dom["launches"] // args.steps,
-        "work_per_launch": "P x 2MNK 16-bit MFMA flop (P = 2), averaged over the launches of this kernel",
-    }
-
-    result = {
-        "metric": "FP32-equiv TFLOP/s of compensated GEMM + % of MFMA roofline; max rel err vs FP64",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {
-            "workload": "llama3_8b_linear: split(fp32 X) + compensated GEMM, P=2, 9 shapes (M <= 64: the split "
-                        "in the GEMM's prologue; M = 1: the row exponent there too)",
-            "shapes_MKN": [list(s) for s in shapes],
-            "activations": "fp32 N(0,1), 1% channels x50",
-            "weights": "bf16 N(0,0.02), pre-split to fp16 once",
-            "flop_per_step_fp32eq": flops_step,
-        },
-        "roofline": roofline,
+    tr = stored_traffic(gemm_symbol(dom_name))
+    row = {
+        "us_per_step": round(step_s * 1e6, 1), "tflops_fp32eq": round(flops_step / step_s / 1e12, 2),
+        "weights_rotated_copies": rotate,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "traffic": None if tr is None else tr["bytes_per_launch"], "kernel": dom_name,
+                     "avg_launch_us": round(avg_dur * 1e6, 2)},
         "per_shape": per_shape,
     }
-
-    # ------------------------------------------------------------------ CPU baseline: the FP64 oracle
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(args, shapes, host_x, host_w, bufs, flops_step)
-
-    if not args.no_rows:
-        result["rows"] = other_rows(heal, workloads, dev)
-
-    print(json.dumps(result), flush=True)
+    if with_cpu:
+        row["cpu_baseline"] = cpu_baseline_llama(shapes, host_x, host_w, bufs)
+    return row
 
 
-def cpu_baseline(args, shapes, host_x, host_w, bufs, flops_step):
-    import ctypes
-
-    import numpy as np
-
+def cpu_baseline_llama(shapes, host_x, host_w, bufs, max_rows=256):
     import oracle
 
-    lib = oracle.lib()
-    try:
-        threads = ctypes.CDLL("libgomp.so.1").omp_get_max_threads()
-    except OSError:
-        threads = os.cpu_count()
-    wd = {}
-    for (K, N), W in host_w.items():
-        wd[(K, N)] = (W.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    flops = 0.0
-    t_cpu = 0.0
-    errs, comps = [], []
+    wd = {k: (W.astype(np.uint32) << 16).view(np.float32).astype(np.float64) for k, W in host_w.items()}
     gpu_c = {(M, K, N): c for (M, K, N, x, ah, al, ea, c) in bufs}
+    flops = t_cpu = 0.0
+    errs = {}
     for (M, K, N) in shapes:
-        rows = min(M, args.cpu_rows)
+        rows = min(M, max_rows)
         X = host_x[(M, K)][:rows].astype(np.float64)
         t = time.perf_counter()
         C = oracle.gemm_f64(X, wd[(K, N)])
         t_cpu += time.perf_counter() - t
         flops += 2.0 * rows * K * N
         G = gpu_c[(M, K, N)][:rows].cpu().numpy().astype(np.float64)
-        errs.append(float(np.linalg.norm(G - C) / np.linalg.norm(C)))
-        absab = np.abs(X) @ np.abs(wd[(K, N)]).T
-        comps.append(float(np.max(np.abs(G - C) / absab)))
-    return {
-        "value": round(flops / t_cpu / 1e12, 5),
-        "unit": "TFLOP/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"FP64 plain-C GEMM on the first min(M, {args.cpu_rows}) rows of each of the 9 shapes "
-                  f"({flops:.3e} flop, {t_cpu:.1f} s)",
-        "gpu_err_vs_fp64_on_sample": {"normwise_max": max(errs), "componentwise_max": max(comps)},
-    }
+        comp = float(np.max(np.abs(G - C) / (np.abs(X) @ np.abs(wd[(K, N)]).T)))
+        errs[f"{M}x{K}x{N}"] = {"normwise": row_err(G, C)[0], "componentwise": comp}
+    worst = max(errs.items(), key=lambda kv: kv[1]["normwise"])
+    return {"value": round(flops / t_cpu / 1e12, 5), "unit": "TFLOP/s", "cores": host_threads(), "kind": "oracle",
+            "sample": f"plain-C FP64 GEMM on the first min(M, {max_rows}) rows of each of the 9 shapes "
+                      f"({flops:.3e} flop, {t_cpu:.1f} s)",
+            "gpu_err_vs_fp64_on_sample": {"normwise_max": worst[1]["normwise"], "normwise_max_shape": worst[0],
+                                          "per_shape": errs}}
 
 
-def other_rows(heal, workloads, dev):
-    """The remaining hot-path steps, each timed on its own workload with HIP events."""
-    import numpy as np
+def row_split_quant(heal, workloads, dev):
     import torch
 
     rows = {}
-    # a1: activation split, 2048 x 14336 fp32 -> fp16 hi + lo + exps (read 4 B, write 4 B per element)
     x = dev(workloads.llama_activations(2048, 14336, seed=1))
     hi, lo, e = heal.heal_split(x)
     t = time_fn(lambda: heal.heal_split(x, hi=hi, lo=lo, exps=e), 20)
-    rows["a1_split_2048x14336"] = {"us": round(t * 1e6, 2), "gbs": round(x.numel() * 8 / t / 1e9, 1)}
+    gbs = x.numel() * 8 / t / 1e9
+    tr = stored_traffic("split_rows_kernel<float, true, false, false>")
+    rows["a1_split_2048x14336"] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "algorithmic_bytes": x.numel() * 8 + 2048 * 4,
+                                   "traffic": None if tr is None else tr["bytes_per_launch"]}
     del x, hi, lo, e
-    # a4 + a6: quantise Q, K, V [4096, 32, 128] then causal Dual-FP16 prefill
     Q, K, V = workloads.qkv_fp32(1, 4096, 32, 128, seed=2)
     qd, kd, vd = dev(Q[0]), dev(K[0]), dev(V[0])
-    qkv = [heal.heal_qkv_quant_i16(t) for t in (qd, kd, vd)]
+    qkv = [heal.heal_qkv_quant_i16(t_) for t_ in (qd, kd, vd)]
+
     def quant_all():
         for src, (q, s) in zip((qd, kd, vd), qkv):
             heal.heal_qkv_quant_i16(src, q=q, scale=s)
     t = time_fn(quant_all, 20)
     nel = 3 * qd.numel()
-    rows["a4_quant_3x4096x32x128"] = {"us": round(t * 1e6, 2), "gbs": round(nel * (4 + 2 + 4 / 128) / t / 1e9, 1)}
-    # the same values with each token's Q, K and V heads side by side ([4096, 96, 128], as a fused QKV
-    # projection writes them): one launch, the same codes and scales
+    gbs = nel * (4 + 2 + 4 / 128) / t / 1e9
+    rows["a4_quant_3x4096x32x128"] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     fused = torch.cat([qd, kd, vd], dim=1)
     fq, fs = heal.heal_qkv_quant_i16(fused)
     t = time_fn(lambda: heal.heal_qkv_quant_i16(fused, q=fq, scale=fs), 20)
-    rows["a4_quant_fused_qkv_4096x96x128"] = {"us": round(t * 1e6, 2),
-                                              "gbs": round(nel * (4 + 2 + 4 / 128) / t / 1e9, 1)}
-    del fused, fq, fs
-    (q, qs), (k, ks), (v, vs) = qkv
-    out = heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None], causal=True)
-    t = time_fn(lambda: heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None],
-                                                 causal=True, out=out), 10)
-    fl = 4.0 * 128 * 32 * (4096 * 4097 / 2)
-    rows["a6_prefill_1x4096x32x128_causal"] = {
-        "us": round(t * 1e6, 2), "tflops_fp32eq": round(fl / t / 1e12, 2),
-        "mfma_frac": round(8 * fl / 2 / t / 1e12 / PEAK_F16_TFLOPS, 4)}
-    # the other readings of the Dual-FP16 pair: shift-10 (4 + 4 products), float-float (3 + 3 products)
-    for reading, prods in (("shift10", 8), ("float", 6)):
-        t = time_fn(lambda: heal.heal_attn_dual_fp16(q[None], qs[None], k[None], ks[None], v[None], vs[None],
-                                                     causal=True, out=out, dual_split=reading), 10)
-        rows[f"a6_prefill_1x4096x32x128_causal_{reading}"] = {
-            "us": round(t * 1e6, 2), "tflops_fp32eq": round(fl / t / 1e12, 2),
-            "mfma_frac": round(prods * fl / 2 / t / 1e12 / PEAK_F16_TFLOPS, 4)}
-    del qd, kd, vd, qkv, q, k, v, out
-    # a7: decode over an INT16 cache, 64 x 8192 keys, 32 q-heads / 8 kv-heads
+    gbs = nel * (4 + 2 + 4 / 128) / t / 1e9
+    tr = stored_traffic("quant_i16_kernel")
+    rows["a4_quant_fused_qkv_4096x96x128"] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1),
+                                              "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                                              "algorithmic_bytes": int(nel * (4 + 2 + 4 / 128)),
+                                              "traffic": None if tr is None else tr["bytes_per_launch"]}
+    return rows, (Q, K, V, qkv)
+
+
+def row_prefill(heal, qkv_host, qkv_dev, with_cpu):
+    (q, qs), (k, ks), (v, vs) = qkv_dev
+    args = (q[None], qs[None], k[None], ks[None], v[None], vs[None])
+    out = heal.heal_attn_dual_fp16(*args, causal=True)
+    fl = 4.0 * 128 * 32 * (4096 * 4097 / 2)  # FP32-equivalent flop: 4 D per visible (query, key) pair
+    rows = {}
+    for reading, prods in (("byte", 8), ("shift10", 8), ("float", 6)):
+        t = time_fn(lambda: heal.heal_attn_dual_fp16(*args, causal=True, out=out, dual_split=reading), 10)
+        ach = prods * fl / 2 / t / 1e12
+        key = "a6_prefill_1x4096x32x128_causal" + ("" if reading == "byte" else f"_{reading}")
+        rows[key] = {"us": round(t * 1e6, 2), "tflops_fp32eq": round(fl / t / 1e12, 2),
+                     "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_F16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(ach / PEAK_F16_TFLOPS, 4),
+                                  "kernel": f"attn_prefill_kernel ({reading} reading, {prods // 2} + {prods // 2} "
+                                            "products)"}}
+    heal.heal_attn_dual_fp16(*args, causal=True, out=out)
+    if with_cpu:
+        rows["a6_prefill_1x4096x32x128_causal"]["cpu_baseline"] = cpu_baseline_attn(
+            qkv_dev, out, causal=True, nrows=96, seed=0, batch_rows=None)
+    return rows
+
+
+def cpu_baseline_attn(qkv_dev, out, causal, nrows, seed, batch_rows):
+    """The FP64 oracle (on the dequantised INT16 inputs) on a sample of output rows, timed; the GPU's error on
+    them; the plain-bf16 contrast on the same rows."""
+    import oracle
+
+    (q, qs), (k, ks), (v, vs) = qkv_dev
+    if q.dim() == 3:  # [T, H, D] of one sequence
+        qh, qsh, kh, ksh, vh, vsh = (t.cpu().numpy()[None] for t in (q, qs, k, ks, v, vs))
+        o = out.cpu().numpy()[0] if out.dim() == 4 else out.cpu().numpy()
+        o = o[None] if o.ndim == 3 else o
+    else:
+        qh, qsh, kh, ksh, vh, vsh = (t.cpu().numpy() for t in (q, qs, k, ks, v, vs))
+        o = out.cpu().numpy()
+    B, Lq, Hq, D = qh.shape
+    Lkv = kh.shape[1]
+    rng = np.random.default_rng(seed)
+    if batch_rows is None:
+        rows = np.stack([rng.integers(0, B, nrows), rng.integers(0, Lq, nrows), rng.integers(0, Hq, nrows)], 1)
+        rows[:4, 1] = [Lq - 1, Lq - 2, Lq // 2, 0]
+    else:  # every head of the given batches (decode)
+        rows = np.array([(b, 0, h) for b in batch_rows for h in range(Hq)], np.int64)
+    t = time.perf_counter()
+    ref = oracle.attn_i16_f64(qh, qsh, kh, ksh, vh, vsh, causal, rows=rows)
+    t_cpu = time.perf_counter() - t
+    pairs = sum(min(Lkv, i + 1 + Lkv - Lq) if causal else Lkv for (_, i, _) in rows)
+    flops = 4.0 * D * pairs
+    got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    nw, wr = row_err(got, ref)
+    qd, kd, vd = oracle.dequant_i16(qh, qsh), oracle.dequant_i16(kh, ksh), oracle.dequant_i16(vh, vsh)
+    cb = bf16_attention_rows(qd, kd, vd, rows, causal, 1.0 / np.sqrt(128.0))
+    res = {"value": round(flops / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": host_threads(), "kind": "oracle",
+           "sample": f"FP64 attention on {len(rows)} (b, i, h) output rows, {pairs} visible (query, key) pairs, "
+                     f"{t_cpu:.2f} s",
+           "gpu_err_vs_fp64_on_sample": {"normwise": nw, "worst_row_normwise": wr},
+           "contrast_plain_bf16_err_on_sample": row_err(cb, ref)[0]}
+    if batch_rows is not None:
+        kv_bytes = len(batch_rows) * Lkv * kh.shape[2] * (2 * 128 * 2 + 8)
+        res["value_gbs"] = round(kv_bytes / t_cpu / 1e9, 3)
+    return res
+
+
+def row_decode(heal, workloads, dev, with_cpu):
+    import torch
+
     B, L, Hq, Hkv = 64, 8192, 32, 8
     k, ks = workloads.int16_cache_device(B, L, Hkv, 128, seed=3)
     v, vs = workloads.int16_cache_device(B, L, Hkv, 128, seed=4)
@@ -584,24 +702,37 @@ def other_rows(heal, workloads, dev):
     out = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device="cuda")
     args = heal.make_attn_args(q, qs, k, ks, v, vs, out, True)
     ws = torch.empty(heal.heal_attn_workspace_bytes(args), dtype=torch.uint8, device="cuda")
-    t = time_fn(lambda: heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws), 10)
     by = attn_decode_bytes(B, L, Hq, Hkv)
-    rows["a7_decode_64x8192_gqa32_8"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
-                                         "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
-    for reading in ("shift10", "float"):
+    rows = {}
+    tr = stored_traffic("attn_decode_kernel<false, 0>")
+    for reading in ("byte", "shift10", "float"):
         t = time_fn(lambda: heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws,
                                                      dual_split=reading), 10)
-        rows[f"a7_decode_64x8192_gqa32_8_{reading}"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
-                                                        "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
-    # the same cache in 64-key pages of a shuffled pool (paged decode): pages gathered by index, no copy
-    # of the keys on the timed path
+        key = "a7_decode_64x8192_gqa32_8" + ("" if reading == "byte" else f"_{reading}")
+        gbs = by / t / 1e9
+        rows[key] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        if reading == "byte":
+            rows[key]["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                     "traffic": None if tr is None else tr["bytes_per_launch"],
+                                     "kernel": "attn_decode_kernel<false, 0> + attn_decode_merge_kernel",
+                                     "algorithmic_bytes": int(by)}
+    heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws)
+    if with_cpu:
+        sub = [0, 37]
+        sel = lambda t: t[sub]
+        rows["a7_decode_64x8192_gqa32_8"]["cpu_baseline"] = cpu_baseline_attn(
+            ((sel(q), sel(qs)), (sel(k), sel(ks)), (sel(v), sel(vs))), sel(out), causal=True, nrows=0, seed=0,
+            batch_rows=list(range(len(sub))))
+    # the same cache in 64-key pages of a shuffled pool (paged decode)
     ps, npg = 64, L // 64
     g = torch.Generator(device="cpu")
     g.manual_seed(6)
     tab = torch.randperm(B * npg, generator=g).to(torch.int32).view(B, npg).to("cuda")
-    def pool(t):
-        p = torch.empty((B * npg, ps) + tuple(t.shape[2:]), dtype=t.dtype, device="cuda")
-        p.index_copy_(0, tab.view(-1).long(), t.reshape((B * npg, ps) + tuple(t.shape[2:])))
+
+    def pool(t_):
+        p = torch.empty((B * npg, ps) + tuple(t_.shape[2:]), dtype=t_.dtype, device="cuda")
+        p.index_copy_(0, tab.view(-1).long(), t_.reshape((B * npg, ps) + tuple(t_.shape[2:])))
         return p
     kp, ksp = pool(k), pool(ks)
     del k, ks
@@ -615,8 +746,7 @@ def other_rows(heal, workloads, dev):
                                                     workspace=pws), 10)
     rows["a7p_paged_decode_64x8192_page64"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
                                                "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
-    # the same pool laid out head-major within each page ([P, Hkv, 64, D], passed through the strides): a
-    # head's 64 keys are one contiguous 16 KB run
+
     def head_major(p):
         return p.transpose(1, 2).contiguous().transpose(1, 2)
     kp, ksp = head_major(kp), head_major(ksp)
@@ -625,10 +755,14 @@ def other_rows(heal, workloads, dev):
                                                     workspace=pws), 10)
     rows["a7p_paged_decode_64x8192_page64_head_major"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
                                                           "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
-    del kp, ksp, vp, vsp, tab, lens, q, qs, out, ws, q1, qs1, o1, pws
-    torch.cuda.empty_cache()
-    # quantise-on-append: the Llama-3-8B QKV projection (2048 tokens x 4096 -> 6144 = 48 heads of 128, bf16
-    # weights, P = 2) with the INT16 quantisation fused into the GEMM epilogue, against GEMM + quantiser
+    return rows
+
+
+def row_fused_and_vendor(heal, workloads, dev):
+    """Quantise-on-append, the split in the GEMM prologue, hipBLASLt at equal matrix work, split-K at medium M."""
+    import torch
+
+    rows = {}
     X = dev(workloads.llama_activations(2048, 4096, seed=7))
     Wq = dev(workloads.llama_weights_bf16(6144, 4096, seed=7).view(np.int16)).view(torch.bfloat16)
     ah, al, ea = heal.heal_split(X)
@@ -636,35 +770,34 @@ def other_rows(heal, workloads, dev):
     qf, sf = heal.heal_gemm_comp_quant_i16(ah, al, ea, bh, None, eb)
     c = heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
     qu, su = heal.heal_qkv_quant_i16(c.view(2048, 48, 128))
+
     def unfused():
         heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
         heal.heal_qkv_quant_i16(c.view(2048, 48, 128), q=qu, scale=su)
-    # the clock moves with heat and data, so the two are timed in turn, three times, best of each
     t_f = t_u = float("inf")
-    for _ in range(3):
+    for _ in range(3):  # the clock moves with heat and data: timed in turn, best of each
         t_f = min(t_f, time_fn(lambda: heal.heal_gemm_comp_quant_i16(ah, al, ea, bh, None, eb, q=qf, scale=sf), 10))
         t_u = min(t_u, time_fn(unfused, 10))
-    fl = 2.0 * 2048 * 4096 * 6144
     rows["qkv_proj_quant_fused_2048x4096x6144"] = {
-        "us": round(t_f * 1e6, 2), "unfused_us": round(t_u * 1e6, 2), "tflops_fp32eq": round(fl / t_f / 1e12, 1),
+        "us": round(t_f * 1e6, 2), "unfused_us": round(t_u * 1e6, 2),
+        "tflops_fp32eq": round(2.0 * 2048 * 4096 * 6144 / t_f / 1e12, 1),
         "kernel": heal.heal_gemm_comp_variant(2048, 6144, 4096, 2)}
     del X, Wq, ah, al, ea, bh, eb, qf, sf, c, qu, su
-    # split in the GEMM prologue: the three Llama-3-8B projections at M = 2048 and at M = 16, FP32
-    # activations split inside the GEMM (row exponents + heal_gemm_comp_f32a) against the split pass + the
-    # GEMM on its parts
     for M in (2048, 16):
         ops = []
-        for K, N in ((4096, 4096), (4096, 14336), (14336, 4096)):
+        for K, N in workloads.LLAMA3_8B_KN:
             X = dev(workloads.llama_activations(M, K, seed=8))
             W = dev(workloads.llama_weights_bf16(N, K, seed=8).view(np.int16)).view(torch.bfloat16)
             bh, _, eb = heal.heal_split(W, residual=False)
             ah, al, ea = heal.heal_split(X)
             c = heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
             ops.append((X, bh, eb, ah, al, ea, c, heal.heal_row_exponents(X)))
+
         def split_then_gemm():
             for X, bh, eb, ah, al, ea, c, _ in ops:
                 heal.heal_split(X, hi=ah, lo=al, exps=ea)
                 heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
+
         def split_in_prologue():
             for X, bh, eb, _, _, _, c, e2 in ops:
                 heal.heal_row_exponents(X, exps=e2)
@@ -675,14 +808,11 @@ def other_rows(heal, workloads, dev):
             t_u = min(t_u, time_fn(split_then_gemm, 10))
         rows[f"split_in_prologue_{M}_llama3_8b_3_shapes"] = {"us": round(t_f * 1e6, 2),
                                                              "split_then_gemm_us": round(t_u * 1e6, 2)}
-        del ops, X, W, bh, eb, ah, al, ea, c
+        del ops
     torch.cuda.empty_cache()
-    # vendor library at equal matrix work: hipBLASLt (torch.matmul, FP16 in, FP32 accumulation inside) on
-    # [M, 2K] x [2K, N] issues the same 16-bit MFMA work as the P = 2 compensated GEMM of each M = 2048 Llama
-    # shape; timed in turn with ours, best of 3 (operands contiguous, no transposed views)
     t_ours = t_blas = 0.0
     pairs = {}
-    for K, N in ((4096, 4096), (4096, 14336), (14336, 4096)):
+    for K, N in workloads.LLAMA3_8B_KN:
         X = dev(workloads.llama_activations(2048, K, seed=9))
         W = dev(workloads.llama_weights_bf16(N, K, seed=9).view(np.int16)).view(torch.bfloat16)
         bh, _, eb = heal.heal_split(W, residual=False)
@@ -703,12 +833,9 @@ def other_rows(heal, workloads, dev):
         "us": round(t_blas * 1e6, 2), "compensated_gemm_us": round(t_ours * 1e6, 2),
         "compensated_over_hipblaslt_time": round(t_ours / t_blas, 3), "per_shape_ours_hipblaslt_us": pairs}
     torch.cuda.empty_cache()
-    # medium M (decode batches, short prefills): heal_gemm_comp_splitk, which cuts K across workgroups where the
-    # plain launch leaves CUs idle, against heal_gemm_comp, on the three Llama projections; the weights rotate
-    # through four copies so they stream from HBM, best of 3 in turn
     per = {}
     t_plain = t_split = 0.0
-    for K, N in ((4096, 4096), (4096, 14336), (14336, 4096)):
+    for K, N in workloads.LLAMA3_8B_KN:
         W = dev(workloads.llama_weights_bf16(N, K, seed=10).view(np.int16)).view(torch.bfloat16)
         bh, _, eb = heal.heal_split(W, residual=False)
         copies = [bh] + [bh.clone() for _ in range(3)]
@@ -717,6 +844,7 @@ def other_rows(heal, workloads, dev):
             c = heal.heal_gemm_comp(ah, al, ea, bh, None, eb)
             need = heal.heal_gemm_comp_workspace_bytes(M, N, K, 2)
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+
             def rotate(fn):
                 def run():
                     for b_ in copies:
@@ -732,21 +860,116 @@ def other_rows(heal, workloads, dev):
             t_split += s_best
             per[f"{M}x{K}x{N}"] = {"slices": heal.heal_gemm_comp_splitk_slices(M, N, K, 2),
                                    "splitk_us": round(s_best * 1e6, 1), "plain_us": round(p_best * 1e6, 1)}
-        del W, bh, eb, copies, ah, al, ea, c, ws
+        del W, bh, eb, copies
     rows["gemm_splitk_medium_m_llama3_8b"] = {"us": round(t_split * 1e6, 1), "plain_us": round(t_plain * 1e6, 1),
                                               "per_shape": per}
     torch.cuda.empty_cache()
-    # config 5a: 8192^3 FP32 x FP32, rows scaled by 10^U(-3,3), P = 3
-    A, Bt = workloads.gemm_rowscaled(8192, 8192, 8192, seed=4)
-    ah, al, ea = heal.heal_split(dev(A))
-    bh, bl, eb = heal.heal_split(dev(Bt))
-    c = heal.heal_gemm_comp(ah, al, ea, bh, bl, eb)
-    t = time_fn(lambda: heal.heal_gemm_comp(ah, al, ea, bh, bl, eb, c=c), 5)
-    fl = 2.0 * 8192 ** 3
-    rows["gemm_8192cube_p3"] = {"us": round(t * 1e6, 1), "tflops_fp32eq": round(fl / t / 1e12, 1),
-                                "mfma_frac": round(3 * fl / t / 1e12 / PEAK_F16_TFLOPS, 4),
-                                "kernel": heal.heal_gemm_comp_variant(8192, 8192, 8192, 3)}
     return rows
+
+
+# ------------------------------------------------------------------------------------ counter-run programs
+def only(args, heal, workloads):
+    """A few launches of one workload and nothing else: the program a rocprofv3 counter run profiles."""
+    import torch
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    w = args.only
+    if w == "gemm8192":
+        _, copies, (ah, al, ea, bh, bl, eb, c) = gemm8192_inputs(heal, workloads, 1)
+        A, Bt = copies[0]
+        for _ in range(3):
+            heal.heal_split(A, hi=ah, lo=al, exps=ea)
+            heal.heal_split(Bt, hi=bh, lo=bl, exps=eb)
+            heal.heal_gemm_comp(ah, al, ea, bh, bl, eb, c=c)
+    elif w == "llama":
+        row_llama(heal, workloads, dev, 3, False, steps=2)
+    elif w == "split":
+        x = dev(workloads.llama_activations(2048, 14336, seed=1))
+        hi, lo, e = heal.heal_split(x)
+        for _ in range(4):
+            heal.heal_split(x, hi=hi, lo=lo, exps=e)
+    elif w == "quant":
+        Q, K, V = workloads.qkv_fp32(1, 4096, 32, 128, seed=2)
+        fused = dev(np.concatenate([Q[0], K[0], V[0]], axis=1))
+        fq, fs = heal.heal_qkv_quant_i16(fused)
+        for _ in range(4):
+            heal.heal_qkv_quant_i16(fused, q=fq, scale=fs)
+    elif w == "prefill":
+        Q, K, V = workloads.qkv_fp32(1, 4096, 32, 128, seed=2)
+        (q, qs), (k, ks), (v, vs) = (heal.heal_qkv_quant_i16(dev(t[0])) for t in (Q, K, V))
+        a = (q[None], qs[None], k[None], ks[None], v[None], vs[None])
+        out = heal.heal_attn_dual_fp16(*a, causal=True)
+        for _ in range(4):
+            heal.heal_attn_dual_fp16(*a, causal=True, out=out)
+    else:
+        B, L, Hq, Hkv = 64, 8192, 32, 8
+        k, ks = workloads.int16_cache_device(B, L, Hkv, 128, seed=3)
+        v, vs = workloads.int16_cache_device(B, L, Hkv, 128, seed=4)
+        q, qs = [dev(a) for a in workloads.int16_cache_host(B, 1, Hq, 128, seed=5)]
+        out = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device="cuda")
+        ws = torch.empty(heal.heal_attn_workspace_bytes(heal.make_attn_args(q, qs, k, ks, v, vs, out, True)),
+                         dtype=torch.uint8, device="cuda")
+        for _ in range(5):
+            heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"{w}: done", flush=True)
+
+
+def main():
+    args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.copy_mib, args.title, args.program)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the hot path shards without communication and multi-GPU runs are not part of it",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import error_compensated_gemm_amd as heal
+    import workloads
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    heal.load()
+    torch.cuda.set_device(0)
+    if args.only:
+        only(args, heal, workloads)
+        return
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    log("headline: 8192^3 FP32 x FP32, split + split + GEMM")
+    result, host0, bufs, first = headline(args, heal, workloads)
+    log(f"headline: {result['value']} TFLOP/s, {result['ms_per_step']} ms per step")
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline_gemm8192(args, heal, host0, bufs, first)
+        result["error_vs_fp64"] = result["cpu_baseline"]["gpu_err_vs_fp64_on_sample"]
+        log(f"cpu baseline: {result['cpu_baseline']['sample']}")
+    del bufs, first
+    torch.cuda.empty_cache()
+    if not args.no_rows:
+        log("row: 256^3 configuration")
+        rows = {"config1_gemm_256cube_p3_and_quant_tile": row_config1(heal, workloads, dev, not args.no_cpu)}
+        log("row: Llama-3-8B linear layers")
+        rows["config2_llama3_8b_linear"] = row_llama(heal, workloads, dev, args.rotate, not args.no_cpu)
+        torch.cuda.empty_cache()
+        log("rows: split, quantiser")
+        sq, (Q, K, V, qkv) = row_split_quant(heal, workloads, dev)
+        rows.update(sq)
+        log("rows: prefill")
+        rows.update(row_prefill(heal, (Q, K, V), qkv, not args.no_cpu))
+        del qkv
+        torch.cuda.empty_cache()
+        log("rows: decode")
+        rows.update(row_decode(heal, workloads, dev, not args.no_cpu))
+        torch.cuda.empty_cache()
+        log("rows: fused variants, vendor GEMM, split-K")
+        rows.update(row_fused_and_vendor(heal, workloads, dev))
+        result["rows"] = rows
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
