@@ -3,6 +3,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,9 +24,24 @@ HIPCC_FLAGS = [
     # IEEE fp32 division and square root: the INT16 quantiser's scale and codes depend on it
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",
-    # no packed-FP32 VALU instructions
+    # no packed-FP32 VALU instructions (the device pass honours this; the host pass warns that it does not know
+    # the feature, which is harmless); packed_fp32_check() verifies the result
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep the gfx950 assembly of each source next to its object, for that check
+    "-save-temps=obj",
 ]
+PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
+
+
+def packed_fp32_check(obj: str) -> None:
+    """Refuse a build whose gfx950 assembly holds a packed-FP32 VALU instruction."""
+    asm = obj[:-2] + "-hip-amdgcn-amd-amdhsa-gfx950.s"
+    if not os.path.exists(asm):
+        raise RuntimeError(f"no device assembly for {os.path.basename(obj)} ({asm})")
+    with open(asm) as f:
+        hits = [l.strip() for l in f if PACKED_FP32.search(l)]
+    if hits:
+        raise RuntimeError(f"{os.path.basename(asm)}: {len(hits)} packed-FP32 instructions, e.g. {hits[0]}")
 
 
 def hipcc() -> str:
@@ -46,6 +62,7 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
         if verbose and r.stderr.strip():
             print(r.stderr[-2000:])
+        packed_fp32_check(obj)
         return obj
 
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + len(GLUE_SOURCES)) as ex:

@@ -560,7 +560,12 @@ constexpr int kSkWaves = 8;
 // just before the MFMAs, so the prefetch never waits on them.
 // SPLITK: as for gemm_comp_kernel, slice blockIdx.y of K into slice blockIdx.y of the unscaled partials C.
 // AEXP (FP32 A, at most 16 rows): A's row exponents are derived in the kernel instead of read from ea.
-template <int PART, int MT, int NC, bool ALO, bool BLO, bool AF32 = false, bool SPLITK = false, bool AEXP = false>
+// ALDS (FP32 A, at most 16 rows, 2 M (ceil(K / 8) + 1) 16-byte chunks of dynamic LDS): the workgroup splits all of
+// A once into FP16 hi and lo planes in LDS, with the same operations as split8, and the K loop reads its A
+// fragments from there.  The loop then carries no split arithmetic between a wait for B and the next B loads,
+// which otherwise leaves the wavefront with one group of B in flight for as long as the split takes.
+template <int PART, int MT, int NC, bool ALO, bool BLO, bool AF32 = false, bool SPLITK = false, bool AEXP = false,
+          bool ALDS = false>
 __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
     const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
@@ -568,6 +573,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     int64_t ldc, const float* __restrict__ af = nullptr, int64_t kslice = 0) {
   static_assert(!AF32 || (ALO && PART == HEAL_F16), "FP32 A: FP16 parts, both A parts");
   static_assert(!SPLITK || !AF32, "split K: 16-bit parts");
+  static_assert(!ALDS || (AF32 && MT == 1), "A split into LDS: FP32 A, at most 16 rows");
   if constexpr (SPLITK) {
     const int64_t k0 = (int64_t)blockIdx.y * kslice;
     K = K - k0 < kslice ? K - k0 : kslice;
@@ -580,6 +586,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     eb = nullptr;
   }
   __shared__ float red[kSkWaves][MT * NC][4][64];
+  extern __shared__ uint4 a_lds[];  // ALDS: hi plane [M][Kc + 1] then lo plane, Kc = ceil(K / 8) chunks
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cl = lane & 15, kg = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16 * NC;
@@ -589,8 +596,8 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   // (16 KB per row at K = 4096, from L2), in place of a launch of its own before the GEMM.
   __shared__ float amax_s[AEXP ? kSkWaves : 1][16];
   __shared__ int aexp_s[AEXP ? 16 : 1];
-  if constexpr (AEXP) {
-    static_assert(AF32 && MT == 1 && !SPLITK, "derived row exponents: FP32 A, at most 16 rows");
+  static_assert(!AEXP || (AF32 && MT == 1 && !SPLITK), "derived row exponents: FP32 A, at most 16 rows");
+  if constexpr (AEXP && !ALDS) {
     const int64_t nch = K >> 2;
     for (int r = 0; r < M; ++r) {
       const float* xr = af + r * lda;
@@ -644,6 +651,93 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   const int64_t nsteps = (K + 31) / 32, nfull = K / 32;
   const int64_t klast = ((K + 7) / 8 - 1) * 8;
   const int64_t s0 = nsteps * wave / kSkWaves, s1 = nsteps * (wave + 1) / kSkWaves;
+  // ALDS: chunk c (8 values from column 8 c) of row r of A's hi plane at a_lds[r * rs + c], of its lo plane at
+  // a_lds[M * rs + r * rs + c], c < Kc; the row stride rs = Kc + 1 chunks puts the 16 rows a fragment read
+  // touches in distinct banks.  Columns at or past K in the last chunk hold zeros; the partial last K step
+  // reads no chunk at or past Kc.
+  const int64_t Kc = (K + 7) / 8, rs = Kc + 1;
+  // ALDS: the first group of B is requested before A is touched (it does not depend on A), then A is read
+  // once into registers (at most 4 chunks of 8 values per thread: M (Kc + 1) <= 2048), the row maxima meet in
+  // LDS by integer max on the magnitudes' bit patterns (order-free, so the same value on every run), and the
+  // chunks are split from the registers into the LDS planes.
+  constexpr int U0 = (MT * NC) >= 4 ? 1 : 4 / (MT * NC);
+  uint4 b_first[U0][NC], bl_first[U0][BLO ? NC : 1];
+  const bool first_full = s0 + U0 <= (s1 < nfull ? s1 : nfull);
+  if constexpr (ALDS) {
+    if (first_full) {
+#pragma unroll
+      for (int u = 0; u < U0; ++u)
+#pragma unroll
+        for (int nc = 0; nc < NC; ++nc) {
+          const int64_t k = (s0 + u) * 32 + 8 * kg;
+          b_first[u][nc] = load_chunk(brow[nc], k, klast);
+          if constexpr (BLO) bl_first[u][nc] = load_chunk(blrow[nc], k, klast);
+        }
+    }
+    __shared__ uint32_t amax_u[ALDS && AEXP ? 16 : 1];
+    if constexpr (AEXP) {
+      if (threadIdx.x < 16) amax_u[threadIdx.x] = 0u;
+    }
+    constexpr int CPT = 2048 / (64 * kSkWaves);
+    uint4 x0[CPT], x1[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int64_t idx = threadIdx.x + 64 * kSkWaves * i;
+      x0[i] = x1[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (idx < M * Kc) {
+        const int64_t r = idx / Kc, k = 8 * (idx - r * Kc);
+        const float* xr = af + r * lda;
+        if (k + 8 <= K) {
+          x0[i] = *reinterpret_cast<const uint4*>(xr + k);
+          x1[i] = *reinterpret_cast<const uint4*>(xr + k + 4);
+        } else {
+          uint32_t w[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = k + j < K ? __builtin_bit_cast(uint32_t, xr[k + j]) : 0u;
+          x0[i] = make_uint4(w[0], w[1], w[2], w[3]);
+          x1[i] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+      }
+    }
+    if constexpr (AEXP) {
+      __syncthreads();  // amax_u cleared
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int64_t idx = threadIdx.x + 64 * kSkWaves * i;
+        if (idx < M * Kc) {
+          // magnitudes' bit patterns: the integer order of non-negative floats is their numeric order
+          const uint32_t w[8] = {x0[i].x, x0[i].y, x0[i].z, x0[i].w, x1[i].x, x1[i].y, x1[i].z, x1[i].w};
+          uint32_t m = 0u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m = max(m, w[j] & 0x7FFFFFFFu);
+          atomicMax(&amax_u[idx / Kc], m);
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x < M) {
+        const float m = __builtin_bit_cast(float, amax_u[threadIdx.x]);
+        aexp_s[threadIdx.x] = m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;  // 14 - ilogb(m)
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int64_t idx = threadIdx.x + 64 * kSkWaves * i;
+      if (idx < M * Kc) {
+        const int64_t r = idx / Kc, c = idx - r * Kc;
+        int e;
+        if constexpr (AEXP)
+          e = aexp_s[r];
+        else
+          e = ea[r];
+        const Split8 sp = split8(x0[i], x1[i], e);
+        a_lds[r * rs + c] = sp.hi;
+        a_lds[M * rs + r * rs + c] = sp.lo;
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t a_row_lds = (int64_t)(cl < M ? cl : M - 1) * rs;  // ALDS: this lane's A row
   f32x4 acc[MT][NC];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -654,7 +748,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     uint4 a[MT], a2[ALO ? MT : 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      if constexpr (AF32) {
+      if constexpr (AF32 && !ALDS) {
         const Split8 sp = split8(a_in[mt], a2_in[mt], ea_l[mt]);  // raw FP32 bits -> hi, lo
         a[mt] = sp.hi;
         a2[mt] = sp.lo;
@@ -702,7 +796,11 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      if constexpr (AF32) {
+      if constexpr (ALDS) {  // the split parts; a chunk wholly past K reads the last one, cleared like B's
+        const int64_t c = (k >> 3) < Kc ? (k >> 3) : Kc - 1;
+        a[mt] = mask_chunk(a_lds[a_row_lds + c], K - k);
+        a2[mt] = mask_chunk(a_lds[M * rs + a_row_lds + c], K - k);
+      } else if constexpr (AF32) {
         const Raw8 r = load_af_tail(mt, k);
         a[mt] = r.x0;
         a2[mt] = r.x1;
@@ -718,7 +816,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   // before the current group's MFMAs, so two groups of B (the HBM stream) are in flight per wavefront.  The
   // prefetch address is clamped to the last full group instead of branching (a conditional load block
   // makes the compiler wait for every outstanding load at its boundary).
-  constexpr int U = (MT * NC) >= 4 ? 1 : 4 / (MT * NC);
+  constexpr int U = U0;
   struct Grp {
     uint4 b[U][NC], b2[U][BLO ? NC : 1], a[U][MT], a2[U][ALO ? MT : 1];
   };
@@ -733,7 +831,10 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if constexpr (AF32) {
+        if constexpr (ALDS) {
+          g.a[u][mt] = a_lds[a_row_lds + (k >> 3)];
+          g.a2[u][mt] = a_lds[M * rs + a_row_lds + (k >> 3)];
+        } else if constexpr (AF32) {
           const Raw8 r = load_af(mt, k);
           g.a[u][mt] = r.x0;
           g.a2[u][mt] = r.x1;
@@ -748,11 +849,31 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) mma1(g.a[u], g.a2[u], g.b[u], g.b2[u]);
   };
+  // ALDS: the A fragments of a group from the LDS planes (its B already requested)
+  auto load_a_lds = [&](Grp& g, int64_t s) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (s + u) * 32 + 8 * kg;
+      g.a[u][0] = a_lds[a_row_lds + (k >> 3)];
+      g.a2[u][0] = a_lds[M * rs + a_row_lds + (k >> 3)];
+    }
+  };
   const int64_t ng = s1f > s0 ? (s1f - s0) / U : 0;  // full groups of this wavefront
   const int64_t s_last = s0 + (ng - 1) * U;           // first step of the last full group
   if (ng > 0) {
     Grp g0, g1;
-    load(g0, s0);
+    if constexpr (ALDS) {  // the first group's B was requested before A's split
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int nc = 0; nc < NC; ++nc) {
+          g0.b[u][nc] = b_first[u][nc];
+          if constexpr (BLO) g0.b2[u][nc] = bl_first[u][nc];
+        }
+      load_a_lds(g0, s0);
+    } else {
+      load(g0, s0);
+    }
     int64_t gi = 0;
     for (; gi + 1 < ng; gi += 2) {
       load(g1, s0 + (gi + 1) * U);
@@ -1005,6 +1126,30 @@ namespace {
 // split does not fit, runs on 256 x 128 tiles with identical output.)
 // BLO: whether this (MT, NC) is instantiated with B's low part; the wide 64-row ones are not (their
 // registers would spill), and the dispatcher sends three-product calls at M > 32 to NC = 1.
+// LDS bytes of A's split hi and lo planes for the ALDS skinny kernel, or 0 when they exceed 64 KB (the kernel
+// then splits A at each step): M (<= 16) rows of ceil(K / 8) + 1 chunks of 16 bytes, two planes.
+size_t skinny_alds_bytes(int64_t M, int64_t K) {
+  if (M < 1 || M > 16) return 0;
+  const int64_t b = 2 * M * ((K + 7) / 8 + 1) * 16;
+  return b <= 65536 ? (size_t)b : 0;
+}
+
+// at most 16 rows: exponents given (AEXP false) or derived; A split per step, or once into LDS (ALDS)
+template <int NC, bool BLO, bool AEXP>
+hipError_t launch_skinny_f32a_m16(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,
+                                  const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
+                                  int64_t ldc, dim3 grid, dim3 block, hipStream_t stream) {
+  const uint16_t* const none = nullptr;
+  const size_t lds = skinny_alds_bytes(M, K);
+  if (lds)
+    hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, 1, NC, true, BLO, true, false, AEXP, true>), grid, block,
+                       (unsigned)lds, stream, M, N, K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af, (int64_t)0);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, 1, NC, true, BLO, true, false, AEXP, false>), grid, block, 0,
+                       stream, M, N, K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af, (int64_t)0);
+  return hipGetLastError();
+}
+
 template <int MT, int NC, bool BLO = true>
 hipError_t launch_skinny_f32a_nc(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,
                                  const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
@@ -1012,36 +1157,35 @@ hipError_t launch_skinny_f32a_nc(int64_t M, int64_t N, int64_t K, const float* a
   if (!grid_fits((N + 16 * NC - 1) / (16 * NC), 64 * kSkWaves)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((N + 16 * NC - 1) / (16 * NC))), block(64 * kSkWaves);
   const uint16_t* const none = nullptr;
-  if (!ea) {  // row exponents derived in the kernel: at most 16 rows
-    if constexpr (MT == 1) {
-      if constexpr (BLO) {
-        if (bl) {
-          hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, 1, NC, true, true, true, false, true>), grid, block, 0,
-                             stream, M, N, K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af, (int64_t)0);
-          return hipGetLastError();
-        }
-      } else if (bl) {
-        return hipErrorInvalidValue;
-      }
-      hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, 1, NC, true, false, true, false, true>), grid, block, 0,
-                         stream, M, N, K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af, (int64_t)0);
-      return hipGetLastError();
-    } else {
-      return hipErrorInvalidValue;
-    }
+  if constexpr (!BLO) {
+    if (bl) return hipErrorInvalidValue;
   }
-  if constexpr (BLO) {
+  if constexpr (MT == 1) {
     if (bl) {
-      hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, true, true>), grid, block, 0, stream, M, N,
-                         K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
-      return hipGetLastError();
+      if constexpr (BLO) {
+        return ea ? launch_skinny_f32a_m16<NC, true, false>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, grid, block,
+                                                            stream)
+                  : launch_skinny_f32a_m16<NC, true, true>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, grid, block,
+                                                           stream);
+      }
     }
-  } else if (bl) {
-    return hipErrorInvalidValue;
+    return ea ? launch_skinny_f32a_m16<NC, false, false>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, grid, block,
+                                                         stream)
+              : launch_skinny_f32a_m16<NC, false, true>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, grid, block,
+                                                        stream);
+  } else {
+    if (!ea) return hipErrorInvalidValue;  // derived exponents: at most 16 rows
+    if constexpr (BLO) {
+      if (bl) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, true, true>), grid, block, 0, stream, M, N,
+                           K, none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, false, true>), grid, block, 0, stream, M, N, K,
+                       none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, MT, NC, true, false, true>), grid, block, 0, stream, M, N, K,
-                     none, none, ea, lda, bh, bl, eb, ldb, c, ldc, af);
-  return hipGetLastError();
 }
 
 hipError_t launch_skinny_f32a(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,

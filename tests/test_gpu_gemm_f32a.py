@@ -42,6 +42,7 @@ def _both(heal, A, Bt, b_residual):
     (1, 300, 77, 2), (16, 7300, 130, 2), (30, 7300, 301, 3), (64, 1000, 1001, 2), (5, 14350, 64, 3),   # skinny
     (30, 14390, 70, 2), (30, 14390, 70, 3), (50, 7300, 130, 2), (64, 14390, 77, 2),                     # NC 2, 4
     (64, 14390, 77, 3),                           # three products at 64 rows: NC 1 against split + GEMM's NC 4
+    (16, 777, 1016, 2), (16, 777, 1024, 3),       # A's split planes just fit the 64 KB of LDS / just do not
     (100, 300, 1003, 2), (129, 257, 999, 3),                                                            # 128 x 128
     (2048, 4096, 258, 2),                                                                               # 128 x 256
     (2048, 4096, 130, 3),                                                                               # 256 x 128
@@ -106,7 +107,8 @@ def test_llama_linear_fused(heal, M, K, N):
 
 
 @pytest.mark.parametrize("M,N,K,P", [(1, 300, 77, 2), (1, 14336, 4096, 2), (1, 4096, 14336, 2), (3, 700, 1001, 3),
-                                     (16, 4096, 4096, 2), (16, 14350, 130, 3), (5, 300, 3, 2), (4, 7300, 64, 2)])
+                                     (16, 4096, 4096, 2), (16, 14350, 130, 3), (5, 300, 3, 2), (4, 7300, 64, 2),
+                                     (16, 777, 1016, 3), (16, 777, 1024, 2), (2, 3000, 8184, 2)])
 def test_derived_row_exponents(heal, M, N, K, P):
     """a_exp = None (at most 16 rows): the kernel derives the row exponents itself, so C is bit for bit what the
     exponents of heal_row_exponents give.  Rows with no nonzero value, a subnormal maximum and a value near
