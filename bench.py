@@ -64,6 +64,7 @@ def parse():
 # ------------------------------------------------------------------ HBM traffic from stored counters
 KERNEL_SOURCES = (("gemm_comp_kernel", "gemm_comp.hip"), ("gemm_skinny_kernel", "gemm_comp.hip"),
                   ("splitk_reduce_kernel", "gemm_comp.hip"), ("split_rows_kernel", "split_quant.hip"),
+                  ("split_row_regs_kernel", "split_quant.hip"),
                   ("quant_i16_kernel", "split_quant.hip"), ("unpack_i16_kernel", "split_quant.hip"),
                   ("attn_", "attn.hip"))
 
@@ -89,8 +90,8 @@ def kernel_source(sym):
 
 def short_symbol(name):
     """'void heal::(anonymous namespace)::gemm_comp_kernel<2, 256, ...>(long, ...)' -> 'gemm_comp_kernel<2, 256, ...>'"""
-    n = name.replace("void ", "")
-    head = n.split("(")[0] if "<" not in n.split("(")[0] else n[:n.index(">") + 1]
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    head = n[:n.index(">") + 1] if "<" in n.split("(")[0] else n.split("(")[0]
     return head.split("::")[-1].strip()
 
 
@@ -361,7 +362,7 @@ def headline(args, heal, workloads):
     parts = {
         "split_a_us": round(durs["split_a"] * 1e6, 1), "split_b_us": round(durs["split_b"] * 1e6, 1),
         "split_gbs": round(split_bytes / ((durs["split_a"] + durs["split_b"]) / 2) / 1e9, 1),
-        "split_symbol": "split_rows_kernel<float, true, false, false>",
+        "split_symbol": "split_row_regs_kernel<2, true, 4>",
         "gemm_us": round(durs["gemm"] * 1e6, 1),
         "gemm_tflops_fp32eq": round(flop / durs["gemm"] / 1e12, 1),
     }
@@ -601,7 +602,7 @@ def row_split_quant(heal, workloads, dev):
     hi, lo, e = heal.heal_split(x)
     t = time_fn(lambda: heal.heal_split(x, hi=hi, lo=lo, exps=e), 20)
     gbs = x.numel() * 8 / t / 1e9
-    tr = stored_traffic("split_rows_kernel<float, true, false, false>")
+    tr = stored_traffic("split_row_regs_kernel<2, true, 8>")
     rows["a1_split_2048x14336"] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                                    "algorithmic_bytes": x.numel() * 8 + 2048 * 4,
                                    "traffic": None if tr is None else tr["bytes_per_launch"]}

@@ -176,6 +176,80 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__
   }
 }
 
+// The same split with each row held in registers: one workgroup of 256 threads per row of 2048 < cols <= 2048 NCH
+// FP32 values (16-byte aligned rows, prescale on), each thread holding NCH chunks of 8.  The row is read once:
+// with many rows in flight the two-pass kernel's second read of a long row misses L2 (its FETCH_SIZE is twice
+// the input at 8192 and 14336 columns).  The operations per element are the two-pass kernel's, so the bits are.
+template <int PART, bool RESID, int NCH>
+__global__ __launch_bounds__(256) void split_row_regs_kernel(const float* __restrict__ x, int64_t cols, int64_t ld_x,
+                                                             uint16_t* __restrict__ hi, uint16_t* __restrict__ lo,
+                                                             int64_t ld_part, int32_t* __restrict__ exps) {
+  __shared__ float wmax[4];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * ld_x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nvec = cols >> 3;
+  float v[NCH][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int64_t c = tid + 256 * j;
+    if (c < nvec) {
+      load8(xr + (c << 3), v[j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
+  }
+  const int64_t tc = (nvec << 3) + tid;  // the last cols % 8 values, one per thread
+  const float tv = tc < cols ? xr[tc] : 0.0f;
+  amax = fmaxf(amax, fabsf(tv));
+  amax = wave_max(amax);
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int e = amax > 0.0f ? 14 - ilogb_pos(amax) : 0;
+  if (tid == 0) exps[row] = e;
+  uint16_t* hr = hi + row * ld_part;
+  uint16_t* lr = RESID ? lo + row * ld_part : nullptr;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int64_t c = tid + 256 * j;
+    if (c < nvec) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t h2[2], l2[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float xs = __builtin_amdgcn_ldexpf(v[j][2 * i + k], e);
+          float hb;
+          h2[k] = round16<PART>(xs, &hb);
+          if constexpr (RESID) {
+            float lb;
+            l2[k] = round16<PART>(xs - hb, &lb);
+          }
+        }
+        hw[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+        if constexpr (RESID) lw[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
+      }
+      *reinterpret_cast<uint4*>(hr + (c << 3)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      if constexpr (RESID) *reinterpret_cast<uint4*>(lr + (c << 3)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+  }
+  if (tc < cols) {
+    const float xs = __builtin_amdgcn_ldexpf(tv, e);
+    float hb;
+    hr[tc] = round16<PART>(xs, &hb);
+    if constexpr (RESID) {
+      float lb;
+      lr[tc] = round16<PART>(xs - hb, &lb);
+    }
+  }
+}
+
 // Dual-FP16 pair of one INT16 value under each reading; every value is an integer (or an integer times
 // 2^10) of at most 11 significant bits, so each conversion to FP16 is exact except the one that defines the
 // float-float hi (round to nearest even).
@@ -360,6 +434,26 @@ hipError_t launch_split_any(const TIn* x, int64_t rows, int64_t cols, int64_t ld
   uint16_t* h = (uint16_t*)hi;
   uint16_t* l = (uint16_t*)lo;
   const bool pre = exps != nullptr, res = lo != nullptr;
+  if constexpr (sizeof(TIn) == 4) {  // FP32 rows of 2049 .. 16384 values: one read, the row in registers
+    if (vec && pre && cols > 2048 && cols <= 16384 && grid_fits(rows, 256)) {
+      const int nch = (int)(((cols >> 3) + 255) / 256);
+#define HEAL_SPLIT_REGS(PART, RES, NCH)                                                                      \
+  if (part == PART && res == RES && nch <= NCH) {                                                             \
+    hipLaunchKernelGGL((split_row_regs_kernel<PART, RES, NCH>), dim3((unsigned)rows), block, 0, stream,       \
+                       (const float*)x, cols, ld_x, h, l, ld_part, exps);                                     \
+    return hipGetLastError();                                                                                 \
+  }
+      HEAL_SPLIT_REGS(HEAL_F16, true, 4)
+      HEAL_SPLIT_REGS(HEAL_F16, true, 8)
+      HEAL_SPLIT_REGS(HEAL_F16, false, 4)
+      HEAL_SPLIT_REGS(HEAL_F16, false, 8)
+      HEAL_SPLIT_REGS(HEAL_BF16, true, 4)
+      HEAL_SPLIT_REGS(HEAL_BF16, true, 8)
+      HEAL_SPLIT_REGS(HEAL_BF16, false, 4)
+      HEAL_SPLIT_REGS(HEAL_BF16, false, 8)
+#undef HEAL_SPLIT_REGS
+    }
+  }
 #define HEAL_SPLIT_CASE(PART, PRE, RES)                                                                \
   if (part == PART && pre == PRE && res == RES) {                                                       \
     hipLaunchKernelGGL((split_rows_kernel<TIn, PART, PRE, RES>), grid, block, 0, stream, x, rows, cols, \

@@ -11,7 +11,9 @@ from gpu_util import banner, bits, dev, host
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 7), (5, 8), (17, 1000), (256, 256), (64, 14336), (2048, 4096)])
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 7), (5, 8), (17, 1000), (256, 256), (64, 14336), (2048, 4096),
+                                       # rows held in registers (2049 .. 16384 columns), ragged, and just past
+                                       (9, 2049), (7, 8195), (5, 16383), (4, 16384), (3, 16385)])
 def test_split_f32_f16_bit_exact(heal, rows, cols):
     banner(f"split f32->f16 {rows}x{cols}")
     rng = np.random.default_rng(rows * 1000 + cols)
@@ -31,19 +33,20 @@ def test_split_f32_f16_bit_exact(heal, rows, cols):
 def test_split_modes(heal):
     banner("split modes: no prescale, no residual, bf16 parts, bf16 input")
     rng = np.random.default_rng(1)
-    x = (rng.standard_normal((37, 203)) * 3).astype(np.float32)
-    x[0, 0] = 7e4  # overflows fp16 without the prescale
-    for part, p in (("f16", oracle.F16), ("bf16", oracle.BF16)):
-        for pre in (True, False):
-            for res in (True, False):
-                hi, lo, e = heal.heal_split(dev(x), part=part, prescale=pre, residual=res)
-                torch.cuda.synchronize()
-                ohi, olo, oe = oracle.split_f32(x, part=p, prescale=pre, residual=res)
-                assert np.array_equal(bits(hi), ohi), (part, pre, res)
-                if res:
-                    assert np.array_equal(bits(lo), olo), (part, pre, res)
-                if pre:
-                    assert np.array_equal(host(e), oe)
+    for cols in (203, 4100):  # the two-pass kernel and the row-in-registers one
+        x = (rng.standard_normal((37, cols)) * 3).astype(np.float32)
+        x[0, 0] = 7e4  # overflows fp16 without the prescale
+        for part, p in (("f16", oracle.F16), ("bf16", oracle.BF16)):
+            for pre in (True, False):
+                for res in (True, False):
+                    hi, lo, e = heal.heal_split(dev(x), part=part, prescale=pre, residual=res)
+                    torch.cuda.synchronize()
+                    ohi, olo, oe = oracle.split_f32(x, part=p, prescale=pre, residual=res)
+                    assert np.array_equal(bits(hi), ohi), (cols, part, pre, res)
+                    if res:
+                        assert np.array_equal(bits(lo), olo), (cols, part, pre, res)
+                    if pre:
+                        assert np.array_equal(host(e), oe)
     W = workloads.llama_weights_bf16(96, 4104, seed=5)  # ragged cols
     wt = dev(W.view(np.int16)).view(torch.bfloat16)
     hi, lo, e = heal.heal_split(wt, residual=False)
