@@ -77,5 +77,47 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_DIR = os.path.join(OBJ, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libheal_asan.so")
+
+
+def asan_runtime() -> str | None:
+    """The clang AddressSanitizer runtime that an -fsanitize=address host build links against, or None."""
+    import glob
+
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_asan() -> str:
+    """libheal with its HOST code built under AddressSanitizer (the device code as usual), for running the
+    argument validation of the C ABI under ASan on the CPU.  Rebuilt only when a source is newer."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    srcs = [os.path.join(CSRC, f) for f in SOURCES] + [os.path.join(CSRC, "heal_internal.h"),
+                                                      os.path.join(HERE, "..", "include", "heal.h")]
+    if os.path.exists(ASAN_LIB) and os.path.getmtime(ASAN_LIB) >= max(os.path.getmtime(f) for f in srcs):
+        return ASAN_LIB
+    flags = [f for f in HIPCC_FLAGS if f != "-save-temps=obj"] + ["-Xarch_host", "-fsanitize=address",
+                                                                  "-Xarch_host", "-fno-omit-frame-pointer"]
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(ASAN_DIR, src.replace(".hip", ".o"))
+        r = subprocess.run([hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj], capture_output=True,
+                           text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (asan) failed on {src}:\n{r.stderr[-4000:]}")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-shared-libasan", *objs, "-o", ASAN_LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed for the asan build:\n{r.stderr[-4000:]}")
+    os.replace(ASAN_LIB + ".tmp", ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

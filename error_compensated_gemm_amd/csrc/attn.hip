@@ -18,15 +18,16 @@
 //     rounding error) so that t - max keeps its precision for logits of any size; online softmax in
 //     base 2, FP32 running maximum and sum.  Prefill keeps u_ij = S_int * s_k,j as the pair and its maximum
 //     in the same units, and multiplies only the difference by the query's factor: t - m = cq (u - m_u).
-//   * P~ = p * (s_v,j * 2^E) with E = 14 - ilogb(max_j s_v,j) over the keys a workgroup reads, so P~ < 2^15
-//     and its FP16 split P~ = P~h + P~l (P~l = fp16(P~ - P~h), exact residual) keeps 22 bits;
+//   * P~ = p * (s_v,j * 2^E) with E = 14 - ilogb(max_j s_v,j) over the keys a workgroup reads (prefill: 8 less,
+//     since its lazily moved maximum lets p reach 2^8), so P~ < 2^15 and its FP16 split P~ = P~h + P~l
+//     (P~l = fp16(P~ - P~h), exact residual) keeps 22 bits;
 //     O += P~h.H + P~h.L + P~l.H + P~l.L (4 products, one FP32 accumulator); O = acc * 2^-E / l.
 //
 // Prefill (q_len > 1): flash-style forward.  A workgroup of 8 wavefronts owns 256 queries of one
-// (batch, head); each wavefront owns 32.  K/V tiles of 64 keys arrive in LDS as raw INT16 rows by
-// direct-to-LDS transfers (double-buffered, one barrier per tile); K fragments are 16-byte LDS reads and
-// the V^T operand comes from the same [key][d] rows through gfx950's transposing LDS read, both unpacked
-// into their FP16 halves in registers.
+// (batch, head); each wavefront owns 32.  K/V tiles of 32 keys (PF_BKV) arrive in LDS as raw INT16 rows by
+// direct-to-LDS transfers; the workgroup unpacks each tile once into FP16 hi / lo planes in LDS while the
+// previous tile is multiplied (two raw stages and two plane stages); K fragments are 16-byte LDS reads and the
+// V^T operand comes from the V planes through gfx950's transposing LDS read.
 // Each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16_f16, so the 16 scores a lane holds all
 // belong to ONE query: the softmax maximum/sum are lane-local plus one exchange with lane ^ 32.  The same
 // registers, in MFMA order, are the P^T operand of O^T = V^T P^T, so P never leaves registers.

@@ -12,8 +12,10 @@
 //
 // Layout of the work: one 64-lane wavefront per matrix row (split) or one 32-lane half-wave per
 // (token, head) row (quantise), 16-byte vector loads and stores, the row maximum reduced with cross-lane
-// shuffles, no atomics (only the column calibration meets its wavefronts in LDS).  Each pass reads every input byte once from HBM (the split's second
-// read of a row hits the cache it was just read into) and writes every output byte once.
+// shuffles, no atomics (only the column calibration meets its wavefronts in LDS).  Rows of 2049 to 16384 FP32
+// values are split by one workgroup per row with the row held in registers, so every input byte is read once;
+// narrower rows take the two-pass wavefront-per-row kernel, whose second read of a row hits L2.  Every output
+// byte is written once.
 #include "heal_internal.h"
 
 namespace heal {
@@ -32,8 +34,6 @@ __device__ __forceinline__ float halfwave_max(float v) {
   return v;
 }
 
-// ilogb of a positive finite float (subnormals included): v_frexp_exp gives e with x = m * 2^e,
-// m in [0.5, 1).
 // Nontemporal (streaming) stores for outputs that this kernel never reads back.  On the INT16 quantiser they
 // took one launch over 4096 tokens x 96 heads x 128 from 69 to 60 us, the plain device-copy rate; the same
 // hint on the loads gained nothing and, combined with it, lost the gain.
@@ -45,6 +45,8 @@ __device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
   __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
 }
 
+// ilogb of a positive finite float (subnormals included): v_frexp_exp gives e with x = m * 2^e,
+// m in [0.5, 1).
 __device__ __forceinline__ int ilogb_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
 
 // round-to-nearest-even into the 16-bit part type; returns the bit pattern and the value back in fp32
