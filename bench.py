@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
     ap.add_argument("--cpu-rows", type=int, default=3072,
                     help="rows of the 8192^3 output the FP64 oracle recomputes (3072: about 10 s on 16 threads)")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 32-layer decoder-stack row (about a minute; its FP64 reference needs ~70 GB of host "
+                         "memory)")
     ap.add_argument("--only", choices=("gemm8192", "llama", "split", "quant", "prefill", "decode"),
                     help="only run a few launches of that workload (the program a counter run profiles)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
@@ -868,6 +871,37 @@ def row_fused_and_vendor(heal, workloads, dev):
     return rows
 
 
+def row_stack_with_cpu_baseline(timeout_s=900):
+    """The model-level configuration: a 32-layer Llama-style stack (d 4096, 32/8 heads, FFN 14336, vocabulary 128256,
+    random bf16 weights, 512-token prompt, 64 greedy steps) run with the HEAL kernels and in plain bf16, both
+    against the FP64 forward, which is this row's oracle leg (timed on the host).  tests/llama_stack.py runs in a
+    child process so that its ~70 GB of host memory is returned when it ends."""
+    import subprocess
+
+    script = os.path.join(ROOT, "tests", "llama_stack.py")
+    t = time.perf_counter()
+    r = subprocess.run([sys.executable, script, "--full"], capture_output=True, text=True, timeout=timeout_s)
+    wall = time.perf_counter() - t
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    if r.returncode != 0 or not lines:
+        return {"error": f"exit {r.returncode}", "stderr_tail": r.stderr[-800:]}
+    res = json.loads(lines[-1])
+    keep = ("teacher_forced_agreement", "disagreeing_steps", "free_running_first_divergence",
+            "final_hidden_normwise_err_max", "final_hidden_normwise_err_mean", "decode_step_ms_median",
+            "decode_step_ms_hip_graph")
+    tokens = res["config"]["prompt"] + res["config"]["steps"]
+    return {
+        "config": res["config"], "seed": res["seed"], "fp64_top2_gap_min": res["fp64_top2_gap_min"],
+        "heal": {k: res["heal"][k] for k in keep if k in res["heal"]},
+        "bf16": {k: res["bf16"][k] for k in keep if k in res["bf16"]},
+        "wall_s": round(wall, 1),
+        "cpu_baseline": {"value": round(tokens / res["fp64_forward_s"], 3), "unit": "tokens/s",
+                         "cores": host_threads(), "kind": "oracle",
+                         "sample": f"the whole FP64 forward (numpy): {res['config']['prompt']}-token prompt then "
+                                   f"{res['config']['steps']} greedy steps, {res['fp64_forward_s']} s"},
+    }
+
+
 # ------------------------------------------------------------------------------------ counter-run programs
 def only(args, heal, workloads):
     """A few launches of one workload and nothing else: the program a rocprofv3 counter run profiles."""
@@ -969,6 +1003,10 @@ def main():
         torch.cuda.empty_cache()
         log("rows: fused variants, vendor GEMM, split-K")
         rows.update(row_fused_and_vendor(heal, workloads, dev))
+        if not args.no_stack and not args.no_cpu:
+            log("row: 32-layer decoder stack against its FP64 forward (about a minute)")
+            torch.cuda.empty_cache()
+            rows["config5b_llama_stack_32layer"] = row_stack_with_cpu_baseline()
         result["rows"] = rows
     print(json.dumps(result), flush=True)
 

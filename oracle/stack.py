@@ -48,15 +48,18 @@ class Stack:
 
     def __init__(self, w: dict, layers: int, hq: int, hkv: int, eps: float = 1e-5, theta: float = 5e5,
                  max_len: int = 1024):
-        self.w, self.layers, self.hq, self.hkv, self.eps = w, layers, hq, hkv, eps
+        self.w = dict(w)  # its own table: widened matrices leave it (the caller's table is untouched)
+        self.layers, self.hq, self.hkv, self.eps = layers, hq, hkv, eps
         self.cos, self.sin = rope_tables(max_len, theta)
         self._f64 = {}
         self.k = [np.zeros((0, hkv, D_HEAD)) for _ in range(layers)]
         self.v = [np.zeros((0, hkv, D_HEAD)) for _ in range(layers)]
 
     def W(self, name: str) -> np.ndarray:
+        """FP64 copy of matrix ``name``, made on first use; the bf16 source is then dropped from ``w`` (every
+        decode step needs every matrix again, so widening on each use would convert all weights per token)."""
         if name not in self._f64:
-            self._f64[name] = bf16_to_f64(self.w[name])
+            self._f64[name] = bf16_to_f64(self.w.pop(name))
         return self._f64[name]
 
     def attention(self, q: np.ndarray, l: int, pos0: int) -> np.ndarray:
@@ -78,7 +81,7 @@ class Stack:
         """Run tokens ``ids`` at positions pos0.. (appending to the cache); returns (final normalised hidden of
         the last token [d], its logits [V])."""
         T = len(ids)
-        x = self.W("emb")[np.asarray(ids)]
+        x = bf16_to_f64(self.w["emb"][np.asarray(ids)])  # only the rows looked up
         cos, sin = self.cos[pos0:pos0 + T], self.sin[pos0:pos0 + T]
         for l in range(self.layers):
             h = rms_norm(x, self.eps)
