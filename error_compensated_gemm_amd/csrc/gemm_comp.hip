@@ -1268,6 +1268,9 @@ namespace {
 
 constexpr int64_t kSplitTileMinK = 1024;   // K per slice, at least, for the tile kernel
 constexpr int64_t kSplitSkinnyMinK = 512;  // and for the skinny kernel
+// rows and K from which a skinny GEMM of at most 16 rows is split
+constexpr int64_t kSplitSkinnyMinRows = 8;
+constexpr int64_t kSplitSkinnyFewRowsMinK = 8192;
 
 struct SplitPlan {
   bool split;      // false: heal_gemm_comp's own launch
@@ -1283,9 +1286,15 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo) {
   const TileKind kind = choose_tile(M, N, a_lo && !b_lo);
   int64_t wgs, target, min_k;
   if (kind == kSkinny) {
-    // split only where every workgroup's re-read of A (M x K x 4 bytes) is over twice its share of B
-    // (16 NC columns x K x 2 bytes): the unsplit launch's column blocks already serve the rest
-    if (M <= 16 * (int64_t)skinny_nc(M, N)) return p;
+    // At most 16 rows, each workgroup of the unsplit launch re-reads all of A (M x K x 4 bytes of parts) for its
+    // 16 NC columns of B: at 16 rows and one column block that is twice B's bytes.  The split launch takes four
+    // column blocks per workgroup (A re-read a quarter as often) and restores the workgroup count with K slices,
+    // at the price of the reduction's launch (a few microseconds): measured on the Llama-3-8B projections, that
+    // pays from 8 rows and K = 8192 (down projection at 16 rows: 52 -> 38 us) and loses below.
+    // Above 16 rows, split only where every workgroup's re-read of A is over twice its share of B (16 NC
+    // columns x K x 2 bytes): the unsplit launch's column blocks already serve the rest.
+    if (M > 16 && M <= 16 * (int64_t)skinny_nc(M, N)) return p;
+    if (M <= 16 && (M < kSplitSkinnyMinRows || K < kSplitSkinnyFewRowsMinK)) return p;
     wgs = (N + 63) / 64;
     target = 512;
     min_k = kSplitSkinnyMinK;
@@ -1344,7 +1353,10 @@ void launch_split_kernel(const SplitPlan& p, int64_t M, int64_t N, int64_t K, co
   const int32_t* const none = nullptr;
   if (p.skinny) {
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)p.S), block(64 * kSkWaves);
-    if (M <= 32)
+    if (M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<PART, 1, 4, ALO, BLO, false, true>), grid, block, 0, stream, M, N, K,
+                         ah, al, none, lda, bh, bl, none, ldb, ws, p.ldw, (const float*)nullptr, p.kslice);
+    else if (M <= 32)
       hipLaunchKernelGGL((gemm_skinny_kernel<PART, 2, 4, ALO, BLO, false, true>), grid, block, 0, stream, M, N, K,
                          ah, al, none, lda, bh, bl, none, ldb, ws, p.ldw, (const float*)nullptr, p.kslice);
     else

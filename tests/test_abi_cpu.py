@@ -288,7 +288,9 @@ def test_splitk_validation_and_plan(heal):
     assert need == 8 * 128 * 4096 * 4
     assert heal.heal_gemm_comp_workspace_bytes(2048, 4096, 4096, 2) == 0
     assert heal.heal_gemm_comp_splitk_slices(2048, 4096, 4096, 2) == 1
-    assert heal.heal_gemm_comp_splitk_slices(16, 4096, 14336, 2) == 1      # 16-row skinny: no split
+    assert heal.heal_gemm_comp_splitk_slices(16, 4096, 14336, 2) == 8      # 16-row skinny, long K: split
+    assert heal.heal_gemm_comp_splitk_slices(16, 4096, 4096, 2) == 1       # 16-row skinny, K < 8192: whole
+    assert heal.heal_gemm_comp_splitk_slices(4, 4096, 14336, 2) == 1       # under 8 rows: whole
     assert heal.heal_gemm_comp_splitk_slices(64, 4096, 14336, 2) == 8      # 64-row skinny: split
     assert heal.heal_gemm_comp_workspace_bytes(-1, 4, 4, 2) == 0 and heal.heal_gemm_comp_splitk_slices(4, 4, 4, 0) == 1
     # K per slice at least 1024 for tiles: 256 x 4096 x 1500 stays whole

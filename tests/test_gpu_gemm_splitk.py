@@ -34,7 +34,8 @@ def _bound_check(C, parts, K):
 # tile and skinny splits, ragged K (a partial last slice and a partial last K step), each product count
 @pytest.mark.parametrize("M,N,K,P", [
     (100, 300, 5001, 3), (129, 257, 4100, 2), (300, 200, 2100, 1),      # 128 x 128 tiles, K split
-    (40, 1000, 3001, 3), (64, 500, 4096, 2), (20, 700, 2003, 3)])       # 17..64-row skinny, K split
+    (40, 1000, 3001, 3), (64, 500, 4096, 2), (20, 700, 2003, 3),        # 17..64-row skinny, K split
+    (16, 1000, 9001, 3), (8, 300, 8200, 2), (13, 520, 16390, 1)])       # 8..16 rows, K >= 8192
 def test_splitk_bound_and_fp64(heal, M, N, K, P):
     S = heal.heal_gemm_comp_splitk_slices(M, N, K, P)
     banner(f"gemm split-K {M}x{N}x{K} P={P} S={S}")
@@ -83,7 +84,7 @@ def test_no_split_is_heal_gemm_comp(heal, M, N, K):
     assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
 
 
-@pytest.mark.parametrize("M", [32, 64, 128, 512])
+@pytest.mark.parametrize("M", [16, 32, 64, 128, 512])
 @pytest.mark.parametrize("K,N", workloads.LLAMA3_8B_KN)
 def test_llama_medium_m_sampled(heal, M, K, N):
     """medium-M Llama-3-8B projections (decode batches, short prefills), sampled against FP64"""
