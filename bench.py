@@ -66,6 +66,7 @@ def parse():
 
 # ------------------------------------------------------------------ HBM traffic from stored counters
 KERNEL_SOURCES = (("gemm_comp_kernel", "gemm_comp.hip"), ("gemm_skinny_kernel", "gemm_comp.hip"),
+                  ("gemm_stream_kernel", "gemm_comp.hip"),
                   ("splitk_reduce_kernel", "gemm_comp.hip"), ("split_rows_kernel", "split_quant.hip"),
                   ("split_row_regs_kernel", "split_quant.hip"),
                   ("quant_i16_kernel", "split_quant.hip"), ("unpack_i16_kernel", "split_quant.hip"),

@@ -25,6 +25,8 @@
 //     running tiles of one XCD share A and B panels in that XCD's L2.
 //   * skinny kernel (M <= 64): 8 wavefronts per 16 NC output columns split K, stream B from memory through
 //     registers with v_mfma_f32_16x16x32, and meet in a fixed-order LDS reduction.
+#include <type_traits>
+
 #include "heal_internal.h"
 
 namespace heal {
@@ -915,6 +917,393 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   }
 }
 
+// ------------------------------------------------------------------------------------------- streamed B, M <= 16
+// At most 16 rows whose split parts fit in LDS.  A persistent workgroup (one per CU) holds all of A's hi and lo
+// planes in LDS (split there from FP32 with the split pass's operations, or copied from the parts) and then walks
+// its column blocks of 16 outputs (blocks x, x + G, x + 2 G, ... for a grid of G): it streams the block's 16 rows
+// of B through a ring of D stages per wavefront by direct-to-LDS transfers, so D x 4 KB per wavefront are in
+// flight with no registers held for them, and the ring runs on from one block into the next.  A stage is 128 of
+// K: four 1 KB transfers, each 4 rows x 256 contiguous bytes (whole 128-byte lines, where the register-prefetch
+// kernel reads 16 rows x 64 bytes per instruction).  Row r's 16-byte chunk c lands in slot c ^ r of that row, so
+// the fragment reads of v_mfma_f32_16x16x32 (16 rows, one chunk each, per group of 16 lanes) hit 16 distinct bank
+// groups.  Wavefront w takes the contiguous stages [ns w / W, ns (w + 1) / W) of each block and accumulates them
+// in order; the partial blocks are added in wavefront order through LDS.  The same bits on every run.
+// ASRC: 0 = 16-bit parts (ah, al; exponents ea or none), 1 = FP32 rows af with exponents ea, 2 = FP32 rows af
+// with the exponents derived here (e = 14 - ilogb(max |a|), the value heal_row_exponents writes).
+constexpr int kStK = 128;       // K per stage
+constexpr int kStACap = 3840;   // 16-byte chunks of A's planes in LDS (60 KB)
+constexpr int kStMaxBlk = 8;    // column blocks per workgroup, at most
+
+// LDS row stride of A's planes, in 16-byte chunks: odd, so the 16 rows of a fragment read fall in distinct bank
+// groups
+__host__ __device__ constexpr int64_t stream_rs(int64_t K) { return ((K + 7) / 8 + 1) | 1; }
+
+template <int PART, int W, int D, int ACAP, bool ALO, bool BLO, int ASRC>
+__global__ __launch_bounds__(64 * W) void gemm_stream_kernel(
+    int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
+    const float* __restrict__ af, const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
+    const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
+    int64_t ldc) {
+  static_assert(D >= 2 && D <= 8, "two to eight stages per wavefront");
+  static_assert(W == 4, "the block epilogue gives each of the 256 threads one of the 4 x 64 outputs");
+  static_assert(ASRC == 0 || (ALO && PART == HEAL_F16), "FP32 A: FP16 parts, both A parts");
+  constexpr int NBP = BLO ? 2 : 1;  // B planes
+  constexpr int SLOT = NBP * 256;   // 16-byte chunks of one wavefront's stage
+  constexpr int NBI = NBP * 4;      // transfers per stage
+  static_assert((D - 1) * NBI < 64, "vmcnt range");
+  __shared__ uint4 st0[W * SLOT];
+  __shared__ uint4 st1[W * SLOT];
+  __shared__ uint4 st2[D > 2 ? W * SLOT : 1];
+  __shared__ uint4 st3[D > 3 ? W * SLOT : 1];
+  __shared__ uint4 st4[D > 4 ? W * SLOT : 1];
+  __shared__ uint4 st5[D > 5 ? W * SLOT : 1];
+  __shared__ uint4 st6[D > 6 ? W * SLOT : 1];
+  __shared__ uint4 st7[D > 7 ? W * SLOT : 1];
+  // the wavefronts' partial blocks, kept until the ring has drained (an LDS read of them while transfers are in
+  // flight makes the compiler wait for all of them); the W partials of an output side by side
+  __shared__ float4 red[kStMaxBlk][4][64];
+  __shared__ uint32_t amax_u[16];
+  __shared__ int aexp_s[16];               // A's row exponents
+  __shared__ int eb_s[kStMaxBlk * 16];     // B's column exponents of this workgroup's blocks
+  // A's hi plane [M][rs], then (ALO) its lo plane.  A static array: the compiler cannot tell dynamic LDS from the
+  // stage slots, and would then wait for every transfer in flight before each A fragment read.
+  __shared__ uint4 a_pl[ACAP];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
+  const int cl = lane & 15, kg = lane >> 4;
+  const int64_t nblk = (N + 15) / 16, G = gridDim.x;
+  const int Q = (int)((nblk - blockIdx.x + G - 1) / G);  // this workgroup's blocks: blockIdx.x + q G, q < Q
+  const int64_t Kc = (K + 7) / 8, rs = stream_rs(K), klast = (Kc - 1) * 8;
+  const int64_t ns = (K + kStK - 1) / kStK;  // at least W (the launcher's condition), so T >= 1
+  const int sbase = (int)(ns * wave / W), T = (int)(ns * (wave + 1) / W) - sbase;
+  const int U = Q * T;  // this wavefront's stages over all its blocks
+  auto blk = [&](int q) { return (int64_t)blockIdx.x + q * G; };
+  // Every workgroup starts its walks at its own place in K (stage index rotated by ns x / G): at any moment the
+  // workgroups read spread-out columns of their rows instead of the same ones.
+  const int rot = (int)(ns * (int64_t)blockIdx.x / G);
+  // a place in the wavefront's sequence of stages: stage t of its share of block q
+  struct Pos {
+    int q, t;
+  };
+  auto advance = [&](Pos& p) {
+    if (++p.t == T) {
+      p.t = 0;
+      ++p.q;
+    }
+  };
+  auto pos_k0 = [&](const Pos& p) -> int64_t {
+    int st = sbase + p.t + rot;
+    if (st >= (int)ns) st -= (int)ns;
+    return (int64_t)st * kStK;
+  };
+
+  // transfer i of a stage carries rows 4 i + (lane >> 4) of the block; the lane's chunk is (lane & 15) ^ row
+  const uint16_t* ibh[4];
+  const uint16_t* ibl[BLO ? 4 : 1];
+  int tch[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tch[i] = (lane & 15) ^ (4 * i + (lane >> 4));
+  auto set_rows = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t n = 16 * blk(q) + 4 * i + (lane >> 4);
+      if (n > N - 1) n = N - 1;  // rows past N feed outputs that are never stored
+      ibh[i] = bh + n * ldb;
+      if constexpr (BLO) ibl[i] = bl + n * ldb;
+    }
+  };
+  Pos pi{0, 0};  // the next stage to request
+  auto issue = [&](uint4* slot) {
+    if (pi.t == 0) set_rows(pi.q);
+    const int64_t k0 = pos_k0(pi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t k = k0 + 8 * tch[i];
+      if (k > klast) k = klast;  // a partial last stage: in-row chunks, cleared when read
+      dma16(ibh[i] + k, slot + wave * SLOT + i * 64);
+      if constexpr (BLO) dma16(ibl[i] + k, slot + wave * SLOT + 256 + i * 64);
+    }
+    advance(pi);
+  };
+  // the first stages do not depend on A: request them before A is split
+  if (U > 0) issue(st0);
+  if (U > 1) issue(st1);
+  if constexpr (D > 2) {
+    if (U > 2) issue(st2);
+  }
+  if constexpr (D > 3) {
+    if (U > 3) issue(st3);
+  }
+  if constexpr (D > 4) {
+    if (U > 4) issue(st4);
+  }
+  if constexpr (D > 5) {
+    if (U > 5) issue(st5);
+  }
+  if constexpr (D > 6) {
+    if (U > 6) issue(st6);
+  }
+  if constexpr (D > 7) {
+    if (U > 7) issue(st7);
+  }
+  // the exponents the block epilogues apply, into LDS (a global load there would wait for the whole ring)
+  for (int idx = threadIdx.x; idx < Q * 16; idx += 64 * W) {
+    const int64_t col = 16 * blk(idx >> 4) + (idx & 15);
+    eb_s[idx] = (eb && col < N) ? eb[col] : 0;
+  }
+  if constexpr (ASRC != 2) {
+    if (threadIdx.x < M) aexp_s[threadIdx.x] = ea ? ea[threadIdx.x] : 0;
+  }
+
+  // ---- A into LDS: 8 values (one 16-byte chunk of each plane) per item, M x Kc items ----
+  // A thread's items (at most CPT) are all requested before any is used, so the prologue waits for memory once:
+  // the loads are branch-free (an item past the end reads item 0, and is dropped), since a load inside a divergent
+  // branch makes the compiler wait for it where the branches meet.
+  const int64_t items = M * Kc;
+  constexpr int CPT = ((ALO ? ACAP / 2 : ACAP) + 64 * W - 1) / (64 * W);
+  if constexpr (ASRC == 0) {
+    uint4 h[CPT], l[ALO ? CPT : 1];
+    if (items > 0) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        int64_t idx = threadIdx.x + 64 * W * i;
+        if (idx >= items) idx = 0;
+        const int64_t r = idx / Kc, c = idx - r * Kc;
+        h[i] = *reinterpret_cast<const uint4*>(ah + r * lda + 8 * c);
+        if constexpr (ALO) l[i] = *reinterpret_cast<const uint4*>(al + r * lda + 8 * c);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int64_t idx = threadIdx.x + 64 * W * i;
+      if (idx < items) {
+        const int64_t r = idx / Kc, c = idx - r * Kc;
+        a_pl[r * rs + c] = mask_chunk(h[i], K - 8 * c);
+        if constexpr (ALO) a_pl[M * rs + r * rs + c] = mask_chunk(l[i], K - 8 * c);
+      }
+    }
+  } else {
+    uint4 x0[CPT], x1[CPT];
+    if (K % 8 == 0) {  // whole 8-value chunks (K >= 8 when there are items)
+      if (items > 0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          int64_t idx = threadIdx.x + 64 * W * i;
+          if (idx >= items) idx = 0;
+          const int64_t r = idx / Kc, k = 8 * (idx - r * Kc);
+          x0[i] = *reinterpret_cast<const uint4*>(af + r * lda + k);
+          x1[i] = *reinterpret_cast<const uint4*>(af + r * lda + k + 4);
+        }
+      }
+    } else {  // a partial last chunk in every row: value by value, columns clamped into the row, zeros past K
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        int64_t idx = threadIdx.x + 64 * W * i;
+        if (idx >= items) idx = 0;
+        const int64_t r = idx / Kc, k = 8 * (idx - r * Kc);
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t v = __builtin_bit_cast(uint32_t, af[r * lda + (k + j < K ? k + j : K - 1)]);
+          w[j] = k + j < K ? v : 0u;
+        }
+        x0[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        x1[i] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+    }
+    if constexpr (ASRC == 2) {
+      if (threadIdx.x < 16) amax_u[threadIdx.x] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int64_t idx = threadIdx.x + 64 * W * i;
+        if (idx < items) {
+          // magnitudes' bit patterns: the integer order of non-negative floats is their numeric order, and a
+          // maximum is the same in any order
+          const uint32_t w[8] = {x0[i].x, x0[i].y, x0[i].z, x0[i].w, x1[i].x, x1[i].y, x1[i].z, x1[i].w};
+          uint32_t m = 0u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m = max(m, w[j] & 0x7FFFFFFFu);
+          atomicMax(&amax_u[idx / Kc], m);
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x < M) {
+        const float m = __builtin_bit_cast(float, amax_u[threadIdx.x]);
+        aexp_s[threadIdx.x] = m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;  // 14 - ilogb(m)
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int64_t idx = threadIdx.x + 64 * W * i;
+      if (idx < items) {
+        const int64_t r = idx / Kc, c = idx - r * Kc;
+        const Split8 sp = split8(x0[i], x1[i], ASRC == 2 ? aexp_s[r] : ea[r]);
+        a_pl[r * rs + c] = sp.hi;
+        a_pl[M * rs + r * rs + c] = sp.lo;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- the stream: wait for stage u, read its fragments, refill its slot with stage u + D, multiply ----
+  const int64_t a_row = (int64_t)(cl < M ? cl : M - 1) * rs;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // block q done by this wavefront: its partial block into LDS
+  auto finish = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) reinterpret_cast<float*>(&red[q][i][lane])[wave] = acc[i];
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // LATER: stages issued after this one that may still be in flight (the wait leaves them outstanding); REFILL:
+  // request the next stage into the slot.  In the steady state both are fixed (D - 1, true), so the compiler sees
+  // the same outstanding transfers on every pass and places no wait of its own before the fragment reads.
+  Pos ps{0, 0};  // the stage to multiply
+  auto step = [&](uint4* slot, auto later_c, bool refill) {
+    constexpr int LATER = decltype(later_c)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<LATER * NBI>());
+    const int64_t k0 = pos_k0(ps);
+    const uint4* sb = slot + wave * SLOT + cl * 16;
+    uint4 b[4][NBP], a[4], a2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ch = 4 * j + kg;
+#pragma unroll
+      for (int p = 0; p < NBP; ++p) b[j][p] = sb[p * 256 + (ch ^ cl)];
+      int64_t c = k0 / 8 + ch;
+      if (c > Kc - 1) c = Kc - 1;  // wholly past K: cleared below
+      a[j] = a_pl[a_row + c];
+      if constexpr (ALO) a2[j] = a_pl[M * rs + a_row + c];
+    }
+    if (k0 + kStK > K) {  // the partial last stage: clear both operands at and past K (padding may hold NaNs)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t valid = K - (k0 + 32 * j + 8 * kg);
+#pragma unroll
+        for (int p = 0; p < NBP; ++p) b[j][p] = mask_chunk(b[j][p], valid);
+        a[j] = mask_chunk(a[j], valid);
+        if constexpr (ALO) a2[j] = mask_chunk(a2[j], valid);
+      }
+    }
+    // the fragments are in registers before the slot is refilled (the transfer writes LDS behind the reads)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+    if (refill) issue(slot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = mfma16<PART>(a[j], b[j][0], acc);
+      if constexpr (BLO) acc = mfma16<PART>(a[j], b[j][1], acc);
+      if constexpr (ALO) acc = mfma16<PART>(a2[j], b[j][0], acc);
+    }
+    if (ps.t == T - 1) finish(ps.q);
+    advance(ps);
+  };
+  using L0 = std::integral_constant<int, 0>;
+  using LD = std::integral_constant<int, D - 1>;
+  int u = 0;
+  // steady state: every step refills its slot, D - 1 later stages in flight
+  for (; u + 2 * D <= U; u += D) {
+    step(st0, LD{}, true);
+    step(st1, LD{}, true);
+    if constexpr (D > 2) step(st2, LD{}, true);
+    if constexpr (D > 3) step(st3, LD{}, true);
+    if constexpr (D > 4) step(st4, LD{}, true);
+    if constexpr (D > 5) step(st5, LD{}, true);
+    if constexpr (D > 6) step(st6, LD{}, true);
+    if constexpr (D > 7) step(st7, LD{}, true);
+  }
+  // the last (fewer than 2 D) stages: refill while stages remain, and wait for everything issued (the first of
+  // these steps finds the ring's last stages in flight and waits for them together)
+  for (; u < U; ++u) {
+    const bool refill = u + D < U;
+    switch (u % D) {
+      case 0: step(st0, L0{}, refill); break;
+      case 1: step(st1, L0{}, refill); break;
+      case 2: if constexpr (D > 2) step(st2, L0{}, refill); break;
+      case 3: if constexpr (D > 3) step(st3, L0{}, refill); break;
+      case 4: if constexpr (D > 4) step(st4, L0{}, refill); break;
+      case 5: if constexpr (D > 5) step(st5, L0{}, refill); break;
+      case 6: if constexpr (D > 6) step(st6, L0{}, refill); break;
+      default: if constexpr (D > 7) step(st7, L0{}, refill); break;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());  // no transfer may still write LDS when the workgroup ends
+
+  // ---- each thread adds one output of every block over the wavefronts, in wavefront order ----
+  __syncthreads();
+  const int i = threadIdx.x >> 6;
+  const int64_t row = 4 * (lane >> 4) + i;
+  for (int q = 0; q < Q; ++q) {
+    const float4 pw = red[q][i][lane];
+    const float sum = (((0.0f + pw.x) + pw.y) + pw.z) + pw.w;
+    const int64_t col = 16 * blk(q) + (lane & 15);
+    if (row < M && col < N)
+      C[row * ldc + col] = __builtin_amdgcn_ldexpf(sum, -(aexp_s[row] + eb_s[q * 16 + (lane & 15)]));
+  }
+}
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
+// Launch shape of the streamed kernel: 4 wavefronts with 4 ring stages of 4 KB each (2 when B has a low part), so
+// 64 KB in flight per CU, and one workgroup per CU (at most 8 column blocks each).  It serves at most 16 rows where
+// A's planes fit their 60 KB, K spans at least one stage per wavefront, and N gives every CU at least three column
+// blocks: measured on MI355X against the register-prefetch kernel (M = 1, weights rotated through HBM, average
+// kernel durations from the trace), 26.2-26.9 against 27.6-27.8 us at N x K = 14336 x 4096 and 44.4-44.6 against
+// 51.6-51.8 at 28672 x 4096, where it splits A once per CU and keeps the ring running from block to block; at
+// 8192 x 4096 the two are level (17.8-19.6 against 18.5-18.9 us), and with one block per workgroup (N = 4096)
+// the register-prefetch kernel's 8 wavefronts are ahead (26.3 against 27.8 us at K = 14336).  Six ring stages
+// instead of four (A's planes in a smaller array) did not help (26.9 against 26.2 us at 14336 x 4096).
+// heal_gemm_comp and heal_gemm_comp_f32a take the same decision from (M, N, K, A's low part), so they keep giving
+// the same bits.
+constexpr int kStW = 4, kStD = 4, kStDLo = 2;
+
+bool stream_fits(int64_t M, int64_t N, int64_t K, bool a_lo) {
+  if (M < 1 || M > 16 || K < (int64_t)kStW * kStK - (kStK - 1)) return false;
+  if ((N + 15) / 16 < 3 * (int64_t)cu_count()) return false;
+  return (a_lo ? 2 : 1) * M * stream_rs(K) <= kStACap;
+}
+
+// ASRC as for gemm_stream_kernel; al / bl select the products
+template <int PART, int ASRC>
+hipError_t launch_stream(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al, const float* af,
+                         const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl, const int32_t* eb,
+                         int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
+  const int64_t nblk = (N + 15) / 16;
+  int64_t wgs = cu_count();
+  if (wgs > nblk) wgs = nblk;
+  if (wgs < (nblk + kStMaxBlk - 1) / kStMaxBlk) wgs = (nblk + kStMaxBlk - 1) / kStMaxBlk;
+  if (!grid_fits(wgs, 64 * kStW)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)wgs), block(64 * kStW);
+  if constexpr (ASRC == 0) {
+    if (al && bl)
+      hipLaunchKernelGGL((gemm_stream_kernel<PART, kStW, kStDLo, kStACap, true, true, 0>), grid, block, 0, stream, M,
+                         N, K, ah, al, af, ea, lda, bh, bl, eb, ldb, c, ldc);
+    else if (al)
+      hipLaunchKernelGGL((gemm_stream_kernel<PART, kStW, kStD, kStACap, true, false, 0>), grid, block, 0, stream, M,
+                         N, K, ah, al, af, ea, lda, bh, bl, eb, ldb, c, ldc);
+    else if (bl)
+      hipLaunchKernelGGL((gemm_stream_kernel<PART, kStW, kStDLo, kStACap, false, true, 0>), grid, block, 0, stream, M,
+                         N, K, ah, al, af, ea, lda, bh, bl, eb, ldb, c, ldc);
+    else
+      hipLaunchKernelGGL((gemm_stream_kernel<PART, kStW, kStD, kStACap, false, false, 0>), grid, block, 0, stream, M,
+                         N, K, ah, al, af, ea, lda, bh, bl, eb, ldb, c, ldc);
+  } else {
+    if (bl)
+      hipLaunchKernelGGL((gemm_stream_kernel<HEAL_F16, kStW, kStDLo, kStACap, true, true, ASRC>), grid, block, 0,
+                         stream, M, N, K, ah, al, af, ea, lda, bh, bl, eb, ldb, c, ldc);
+    else
+      hipLaunchKernelGGL((gemm_stream_kernel<HEAL_F16, kStW, kStD, kStACap, true, false, ASRC>), grid, block, 0,
+                         stream, M, N, K, ah, al, af, ea, lda, bh, bl, eb, ldb, c, ldc);
+  }
+  return hipGetLastError();
+}
+
 // Column blocks per skinny workgroup.  Each workgroup re-reads A (M x K) from L2, so more columns per
 // workgroup save that traffic, but fewer workgroups keep fewer loads in flight.  Measured on MI355X at
 // K = 4096 / 14336 (M = 1 .. 64; weights rotated through four copies, so read from HBM): N = 4096 runs
@@ -953,6 +1342,8 @@ template <int PART>
 hipError_t launch_skinny(int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
                          const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl,
                          const int32_t* eb, int64_t ldb, float* c, int64_t ldc, hipStream_t stream) {
+  if (stream_fits(M, N, K, al != nullptr))
+    return launch_stream<PART, 0>(M, N, K, ah, al, nullptr, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
   const int nc = skinny_nc(M, N);
   if (M <= 16) {
     if (nc >= 4) return launch_skinny_nc<PART, 1, 4>(M, N, K, ah, al, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
@@ -1044,7 +1435,6 @@ hipError_t launch_part(int64_t M, int64_t N, int64_t K, const uint16_t* ah, cons
 }  // namespace
 
 const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
-  (void)K;
   static const char* names[4][3] = {
       {"gemm_comp_kernel 256x256 P1", "gemm_comp_kernel 256x256 P2", "gemm_comp_kernel 256x256 P3"},
       {"gemm_comp_kernel 256x128 P1", "gemm_comp_kernel 256x128 P2", "gemm_comp_kernel 256x128 P3"},
@@ -1053,6 +1443,11 @@ const char* gemm_comp_variant(int64_t M, int64_t N, int64_t K, int products) {
   if (M <= 0 || N <= 0 || products < 1 || products > 3) return "none";
   const TileKind kind = choose_tile(M, N, products == 2);
   if (kind == kTile128x256) return "gemm_comp_kernel 128x256 P2";
+  if (kind == kSkinny && stream_fits(M, N, K, products >= 2)) {
+    static const char* st[3] = {"gemm_stream_kernel M<=16 P1", "gemm_stream_kernel M<=16 P2",
+                                "gemm_stream_kernel M<=16 P3"};
+    return st[products - 1];
+  }
   if (kind == kSkinny) {
     // [rows class][column blocks 1, 2, 4][products]
     static const char* sk[3][3][3] = {
@@ -1191,6 +1586,9 @@ hipError_t launch_skinny_f32a_nc(int64_t M, int64_t N, int64_t K, const float* a
 hipError_t launch_skinny_f32a(int64_t M, int64_t N, int64_t K, const float* af, const int32_t* ea, int64_t lda,
                               const uint16_t* bh, const uint16_t* bl, const int32_t* eb, int64_t ldb, float* c,
                               int64_t ldc, hipStream_t stream) {
+  if (stream_fits(M, N, K, true))
+    return ea ? launch_stream<HEAL_F16, 1>(M, N, K, nullptr, nullptr, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream)
+              : launch_stream<HEAL_F16, 2>(M, N, K, nullptr, nullptr, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
   const int nc = skinny_nc(M, N);
   if (M <= 16) {
     if (nc >= 4) return launch_skinny_f32a_nc<1, 4>(M, N, K, af, ea, lda, bh, bl, eb, ldb, c, ldc, stream);
