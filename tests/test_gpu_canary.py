@@ -1,7 +1,7 @@
 """Canary bands: every output is written into a view of a larger buffer whose other bytes hold a sentinel
 pattern (0x7FA5A5A5, a NaN), and must leave them untouched while the view equals, bit for bit, the output
-written into a plain allocation.  Covers the GEMM kernels (skinny, skinny with A split in LDS, 128 x 128,
-128 x 256, 256 x 256 with three products, split K), the split's part padding, the quantiser writing into a
+written into a plain allocation.  Covers the GEMM kernels (skinny, skinny with A split in LDS, the persistent
+streamed-B kernel, 128 x 128, 128 x 256, 256 x 256 with three products, split K), the split's part padding, the quantiser writing into a
 cache view, and prefill and decode attention writing a strided output."""
 import numpy as np
 import pytest
@@ -37,7 +37,8 @@ def _outside_untouched(buf, view):
 
 
 @pytest.mark.parametrize("M,N,K,P,f32a", [(1, 4100, 1032, 2, True), (16, 3000, 777, 3, False), (300, 520, 300, 3, False),
-                                        (2050, 4100, 96, 2, False), (4000, 4100, 64, 3, False), (100, 600, 4096, 2, False)])
+                                        (2050, 4100, 96, 2, False), (4000, 4100, 64, 3, False), (100, 600, 4096, 2, False),
+                                        (3, 12300, 1000, 2, True), (5, 12300, 1000, 3, False)])
 def test_gemm_writes_only_its_view(heal, M, N, K, P, f32a):
     banner(f"canary gemm {M}x{N}x{K} P={P} f32a={f32a}: {heal.heal_gemm_comp_variant(M, N, K, P)}")
     A, Bt = workloads.gemm_rowscaled(M, N, K, seed=5)
