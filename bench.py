@@ -111,17 +111,17 @@ def gemm_symbol(variant):
     return f"gemm_comp_kernel<2, {bm}, {bn}, {str(p >= 2).lower()}, {str(p >= 3).lower()}, false, false, false>"
 
 
-def stored_traffic(sym):
-    """HBM bytes per launch of kernel `sym` from the committed counter summaries under profiles/, or None when
-    there is none or the kernel's source changed since the counters were taken."""
-    import glob
+def stored_traffic(sym, profile):
+    """HBM bytes per launch of kernel `sym` in the workload of the committed counter summary profiles/<profile>
+    (the same kernel instance moves different bytes in other workloads), or None when the summary does not hold
+    it or the kernel's source changed since the counters were taken."""
     if sym is None:
         return None
     src = kernel_source(sym)
     if src is None:
         return None
     sha = source_sha256(os.path.join(CSRC, src))
-    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+    for f in [os.path.join(PROFILES, profile)] if os.path.exists(os.path.join(PROFILES, profile)) else []:
         for line in open(f):
             if not line.startswith(TRAFFIC_TAG):
                 continue
@@ -354,7 +354,7 @@ def headline(args, heal, workloads):
     kernel = heal.heal_gemm_comp_variant(M, N, K, 3)
     sym = gemm_symbol(kernel)
     achieved = 3 * flop / durs["gemm"] / 1e12
-    tr = stored_traffic(sym)
+    tr = stored_traffic(sym, "gemm_comp_8192cube_p3_hbm_traffic.md")
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None if tr is None else tr["bytes_per_launch"],
@@ -370,7 +370,7 @@ def headline(args, heal, workloads):
         "gemm_us": round(durs["gemm"] * 1e6, 1),
         "gemm_tflops_fp32eq": round(flop / durs["gemm"] / 1e12, 1),
     }
-    st = stored_traffic(parts["split_symbol"])
+    st = stored_traffic(parts["split_symbol"], "gemm_comp_8192cube_p3_hbm_traffic.md")
     parts["split_traffic"] = None if st is None else st["bytes_per_launch"]
     result = {
         "metric": "FP32-equiv TFLOP/s of compensated GEMM + % of MFMA roofline; max rel err vs FP64",
@@ -561,7 +561,7 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10):
     dom_name, dom = max(by_variant.items(), key=lambda kv: kv[1]["time"])
     avg_dur = dom["time"] / dom["launches"]
     achieved = dom["mfma_flop"] / dom["launches"] / avg_dur / 1e12
-    tr = stored_traffic(gemm_symbol(dom_name))
+    tr = stored_traffic(gemm_symbol(dom_name), "gemm_comp_llama3_8b_hbm_traffic.md")
     row = {
         "us_per_step": round(step_s * 1e6, 1), "tflops_fp32eq": round(flops_step / step_s / 1e12, 2),
         "weights_rotated_copies": rotate,
@@ -648,7 +648,7 @@ def row_split_quant(heal, workloads, dev):
     hi, lo, e = heal.heal_split(x)
     t = time_fn(lambda: heal.heal_split(x, hi=hi, lo=lo, exps=e), 20)
     gbs = x.numel() * 8 / t / 1e9
-    tr = stored_traffic("split_row_regs_kernel<2, true, 8>")
+    tr = stored_traffic("split_row_regs_kernel<2, true, 8>", "split_rows_2048x14336_hbm_traffic.md")
     rows["a1_split_2048x14336"] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                                    "algorithmic_bytes": x.numel() * 8 + 2048 * 4,
                                    "traffic": None if tr is None else tr["bytes_per_launch"]}
@@ -668,7 +668,7 @@ def row_split_quant(heal, workloads, dev):
     fq, fs = heal.heal_qkv_quant_i16(fused)
     t = time_fn(lambda: heal.heal_qkv_quant_i16(fused, q=fq, scale=fs), 20)
     gbs = nel * (4 + 2 + 4 / 128) / t / 1e9
-    tr = stored_traffic("quant_i16_kernel")
+    tr = stored_traffic("quant_i16_kernel<1>", "quant_i16_4096x96x128_hbm_traffic.md")
     rows["a4_quant_fused_qkv_4096x96x128"] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1),
                                               "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                                               "algorithmic_bytes": int(nel * (4 + 2 + 4 / 128)),
@@ -751,7 +751,7 @@ def row_decode(heal, workloads, dev, with_cpu):
     ws = torch.empty(heal.heal_attn_workspace_bytes(args), dtype=torch.uint8, device="cuda")
     by = attn_decode_bytes(B, L, Hq, Hkv)
     rows = {}
-    tr = stored_traffic("attn_decode_kernel<false, 0>")
+    tr = stored_traffic("attn_decode_kernel<false, 0>", "attn_decode_64x8192_hbm_traffic.md")
     for reading in ("byte", "shift10", "float"):
         t = time_fn(lambda: heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws,
                                                      dual_split=reading), 10)
