@@ -592,6 +592,19 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cl = lane & 15, kg = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16 * NC;
+  // The exponents the epilogue applies (wavefront 0: this workgroup's rows, 1: its columns) are requested now and
+  // kept in a register through the main loop, so their latency overlaps it instead of closing the kernel.  The
+  // branch is on the wavefront index (uniform), and every lane loads an in-range element.
+  __shared__ int exp_s[2][64];
+  int exp_pre = 0;
+  {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    if (wv == 0) {
+      if (!AEXP && ea) exp_pre = ea[lane < M ? lane : M - 1];
+    } else if (wv == 1) {
+      if (eb) exp_pre = eb[n0 + lane < N ? n0 + lane : N - 1];
+    }
+  }
   // AEXP: e = 14 - ilogb(max_k |a[m, k]|) for each row (0 for a row without a nonzero value), the value
   // heal_row_exponents writes (a maximum is exact in any order).  The 512 threads stride over each row in
   // float4 chunks and the wavefront maxima meet in LDS.  Every workgroup reads all of A for this once more
@@ -898,6 +911,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     for (int nc = 0; nc < NC; ++nc)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][mt * NC + nc][i][lane] = acc[mt][nc][i];
+  if (wave < 2) exp_s[wave][lane] = exp_pre;
   __syncthreads();
   for (int idx = threadIdx.x; idx < MT * NC * 4 * 64; idx += 64 * kSkWaves) {
     const int blk = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
@@ -907,11 +921,11 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     for (int w = 0; w < kSkWaves; ++w) s += red[w][blk][i][l];
     const int64_t row = 16 * mt + 4 * (l >> 4) + i, col = n0 + 16 * nc + (l & 15);
     if (row < M && col < N) {
-      int e = eb ? eb[col] : 0;
+      int e = exp_s[1][16 * nc + (l & 15)];
       if constexpr (AEXP)
         e += aexp_s[row];
       else
-        e += ea ? ea[row] : 0;
+        e += exp_s[0][row];
       C[row * ldc + col] = __builtin_amdgcn_ldexpf(s, -e);
     }
   }
