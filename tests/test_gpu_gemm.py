@@ -154,3 +154,9 @@ def test_config5_8192_sampled(heal):
     err = normwise(got, ref)
     print(f"[gemm] 8192^3 sampled normwise {err:.3e}")
     assert err <= TOL
+    # 24 whole rows (every column, the launch the bench times) element by element against the oracle's exact
+    # sum of the same 16-bit products, within the FP32-accumulation bound (3 K + 2) 2^-24 G
+    rows = np.sort(rng.choice(M, 24, replace=False))
+    Ce, G = oracle.gemm_emul(bits(ah)[rows], bits(al)[rows], host(ea)[rows], bits(bh), bits(bl), host(eb))
+    viol = np.abs(host(C)[rows].astype(np.float64) - Ce) - (3 * K + 2) * 2.0 ** -24 * G
+    assert float(viol.max()) <= 0, f"per-element bound violated, excess {viol.max():.3e}"
