@@ -25,6 +25,11 @@
 //     running tiles of one XCD share A and B panels in that XCD's L2.
 //   * skinny kernel (M <= 64): 8 wavefronts per 16 NC output columns split K, stream B from memory through
 //     registers with v_mfma_f32_16x16x32, and meet in a fixed-order LDS reduction.
+//   * streamed-B kernel (M <= 16, N of at least three 16-column blocks per CU, A's parts within 60 KB): one
+//     persistent workgroup per CU splits A once into LDS and walks its column blocks, B arriving through a
+//     ring of direct-to-LDS stages that runs on from one block into the next.
+//   * split K (heal_gemm_comp_splitk only): the tile or skinny kernel on slices of K into FP32 partials, then
+//     an ordered reduction that applies the exponents.
 #include <type_traits>
 
 #include "heal_internal.h"
