@@ -694,7 +694,7 @@ def row_prefill(heal, qkv_host, qkv_dev, with_cpu):
     heal.heal_attn_dual_fp16(*args, causal=True, out=out)
     if with_cpu:
         rows["a6_prefill_1x4096x32x128_causal"]["cpu_baseline"] = cpu_baseline_attn(
-            qkv_dev, out, causal=True, nrows=4096, seed=0, batch_rows=None)
+            qkv_dev, out, causal=True, nrows=-1, seed=0, batch_rows=None)
     return rows
 
 
@@ -717,7 +717,12 @@ def cpu_baseline_attn(qkv_dev, out, causal, nrows, seed, batch_rows):
     B, Lq, Hq, D = qh.shape
     Lkv = kh.shape[1]
     rng = np.random.default_rng(seed)
-    if batch_rows is None:
+    if batch_rows is None and nrows < 0:
+        bb, ii, hh = np.meshgrid(np.arange(B), np.arange(Lq), np.arange(Hq), indexing="ij")
+        allrows = np.stack([bb.ravel(), ii.ravel(), hh.ravel()], 1)
+        perm = rng.permutation(len(allrows))
+        rows = allrows[perm]  # every row once, in a seeded order whose first rows form the contrast subset
+    elif batch_rows is None:
         rows = np.stack([rng.integers(0, B, nrows), rng.integers(0, Lq, nrows), rng.integers(0, Hq, nrows)], 1)
         rows[:4, 1] = [Lq - 1, Lq - 2, Lq // 2, 0]
     else:  # every head of the given batches (decode)
