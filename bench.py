@@ -227,15 +227,23 @@ class Timer:
         return out
 
 
-def time_fn(fn, reps, warm=10, rounds=1):
-    """Average time of `reps` back-to-back calls after `warm` untimed ones, the best of `rounds` such averages (the
-    clock settles over the first milliseconds of work, and a memory-bound call timed right after a long
-    MFMA-bound row can run a few percent slow for a while)."""
+def time_fn(fn, reps, warm=10, rounds=1, warm_s=0.0):
+    """Average time of `reps` back-to-back calls after `warm` untimed ones (and after at least `warm_s` seconds of
+    untimed calls), the best of `rounds` such averages.  The clock takes tens of milliseconds to settle after a
+    change of load: a 0.5 ms attention call timed right after a row of short memory-bound kernels runs up to
+    10% slow for its first few dozen calls."""
+    import time
+
     import torch
 
+    t0 = time.perf_counter()
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(max(warm, 1)):
+            fn()
+        torch.cuda.synchronize()
     best = float("inf")
     for _ in range(rounds):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -690,7 +698,7 @@ def row_prefill(heal, qkv_host, qkv_dev, with_cpu):
     rows = {}
     for reading, prods in (("byte", 8), ("shift10", 8), ("float", 6)):
         t = time_fn(lambda: heal.heal_attn_dual_fp16(*args, causal=True, out=out, dual_split=reading), 20,
-                    warm=20, rounds=3)
+                    warm=20, rounds=3, warm_s=0.3)
         ach = prods * fl / 2 / t / 1e12
         key = "a6_prefill_1x4096x32x128_causal" + ("" if reading == "byte" else f"_{reading}")
         rows[key] = {"us": round(t * 1e6, 2), "tflops_fp32eq": round(fl / t / 1e12, 2),
@@ -770,7 +778,7 @@ def row_decode(heal, workloads, dev, with_cpu):
     tr = stored_traffic("attn_decode_kernel<false, 0>", "attn_decode_64x8192_hbm_traffic.md")
     for reading in ("byte", "shift10", "float"):
         t = time_fn(lambda: heal.heal_attn_dual_fp16(q, qs, k, ks, v, vs, causal=True, out=out, workspace=ws,
-                                                     dual_split=reading), 20, warm=20, rounds=3)
+                                                     dual_split=reading), 20, warm=20, rounds=3, warm_s=0.3)
         key = "a7_decode_64x8192_gqa32_8" + ("" if reading == "byte" else f"_{reading}")
         gbs = by / t / 1e9
         rows[key] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
@@ -806,7 +814,7 @@ def row_decode(heal, workloads, dev, with_cpu):
     pargs = heal.make_paged_args(q1, qs1, kp, ksp, vp, vsp, tab, lens, L, o1)
     pws = torch.empty(heal.heal_attn_paged_workspace_bytes(pargs), dtype=torch.uint8, device="cuda")
     t = time_fn(lambda: heal.heal_attn_decode_paged(q1, qs1, kp, ksp, vp, vsp, tab, lens, L, out=o1,
-                                                    workspace=pws), 20, warm=20, rounds=3)
+                                                    workspace=pws), 20, warm=20, rounds=3, warm_s=0.3)
     rows["a7p_paged_decode_64x8192_page64"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
                                                "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
 
@@ -815,7 +823,7 @@ def row_decode(heal, workloads, dev, with_cpu):
     kp, ksp = head_major(kp), head_major(ksp)
     vp, vsp = head_major(vp), head_major(vsp)
     t = time_fn(lambda: heal.heal_attn_decode_paged(q1, qs1, kp, ksp, vp, vsp, tab, lens, L, out=o1,
-                                                    workspace=pws), 20, warm=20, rounds=3)
+                                                    workspace=pws), 20, warm=20, rounds=3, warm_s=0.3)
     rows["a7p_paged_decode_64x8192_page64_head_major"] = {"us": round(t * 1e6, 2), "gbs": round(by / t / 1e9, 1),
                                                           "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
     return rows

@@ -6,14 +6,15 @@
 // LLM Inference: Achieving Reproducible Inference for Mission-Critical Tasks with HEAL", Technical Summary.
 //
 // Arithmetic (identical in both kernels):
-//   * unpack (default, the byte split)  q = 256 * (q >> 8) + (q & 0xFF):  H = fp16(q & ~0xFF) (multiple of
-//     256, |H| <= 32768) and L = fp16(q & 0xFF) (0..255), both exact, H + L = q.  Two other exact readings
-//     of the pair are selectable: the shift-10 split H = 1024 * (q >> 10), L = q & 0x3FF, and the
-//     float-float pair H = fp16_rn(q), L = q - H.
-//   * S_int = q_i . k_j as two FP32 accumulators: Hq.Hk (byte split: every partial sum is a multiple of
-//     2^16 below 2^37, exact; shift-10: multiples of 2^20 below 2^37, exact) and Hq.Lk + Lq.Hk + Lq.Lk
-//     (about 2^-7 of the first); S_int = their FP32 sum.  The float-float pair drops Lq.Lk and Lv.P~l
-//     (3 + 3 products), and its Hq.Hk sum rounds: about 2^-24 of sum |Hq Hk| per logit.
+//   * unpack (default, the byte split)  q = 256 * (q >> 8) + (q & 0xFF):  H = q >> 8 (-128..127) and
+//     L = (q & 0xFF) / 256, both exact FP16 values, H + L = q / 256.  Two other exact readings of the pair
+//     are selectable: the shift-10 split H = q >> 10, L = (q & 0x3FF) / 1024 (H + L = q / 1024), and the
+//     float-float pair H = fp16_rn(q), L = q - H.  The power of two the halves carry (2^-8, 2^-10, 1) is
+//     given back through the k-scales (squared) and the output exponent, exactly.
+//   * S_int = q_i . k_j as two FP32 accumulators: Hq.Hk (byte split: integer partial sums below 2^21,
+//     exact; shift-10: below 2^17, exact) and Hq.Lk + Lq.Hk + Lq.Lk (about 2^-7 of the first); S_int =
+//     their FP32 sum.  The float-float pair drops Lq.Lk and Lv.P~l (3 + 3 products), and its Hq.Hk sum
+//     rounds: about 2^-24 of sum |Hq Hk| per logit.
 //   * t_ij = S_int * s_k,j * (s_q,i * softmax_scale * log2 e), carried as an FP32 pair (hi + FMA-captured
 //     rounding error) so that t - max keeps its precision for logits of any size; online softmax in
 //     base 2, FP32 running maximum and sum.  Prefill keeps u_ij = S_int * s_k,j as the pair and its maximum
@@ -21,7 +22,8 @@
 //   * P~ = p * (s_v,j * 2^E) with E = 14 - ilogb(max_j s_v,j) over the keys a workgroup reads (prefill: 8 less,
 //     since its lazily moved maximum lets p reach 2^8), so P~ < 2^15 and its FP16 split P~ = P~h + P~l
 //     (P~l = fp16(P~ - P~h), exact residual) keeps 22 bits;
-//     O += P~h.H + P~h.L + P~l.H + P~l.L (4 products, one FP32 accumulator); O = acc * 2^-E / l.
+//     O += P~h.H + P~h.L + P~l.H + P~l.L (4 products, one FP32 accumulator); O = acc * 2^(shift - E) / l
+//     for the halves' scale 2^-shift.
 //
 // Prefill (q_len > 1): flash-style forward.  A workgroup of 8 wavefronts owns 256 queries of one
 // (batch, head); each wavefront owns 32.  K/V tiles of 32 keys (PF_BKV) arrive in LDS as raw INT16 rows by
@@ -65,33 +67,41 @@ __device__ __forceinline__ uint32_t pack2(_Float16 a, _Float16 b) {
 }
 
 // Dual-FP16 unpack of 8 INT16 values (one 16-byte chunk) into FP16 halves H + L, two values per 32-bit
-// word.  The halves are scaled so that every product of two operands lands in the same accumulators:
-//   HEAL_DUAL_BYTE     H = 256 * (q >> 8), L = q & 0xFF;  H + L = q, both exact.  Packed FP16 arithmetic:
-//     L: the FP16 pattern 0x5C00 | (l << 2) is 256 + l (exponent 2^8, l in the top 8 mantissa bits), minus 256.
-//     H: with b = the signed high byte, 0x6400 | (b ^ 0x80) is 1024 + b + 128; minus 1152 gives b, times 256
-//        gives H (|H| <= 2^15).  Every intermediate is an integer below 2^11, so no step rounds.
-//   HEAL_DUAL_SHIFT10  H = 1024 * (q >> 10), L = q & 0x3FF;  H + L = q, both exact.
-//     L: 0x6400 | l is 1024 + l (ulp 1 in [1024, 2048)), minus 1024.
-//     H: with b = q >> 10 in [-32, 31] (the top 6 bits), 0x6400 | (f ^ 0x20) for the 6-bit field f is
-//        1024 + b + 32; minus 1056 gives b, times 1024 gives H.
-//   HEAL_DUAL_FLOAT    H = fp16_rn(q), L = q - H (an integer, |L| <= 16): the float-float pair, exact.
+// word.  Each reading's two exact parts are held scaled by 2^-kShift<SPLIT>, so that H + L = q 2^-kShift and
+// the products of any two operands land in the same accumulators; a score then carries 2^-2 kShift and an O
+// accumulator 2^-kShift, powers of two that the k-scales and the output exponent take back exactly.
+//   HEAL_DUAL_BYTE     hi = q >> 8, lo = q & 0xFF, H = hi, L = lo / 256 (kShift 8).  With x = q ^ 0x8000 (the
+//     high byte becomes hi + 128), a byte permute places each byte of x under the FP16 pattern 0x64__, the
+//     value 1024 + byte (ulp 1 in [1024, 2048)): 1024 + lo and 1024 + hi + 128.  Then L = (1024 + lo) 2^-8 - 4
+//     by one packed FMA (exact: the result needs 8 fraction bits) and H = (1152 + hi) - 1152.  No step rounds.
+//   HEAL_DUAL_SHIFT10  hi = q >> 10, lo = q & 0x3FF, H = hi, L = lo / 1024 (kShift 10).
+//     L: 0x6400 | lo is 1024 + lo, times 2^-10 minus 1.
+//     H: with the 6-bit field f of q >> 10, 0x6400 | (f ^ 0x20) is 1024 + hi + 32; minus 1056 gives hi.
+//   HEAL_DUAL_FLOAT    H = fp16_rn(q), L = q - H (an integer, |L| <= 16): the float-float pair, exact
+//     (kShift 0).
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <int SPLIT>
+constexpr int kShift = SPLIT == HEAL_DUAL_BYTE ? 8 : (SPLIT == HEAL_DUAL_SHIFT10 ? 10 : 0);
 template <int SPLIT>
 __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t& h, uint32_t& l) {
   if constexpr (SPLIT == HEAL_DUAL_BYTE) {
-    const f16x2 lo = __builtin_bit_cast(f16x2, ((w & 0x00FF00FFu) << 2) | 0x5C005C00u);
-    const f16x2 hb = __builtin_bit_cast(f16x2, ((w >> 8) & 0x00FF00FFu) ^ 0x64806480u);
-    const f16x2 c256 = {(_Float16)256.0f, (_Float16)256.0f};
+    const uint32_t x = w ^ 0x80008000u;
+    // v_perm_b32: selector bytes 0..3 pick bytes of x, 4 picks a byte of 0x64646464
+    const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, x, 0x04020400u));
+    const f16x2 hb = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030401u));
+    const f16x2 c2m8 = {(_Float16)0.00390625f, (_Float16)0.00390625f};
+    const f16x2 cm4 = {(_Float16)-4.0f, (_Float16)-4.0f};
     const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
-    l = __builtin_bit_cast(uint32_t, lo - c256);
-    h = __builtin_bit_cast(uint32_t, (hb - c1152) * c256);
+    l = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(lo, c2m8, cm4));
+    h = __builtin_bit_cast(uint32_t, hb - c1152);
   } else if constexpr (SPLIT == HEAL_DUAL_SHIFT10) {
     const f16x2 lo = __builtin_bit_cast(f16x2, (w & 0x03FF03FFu) | 0x64006400u);
     const f16x2 hb = __builtin_bit_cast(f16x2, ((w >> 10) & 0x003F003Fu) ^ 0x64206420u);
-    const f16x2 c1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const f16x2 c2m10 = {(_Float16)0.0009765625f, (_Float16)0.0009765625f};
+    const f16x2 cm1 = {(_Float16)-1.0f, (_Float16)-1.0f};
     const f16x2 c1056 = {(_Float16)1056.0f, (_Float16)1056.0f};
-    l = __builtin_bit_cast(uint32_t, lo - c1024);
-    h = __builtin_bit_cast(uint32_t, (hb - c1056) * c1024);
+    l = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(lo, c2m10, cm1));
+    h = __builtin_bit_cast(uint32_t, hb - c1056);
   } else {
     const float f0 = (float)(int16_t)(w & 0xFFFFu), f1 = (float)(int16_t)(w >> 16);
     const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;  // round to nearest even
@@ -337,7 +347,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
     P.vl[vt_pos<VT_PREFILL>(ckey, cchunk)] = lo;
     if (wave == 0) {
       const float s = R.sc[lane];
-      P.sc[lane] = lane < 32 ? s : __builtin_amdgcn_ldexpf(s, E);
+      P.sc[lane] = __builtin_amdgcn_ldexpf(s, lane < 32 ? 2 * kShift<SPLIT> : E);
     }
   };
 
@@ -506,10 +516,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       float4 o;
-      o.x = __builtin_amdgcn_ldexpf(O[dt][4 * g + 0], -E) * inv;
-      o.y = __builtin_amdgcn_ldexpf(O[dt][4 * g + 1], -E) * inv;
-      o.z = __builtin_amdgcn_ldexpf(O[dt][4 * g + 2], -E) * inv;
-      o.w = __builtin_amdgcn_ldexpf(O[dt][4 * g + 3], -E) * inv;
+      o.x = __builtin_amdgcn_ldexpf(O[dt][4 * g + 0], kShift<SPLIT> - E) * inv;
+      o.y = __builtin_amdgcn_ldexpf(O[dt][4 * g + 1], kShift<SPLIT> - E) * inv;
+      o.z = __builtin_amdgcn_ldexpf(O[dt][4 * g + 2], kShift<SPLIT> - E) * inv;
+      o.w = __builtin_amdgcn_ldexpf(O[dt][4 * g + 3], kShift<SPLIT> - E) * inv;
       *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * half) = o;
     }
 }
@@ -597,7 +607,10 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
       unpack8<SPLIT>(raw, QH[ks], QL[ks]);
     }
   }
-  const float cq = qvalid ? a.qs[b * a.qs_st[0] + hq * a.qs_st[2]] * a.scale_log2 : 0.0f;
+  // the query's factor of every logit, times 2^(2 kShift) for the scale the unpacked halves carry
+  const float cq = qvalid ? __builtin_amdgcn_ldexpf(a.qs[b * a.qs_st[0] + hq * a.qs_st[2]] * a.scale_log2,
+                                                    2 * kShift<SPLIT>)
+                          : 0.0f;
 
   // one step's loads: K straight into operand registers (key 16 mt + qc, d 32 ks + 8 grp .. + 7), V and the
   // scales direct-to-LDS (position p = 64 i + l holds key p / 16 in the VT_DECODE layout)
@@ -805,7 +818,7 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pw[4 + 16 * dt + 4 * grp + i] = __builtin_amdgcn_ldexpf(O[dt][i], -E);
+      for (int i = 0; i < 4; ++i) pw[4 + 16 * dt + 4 * grp + i] = __builtin_amdgcn_ldexpf(O[dt][i], kShift<SPLIT> - E);
   }
   __syncthreads();
   // ---- merge the 4 wavefronts in order: thread -> (column, 8 d values) ----
