@@ -58,8 +58,13 @@ def parse():
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="only print the HBM traffic summary of the rocprofv3 --pmc runs under DIR "
                          "(fetch/, write/, copy_fetch/, copy_write/)")
-    ap.add_argument("--title", default="", help="title of the --summarize-pmc summary")
-    ap.add_argument("--program", default="", help="the bench.py arguments the --summarize-pmc runs profiled")
+    ap.add_argument("--summarize-sq", metavar="DIR",
+                    help="only print the clock / matrix-unit / vector-unit summary of a rocprofv3 --pmc run under DIR "
+                         "that collected GRBM_GUI_ACTIVE, SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES and "
+                         "SQ_BUSY_CYCLES")
+    ap.add_argument("--title", default="", help="title of the --summarize-pmc / --summarize-sq summary")
+    ap.add_argument("--program", default="",
+                    help="the bench.py arguments the --summarize-pmc / --summarize-sq runs profiled")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (MiB)")
     return ap.parse_args()
 
@@ -198,6 +203,56 @@ def summarize_pmc(d, copy_mib, title, program):
     print("\nbench.py reads the record below and reports a kernel's traffic only while its source file still has "
           "the SHA-256 stored with it (comments and whitespace ignored).\n")
     print(TRAFFIC_TAG + json.dumps(rec))
+
+
+SQ_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES")
+
+
+def summarize_sq(d, title, program, simds=1024, xcds=8):
+    """Markdown summary, per HEAL kernel, of one rocprofv3 --pmc run of SQ_COUNTERS: the clock (GRBM_GUI_ACTIVE
+    per XCD over the dispatch's duration), and per SIMD the cycles, the matrix-unit busy cycles and the vector
+    instructions other than MFMA (chip-wide counts over the MI355X's 1024 SIMDs)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    disp = defaultdict(dict)
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            disp[key][r["Counter_Name"]] = float(r["Counter_Value"])
+            disp[key]["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    per = defaultdict(list)
+    for (_, name), c in disp.items():
+        sym = short_symbol(name)
+        if kernel_source(sym) is not None and all(k in c for k in SQ_COUNTERS):
+            per[sym].append(c)
+    print(f"# Clock, matrix-unit and vector-unit counters: {title}\n")
+    print("Command (from the repository root on one MI355X, ROCm 7.2; D = an output directory):\n")
+    print("```")
+    print("cd /tmp && export TMPDIR=/tmp")
+    print(f"timeout -s KILL 120 rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --kernel-trace --output-format csv -d $D "
+          f"-o pmc -- python3 /root/repo/bench.py {program}")
+    print(f"python3 /root/repo/bench.py --summarize-sq $D --title '{title}' --program '{program}'")
+    print("```\n")
+    print(f"Averages over the dispatches.  Clock = GRBM_GUI_ACTIVE / {xcds} XCDs / duration.  Per SIMD = chip-wide "
+          f"count / {simds}.  SQ_VALU_MFMA_BUSY_CYCLES counts 32 cycles per v_mfma_f32_32x32x16_f16 (16 per "
+          "v_mfma_f32_16x16x32_f16); a vector instruction of a 64-wide wavefront occupies a 16-lane SIMD for 4 "
+          "cycles.  The counter window of a dispatch of a few microseconds is longer than the kernel, so the clock "
+          "(and the fractions) hold for long dispatches only.\n")
+    print("| kernel | dispatches | duration (us) | clock (GHz) | cycles / SIMD | MFMA busy / SIMD | MFMA busy fraction "
+          "| VALU instructions (non-MFMA) / SIMD | VALU cycles fraction |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for sym in sorted(per):
+        cs = per[sym]
+        avg = lambda k: sum(c[k] for c in cs) / len(cs)
+        ns = avg("_ns")
+        clock = avg("GRBM_GUI_ACTIVE") / xcds / ns
+        cyc = clock * ns
+        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / simds
+        valu = (avg("SQ_INSTS_VALU") - avg("SQ_INSTS_MFMA")) / simds
+        print(f"| `{sym}` | {len(cs)} | {ns / 1e3:.1f} | {clock:.2f} | {cyc:.3g} | {busy:.3g} | {busy / cyc:.3f} | "
+              f"{valu:.3g} | {4 * valu / cyc:.3f} |")
 
 
 # ------------------------------------------------------------------------------------------------- timing
@@ -1021,6 +1076,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.copy_mib, args.title, args.program)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.title, args.program)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
