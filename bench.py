@@ -578,8 +578,17 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10):
     torch.cuda.synchronize()
     fused = lambda M: M <= 64      # the split in the GEMM's prologue (same bits as split + GEMM)
     derived = lambda M: M == 1     # and the row exponent there too
+    # K split across workgroups where heal_gemm_comp_f32a_splitk cuts it (16 rows, K = 14336), with its workspace
+    ws = {}
+    for (M, K, N) in shapes:
+        S = heal.heal_gemm_comp_f32a_splitk_slices(M, N, K, 2) if fused(M) and not derived(M) else 1
+        if S > 1:
+            ws[(M, K, N)] = (S, torch.empty(heal.heal_gemm_comp_f32a_workspace_bytes(M, N, K, 2), dtype=torch.uint8,
+                                            device="cuda"))
     variants = {(M, K, N): heal.heal_gemm_comp_variant(M, N, K, 2) + (" FP32-A" if fused(M) else "")
-                + (", exponent in the kernel" if derived(M) else "") for (M, K, N) in shapes}
+                + (", exponent in the kernel" if derived(M) else "")
+                + (f", K split in {ws[(M, K, N)][0]} (heal_gemm_comp_f32a_splitk: NC4 slices + reduce)"
+                   if (M, K, N) in ws else "") for (M, K, N) in shapes}
     timer = Timer()
 
     def step(i, record):
@@ -593,10 +602,7 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10):
             else:
                 heal.heal_split(x, hi=ah, lo=al, exps=ea)
             e0 = timer.start() if record else None
-            if fused(M):
-                heal.heal_gemm_comp_f32a(x, None if derived(M) else ea, bh, None, eb, c=c)
-            else:
-                heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
+            llama_gemm(heal, M, K, N, x, ah, al, ea, bh, eb, c, fused, derived, ws)
             if record:
                 timer.stop((M, K, N), e0)
 
@@ -612,7 +618,7 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10):
     step_s = t0.elapsed_time(t1) * 1e-3 / steps
     flops_step = sum(2.0 * M * N * K for (M, K, N) in shapes)
     durs = timer.durations()
-    graph_s = per_launch_in_graph(heal, bufs, weights, fused, derived)
+    graph_s = per_launch_in_graph(heal, bufs, weights, fused, derived, ws)
     per_shape, by_variant = {}, {}
     for (M, K, N) in shapes:
         d = durs[(M, K, N)]
@@ -645,7 +651,18 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10):
     return row
 
 
-def per_launch_in_graph(heal, bufs, weights, fused, derived, launches=24, min_bytes=300e6):
+def llama_gemm(heal, M, K, N, x, ah, al, ea, bh, eb, c, fused, derived, ws):
+    """one projection of the Llama row: FP32 activations split in the GEMM's prologue for M <= 64 (with K cut into
+    slices where `ws` holds a workspace for the shape), else the split parts"""
+    if (M, K, N) in ws:
+        heal.heal_gemm_comp_f32a_splitk(x, ea, bh, None, eb, c=c, workspace=ws[(M, K, N)][1])
+    elif fused(M):
+        heal.heal_gemm_comp_f32a(x, None if derived(M) else ea, bh, None, eb, c=c)
+    else:
+        heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
+
+
+def per_launch_in_graph(heal, bufs, weights, fused, derived, ws, launches=24, min_bytes=300e6):
     """Per-launch time of each shape's GEMM alone: `launches` back-to-back launches captured in one HIP graph and
     replayed three times (no host launch cost between them), walking through enough copies of the shape's weights
     (>= min_bytes, beyond the 256 MB memory-side cache) that every launch reads them from HBM."""
@@ -658,10 +675,7 @@ def per_launch_in_graph(heal, bufs, weights, fused, derived, launches=24, min_by
         copies = list(base) + [base[0].clone() for _ in range(need - len(base))]
 
         def launch(bh):
-            if fused(M):
-                heal.heal_gemm_comp_f32a(x, None if derived(M) else ea, bh, None, eb, c=c)
-            else:
-                heal.heal_gemm_comp(ah, al, ea, bh, None, eb, c=c)
+            llama_gemm(heal, M, K, N, x, ah, al, ea, bh, eb, c, fused, derived, ws)
 
         for i in range(len(copies)):
             launch(copies[i])

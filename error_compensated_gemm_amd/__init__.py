@@ -97,6 +97,12 @@ def load():
     L.heal_gemm_comp_workspace_bytes.argtypes = [i64, i64, i64, i32]
     L.heal_gemm_comp_splitk_slices.restype = i32
     L.heal_gemm_comp_splitk_slices.argtypes = [i64, i64, i64, i32]
+    L.heal_gemm_comp_f32a_splitk.restype = i32
+    L.heal_gemm_comp_f32a_splitk.argtypes = [i64, i64, i64, p, i64, p, p, p, p, i64, p, i64, p, ctypes.c_size_t, p]
+    L.heal_gemm_comp_f32a_workspace_bytes.restype = ctypes.c_size_t
+    L.heal_gemm_comp_f32a_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    L.heal_gemm_comp_f32a_splitk_slices.restype = i32
+    L.heal_gemm_comp_f32a_splitk_slices.argtypes = [i64, i64, i64, i32]
     L.heal_qkv_quant_i16.restype = i32
     L.heal_qkv_quant_i16.argtypes = [p, i64, i64, i64, i64, p, i64, p, i64, p]
     L.heal_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -118,7 +124,8 @@ EXPORTED = ("heal_status_str", "heal_abi_version", "heal_split", "heal_gemm_comp
             "heal_attn_paged_workspace_bytes", "heal_attn_decode_paged", "heal_gemm_comp_quant_i16",
             "heal_channel_exponents", "heal_split_scaled", "heal_unpack_i16", "heal_row_exponents",
             "heal_gemm_comp_f32a", "heal_gemm_comp_splitk", "heal_gemm_comp_workspace_bytes",
-            "heal_gemm_comp_splitk_slices", "heal_attn_dual_fp16_noalloc")
+            "heal_gemm_comp_splitk_slices", "heal_attn_dual_fp16_noalloc", "heal_gemm_comp_f32a_splitk",
+            "heal_gemm_comp_f32a_workspace_bytes", "heal_gemm_comp_f32a_splitk_slices")
 HEAL_ATTN_NOALLOC_MAX_WORKSPACE = 8 << 20
 
 
@@ -325,6 +332,41 @@ def heal_gemm_comp_f32a(a, a_exp, b_hi, b_lo, b_exp, c=None):
         raise ValueError("b_lo must match b_hi's shape and strides")
     _check(load().heal_gemm_comp_f32a(M, N, K, _ptr(a), _ld(a), _ptr(a_exp), _ptr(b_hi), _ptr(b_lo), _ptr(b_exp),
                                       _ld(b_hi), _ptr(c), _ld(c), _stream(a.device)))
+    return c
+
+
+def heal_gemm_comp_f32a_workspace_bytes(M: int, N: int, K: int, products: int) -> int:
+    """Workspace bytes heal_gemm_comp_f32a_splitk needs with row exponents given (0 when it does not split K)."""
+    return int(load().heal_gemm_comp_f32a_workspace_bytes(M, N, K, products))
+
+
+def heal_gemm_comp_f32a_splitk_slices(M: int, N: int, K: int, products: int) -> int:
+    """K slices heal_gemm_comp_f32a_splitk uses with row exponents given (1: no split)."""
+    return int(load().heal_gemm_comp_f32a_splitk_slices(M, N, K, products))
+
+
+def heal_gemm_comp_f32a_splitk(a, a_exp, b_hi, b_lo, b_exp, c=None, workspace=None):
+    """heal_gemm_comp_f32a with K split across workgroups for 8..16 rows and K >= 8192 (row exponents ``a_exp``
+    required for the split; partials added in slice order): bit for bit heal_split + heal_gemm_comp_splitk.  A
+    workspace of heal_gemm_comp_f32a_workspace_bytes() is allocated with torch when none is given."""
+    import torch
+
+    L = load()
+    M, K = a.shape
+    N = b_hi.shape[0]
+    if c is None:
+        c = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.float32, device=a.device)[:, :N]
+    if b_lo is not None and (b_lo.shape != b_hi.shape or b_lo.stride() != b_hi.stride()):
+        raise ValueError("b_lo must match b_hi's shape and strides")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is None and a_exp is not None:
+        need = heal_gemm_comp_f32a_workspace_bytes(M, N, K, 3 if b_lo is not None else 2)
+        if need:
+            workspace = torch.empty((need + 255) // 256 * 256, dtype=torch.uint8, device=a.device)
+    if workspace is not None:
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check(L.heal_gemm_comp_f32a_splitk(M, N, K, _ptr(a), _ld(a), _ptr(a_exp), _ptr(b_hi), _ptr(b_lo), _ptr(b_exp),
+                                        _ld(b_hi), _ptr(c), _ld(c), ws_ptr, ws_bytes, _stream(a.device)))
     return c
 
 

@@ -213,6 +213,36 @@ heal_status heal_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const void* a
                                                 c, ldc, workspace, (hipStream_t)stream));
 }
 
+size_t heal_gemm_comp_f32a_workspace_bytes(int64_t M, int64_t N, int64_t K, int products) {
+  if (!gemm_sizes_ok(M, N, K) || products < 2 || products > 3) return 0;
+  return heal::gemm_comp_f32a_workspace(M, N, K, products == 3);
+}
+
+int heal_gemm_comp_f32a_splitk_slices(int64_t M, int64_t N, int64_t K, int products) {
+  if (!gemm_sizes_ok(M, N, K) || products < 2 || products > 3) return 1;
+  return heal::gemm_comp_f32a_slices(M, N, K, products == 3);
+}
+
+heal_status heal_gemm_comp_f32a_splitk(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda,
+                                       const int32_t* a_exp, const void* b_hi, const void* b_lo,
+                                       const int32_t* b_exp, int64_t ldb, float* c, int64_t ldc, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (!gemm_sizes_ok(M, N, K)) return HEAL_ERR_SHAPE;
+  if (M == 0 || N == 0) return HEAL_OK;
+  if (!c || (!a_exp && M > 16) || (K > 0 && (!a || !b_hi))) return HEAL_ERR_NULL;
+  if (lda < K || ldb < K || ldc < N) return HEAL_ERR_STRIDE;
+  if ((a && !aligned16(a)) || (b_hi && !aligned16(b_hi)) || (b_lo && !aligned16(b_lo)) || !aligned16(c) ||
+      (a_exp && !aligned4(a_exp)) || (b_exp && !aligned4(b_exp)) || (lda & 3) || (ldb & 7) || (ldc & 3))
+    return HEAL_ERR_ALIGN;
+  // without row exponents the call is heal_gemm_comp_f32a (exponents derived in the kernel), unsplit
+  const size_t need = a_exp ? heal::gemm_comp_f32a_workspace(M, N, K, b_lo != nullptr) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return HEAL_ERR_WORKSPACE;
+  return launched(heal::launch_gemm_comp_f32a_splitk(M, N, K, a, lda, a_exp, (const uint16_t*)b_hi,
+                                                     (const uint16_t*)b_lo, b_exp, ldb, c, ldc, workspace,
+                                                     (hipStream_t)stream));
+}
+
 heal_status heal_qkv_quant_i16(const float* x, int64_t tokens, int64_t heads, int64_t head_dim,
                                int64_t ld_x, int16_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                                void* stream) {

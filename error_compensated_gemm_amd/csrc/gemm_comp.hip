@@ -28,8 +28,8 @@
 //   * streamed-B kernel (M <= 16, N of at least three 16-column blocks per CU, A's parts within 60 KB): one
 //     persistent workgroup per CU splits A once into LDS and walks its column blocks, B arriving through a
 //     ring of direct-to-LDS stages that runs on from one block into the next.
-//   * split K (heal_gemm_comp_splitk only): the tile or skinny kernel on slices of K into FP32 partials, then
-//     an ordered reduction that applies the exponents.
+//   * split K (heal_gemm_comp_splitk, and heal_gemm_comp_f32a_splitk for FP32 A at 8..16 rows): the tile or
+//     skinny kernel on slices of K into FP32 partials, then an ordered reduction that applies the exponents.
 #include <type_traits>
 
 #include "heal_internal.h"
@@ -579,17 +579,23 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
     const uint16_t* __restrict__ bl, const int32_t* __restrict__ eb, int64_t ldb, float* __restrict__ C,
     int64_t ldc, const float* __restrict__ af = nullptr, int64_t kslice = 0) {
   static_assert(!AF32 || (ALO && PART == HEAL_F16), "FP32 A: FP16 parts, both A parts");
-  static_assert(!SPLITK || !AF32, "split K: 16-bit parts");
+  static_assert(!SPLITK || !AF32 || (MT == 1 && !AEXP && !ALDS),
+                "split K with FP32 A: at most 16 rows, given exponents, A split per step");
   static_assert(!ALDS || (AF32 && MT == 1), "A split into LDS: FP32 A, at most 16 rows");
+  // SPLITK: this workgroup's slice [k0, k0 + kslice) of K; the partial goes to slice blockIdx.y of C (rows of
+  // ldc floats) without exponents, which the reduction applies.  FP32 A keeps ea: it prescales the split.
   if constexpr (SPLITK) {
     const int64_t k0 = (int64_t)blockIdx.y * kslice;
     K = K - k0 < kslice ? K - k0 : kslice;
-    ah += k0;
+    if constexpr (AF32) {
+      af += k0;
+    } else {
+      ah += k0;
+      if constexpr (ALO) al += k0;
+    }
     bh += k0;
-    if constexpr (ALO) al += k0;
     if constexpr (BLO) bl += k0;
     C += (int64_t)blockIdx.y * M * ldc;
-    ea = nullptr;
     eb = nullptr;
   }
   __shared__ float red[kSkWaves][MT * NC][4][64];
@@ -605,7 +611,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(
   {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     if (wv == 0) {
-      if (!AEXP && ea) exp_pre = ea[lane < M ? lane : M - 1];
+      if (!AEXP && !SPLITK && ea) exp_pre = ea[lane < M ? lane : M - 1];
     } else if (wv == 1) {
       if (eb) exp_pre = eb[n0 + lane < N ? n0 + lane : N - 1];
     }
@@ -1787,6 +1793,23 @@ void launch_split_kernel(const SplitPlan& p, int64_t M, int64_t N, int64_t K, co
   }
 }
 
+// FP32 A (split in the kernel with the given row exponents): the skinny plan at 8..16 rows only
+SplitPlan plan_split_f32a(int64_t M, int64_t N, int64_t K, bool b_lo) {
+  SplitPlan p = plan_split(M, N, K, true, b_lo);
+  if (!p.skinny || M > 16) p = SplitPlan{false, false, 1, K, 0};
+  return p;
+}
+
+template <bool BLO>
+void launch_split_kernel_f32a(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const float* af,
+                              const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl, int64_t ldb,
+                              float* ws, hipStream_t stream) {
+  const uint16_t* const none = nullptr;
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)p.S), block(64 * kSkWaves);
+  hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, 1, 4, true, BLO, true, true>), grid, block, 0, stream, M, N, K,
+                     none, none, ea, lda, bh, bl, (const int32_t*)nullptr, ldb, ws, p.ldw, af, p.kslice);
+}
+
 template <int PART>
 void launch_split_part(const SplitPlan& p, int64_t M, int64_t N, int64_t K, const uint16_t* ah, const uint16_t* al,
                        int64_t lda, const uint16_t* bh, const uint16_t* bl, int64_t ldb, float* ws,
@@ -1810,6 +1833,36 @@ size_t gemm_comp_workspace(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo
 
 int gemm_comp_slices(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo) {
   return (int)plan_split(M, N, K, a_lo, b_lo).S;
+}
+
+size_t gemm_comp_f32a_workspace(int64_t M, int64_t N, int64_t K, bool b_lo) {
+  const SplitPlan p = plan_split_f32a(M, N, K, b_lo);
+  return p.split ? (size_t)mul_sat(mul_sat(p.S, M), p.ldw * (int64_t)sizeof(float)) : 0;
+}
+
+int gemm_comp_f32a_slices(int64_t M, int64_t N, int64_t K, bool b_lo) {
+  return (int)plan_split_f32a(M, N, K, b_lo).S;
+}
+
+hipError_t launch_gemm_comp_f32a_splitk(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda,
+                                        const int32_t* a_exp, const uint16_t* b_hi, const uint16_t* b_lo,
+                                        const int32_t* b_exp, int64_t ldb, float* c, int64_t ldc, void* workspace,
+                                        hipStream_t stream) {
+  const SplitPlan p = plan_split_f32a(M, N, K, b_lo != nullptr);
+  if (!p.split || !a_exp)
+    return launch_gemm_comp_f32a(M, N, K, a, lda, a_exp, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
+  const int64_t red_blocks = (M * (p.ldw / 4) + 255) / 256;
+  if (!grid_fits((N + 63) / 64, 64 * kSkWaves) || !grid_fits(red_blocks, 256)) return hipErrorInvalidConfiguration;
+  float* ws = reinterpret_cast<float*>(workspace);
+  if (b_lo)
+    launch_split_kernel_f32a<true>(p, M, N, K, a, a_exp, lda, b_hi, b_lo, ldb, ws, stream);
+  else
+    launch_split_kernel_f32a<false>(p, M, N, K, a, a_exp, lda, b_hi, b_lo, ldb, ws, stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)red_blocks), dim3(256), 0, stream, (const float*)ws,
+                     (int)p.S, M, N, p.ldw, a_exp, b_exp, c, ldc);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,

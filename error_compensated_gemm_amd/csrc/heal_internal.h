@@ -48,6 +48,12 @@ hipError_t launch_gemm_comp_f32a(int64_t M, int64_t N, int64_t K, const float* a
                                  const uint16_t* b_hi, const uint16_t* b_lo, const int32_t* b_exp, int64_t ldb,
                                  float* c, int64_t ldc, hipStream_t stream);
 size_t gemm_comp_workspace(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo);
+size_t gemm_comp_f32a_workspace(int64_t M, int64_t N, int64_t K, bool b_lo);
+int gemm_comp_f32a_slices(int64_t M, int64_t N, int64_t K, bool b_lo);
+hipError_t launch_gemm_comp_f32a_splitk(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda,
+                                        const int32_t* a_exp, const uint16_t* b_hi, const uint16_t* b_lo,
+                                        const int32_t* b_exp, int64_t ldb, float* c, int64_t ldc, void* workspace,
+                                        hipStream_t stream);
 int gemm_comp_slices(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo);
 hipError_t launch_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const uint16_t* a_hi, const uint16_t* a_lo,
                                    const int32_t* a_exp, int64_t lda, const uint16_t* b_hi, const uint16_t* b_lo,

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define HEAL_ABI_VERSION 6
+#define HEAL_ABI_VERSION 7
 
 #if defined(__GNUC__) || defined(__clang__)
 #define HEAL_API __attribute__((visibility("default")))
@@ -246,6 +246,30 @@ HEAL_API heal_status heal_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, cons
  */
 HEAL_API size_t heal_gemm_comp_workspace_bytes(int64_t M, int64_t N, int64_t K, int products);
 HEAL_API int heal_gemm_comp_splitk_slices(int64_t M, int64_t N, int64_t K, int products);
+
+/*
+ * heal_gemm_comp_f32a_splitk -- heal_gemm_comp_f32a (A given as FP32 and split in the kernel, [TS 2B Mechanism])
+ * with K cut into slices as heal_gemm_comp_splitk cuts it, for 8..16 rows with K >= 8192 (a decode batch
+ * through a down projection), where each workgroup of the unsplit launch would re-read and re-split all of A
+ * for its 16 columns.  The slices, their kernel and the fixed-order reduction are those of
+ * heal_gemm_comp_splitk, so the result equals heal_split (FP32 A, HEAL_F16 parts, prescale, residual)
+ * followed by heal_gemm_comp_splitk bit for bit.  It splits only with row exponents given (a_exp non-NULL,
+ * e.g. from heal_row_exponents): with a_exp NULL, or where no split helps, the call is heal_gemm_comp_f32a
+ * itself, bit for bit, and needs no workspace.  Arguments as heal_gemm_comp_f32a.
+ * workspace: device memory of at least heal_gemm_comp_f32a_workspace_bytes(M, N, K, P) bytes (P = 2 with
+ * b_lo NULL, else 3), 256-byte aligned, owned by the caller, scratch on return.  Calls that share a workspace
+ * must not overlap.
+ * Errors: as heal_gemm_comp_f32a, and HEAL_ERR_WORKSPACE (workspace needed but NULL, too small or misaligned).
+ * heal_gemm_comp_f32a_workspace_bytes / heal_gemm_comp_f32a_splitk_slices: the workspace (0 when it does not
+ * split) and slice count (1 = no split) of a call with a_exp given; pure host functions; P outside 2..3 or
+ * sizes out of range give 0 bytes and 1 slice.
+ */
+HEAL_API heal_status heal_gemm_comp_f32a_splitk(int64_t M, int64_t N, int64_t K, const float* a, int64_t lda,
+                                       const int32_t* a_exp, const void* b_hi, const void* b_lo,
+                                       const int32_t* b_exp, int64_t ldb, float* c, int64_t ldc,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+HEAL_API size_t heal_gemm_comp_f32a_workspace_bytes(int64_t M, int64_t N, int64_t K, int products);
+HEAL_API int heal_gemm_comp_f32a_splitk_slices(int64_t M, int64_t N, int64_t K, int products);
 
 /*
  * heal_qkv_quant_i16 -- INT16 quantisation of Q, K or V per (token, head) ([TS 2A Solution]; [ABS]):

@@ -70,7 +70,7 @@ def test_glue_grid_limits_refused_before_launch():
 
 def test_version_and_status_strings(heal):
     lib = heal.load()
-    assert lib.heal_abi_version() == 6
+    assert lib.heal_abi_version() == 7
     for s in range(9):
         assert lib.heal_status_str(s).decode().startswith("HEAL")
     assert b"unknown" in lib.heal_status_str(99)
@@ -307,6 +307,40 @@ def test_splitk_validation_and_plan(heal):
     assert call(ah=None) == 1 and call(c=None) == 1
     assert call(lda=100) == 3 and call(ldc=100) == 3
     assert call(ah=MIS) == 4 and call(ldc=4098) == 4
+    assert call(ws=None) == 8                       # workspace needed, none given
+    assert call(ws_bytes=need - 4) == 8             # too small
+    assert call(ws=FAKE + 16) == 8                  # not 256-byte aligned
+    assert call(M=0) == 0                           # empty: nothing to do
+
+
+def test_f32a_splitk_validation_and_plan(heal):
+    """heal_gemm_comp_f32a_splitk: heal_gemm_comp_f32a's checks, then the workspace, needed only where K is split:
+    8..16 rows with K >= 8192 and row exponents given, the slices of heal_gemm_comp_splitk"""
+    lib = heal.load()
+    for M, N, K, P_ in ((16, 4096, 14336, 2), (16, 4096, 14336, 3), (8, 4096, 8192, 2), (13, 1000, 9001, 3)):
+        assert heal.heal_gemm_comp_f32a_splitk_slices(M, N, K, P_) == heal.heal_gemm_comp_splitk_slices(M, N, K, P_)
+        assert heal.heal_gemm_comp_f32a_workspace_bytes(M, N, K, P_) == heal.heal_gemm_comp_workspace_bytes(M, N, K, P_)
+    assert heal.heal_gemm_comp_f32a_splitk_slices(16, 4096, 14336, 2) == 8
+    need = heal.heal_gemm_comp_f32a_workspace_bytes(16, 4096, 14336, 2)
+    assert need == 8 * 16 * 4096 * 4
+    assert heal.heal_gemm_comp_f32a_splitk_slices(16, 4096, 4096, 2) == 1     # K < 8192: whole
+    assert heal.heal_gemm_comp_f32a_splitk_slices(4, 4096, 14336, 2) == 1     # under 8 rows: whole
+    assert heal.heal_gemm_comp_f32a_splitk_slices(64, 4096, 14336, 2) == 1    # over 16 rows: whole (FP32 A)
+    assert heal.heal_gemm_comp_f32a_splitk_slices(128, 4096, 14336, 2) == 1   # tile kernels: whole (FP32 A)
+    assert heal.heal_gemm_comp_f32a_workspace_bytes(16, 4096, 14336, 1) == 0   # A always has its low part
+    assert heal.heal_gemm_comp_f32a_splitk_slices(16, 4096, 14336, 4) == 1
+    assert heal.heal_gemm_comp_f32a_workspace_bytes(-1, 4, 4, 2) == 0
+
+    def call(M=16, N=4096, K=14336, a=FAKE, ea=FAKE, bh=FAKE, c=FAKE, lda=14336, ldb=14336, ldc=4096, ws=FAKE,
+             ws_bytes=need):
+        return lib.heal_gemm_comp_f32a_splitk(M, N, K, P(a) if a else None, lda, P(ea) if ea else None,
+                                              P(bh) if bh else None, None, None, ldb, P(c) if c else None, ldc,
+                                              P(ws) if ws else None, ws_bytes, None)
+    assert call(M=-1) == 2
+    assert call(K=(1 << 31) + 8, lda=(1 << 31) + 8, ldb=(1 << 31) + 8) == 2
+    assert call(a=None) == 1 and call(c=None) == 1 and call(M=17, ea=None) == 1
+    assert call(lda=100) == 3 and call(ldc=100) == 3
+    assert call(a=MIS) == 4 and call(lda=14338) == 4 and call(ldc=4098) == 4
     assert call(ws=None) == 8                       # workspace needed, none given
     assert call(ws_bytes=need - 4) == 8             # too small
     assert call(ws=FAKE + 16) == 8                  # not 256-byte aligned
