@@ -585,10 +585,10 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10):
         if S > 1:
             ws[(M, K, N)] = (S, torch.empty(heal.heal_gemm_comp_f32a_workspace_bytes(M, N, K, 2), dtype=torch.uint8,
                                             device="cuda"))
-    variants = {(M, K, N): heal.heal_gemm_comp_variant(M, N, K, 2) + (" FP32-A" if fused(M) else "")
-                + (", exponent in the kernel" if derived(M) else "")
-                + (f", K split in {ws[(M, K, N)][0]} (heal_gemm_comp_f32a_splitk: NC4 slices + reduce)"
-                   if (M, K, N) in ws else "") for (M, K, N) in shapes}
+    variants = {(M, K, N): (f"gemm_skinny_kernel M<=16 NC4 P2 FP32-A, K in {ws[(M, K, N)][0]} slices + "
+                            "splitk_reduce_kernel (heal_gemm_comp_f32a_splitk)") if (M, K, N) in ws else
+                (heal.heal_gemm_comp_variant(M, N, K, 2) + (" FP32-A" if fused(M) else "")
+                 + (", exponent in the kernel" if derived(M) else "")) for (M, K, N) in shapes}
     timer = Timer()
 
     def step(i, record):
