@@ -385,14 +385,23 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
       shh[r] = 0.0f;
       srest[r] = 0.0f;
     }
+    // K fragments one k step ahead: step ks + 1's reads are issued before step ks's MFMAs (a scheduling barrier
+    // keeps the compiler from sinking them), so the LDS latency runs under the matrix work
+    uint4 KH = P.kh[kv_pos(qcol, half)], KL = P.kl[kv_pos(qcol, half)];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const uint4 KH = P.kh[kv_pos(qcol, 2 * ks + half)];
-      const uint4 KL = P.kl[kv_pos(qcol, 2 * ks + half)];
+      uint4 KHn = KH, KLn = KL;
+      if (ks + 1 < 8) {
+        KHn = P.kh[kv_pos(qcol, 2 * (ks + 1) + half)];
+        KLn = P.kl[kv_pos(qcol, 2 * (ks + 1) + half)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
       shh = mfma32(KH, QH[ks], shh);
       srest = mfma32(KH, QL[ks], srest);
       srest = mfma32(KL, QH[ks], srest);
       if constexpr (kLoLo<SPLIT>) srest = mfma32(KL, QL[ks], srest);
+      KH = KHn;
+      KL = KLn;
     }
     // ---- scores of this lane's query for its 16 keys: key = 8 (r/4) + 4 half + r%4.  Keys past the end
     //      or above this query's causal limit are hidden: tile key kk is visible iff kk < lim, so the lane's
@@ -464,21 +473,28 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
     // ---- O^T [128 d x 32 queries] += V^T P~^T over these 32 keys (2 k-steps of 16).  The V^T operand of
     //      lane (d = 32 dt + l % 32, k-group g = l / 32) holds keys 16 kk2 + 4 g + 0..3 and
     //      16 kk2 + 8 + 4 g + 0..3: the same keys, in the same order, as the P~ registers ----
+    // the V^T fragments of (kk2, dt) step i = 4 kk2 + dt, read one step ahead of their MFMAs as K's above
+    auto read_v = [&](int i, uint4& VH, uint4& VL) {
+      const int k1 = 16 * (i >> 2) + 4 * (vq >> 1), d0 = 32 * (i & 3) + 16 * (vq & 1);
+      VH = join_v4i16(read_vt<VT_PREFILL>(P.vh, k1, d0, vi), read_vt<VT_PREFILL>(P.vh, k1 + 8, d0, vi));
+      VL = join_v4i16(read_vt<VT_PREFILL>(P.vl, k1, d0, vi), read_vt<VT_PREFILL>(P.vl, k1 + 8, d0, vi));
+    };
+    uint4 VH, VL;
+    read_v(0, VH, VL);
 #pragma unroll
-    for (int kk2 = 0; kk2 < 2; ++kk2) {
+    for (int i = 0; i < 8; ++i) {
+      const int kk2 = i >> 2, dt = i & 3;
       const uint4 PH = make_uint4(ph[4 * kk2], ph[4 * kk2 + 1], ph[4 * kk2 + 2], ph[4 * kk2 + 3]);
       const uint4 PL = make_uint4(pl[4 * kk2], pl[4 * kk2 + 1], pl[4 * kk2 + 2], pl[4 * kk2 + 3]);
-      const int k1 = 16 * kk2 + 4 * (vq >> 1);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d0 = 32 * dt + 16 * (vq & 1);
-        const uint4 VH = join_v4i16(read_vt<VT_PREFILL>(P.vh, k1, d0, vi), read_vt<VT_PREFILL>(P.vh, k1 + 8, d0, vi));
-        const uint4 VL = join_v4i16(read_vt<VT_PREFILL>(P.vl, k1, d0, vi), read_vt<VT_PREFILL>(P.vl, k1 + 8, d0, vi));
-        O[dt] = mfma32(VH, PH, O[dt]);
-        O[dt] = mfma32(VL, PH, O[dt]);
-        O[dt] = mfma32(VH, PL, O[dt]);
-        if constexpr (kLoLo<SPLIT>) O[dt] = mfma32(VL, PL, O[dt]);
-      }
+      uint4 VHn = VH, VLn = VL;
+      if (i + 1 < 8) read_v(i + 1, VHn, VLn);
+      __builtin_amdgcn_sched_barrier(0);
+      O[dt] = mfma32(VH, PH, O[dt]);
+      O[dt] = mfma32(VL, PH, O[dt]);
+      O[dt] = mfma32(VH, PL, O[dt]);
+      if constexpr (kLoLo<SPLIT>) O[dt] = mfma32(VL, PL, O[dt]);
+      VH = VHn;
+      VL = VLn;
     }
   };
 
