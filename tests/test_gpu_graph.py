@@ -104,3 +104,44 @@ def test_splitk_and_fp32a_graph_replays_equal_eager(heal):
         torch.cuda.synchronize()
         for w, t in zip(want, (c1, e2, c2)):
             assert torch.equal(w.view(torch.uint8), t.view(torch.uint8)), f"replay {rep}"
+
+
+def test_fp32a_splitk_graph_replays_equal_eager(heal):
+    """the FP32-A split-K GEMM of a 16-row down projection (row exponents, slices into the caller workspace,
+    the ordered reduction) under capture; the workspace is clobbered with NaN between replays"""
+    M, K, N = 16, 14336, 1024
+    banner(f"graph capture: row exponents + FP32-A split-K gemm {M}x{K}->{N}, 4 replays")
+    X = dev(workloads.llama_activations(M, K, seed=8))
+    W = dev(workloads.llama_weights_bf16(N, K, seed=8).view(np.int16)).view(torch.bfloat16)
+    bh, _, eb = heal.heal_split(W, residual=False)
+    assert heal.heal_gemm_comp_f32a_splitk_slices(M, N, K, 2) >= 2
+    ws = torch.empty(heal.heal_gemm_comp_f32a_workspace_bytes(M, N, K, 2), dtype=torch.uint8, device="cuda")
+    e = heal.heal_row_exponents(X)
+    c = heal.heal_gemm_comp_f32a_splitk(X, e, bh, None, eb, workspace=ws)
+
+    def path():
+        heal.heal_row_exponents(X, exps=e)
+        heal.heal_gemm_comp_f32a_splitk(X, e, bh, None, eb, c=c, workspace=ws)
+
+    path()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (e, c)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        c.fill_(float("nan"))
+        e.fill_(-99)
+        ws.view(torch.float32).fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for w, t in zip(want, (e, c)):
+            assert torch.equal(w.view(torch.uint8), t.view(torch.uint8)), f"replay {rep}"
