@@ -1695,6 +1695,8 @@ constexpr int64_t kSplitSkinnyMinK = 512;  // and for the skinny kernel
 constexpr int64_t kSplitSkinnyMinRows = 8;
 constexpr int64_t kSplitSkinnyFewRowsMinK = 8192;
 
+constexpr int kMaxSlices = 16;             // K slices, at most
+
 struct SplitPlan {
   bool split;      // false: heal_gemm_comp's own launch
   bool skinny;     // skinny kernel (four column blocks) or 128 x 128 tiles
@@ -1730,7 +1732,7 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo) {
   }
   int64_t S = target / wgs;  // at most one round: a partial second round costs more than the split gains
   if (S > K / min_k) S = K / min_k;
-  if (S > 16) S = 16;
+  if (S > kMaxSlices) S = kMaxSlices;
   if (S < 2) return p;
   const int64_t ks = ((K + S - 1) / S + 63) / 64 * 64;
   p.split = true;
@@ -1752,13 +1754,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t i = idx / nq, j0 = (idx - i * nq) * 4;
   const float* p = ws + i * ldw + j0;  // columns N .. ldw - 1 of a partial are never written and never stored
   const int64_t slice = M * ldw;
-  float4 acc = *reinterpret_cast<const float4*>(p);
-  for (int s = 1; s < S; ++s) {
-    const float4 v = *reinterpret_cast<const float4*>(p + s * slice);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  // all S partials are requested before the first addition (one memory latency instead of S in a row); the
+  // additions then run in slice order
+  float4 v[kMaxSlices];
+#pragma unroll
+  for (int s = 0; s < kMaxSlices; ++s)
+    if (s < S) v[s] = *reinterpret_cast<const float4*>(p + s * slice);
+  float4 acc = v[0];
+#pragma unroll
+  for (int s = 1; s < kMaxSlices; ++s) {
+    if (s < S) {
+      acc.x += v[s].x;
+      acc.y += v[s].y;
+      acc.z += v[s].z;
+      acc.w += v[s].w;
+    }
   }
   const int e = ea ? ea[i] : 0;
   const float r[4] = {acc.x, acc.y, acc.z, acc.w};
