@@ -185,12 +185,17 @@ __device__ __forceinline__ void split_p(float p, _Float16& h, _Float16& l) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+// CPOL: the transfer's cache policy bits (kNT: non-temporal, for cache rows that one launch reads once)
+constexpr int kNT = 2;
+template <int CPOL = 0>
 __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, CPOL);
 }
+template <int CPOL = 0>
 __device__ __forceinline__ void dma4(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, CPOL);
 }
+
 // s_waitcnt immediate: at most N vector-memory operations outstanding, all LDS operations done
 template <int N>
 constexpr int waitcnt_vm() {
@@ -629,7 +634,10 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
                           : 0.0f;
 
   // one step's loads: K straight into operand registers (key 16 mt + qc, d 32 ks + 8 grp .. + 7), V and the
-  // scales direct-to-LDS (position p = 64 i + l holds key p / 16 in the VT_DECODE layout)
+  // scales direct-to-LDS (position p = 64 i + l holds key p / 16 in the VT_DECODE layout).  The V and scale
+  // transfers are non-temporal (each launch reads the cache once; each V transfer covers whole 256-byte rows):
+  // 397 against 411 us at 64 x 8192 x 8 heads, 362 against 390 us for head-major pages.  K's loads stay plain:
+  // each reads 64 bytes of 16 rows, and non-temporal K loads ran slower (415 us).
   //  A step's keys past this wavefront's range are clamped to its last key (read, never used).  Paged: the
   //  page size is a power of two >= 32 and steps start at multiples of 32, so after that clamp every key of
   //  a step lies in the page of its first (clamped) key.  The wavefront's range (kpw <= 512 keys,
@@ -672,11 +680,11 @@ __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
       const int p = 64 * i + lane, key = p >> 4, c = (p & 15) ^ vt_swz<VT_DECODE>(key);
       int64_t j = j0 + key;
       if (j > jmax) j = jmax;
-      dma16(vb + (j & jmask) * kvs1 + 8 * c, &S.v[64 * i]);
+      dma16<kNT>(vb + (j & jmask) * kvs1 + 8 * c, &S.v[64 * i]);
     }
     int64_t j = j0 + (lane & 31);
     if (j > jmax) j = jmax;
-    dma4((lane < 32 ? ksp : vsp) + (j & jmask) * ss1, &S.sc[0]);
+    dma4<kNT>((lane < 32 ? ksp : vsp) + (j & jmask) * ss1, &S.sc[0]);
   };
 
   f32x4 O[8];

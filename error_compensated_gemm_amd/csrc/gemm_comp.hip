@@ -133,9 +133,12 @@ constexpr int waitcnt_vm() {
 }
 
 // one 16-byte direct global -> LDS transfer per lane: lane l's bytes land at lds_wave_base + 16 l
+// CPOL: the transfer's cache policy bits (kNT: non-temporal, for a stream read once per launch)
+constexpr int kNT = 2;
+template <int CPOL = 0>
 __device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                   (lds_void_t*)(lds_wave_base), 16, 0, 0);
+                                   (lds_void_t*)(lds_wave_base), 16, 0, CPOL);
 }
 
 // QUANT: instead of storing C, quantise each (row, 128-column head) of it to INT16 exactly as
@@ -1045,8 +1048,8 @@ __global__ __launch_bounds__(64 * W) void gemm_stream_kernel(
     for (int i = 0; i < 4; ++i) {
       int64_t k = k0 + 8 * tch[i];
       if (k > klast) k = klast;  // a partial last stage: in-row chunks, cleared when read
-      dma16(ibh[i] + k, slot + wave * SLOT + i * 64);
-      if constexpr (BLO) dma16(ibl[i] + k, slot + wave * SLOT + 256 + i * 64);
+      dma16<kNT>(ibh[i] + k, slot + wave * SLOT + i * 64);
+      if constexpr (BLO) dma16<kNT>(ibl[i] + k, slot + wave * SLOT + 256 + i * 64);
     }
     advance(pi);
   };
@@ -1276,21 +1279,22 @@ int cu_count() {
 }
 
 // Launch shape of the streamed kernel: 4 wavefronts with 4 ring stages of 4 KB each (2 when B has a low part), so
-// 64 KB in flight per CU, and one workgroup per CU (at most 8 column blocks each).  It serves at most 16 rows where
-// A's planes fit their 60 KB, K spans at least one stage per wavefront, and N gives every CU at least three column
-// blocks: measured on MI355X against the register-prefetch kernel (M = 1, weights rotated through HBM, average
-// kernel durations from the trace), 26.2-26.9 against 27.6-27.8 us at N x K = 14336 x 4096 and 44.4-44.6 against
-// 51.6-51.8 at 28672 x 4096, where it splits A once per CU and keeps the ring running from block to block; at
-// 8192 x 4096 the two are level (17.8-19.6 against 18.5-18.9 us), and with one block per workgroup (N = 4096)
-// the register-prefetch kernel's 8 wavefronts are ahead (26.3 against 27.8 us at K = 14336).  Six ring stages
-// instead of four (A's planes in a smaller array) did not help (26.9 against 26.2 us at 14336 x 4096).
-// heal_gemm_comp and heal_gemm_comp_f32a take the same decision from (M, N, K, A's low part), so they keep giving
-// the same bits.
+// 64 KB in flight per CU, and one workgroup per CU (at most 8 column blocks each).  The ring's transfers are
+// non-temporal (B is read once per launch): a 117 MB stream then takes 24.7 instead of 26.5 us (M = 1, N x K =
+// 14336 x 4096), 41.9 instead of 46.0 us at 28672 x 4096.  It serves at most 16 rows where A's planes fit their
+// 60 KB, K spans at least one stage per wavefront, every CU gets a column block, and the CUs' stages (column blocks
+// x stages of 128 of K) come to at least 64 each: measured on MI355X against the register-prefetch kernel (M = 1,
+// weights rotated through HBM, graph-replayed launches), 26.2 against 27.0 us at N x K = 4096 x 14336 (one block
+// and 112 stages per CU), 17.2 against 17.6 us at 8192 x 4096 (64 stages), but 11.9 against 10.4 us at 4096 x 4096
+// (32 stages: the ring barely fills before the block ends).  Six ring stages instead of four (A's planes in a
+// smaller array, plain transfers) did not help (26.9 against 26.2 us at 14336 x 4096).  heal_gemm_comp and
+// heal_gemm_comp_f32a take the same decision from (M, N, K, A's low part), so they keep giving the same bits.
 constexpr int kStW = 4, kStD = 4, kStDLo = 2;
 
 bool stream_fits(int64_t M, int64_t N, int64_t K, bool a_lo) {
   if (M < 1 || M > 16 || K < (int64_t)kStW * kStK - (kStK - 1)) return false;
-  if ((N + 15) / 16 < 3 * (int64_t)cu_count()) return false;
+  const int64_t nblk = (N + 15) / 16, cus = cu_count(), ns = (K + kStK - 1) / kStK;
+  if (nblk < cus || nblk * ns < 64 * cus) return false;
   return (a_lo ? 2 : 1) * M * stream_rs(K) <= kStACap;
 }
 

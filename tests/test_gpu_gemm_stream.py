@@ -1,5 +1,6 @@
 """Element-wise GPU parity of the streamed-B kernel (gemm_stream_kernel) that serves at most 16 rows when N gives
-every CU at least three column blocks of 16 and A's split parts fit in LDS: each persistent workgroup walks several
+every CU a column block of 16, the CUs' blocks times K's stages of 128 come to at least 64 per CU, and A's split
+parts fit in LDS: each persistent workgroup walks several
 column blocks, and each block's 16 rows of B stream through a ring of direct-to-LDS stages of 128 of K.
 
 Covered: both A sources (16-bit parts, and FP32 rows split in the kernel with given or derived row exponents),
