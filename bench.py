@@ -1010,7 +1010,8 @@ def row_fused_and_vendor(heal, workloads, dev):
 def row_stack_with_cpu_baseline(timeout_s=900):
     """The model-level configuration: a 32-layer Llama-style stack (d 4096, 32/8 heads, FFN 14336, vocabulary 128256,
     random bf16 weights, 512-token prompt, 64 greedy steps) run with the HEAL kernels and in plain bf16, both
-    against the FP64 forward, which is this row's oracle leg (timed on the host).  tests/llama_stack.py runs in a
+    against the FP64 forward, which is this row's oracle leg (timed on the host); plus the time per output token
+    of one graph-replayed decode step for HEAL, a native bf16 pipeline and a global FP32 pipeline.  tests/llama_stack.py runs in a
     child process so that its ~70 GB of host memory is returned when it ends."""
     import subprocess
 
@@ -1030,6 +1031,8 @@ def row_stack_with_cpu_baseline(timeout_s=900):
         "config": res["config"], "seed": res["seed"], "fp64_top2_gap_min": res["fp64_top2_gap_min"],
         "heal": {k: res["heal"][k] for k in keep if k in res["heal"]},
         "bf16": {k: res["bf16"][k] for k in keep if k in res["bf16"]},
+        # time per output token of one decode step (HIP-graph replays): HEAL, native bf16, global FP32
+        "tpot": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.get("tpot", {}).items()},
         "wall_s": round(wall, 1),
         "cpu_baseline": {"value": round(tokens / res["fp64_forward_s"], 3), "unit": "tokens/s",
                          "cores": host_threads(), "kind": "oracle",

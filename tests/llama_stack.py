@@ -10,8 +10,10 @@
   * FP64: ``oracle.stack``.
 The FP64 model decodes greedily; the two 16-bit paths are then fed its tokens (teacher forcing) and their
 argmax compared with its argmax at every step, and each also decodes on its own to find its first divergence.
-Reported: per-step argmax agreement, first divergence, final-hidden normwise error against FP64, and the
-median time of one decode step (informational; the bf16 path is plain torch, not an inference engine).
+Reported: per-step argmax agreement, first divergence, final-hidden normwise error against FP64, the median
+time of one decode step (informational; the bf16 path is plain torch, not an inference engine), and the time per
+output token of one decode step captured as a HIP graph for HEAL, a native bf16 pipeline and a global FP32
+pipeline (TorchStep, plain torch with the HEAL path's fusion of the projections).
 
 Run as a script for the full-size stack (32 layers, d 4096, 32/8 heads, FFN 14336, vocab 128256, 512-token
 prompt, 64 steps; it needs ~100 GB of host memory for the FP64 weights):
@@ -227,19 +229,74 @@ class Bf16Path:
         return hn[0], logits, torch.argmax(logits)
 
 
-def graph_step_ms(path: HealPath, tok: int, pos: int, reps: int = 20) -> float:
-    """GPU time of one decode step of the HEAL path, captured once as a HIP graph and replayed (it rewrites the
-    same cache slot with the same values every time)."""
-    ids = torch.tensor([tok], dtype=torch.int32, device="cuda")
+class TorchStep:
+    """One decode step of the same stack in plain torch in one dtype, for the time-per-token comparison:
+    bfloat16 is the native 16-bit pipeline (bf16 weights, activations and KV cache; matrix products on the
+    16-bit matrix units), float32 the global FP32 pipeline (FP32 weights, activations and KV cache; TF32 off).
+    The projections are fused as the HEAL path fuses them (Q, K and V in one product, gate and up in one), the
+    cache holds ``ctx`` positions, and attention at position ``pos`` is two batched products over the first
+    pos + 1 keys around an FP32 softmax; norms also reduce in FP32.  It times the launch structure; its
+    arithmetic is not checked against FP64."""
+
+    def __init__(self, w: dict, cfg: dict, dtype, ctx: int):
+        self.cfg, self.dt = cfg, dtype
+        L = cfg["layers"]
+        t = lambda *ks: torch.cat([w[k] for k in ks]).to(dtype)  # [N, K], as torch.nn.Linear holds it
+        self.wqkv = [t(f"{l}.wq", f"{l}.wk", f"{l}.wv") for l in range(L)]
+        self.wo = [t(f"{l}.wo") for l in range(L)]
+        self.wgu = [t(f"{l}.wg", f"{l}.wu") for l in range(L)]
+        self.wd = [t(f"{l}.wd") for l in range(L)]
+        self.head = t("head")
+        self.emb = w["emb"].to(dtype)
+        cs = rope_table(ctx)
+        self.cos, self.sin = cs[..., 0].to(dtype), cs[..., 1].to(dtype)
+        self.k = [torch.zeros((cfg["hkv"], ctx, 128), dtype=dtype, device="cuda") for _ in range(L)]
+        self.v = [torch.zeros((cfg["hkv"], ctx, 128), dtype=dtype, device="cuda") for _ in range(L)]
+
+    def rms(self, x):
+        xf = x.float()
+        return (xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + EPS)).to(self.dt)
+
+    def rope(self, x, pos):  # x [H, 128]
+        a, b = x[:, :64], x[:, 64:]
+        c, s = self.cos[pos], self.sin[pos]
+        return torch.cat([a * c - b * s, b * c + a * s], -1)
+
+    def step(self, ids: torch.Tensor, pos: int):
+        cfg = self.cfg
+        hq, hkv, F = cfg["hq"], cfg["hkv"], cfg["f"]
+        g = hq // hkv
+        lin = torch.nn.functional.linear  # x W^T
+        x = self.emb[ids.long()]  # [1, d]
+        for l in range(cfg["layers"]):
+            qkv = lin(self.rms(x), self.wqkv[l])
+            q = self.rope(qkv[0, :hq * 128].view(hq, 128), pos)
+            k = self.rope(qkv[0, hq * 128:(hq + hkv) * 128].view(hkv, 128), pos)
+            self.k[l][:, pos] = k
+            self.v[l][:, pos] = qkv[0, (hq + hkv) * 128:].view(hkv, 128)
+            K, V = self.k[l][:, :pos + 1], self.v[l][:, :pos + 1]  # [hkv, pos + 1, 128], rows contiguous
+            qt = q.view(hkv, g, 128).transpose(1, 2).contiguous()  # [hkv, 128, g]
+            sc = torch.matmul(K, qt).float() * (1.0 / np.sqrt(128.0))  # [hkv, pos + 1, g]
+            pt = torch.softmax(sc, dim=1).to(self.dt).transpose(1, 2).contiguous()  # [hkv, g, pos + 1]
+            o = torch.matmul(pt, V)  # [hkv, g, 128]
+            x = x + lin(o.reshape(1, hq * 128), self.wo[l])
+            gu = lin(self.rms(x), self.wgu[l])
+            x = x + lin(torch.nn.functional.silu(gu[:, :F]) * gu[:, F:], self.wd[l])
+        return torch.argmax(lin(self.rms(x), self.head))
+
+
+def graph_ms(fn, reps: int = 20) -> float:
+    """GPU time of ``fn()`` (one decode step), captured once as a HIP graph and replayed (each replay rewrites the
+    same cache slot with the same values)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        path.forward_dev(ids, pos)
+        fn()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        path.forward_dev(ids, pos)
+        fn()
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
@@ -250,6 +307,31 @@ def graph_step_ms(path: HealPath, tok: int, pos: int, reps: int = 20) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def graph_step_ms(path: HealPath, tok: int, pos: int, reps: int = 20) -> float:
+    """GPU time of one decode step of the HEAL path, captured once as a HIP graph and replayed."""
+    ids = torch.tensor([tok], dtype=torch.int32, device="cuda")
+    return graph_ms(lambda: path.forward_dev(ids, pos), reps)
+
+
+def tpot_compare(w: dict, cfg: dict, tok: int, pos: int, heal_ms: float) -> dict:
+    """Time per output token of one decode step at position ``pos``, each pipeline captured as a HIP graph and
+    replayed: HEAL (measured by the caller), native bf16 and global FP32 (TorchStep); the ratios the pages report
+    are FP32 / bf16 (the global FP32 pipeline's overhead) and HEAL / bf16."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    torch.set_float32_matmul_precision("highest")
+    out = {"position": pos, "heal_ms": heal_ms}
+    ids = torch.tensor([tok], dtype=torch.int32, device="cuda")
+    for name, dt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+        st = TorchStep(w, cfg, dt, pos + 1)
+        out[f"{name}_ms"] = graph_ms(lambda: st.step(ids, pos))
+        del st
+        torch.cuda.empty_cache()
+    out["fp32_over_bf16"] = out["fp32_ms"] / out["bf16_ms"]
+    out["heal_over_bf16"] = heal_ms / out["bf16_ms"]
+    out["heal_over_fp32"] = heal_ms / out["fp32_ms"]
+    return out
 
 
 def _nw(a, b):
@@ -313,6 +395,9 @@ def run(cfg: dict, seed: int = 0, log=print) -> dict:
         log(f"[stack] {name}: {json.dumps(out[name])} ({time.time() - t0:.0f} s)")
         del path
         torch.cuda.empty_cache()
+    pos = cfg["prompt"] + cfg["steps"] - 1
+    out["tpot"] = tpot_compare(w, cfg, toks[-1], pos, out["heal"]["decode_step_ms_hip_graph"])
+    log(f"[stack] tpot: {json.dumps(out['tpot'])} ({time.time() - t0:.0f} s)")
     return out
 
 

@@ -44,3 +44,8 @@ def test_full_stack_agrees_with_fp64(heal):
     assert h["final_hidden_normwise_err_max"] < 2e-3, summary
     assert h["final_hidden_normwise_err_max"] < b["final_hidden_normwise_err_max"] / 20, summary
     assert h["teacher_forced_agreement"] >= b["teacher_forced_agreement"], summary
+    # time per output token, one graph-replayed decode step each: the global FP32 pipeline streams twice the
+    # weight bytes of the native bf16 one
+    t = res["tpot"]
+    print(f"[stack] tpot {t}")
+    assert 0 < t["bf16_ms"] < t["fp32_ms"] and t["heal_ms"] > 0, t
