@@ -50,6 +50,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "heal_internal.h"
 
@@ -380,7 +381,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
   float m_run = -INFINITY, m_run_lo = 0.0f, l_run = 0.0f;
   const int vq = lane >> 4, vi = lane & 15;  // 16-lane group and position for the transposing reads
 
-  auto compute = [&](const PfPlanes& P, int t) {
+  // MASK: the tile holds keys this wavefront's queries cannot all see (past the end, or above the causal limit
+  // of some query); without it every score of the tile is visible and the mask's vector work is skipped
+  auto compute = [&](const PfPlanes& P, int t, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int64_t kb = (int64_t)t * PF_BKV;
     if (a.causal && kb > wq_last + off) return;  // every key masked for this wave (wave-uniform)
     // ---- S^T tile [32 keys x 32 queries] = K Q^T, two accumulators ----
@@ -412,9 +416,12 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
     //      or above this query's causal limit are hidden: tile key kk is visible iff kk < lim, so the lane's
     //      key 8 (r/4) + 4 half + r%4 is hidden iff 8 (r/4) + r%4 >= lim - 4 half.  A hidden key's lo stays
     //      finite, so its p = exp2(-inf + ...) is 0 all the same. ----
-    int64_t lim = a.Lkv - kb;
-    if (a.causal && qi + off + 1 - kb < lim) lim = qi + off + 1 - kb;
-    const int lim2 = (int)(lim < 0 ? 0 : (lim > PF_BKV ? PF_BKV : lim)) - 4 * half;
+    int lim2 = PF_BKV;
+    if constexpr (MASK) {
+      int64_t lim = a.Lkv - kb;
+      if (a.causal && qi + off + 1 - kb < lim) lim = qi + off + 1 - kb;
+      lim2 = (int)(lim < 0 ? 0 : (lim > PF_BKV ? PF_BKV : lim)) - 4 * half;
+    }
     // u = S_int * s_k per key (logit / cq), as a pair; hidden keys get u = -inf
     float tv[16], tl[16];
 #pragma unroll
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
         score2(shh[r], srest[r], skv[i], tv[r], tl[r]);
-        tv[r] = 8 * g + i >= lim2 ? -INFINITY : tv[r];
+        if constexpr (MASK) tv[r] = 8 * g + i >= lim2 ? -INFINITY : tv[r];
       }
     }
     // (hi, lo) maximum of the 16: the largest hi, then the lo of a key attaining it.  When keys tie in hi,
@@ -512,17 +519,31 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(AttnParams a) 
     unpack(r0, p0);
   }
   __syncthreads();
+  // tile t is wholly visible to this wavefront (wave-uniform): all its keys exist and lie at or below the causal
+  // limit of the wavefront's first query
+  auto whole = [&](int t) {
+    const int64_t kl = (int64_t)t * PF_BKV + PF_BKV - 1;
+    return kl < a.Lkv && (!a.causal || kl <= wq_first + off);
+  };
+  using Unmasked = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
   for (int t = 0; t < ntk; t += 2) {
     issue(r0, t + 2);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm<2>());
     unpack(r1, p1);
-    compute(p0, t);
+    if (whole(t))
+      compute(p0, t, Unmasked{});
+    else
+      compute(p0, t, Masked{});
     __syncthreads();
     if (t + 1 >= ntk) break;
     issue(r1, t + 3);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm<2>());
     unpack(r0, p0);
-    compute(p1, t + 1);
+    if (whole(t + 1))
+      compute(p1, t + 1, Unmasked{});
+    else
+      compute(p1, t + 1, Masked{});
     __syncthreads();
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
