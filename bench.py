@@ -1007,6 +1007,31 @@ def row_fused_and_vendor(heal, workloads, dev):
     return rows
 
 
+def row_vendor_8192(heal, workloads):
+    """hipBLASLt (torch.matmul, FP16 operands with full random mantissas) at the headline GEMM's matrix work:
+    [8192, 24576] x [24576, 8192] issues the same 16-bit MFMA work as the three-product 8192^3 compensated GEMM.
+    The two are timed in turn in one process (best of three rounds of 5 launches each), so the comparison sees
+    one box and one clock regime."""
+    import torch
+
+    _, _, (ah, al, ea, bh, bl, eb, c) = gemm8192_inputs(heal, workloads, 1)
+    A2 = torch.randn((8192, 3 * 8192), device="cuda").to(torch.float16)
+    B2 = torch.randn((3 * 8192, 8192), device="cuda").to(torch.float16)
+    C2 = torch.matmul(A2, B2)
+    o_best = b_best = float("inf")
+    for _ in range(3):
+        o_best = min(o_best, time_fn(lambda: heal.heal_gemm_comp(ah, al, ea, bh, bl, eb, c=c), 5))
+        b_best = min(b_best, time_fn(lambda: torch.matmul(A2, B2, out=C2), 5))
+    work = 3 * 2.0 * 8192 ** 3  # 16-bit MFMA flop of either
+    frac = lambda t: round(work / t / 1e12 / PEAK_F16_TFLOPS, 4)
+    del A2, B2, C2, ah, al, ea, bh, bl, eb, c
+    torch.cuda.empty_cache()
+    return {"hipblaslt_fp16_equal_mfma_work_8192cube_p3": {
+        "us": round(b_best * 1e6, 1), "mfma_frac": frac(b_best),
+        "compensated_gemm_us": round(o_best * 1e6, 1), "compensated_gemm_mfma_frac": frac(o_best),
+        "compensated_over_hipblaslt_time": round(o_best / b_best, 3)}}
+
+
 def row_stack_with_cpu_baseline(timeout_s=900):
     """The model-level configuration: a 32-layer Llama-style stack (d 4096, 32/8 heads, FFN 14336, vocabulary 128256,
     random bf16 weights, 512-token prompt, 64 greedy steps) run with the HEAL kernels and in plain bf16, both
@@ -1145,6 +1170,8 @@ def main():
         torch.cuda.empty_cache()
         log("rows: fused variants, vendor GEMM, split-K")
         rows.update(row_fused_and_vendor(heal, workloads, dev))
+        log("row: hipBLASLt at the headline GEMM's matrix work")
+        rows.update(row_vendor_8192(heal, workloads))
         if not args.no_stack and not args.no_cpu:
             log("row: 32-layer decoder stack against its FP64 forward (about a minute)")
             torch.cuda.empty_cache()
