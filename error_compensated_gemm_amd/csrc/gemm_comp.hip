@@ -1270,6 +1270,268 @@ __global__ __launch_bounds__(64 * W) void gemm_stream_kernel(
   }
 }
 
+// ------------------------------------------------------------------------- streamed B, K in slices, 8..16 rows
+// Split K for at most 16 rows: workgroup (x, y) multiplies slice y of K ([y kslice, (y + 1) kslice)) for the
+// column blocks x, x + G, ... and writes its FP32 sums unscaled into slice y of the partials (splitk_reduce_kernel
+// adds the slices in order and applies the exponents).  The slice's A parts sit in LDS (from the 16-bit parts,
+// or split there from FP32 with the split pass's operations and the given row exponents, so both sources give the
+// same parts), and B streams through the same non-temporal direct-to-LDS ring as in gemm_stream_kernel.  Unlike
+// there, each ring wavefront owns whole blocks (blocks q = w, w + 4, ... of the workgroup) and runs all of the
+// slice's stages of one block before the next, keeping each block's sum in its own registers: no cross-wavefront
+// reduction, so a workgroup can hold many blocks and the S x G grid stays near one workgroup per CU.
+constexpr int kSkACap = 6016;  // 16-byte chunks of A's slice planes in LDS (94 KB)
+constexpr int kSkMaxJ = 8;     // blocks per wavefront, at most (32 per workgroup)
+
+template <int PART, int D, bool ALO, bool BLO, int ASRC>
+__global__ __launch_bounds__(256) void gemm_stream_sk_kernel(
+    int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ ah, const uint16_t* __restrict__ al,
+    const float* __restrict__ af, const int32_t* __restrict__ ea, int64_t lda, const uint16_t* __restrict__ bh,
+    const uint16_t* __restrict__ bl, int64_t ldb, float* __restrict__ C, int64_t ldc, int64_t kslice) {
+  constexpr int W = 4;
+  static_assert(D >= 2 && D <= 4, "two to four stages per wavefront");
+  static_assert(ASRC == 0 || (ASRC == 1 && ALO && PART == HEAL_F16), "FP32 A: FP16 parts, both A parts");
+  constexpr int NBP = BLO ? 2 : 1;
+  constexpr int SLOT = NBP * 256;
+  constexpr int NBI = NBP * 4;
+  static_assert((D - 1) * NBI < 64, "vmcnt range");
+  // this workgroup's slice
+  {
+    const int64_t k0 = (int64_t)blockIdx.y * kslice;
+    K = K - k0 < kslice ? K - k0 : kslice;
+    if constexpr (ASRC == 0) {
+      ah += k0;
+      if constexpr (ALO) al += k0;
+    } else {
+      af += k0;
+    }
+    bh += k0;
+    if constexpr (BLO) bl += k0;
+    C += (int64_t)blockIdx.y * M * ldc;
+  }
+  __shared__ uint4 st0[W * SLOT];
+  __shared__ uint4 st1[W * SLOT];
+  __shared__ uint4 st2[D > 2 ? W * SLOT : 1];
+  __shared__ uint4 st3[D > 3 ? W * SLOT : 1];
+  __shared__ uint4 a_pl[kSkACap];  // A's hi plane [M][rs], then (ALO) its lo plane
+  __shared__ int aexp_s[16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cl = lane & 15, kg = lane >> 4;
+  const int64_t nblk = (N + 15) / 16, G = gridDim.x;
+  const int Q = (int)((nblk - blockIdx.x + G - 1) / G);  // this workgroup's blocks: blockIdx.x + q G
+  const int Qw = Q > wave ? (Q - wave + W - 1) / W : 0;  // this wavefront's: q = wave + W j, j < Qw
+  const int64_t Kc = (K + 7) / 8, rs = stream_rs(K), klast = (Kc - 1) * 8;
+  const int ns = (int)((K + kStK - 1) / kStK);
+  const int U = Qw * ns;
+  auto blk = [&](int j) { return (int64_t)blockIdx.x + (int64_t)(wave + W * j) * G; };
+  // every workgroup starts its walk of a block's stages at its own place (spread-out columns at any moment)
+  const int rot = (int)((int64_t)ns * blockIdx.x / G);
+  struct Pos {
+    int j, t;
+  };
+  auto advance = [&](Pos& p) {
+    if (++p.t == ns) {
+      p.t = 0;
+      ++p.j;
+    }
+  };
+  auto pos_k0 = [&](const Pos& p) -> int64_t {
+    int st = p.t + rot;
+    if (st >= ns) st -= ns;
+    return (int64_t)st * kStK;
+  };
+  const uint16_t* ibh[4];
+  const uint16_t* ibl[BLO ? 4 : 1];
+  int tch[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tch[i] = (lane & 15) ^ (4 * i + (lane >> 4));
+  Pos pi{0, 0};
+  auto issue = [&](uint4* slot) {
+    if (pi.t == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int64_t n = 16 * blk(pi.j) + 4 * i + (lane >> 4);
+        if (n > N - 1) n = N - 1;  // rows past N feed outputs that are never stored
+        ibh[i] = bh + n * ldb;
+        if constexpr (BLO) ibl[i] = bl + n * ldb;
+      }
+    }
+    const int64_t k0 = pos_k0(pi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t k = k0 + 8 * tch[i];
+      if (k > klast) k = klast;  // a partial last stage: in-row chunks, cleared when read
+      dma16<kNT>(ibh[i] + k, slot + wave * SLOT + i * 64);
+      if constexpr (BLO) dma16<kNT>(ibl[i] + k, slot + wave * SLOT + 256 + i * 64);
+    }
+    advance(pi);
+  };
+  if (U > 0) issue(st0);
+  if (U > 1) issue(st1);
+  if constexpr (D > 2) {
+    if (U > 2) issue(st2);
+  }
+  if constexpr (D > 3) {
+    if (U > 3) issue(st3);
+  }
+  if constexpr (ASRC == 1) {
+    if (threadIdx.x < M) aexp_s[threadIdx.x] = ea[threadIdx.x];
+    __syncthreads();
+  }
+
+  // ---- the slice of A into LDS: 8 values (one 16-byte chunk of each plane) per item, M x Kc items, every item
+  //      of a thread requested before any is used (branch-free: an item past the end reads item 0, dropped) ----
+  const int64_t items = M * Kc;
+  constexpr int CPT = ((ALO ? kSkACap / 2 : kSkACap) + 64 * W - 1) / (64 * W);
+  if constexpr (ASRC == 0) {
+    uint4 h[CPT], l[ALO ? CPT : 1];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      int64_t idx = threadIdx.x + 64 * W * i;
+      if (idx >= items) idx = 0;
+      const int64_t r = idx / Kc, c = idx - r * Kc;
+      h[i] = *reinterpret_cast<const uint4*>(ah + r * lda + 8 * c);
+      if constexpr (ALO) l[i] = *reinterpret_cast<const uint4*>(al + r * lda + 8 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int64_t idx = threadIdx.x + 64 * W * i;
+      if (idx < items) {
+        const int64_t r = idx / Kc, c = idx - r * Kc;
+        a_pl[r * rs + c] = mask_chunk(h[i], K - 8 * c);
+        if constexpr (ALO) a_pl[M * rs + r * rs + c] = mask_chunk(l[i], K - 8 * c);
+      }
+    }
+  } else {
+    uint4 x0[CPT], x1[CPT];
+    if (K % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        int64_t idx = threadIdx.x + 64 * W * i;
+        if (idx >= items) idx = 0;
+        const int64_t r = idx / Kc, k = 8 * (idx - r * Kc);
+        x0[i] = *reinterpret_cast<const uint4*>(af + r * lda + k);
+        x1[i] = *reinterpret_cast<const uint4*>(af + r * lda + k + 4);
+      }
+    } else {  // a partial last chunk in every row: value by value, columns clamped into the slice, zeros past it
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        int64_t idx = threadIdx.x + 64 * W * i;
+        if (idx >= items) idx = 0;
+        const int64_t r = idx / Kc, k = 8 * (idx - r * Kc);
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t v = __builtin_bit_cast(uint32_t, af[r * lda + (k + j < K ? k + j : K - 1)]);
+          w[j] = k + j < K ? v : 0u;
+        }
+        x0[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        x1[i] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int64_t idx = threadIdx.x + 64 * W * i;
+      if (idx < items) {
+        const int64_t r = idx / Kc, c = idx - r * Kc;
+        const Split8 sp = split8(x0[i], x1[i], aexp_s[r]);
+        a_pl[r * rs + c] = sp.hi;
+        a_pl[M * rs + r * rs + c] = sp.lo;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- the ring: wait for stage u, read its fragments, refill its slot with stage u + D, multiply into the
+  //      block's accumulator ----
+  const int64_t a_row = (int64_t)(cl < M ? cl : M - 1) * rs;
+  f32x4 acc[kSkMaxJ];
+#pragma unroll
+  for (int j = 0; j < kSkMaxJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Pos ps{0, 0};
+  auto step = [&](uint4* slot, auto later_c, bool refill) {
+    constexpr int LATER = decltype(later_c)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<LATER * NBI>());
+    const int64_t k0 = pos_k0(ps);
+    const uint4* sb = slot + wave * SLOT + cl * 16;
+    uint4 b[4][NBP], a[4], a2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ch = 4 * j + kg;
+#pragma unroll
+      for (int p = 0; p < NBP; ++p) b[j][p] = sb[p * 256 + (ch ^ cl)];
+      int64_t c = k0 / 8 + ch;
+      if (c > Kc - 1) c = Kc - 1;  // wholly past K: cleared below
+      a[j] = a_pl[a_row + c];
+      if constexpr (ALO) a2[j] = a_pl[M * rs + a_row + c];
+    }
+    if (k0 + kStK > K) {  // the partial last stage: clear both operands at and past K (padding may hold NaNs)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t valid = K - (k0 + 32 * j + 8 * kg);
+#pragma unroll
+        for (int p = 0; p < NBP; ++p) b[j][p] = mask_chunk(b[j][p], valid);
+        a[j] = mask_chunk(a[j], valid);
+        if constexpr (ALO) a2[j] = mask_chunk(a2[j], valid);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the fragments are in registers before the slot is refilled
+    if (refill) issue(slot);
+    auto mma = [&](f32x4& c) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c = mfma16<PART>(a[j], b[j][0], c);
+        if constexpr (BLO) c = mfma16<PART>(a[j], b[j][1], c);
+        if constexpr (ALO) c = mfma16<PART>(a2[j], b[j][0], c);
+      }
+    };
+    switch (ps.j) {  // uniform: each block's accumulator stays a fixed set of registers
+      case 0: mma(acc[0]); break;
+      case 1: mma(acc[1]); break;
+      case 2: mma(acc[2]); break;
+      case 3: mma(acc[3]); break;
+      case 4: mma(acc[4]); break;
+      case 5: mma(acc[5]); break;
+      case 6: mma(acc[6]); break;
+      default: mma(acc[7]); break;
+    }
+    advance(ps);
+  };
+  static_assert(kSkMaxJ == 8, "one switch case per block");
+  using L0 = std::integral_constant<int, 0>;
+  using LD = std::integral_constant<int, D - 1>;
+  int u = 0;
+  for (; u + 2 * D <= U; u += D) {
+    step(st0, LD{}, true);
+    step(st1, LD{}, true);
+    if constexpr (D > 2) step(st2, LD{}, true);
+    if constexpr (D > 3) step(st3, LD{}, true);
+  }
+  for (; u < U; ++u) {
+    const bool refill = u + D < U;
+    switch (u % D) {
+      case 0: step(st0, L0{}, refill); break;
+      case 1: step(st1, L0{}, refill); break;
+      case 2: if constexpr (D > 2) step(st2, L0{}, refill); break;
+      default: if constexpr (D > 3) step(st3, L0{}, refill); break;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());  // no transfer may still write LDS when the workgroup ends
+
+  // ---- this wavefront's blocks: the unscaled sums into the slice's partials (row 4 (lane / 16) + i) ----
+#pragma unroll
+  for (int j = 0; j < kSkMaxJ; ++j) {
+    if (j < Qw) {
+      const int64_t col = 16 * blk(j) + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = 4 * (lane >> 4) + i;
+        if (row < M && col < N) C[row * ldc + col] = acc[j][i];
+      }
+    }
+  }
+}
+
 int cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
@@ -1701,12 +1963,47 @@ constexpr int64_t kSplitSkinnyFewRowsMinK = 8192;
 
 constexpr int kMaxSlices = 16;             // K slices, at most
 
+// Split K for 8..16 rows through gemm_stream_sk_kernel: slices of whole 128-column stages, as wide as A's parts
+// allow in its LDS (1408 columns at 16 rows with both parts), the same width for every slice but the last, and
+// about one workgroup per CU over the S x G grid.  Measured on MI355X (16 x 14336 -> 4096, FP32 A, bf16 weights
+// rotated through HBM, graph-replayed, the reduction included): 35.6-36.3 us in 11 slices, against 38.2-38.4 us
+// for the skinny kernel's 8 slices of four column blocks.  Splitting from K = 4096 instead of 8192 lost: 20.8
+// against 16.7 us unsplit at 16 x 4096 -> 4096, and no gain at 16 x 4096 -> 14336.
+struct StreamSkPlan {
+  bool ok;
+  int64_t S, kslice, G;
+};
+StreamSkPlan plan_stream_sk(int64_t M, int64_t N, int64_t K, bool a_lo) {
+  StreamSkPlan q{false, 1, K, 0};
+  if (M < 1 || M > 16 || N < 1 || K < 1) return q;
+  const int64_t rs_max = kSkACap / ((a_lo ? 2 : 1) * M);
+  int64_t wmax = 0;  // the widest slice whose planes fit
+  for (int64_t w = kStK; stream_rs(w) <= rs_max; w += kStK) wmax = w;
+  if (wmax < kStK) return q;
+  int64_t S = (K + wmax - 1) / wmax;
+  if (S < 2 || S > kMaxSlices) return q;
+  const int64_t ks = ((K + S - 1) / S + kStK - 1) / kStK * kStK;  // equal slices, whole stages
+  S = (K + ks - 1) / ks;
+  const int64_t nblk = (N + 15) / 16;
+  int64_t G = cu_count() / S;
+  if (G < 1) G = 1;
+  if (G > nblk) G = nblk;
+  if ((nblk + G - 1) / G > 4 * kSkMaxJ) G = (nblk + 4 * kSkMaxJ - 1) / (4 * kSkMaxJ);
+  q.ok = S >= 2;
+  q.S = S;
+  q.kslice = ks;
+  q.G = G;
+  return q;
+}
+
 struct SplitPlan {
   bool split;      // false: heal_gemm_comp's own launch
   bool skinny;     // skinny kernel (four column blocks) or 128 x 128 tiles
   int64_t S;       // slices
   int64_t kslice;  // K per slice (a multiple of 64; the last slice takes the rest)
   int64_t ldw;     // row stride of a partial (N rounded up to 4 floats)
+  bool stream = false;  // 8..16 rows: gemm_stream_sk_kernel over a G x S grid
+  int64_t G = 0;
 };
 
 SplitPlan plan_split(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo) {
@@ -1719,11 +2016,24 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, bool a_lo, bool b_lo) {
     // 16 NC columns of B: at 16 rows and one column block that is twice B's bytes.  The split launch takes four
     // column blocks per workgroup (A re-read a quarter as often) and restores the workgroup count with K slices,
     // at the price of the reduction's launch (a few microseconds): measured on the Llama-3-8B projections, that
-    // pays from 8 rows and K = 8192 (down projection at 16 rows: 52 -> 38 us) and loses below.
+    // pays from 8 rows and K = 8192 (down projection at 16 rows: 52 -> 38 us) and loses below.  Where A's
+    // slice parts fit in LDS, the slices run on gemm_stream_sk_kernel instead (plan_stream_sk: 38 -> 36 us).
     // Above 16 rows, split only where every workgroup's re-read of A is over twice its share of B (16 NC
     // columns x K x 2 bytes): the unsplit launch's column blocks already serve the rest.
     if (M > 16 && M <= 16 * (int64_t)skinny_nc(M, N)) return p;
     if (M <= 16 && (M < kSplitSkinnyMinRows || K < kSplitSkinnyFewRowsMinK)) return p;
+    if (M <= 16) {
+      const StreamSkPlan q = plan_stream_sk(M, N, K, a_lo);
+      if (q.ok) {
+        p.split = true;
+        p.S = q.S;
+        p.kslice = q.kslice;
+        p.ldw = (N + 3) / 4 * 4;
+        p.stream = true;
+        p.G = q.G;
+        return p;
+      }
+    }
     wgs = (N + 63) / 64;
     target = 512;
     min_k = kSplitSkinnyMinK;
@@ -1788,7 +2098,12 @@ void launch_split_kernel(const SplitPlan& p, int64_t M, int64_t N, int64_t K, co
                          const uint16_t* al, int64_t lda, const uint16_t* bh, const uint16_t* bl, int64_t ldb,
                          float* ws, hipStream_t stream) {
   const int32_t* const none = nullptr;
-  if (p.skinny) {
+  if (p.stream) {
+    constexpr int D = BLO ? kStDLo : kStD;
+    hipLaunchKernelGGL((gemm_stream_sk_kernel<PART, D, ALO, BLO, 0>), dim3((unsigned)p.G, (unsigned)p.S), dim3(256),
+                       0, stream, M, N, K, ah, al, (const float*)nullptr, none, lda, bh, bl, ldb, ws, p.ldw,
+                       p.kslice);
+  } else if (p.skinny) {
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)p.S), block(64 * kSkWaves);
     if (M <= 16)
       hipLaunchKernelGGL((gemm_skinny_kernel<PART, 1, 4, ALO, BLO, false, true>), grid, block, 0, stream, M, N, K,
@@ -1810,7 +2125,7 @@ void launch_split_kernel(const SplitPlan& p, int64_t M, int64_t N, int64_t K, co
 // FP32 A (split in the kernel with the given row exponents): the skinny plan at 8..16 rows only
 SplitPlan plan_split_f32a(int64_t M, int64_t N, int64_t K, bool b_lo) {
   SplitPlan p = plan_split(M, N, K, true, b_lo);
-  if (!p.skinny || M > 16) p = SplitPlan{false, false, 1, K, 0};
+  if (!(p.skinny || p.stream) || M > 16) p = SplitPlan{false, false, 1, K, 0};
   return p;
 }
 
@@ -1819,6 +2134,12 @@ void launch_split_kernel_f32a(const SplitPlan& p, int64_t M, int64_t N, int64_t 
                               const int32_t* ea, int64_t lda, const uint16_t* bh, const uint16_t* bl, int64_t ldb,
                               float* ws, hipStream_t stream) {
   const uint16_t* const none = nullptr;
+  if (p.stream) {
+    constexpr int D = BLO ? kStDLo : kStD;
+    hipLaunchKernelGGL((gemm_stream_sk_kernel<HEAL_F16, D, true, BLO, 1>), dim3((unsigned)p.G, (unsigned)p.S),
+                       dim3(256), 0, stream, M, N, K, none, none, af, ea, lda, bh, bl, ldb, ws, p.ldw, p.kslice);
+    return;
+  }
   const dim3 grid((unsigned)((N + 63) / 64), (unsigned)p.S), block(64 * kSkWaves);
   hipLaunchKernelGGL((gemm_skinny_kernel<HEAL_F16, 1, 4, true, BLO, true, true>), grid, block, 0, stream, M, N, K,
                      none, none, ea, lda, bh, bl, (const int32_t*)nullptr, ldb, ws, p.ldw, af, p.kslice);
@@ -1866,7 +2187,8 @@ hipError_t launch_gemm_comp_f32a_splitk(int64_t M, int64_t N, int64_t K, const f
   if (!p.split || !a_exp)
     return launch_gemm_comp_f32a(M, N, K, a, lda, a_exp, b_hi, b_lo, b_exp, ldb, c, ldc, stream);
   const int64_t red_blocks = (M * (p.ldw / 4) + 255) / 256;
-  if (!grid_fits((N + 63) / 64, 64 * kSkWaves) || !grid_fits(red_blocks, 256)) return hipErrorInvalidConfiguration;
+  if (!grid_fits(p.stream ? p.G : (N + 63) / 64, p.stream ? 256 : 64 * kSkWaves) || !grid_fits(red_blocks, 256))
+    return hipErrorInvalidConfiguration;
   float* ws = reinterpret_cast<float*>(workspace);
   if (b_lo)
     launch_split_kernel_f32a<true>(p, M, N, K, a, a_exp, lda, b_hi, b_lo, ldb, ws, stream);
@@ -1886,9 +2208,9 @@ hipError_t launch_gemm_comp_splitk(int64_t M, int64_t N, int64_t K, const uint16
   const SplitPlan p = plan_split(M, N, K, a_lo != nullptr, b_lo != nullptr);
   if (!p.split)
     return launch_gemm_comp(M, N, K, a_hi, a_lo, a_exp, lda, b_hi, b_lo, b_exp, ldb, part, c, ldc, stream);
-  const int64_t gemm_blocks = p.skinny ? (N + 63) / 64 : ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t gemm_blocks = p.stream ? p.G : p.skinny ? (N + 63) / 64 : ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t red_blocks = (M * (p.ldw / 4) + 255) / 256;
-  if (!grid_fits(gemm_blocks, p.skinny ? 64 * kSkWaves : kThreads) || !grid_fits(red_blocks, 256))
+  if (!grid_fits(gemm_blocks, p.stream ? 256 : p.skinny ? 64 * kSkWaves : kThreads) || !grid_fits(red_blocks, 256))
     return hipErrorInvalidConfiguration;
   float* ws = reinterpret_cast<float*>(workspace);
   if (part == HEAL_F16)

@@ -288,7 +288,7 @@ def test_splitk_validation_and_plan(heal):
     assert need == 8 * 128 * 4096 * 4
     assert heal.heal_gemm_comp_workspace_bytes(2048, 4096, 4096, 2) == 0
     assert heal.heal_gemm_comp_splitk_slices(2048, 4096, 4096, 2) == 1
-    assert heal.heal_gemm_comp_splitk_slices(16, 4096, 14336, 2) == 8      # 16-row skinny, long K: split
+    assert heal.heal_gemm_comp_splitk_slices(16, 4096, 14336, 2) == 11     # 16 rows, long K: slices of 1408
     assert heal.heal_gemm_comp_splitk_slices(16, 4096, 4096, 2) == 1       # 16-row skinny, K < 8192: whole
     assert heal.heal_gemm_comp_splitk_slices(4, 4096, 14336, 2) == 1       # under 8 rows: whole
     assert heal.heal_gemm_comp_splitk_slices(64, 4096, 14336, 2) == 8      # 64-row skinny: split
@@ -320,9 +320,9 @@ def test_f32a_splitk_validation_and_plan(heal):
     for M, N, K, P_ in ((16, 4096, 14336, 2), (16, 4096, 14336, 3), (8, 4096, 8192, 2), (13, 1000, 9001, 3)):
         assert heal.heal_gemm_comp_f32a_splitk_slices(M, N, K, P_) == heal.heal_gemm_comp_splitk_slices(M, N, K, P_)
         assert heal.heal_gemm_comp_f32a_workspace_bytes(M, N, K, P_) == heal.heal_gemm_comp_workspace_bytes(M, N, K, P_)
-    assert heal.heal_gemm_comp_f32a_splitk_slices(16, 4096, 14336, 2) == 8
+    assert heal.heal_gemm_comp_f32a_splitk_slices(16, 4096, 14336, 2) == 11  # slices of 1408 (A's parts in LDS)
     need = heal.heal_gemm_comp_f32a_workspace_bytes(16, 4096, 14336, 2)
-    assert need == 8 * 16 * 4096 * 4
+    assert need == 11 * 16 * 4096 * 4
     assert heal.heal_gemm_comp_f32a_splitk_slices(16, 4096, 4096, 2) == 1     # K < 8192: whole
     assert heal.heal_gemm_comp_f32a_splitk_slices(4, 4096, 14336, 2) == 1     # under 8 rows: whole
     assert heal.heal_gemm_comp_f32a_splitk_slices(64, 4096, 14336, 2) == 1    # over 16 rows: whole (FP32 A)
