@@ -1,7 +1,8 @@
 """Canary bands: every output is written into a view of a larger buffer whose other bytes hold a sentinel
 pattern (0x7FA5A5A5, a NaN), and must leave them untouched while the view equals, bit for bit, the output
 written into a plain allocation.  Covers the GEMM kernels (skinny, skinny with A split in LDS, the persistent
-streamed-B kernel, 128 x 128, 128 x 256, 256 x 256 with three products, split K), the split's part padding, the quantiser writing into a
+streamed-B kernel, 128 x 128, 128 x 256, 256 x 256 with three products, split K, the 16-row split-K streamed-B
+kernel and its workspace), the split's part padding, the quantiser writing into a
 cache view, and prefill and decode attention writing a strided output."""
 import numpy as np
 import pytest
@@ -34,6 +35,37 @@ def _outside_untouched(buf, view):
     raw = buf.view(torch.int32 if buf.element_size() == 4 else torch.int16)
     want = SENTINEL if buf.element_size() == 4 else int(np.uint16(0xA5A5).astype(np.int16))
     return bool((raw[mask] == want).all())
+
+
+@pytest.mark.parametrize("P,f32a", [(2, False), (3, False), (2, True)])
+def test_stream_splitk_writes_only_its_view_and_workspace(heal, P, f32a):
+    """the 16-row split-K launch (gemm_stream_sk_kernel writing each slice's partials into the caller workspace,
+    then the ordered reduction) into a strided view: the view's guard bands and a sentinel band past the end of
+    the workspace stay untouched, and the view equals the same call into a plain allocation"""
+    M, N, K = 16, 1003, 9000
+    A, Bt = workloads.gemm_rowscaled(M, N, K, seed=6)
+    ah, al, ea = heal.heal_split(dev(A))
+    bh, bl, eb = heal.heal_split(dev(Bt), residual=(P == 3))
+    bl = bl if P == 3 else None
+    a = dev(np.pad(A, ((0, 0), (0, (K + 3) // 4 * 4 - K))))[:, :K]
+    if f32a:
+        S, need = heal.heal_gemm_comp_f32a_splitk_slices(M, N, K, P), heal.heal_gemm_comp_f32a_workspace_bytes(M, N, K, P)
+    else:
+        S, need = heal.heal_gemm_comp_splitk_slices(M, N, K, P), heal.heal_gemm_comp_workspace_bytes(M, N, K, P)
+    banner(f"canary stream split-K {M}x{N}x{K} P={P} f32a={f32a} S={S}")
+    assert S > 1 and need == S * M * ((N + 3) // 4 * 4) * 4
+    wsbuf = torch.empty(need // 4 + 4096, dtype=torch.int32, device="cuda")
+    wsbuf.fill_(SENTINEL)
+    ws = wsbuf[:need // 4].view(torch.uint8)
+    run = ((lambda c: heal.heal_gemm_comp_f32a_splitk(a, heal.heal_row_exponents(a), bh, bl, eb, c=c, workspace=ws))
+           if f32a else (lambda c: heal.heal_gemm_comp_splitk(ah, al, ea, bh, bl, eb, c=c, workspace=ws)))
+    ref = run(None)  # the binding's own output (rows padded to 16 bytes)
+    buf, view = _guarded(M, N, torch.float32, pad_cols=4)
+    run(view)
+    torch.cuda.synchronize()
+    assert bool((wsbuf[need // 4:] == SENTINEL).all()), "written past the workspace"
+    assert _outside_untouched(buf, view)
+    assert torch.equal(view.contiguous().view(torch.int32), ref.contiguous().view(torch.int32))
 
 
 @pytest.mark.parametrize("M,N,K,P,f32a", [(1, 4100, 1032, 2, True), (16, 3000, 777, 3, False), (300, 520, 300, 3, False),
