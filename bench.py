@@ -1007,6 +1007,65 @@ def row_fused_and_vendor(heal, workloads, dev):
     return rows
 
 
+def row_channels(heal, workloads, dev, with_cpu, M=2048, K=4096, N=4096, T=-12, sample_rows=128):
+    """Calibrated outlier channels on massive-activation inputs: a fixed 1% of the K channels carry +-1e5 in every
+    row, the rest 1e-5 N(0, 1); FP32 weights N(0, 0.02) whose first N/2 rows skip the massive channels, so half of
+    the outputs are made of ordinary values only.  Timed: the calibration pass (channel exponents, a read of x),
+    the column-scaled split of x (read x, write both parts), the plain split beside it, and the three-product GEMM
+    on the calibrated parts.  The oracle leg (FP64 GEMM on the first sample_rows rows) gives the error of the
+    calibrated and the uncalibrated GEMM on the ordinary outputs and on all of them."""
+    import torch
+
+    x, idx = workloads.massive_channels(M, K, seed=12)
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[: N // 2][:, idx] = 0.0
+    xd, wd = dev(x), dev(w)
+    c = heal.heal_channel_exponents(xd, T)
+    ah, al, ea = heal.heal_split_scaled(xd, c, +1)
+    bh, bl, eb = heal.heal_split_scaled(wd, c, -1)
+    cal = heal.heal_gemm_comp(ah, al, ea, bh, bl, eb)
+    ph, pl, pe = heal.heal_split(xd)
+    qh, ql, qe = heal.heal_split(wd)
+    plain = heal.heal_gemm_comp(ph, pl, pe, qh, ql, qe)
+    t_cal = t_split = t_plain = t_gemm = float("inf")
+    for _ in range(3):
+        t_cal = min(t_cal, time_fn(lambda: heal.heal_channel_exponents(xd, T, col_exps=c), 20))
+        t_split = min(t_split, time_fn(lambda: heal.heal_split_scaled(xd, c, +1, hi=ah, lo=al, exps=ea), 20))
+        t_plain = min(t_plain, time_fn(lambda: heal.heal_split(xd, hi=ph, lo=pl, exps=pe), 20))
+        t_gemm = min(t_gemm, time_fn(lambda: heal.heal_gemm_comp(ah, al, ea, bh, bl, eb, c=cal), 10))
+    by_cal, by_split = 4.0 * M * K, 8.0 * M * K + 4.0 * M
+    gbs = lambda by, t: round(by / t / 1e9, 1)
+    row = {"us_calibration": round(t_cal * 1e6, 2), "calibration_gbs": gbs(by_cal, t_cal),
+           "us_split_scaled": round(t_split * 1e6, 2), "split_scaled_gbs": gbs(by_split, t_split),
+           "us_split_plain": round(t_plain * 1e6, 2), "us_gemm_p3": round(t_gemm * 1e6, 2),
+           "gemm_tflops_fp32eq": round(2.0 * M * N * K / t_gemm / 1e12, 1),
+           "roofline": {"bound": "hbm", "achieved": gbs(by_split, t_split), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(by_split / t_split / 1e9 / PEAK_HBM_GBS, 4),
+                        "kernel": "split_rows_kernel (columns scaled)", "algorithmic_bytes": int(by_split)},
+           "outlier_channels": int(idx.size)}
+    if with_cpu:
+        import oracle
+
+        rows = sample_rows
+        t0 = time.perf_counter()
+        ref = oracle.gemm_f64(x[:rows].astype(np.float64), w.astype(np.float64))
+        t_cpu = time.perf_counter() - t0
+        half = slice(0, N // 2)
+        gc, gp = cal[:rows].cpu().numpy().astype(np.float64), plain[:rows].cpu().numpy().astype(np.float64)
+        nw = lambda a, b: float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        row["cpu_baseline"] = {
+            "value": round(2.0 * rows * N * K / t_cpu / 1e12, 5), "unit": "TFLOP/s", "cores": host_threads(),
+            "kind": "oracle", "sample": f"plain-C FP64 GEMM of the first {rows} rows ({t_cpu:.2f} s)",
+            "gpu_err_vs_fp64_on_sample": {
+                "calibrated_ordinary_outputs": nw(gc[:, half], ref[:, half]),
+                "uncalibrated_ordinary_outputs": nw(gp[:, half], ref[:, half]),
+                "calibrated_all_outputs": nw(gc, ref), "uncalibrated_all_outputs": nw(gp, ref)}}
+    del xd, wd, ah, al, bh, bl, ph, pl, qh, ql, cal, plain
+    torch.cuda.empty_cache()
+    return {"f3_outlier_channels_2048x4096x4096": row}
+
+
 def row_vendor_8192(heal, workloads):
     """hipBLASLt (torch.matmul, FP16 operands with full random mantissas) at the headline GEMM's matrix work:
     [8192, 24576] x [24576, 8192] issues the same 16-bit MFMA work as the three-product 8192^3 compensated GEMM.
@@ -1170,6 +1229,8 @@ def main():
         torch.cuda.empty_cache()
         log("rows: fused variants, vendor GEMM, split-K")
         rows.update(row_fused_and_vendor(heal, workloads, dev))
+        log("row: calibrated outlier channels")
+        rows.update(row_channels(heal, workloads, dev, not args.no_cpu))
         log("row: hipBLASLt at the headline GEMM's matrix work")
         rows.update(row_vendor_8192(heal, workloads))
         if not args.no_stack and not args.no_cpu:
