@@ -182,10 +182,14 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const TIn* __restrict__
 // FP32 values (16-byte aligned rows, prescale on), each thread holding NCH chunks of 8.  The row is read once:
 // with many rows in flight the two-pass kernel's second read of a long row misses L2 (its FETCH_SIZE is twice
 // the input at 8192 and 14336 columns).  The operations per element are the two-pass kernel's, so the bits are.
-template <int PART, bool RESID, int NCH>
+// COLS: every value is first scaled by its column's power of two, x' = fl32(x * 2^(col_sign * col_e[c])), with
+// the two-pass kernel's operation, and the row is split as x' (col_e 16-byte aligned).
+template <int PART, bool RESID, int NCH, bool COLS = false>
 __global__ __launch_bounds__(256) void split_row_regs_kernel(const float* __restrict__ x, int64_t cols, int64_t ld_x,
                                                              uint16_t* __restrict__ hi, uint16_t* __restrict__ lo,
-                                                             int64_t ld_part, int32_t* __restrict__ exps) {
+                                                             int64_t ld_part, int32_t* __restrict__ exps,
+                                                             const int32_t* __restrict__ col_e = nullptr,
+                                                             int col_sign = 0) {
   __shared__ float wmax[4];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * ld_x;
@@ -198,6 +202,13 @@ __global__ __launch_bounds__(256) void split_row_regs_kernel(const float* __rest
     const int64_t c = tid + 256 * j;
     if (c < nvec) {
       load8(xr + (c << 3), v[j]);
+      if constexpr (COLS) {
+        const int4 a = *reinterpret_cast<const int4*>(col_e + (c << 3));
+        const int4 b = *reinterpret_cast<const int4*>(col_e + (c << 3) + 4);
+        const int ce[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[j][i] = __builtin_amdgcn_ldexpf(v[j][i], col_sign * ce[i]);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
@@ -206,7 +217,10 @@ __global__ __launch_bounds__(256) void split_row_regs_kernel(const float* __rest
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
   }
   const int64_t tc = (nvec << 3) + tid;  // the last cols % 8 values, one per thread
-  const float tv = tc < cols ? xr[tc] : 0.0f;
+  float tv = tc < cols ? xr[tc] : 0.0f;
+  if constexpr (COLS) {
+    if (tc < cols) tv = __builtin_amdgcn_ldexpf(tv, col_sign * col_e[tc]);
+  }
   amax = fmaxf(amax, fabsf(tv));
   amax = wave_max(amax);
   if (lane == 0) wmax[wave] = amax;
@@ -362,24 +376,47 @@ __global__ __launch_bounds__(256) void quant_i16_kernel(const float* __restrict_
 }
 
 // Outlier-channel calibration: per column c, m = max_r |x[r, c]| and col_e[c] = T - ilogb(m) where
-// ilogb(m) > T (0 otherwise, and for an all-zero column).  A workgroup owns 64 columns; its 4 wavefronts
-// split the rows (each reads 256 consecutive bytes per row) and meet in LDS.
+// ilogb(m) > T (0 otherwise, and for an all-zero column).  A workgroup owns 64 columns of one block of rows; its 4
+// wavefronts split the block's rows (each reads 256 consecutive bytes per row, 8 rows requested at a time) and
+// meet in LDS.  The row blocks of a column combine through an integer atomicMin on the exponent itself:
+// min(0, T - ilogb(m)) only falls as m grows, so the minimum over the blocks is the exponent of the column's
+// maximum, in any order (col_e is zeroed by zero_i32_kernel first).  A whole column in one workgroup read at
+// 0.62 TB/s (64 workgroups at 4096 columns).
 __global__ __launch_bounds__(256) void channel_exps_kernel(const float* __restrict__ x, int64_t rows,
                                                            int64_t cols, int64_t ld_x, int T,
-                                                           int32_t* __restrict__ col_e) {
+                                                           int32_t* __restrict__ col_e, int64_t rows_per_block) {
   __shared__ float red[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t r1 = r0 + rows_per_block < rows ? r0 + rows_per_block : rows;  // r0 < r1 (grid of row blocks)
   float m = 0.0f;
-  if (c < cols)
-    for (int64_t r = wave; r < rows; r += 4) m = fmaxf(m, fabsf(x[r * ld_x + c]));
+  if (c < cols) {
+    for (int64_t r = r0 + wave; r < r1; r += 32) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t rr = r + 4 * u < r1 ? r + 4 * u : r1 - 1;  // a repeated row leaves the maximum unchanged
+        v[u] = fabsf(x[rr * ld_x + c]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) m = fmaxf(m, v[u]);
+    }
+  }
   red[wave][lane] = m;
   __syncthreads();
   if (wave == 0 && c < cols) {
     m = fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
-    const int il = m > 0.0f ? ilogb_pos(m) : 0;
-    col_e[c] = (m > 0.0f && il > T) ? T - il : 0;
+    if (m > 0.0f) {
+      const int il = ilogb_pos(m);
+      if (il > T) atomicMin(&col_e[c], T - il);
+    }
   }
+}
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 inline unsigned blocks_for_rows(int64_t rows, int64_t per_block) {
@@ -400,6 +437,26 @@ hipError_t launch_split_cols(const TIn* x, int64_t rows, int64_t cols, int64_t l
   uint16_t* h = (uint16_t*)hi;
   uint16_t* l = (uint16_t*)lo;
   const bool pre = exps != nullptr, res = lo != nullptr;
+  if constexpr (sizeof(TIn) == 4) {  // FP32 rows of 2049 .. 16384 values: one read, the row in registers
+    if (vec && pre && cols > 2048 && cols <= 16384 && grid_fits(rows, 256)) {
+      const int nch = (int)(((cols >> 3) + 255) / 256);
+#define HEAL_SPLIT_REGS(PART, RES, NCH)                                                                      \
+  if (part == PART && res == RES && nch <= NCH) {                                                             \
+    hipLaunchKernelGGL((split_row_regs_kernel<PART, RES, NCH, true>), dim3((unsigned)rows), block, 0, stream, \
+                       (const float*)x, cols, ld_x, h, l, ld_part, exps, col_e, col_sign);                    \
+    return hipGetLastError();                                                                                 \
+  }
+      HEAL_SPLIT_REGS(HEAL_F16, true, 4)
+      HEAL_SPLIT_REGS(HEAL_F16, true, 8)
+      HEAL_SPLIT_REGS(HEAL_F16, false, 4)
+      HEAL_SPLIT_REGS(HEAL_F16, false, 8)
+      HEAL_SPLIT_REGS(HEAL_BF16, true, 4)
+      HEAL_SPLIT_REGS(HEAL_BF16, true, 8)
+      HEAL_SPLIT_REGS(HEAL_BF16, false, 4)
+      HEAL_SPLIT_REGS(HEAL_BF16, false, 8)
+#undef HEAL_SPLIT_REGS
+    }
+  }
 #define HEAL_SPLIT_CASE(PART, PRE, RES)                                                                      \
   if (part == PART && pre == PRE && res == RES) {                                                             \
     hipLaunchKernelGGL((split_rows_kernel<TIn, PART, PRE, RES, true>), grid, block, 0, stream, x, rows, cols, \
@@ -514,9 +571,18 @@ hipError_t launch_split_scaled(const void* x, int x_type, int64_t rows, int64_t 
 hipError_t launch_channel_exps(const float* x, int64_t rows, int64_t cols, int64_t ld_x, int threshold_log2,
                                int32_t* col_e, hipStream_t stream) {
   if (cols == 0) return hipSuccess;
-  if (!grid_fits((cols + 63) / 64, 256)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(channel_exps_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(256), 0, stream, x, rows, cols,
-                     ld_x, threshold_log2, col_e);
+  const int64_t groups = (cols + 63) / 64;
+  if (!grid_fits(groups, 256) || !grid_fits((cols + 255) / 256, 256)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, stream, col_e, cols);
+  if (rows == 0) return hipGetLastError();
+  // about 1024 workgroups over the (column group, row block) grid, each row block at least 32 rows
+  int64_t blocks = 1024 / groups;
+  if (blocks > (rows + 31) / 32) blocks = (rows + 31) / 32;
+  if (blocks < 1) blocks = 1;
+  const int64_t per = (rows + blocks - 1) / blocks;
+  blocks = (rows + per - 1) / per;
+  hipLaunchKernelGGL(channel_exps_kernel, dim3((unsigned)groups, (unsigned)blocks), dim3(256), 0, stream, x, rows,
+                     cols, ld_x, threshold_log2, col_e, per);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ def test_channel_exponents_strided_rows(heal):
     assert np.array_equal(got, oracle.channel_exponents(x, -10))
 
 
-@pytest.mark.parametrize("M,K", [(256, 4096), (33, 1003), (5, 7)])
+@pytest.mark.parametrize("M,K", [(256, 4096), (64, 14336), (17, 5004), (33, 1003), (5, 7)])
 def test_split_scaled_exact(heal, M, K):
     banner(f"split scaled {M}x{K}")
     x, _ = workloads.massive_channels(M, K, seed=7)
