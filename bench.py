@@ -435,7 +435,7 @@ def headline(args, heal, workloads):
     parts = {
         "split_a_us": round(durs["split_a"] * 1e6, 1), "split_b_us": round(durs["split_b"] * 1e6, 1),
         "split_gbs": round(split_bytes / ((durs["split_a"] + durs["split_b"]) / 2) / 1e9, 1),
-        "split_symbol": "split_row_regs_kernel<2, true, 4>",
+        "split_symbol": "split_row_regs_kernel<2, true, 4, false>",
         "gemm_us": round(durs["gemm"] * 1e6, 1),
         "gemm_tflops_fp32eq": round(flop / durs["gemm"] / 1e12, 1),
     }
@@ -731,7 +731,7 @@ def row_split_quant(heal, workloads, dev):
     hi, lo, e = heal.heal_split(x)
     t = time_fn(lambda: heal.heal_split(x, hi=hi, lo=lo, exps=e), 20)
     gbs = x.numel() * 8 / t / 1e9
-    tr = stored_traffic("split_row_regs_kernel<2, true, 8>", "split_rows_2048x14336_hbm_traffic.md")
+    tr = stored_traffic("split_row_regs_kernel<2, true, 8, false>", "split_rows_2048x14336_hbm_traffic.md")
     rows["a1_split_2048x14336"] = {"us": round(t * 1e6, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                                    "algorithmic_bytes": x.numel() * 8 + 2048 * 4,
                                    "traffic": None if tr is None else tr["bytes_per_launch"]}
