@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 32-layer decoder-stack row (about a minute; its FP64 reference needs ~70 GB of host "
                          "memory)")
-    ap.add_argument("--only", choices=("gemm8192", "llama", "split", "quant", "prefill", "decode"),
+    ap.add_argument("--only", choices=("gemm8192", "llama", "split", "quant", "prefill", "decode", "channels"),
                     help="only run a few launches of that workload (the program a counter run profiles)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (scale run for the HBM byte counters)")
@@ -70,12 +70,15 @@ def parse():
 
 
 # ------------------------------------------------------------------ HBM traffic from stored counters
+# every kernel of the library, by name, with the source that holds it (a kernel missing here is left out of the
+# counter summaries; tests/test_bench_cpu.py checks the list against the sources)
 KERNEL_SOURCES = (("gemm_comp_kernel", "gemm_comp.hip"), ("gemm_skinny_kernel", "gemm_comp.hip"),
-                  ("gemm_stream_kernel", "gemm_comp.hip"),
+                  ("gemm_stream_kernel", "gemm_comp.hip"), ("gemm_stream_sk_kernel", "gemm_comp.hip"),
                   ("splitk_reduce_kernel", "gemm_comp.hip"), ("split_rows_kernel", "split_quant.hip"),
-                  ("split_row_regs_kernel", "split_quant.hip"),
+                  ("split_row_regs_kernel", "split_quant.hip"), ("channel_exps_kernel", "split_quant.hip"),
+                  ("zero_i32_kernel", "split_quant.hip"),
                   ("quant_i16_kernel", "split_quant.hip"), ("unpack_i16_kernel", "split_quant.hip"),
-                  ("attn_", "attn.hip"))
+                  ("attn_", "attn.hip"), ("zero_rows_kernel", "attn.hip"))
 
 
 def source_sha256(path):
@@ -585,7 +588,8 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10):
         if S > 1:
             ws[(M, K, N)] = (S, torch.empty(heal.heal_gemm_comp_f32a_workspace_bytes(M, N, K, 2), dtype=torch.uint8,
                                             device="cuda"))
-    variants = {(M, K, N): (f"gemm_skinny_kernel M<=16 NC4 P2 FP32-A, K in {ws[(M, K, N)][0]} slices + "
+    # (8..16 rows split into slices whose A parts fit in LDS run on the streamed-B split kernel)
+    variants = {(M, K, N): (f"gemm_stream_sk_kernel M<=16 P2 FP32-A, K in {ws[(M, K, N)][0]} slices + "
                             "splitk_reduce_kernel (heal_gemm_comp_f32a_splitk)") if (M, K, N) in ws else
                 (heal.heal_gemm_comp_variant(M, N, K, 2) + (" FP32-A" if fused(M) else "")
                  + (", exponent in the kernel" if derived(M) else "")) for (M, K, N) in shapes}
@@ -1036,13 +1040,21 @@ def row_channels(heal, workloads, dev, with_cpu, M=2048, K=4096, N=4096, T=-12, 
         t_gemm = min(t_gemm, time_fn(lambda: heal.heal_gemm_comp(ah, al, ea, bh, bl, eb, c=cal), 10))
     by_cal, by_split = 4.0 * M * K, 8.0 * M * K + 4.0 * M
     gbs = lambda by, t: round(by / t / 1e9, 1)
+    prof = "split_scaled_2048x4096_hbm_traffic.md"
+    split_sym = "split_row_regs_kernel<2, true, 4, true>"  # FP32 rows of 4096 columns, columns scaled
+    tr_split, tr_cal = stored_traffic(split_sym, prof), stored_traffic("channel_exps_kernel", prof)
     row = {"us_calibration": round(t_cal * 1e6, 2), "calibration_gbs": gbs(by_cal, t_cal),
            "us_split_scaled": round(t_split * 1e6, 2), "split_scaled_gbs": gbs(by_split, t_split),
            "us_split_plain": round(t_plain * 1e6, 2), "us_gemm_p3": round(t_gemm * 1e6, 2),
            "gemm_tflops_fp32eq": round(2.0 * M * N * K / t_gemm / 1e12, 1),
            "roofline": {"bound": "hbm", "achieved": gbs(by_split, t_split), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(by_split / t_split / 1e9 / PEAK_HBM_GBS, 4),
-                        "kernel": "split_rows_kernel (columns scaled)", "algorithmic_bytes": int(by_split)},
+                        "traffic": tr_split["bytes_per_launch"] if tr_split else None,
+                        "traffic_profile": tr_split["profile"] if tr_split else None,
+                        "kernel": "split_row_regs_kernel (columns scaled)", "symbol": split_sym,
+                        "algorithmic_bytes": int(by_split)},
+           "calibration_traffic": tr_cal["bytes_per_launch"] if tr_cal else None,
+           "calibration_algorithmic_bytes": int(by_cal),
            "outlier_channels": int(idx.size)}
     if with_cpu:
         import oracle
@@ -1146,6 +1158,14 @@ def only(args, heal, workloads):
         hi, lo, e = heal.heal_split(x)
         for _ in range(4):
             heal.heal_split(x, hi=hi, lo=lo, exps=e)
+    elif w == "channels":
+        x, _ = workloads.massive_channels(2048, 4096, seed=12)
+        xd = dev(x)
+        c = heal.heal_channel_exponents(xd, -12)
+        ah, al, ea = heal.heal_split_scaled(xd, c, +1)
+        for _ in range(4):
+            heal.heal_channel_exponents(xd, -12, col_exps=c)
+            heal.heal_split_scaled(xd, c, +1, hi=ah, lo=al, exps=ea)
     elif w == "quant":
         Q, K, V = workloads.qkv_fp32(1, 4096, 32, 128, seed=2)
         fused = dev(np.concatenate([Q[0], K[0], V[0]], axis=1))
