@@ -614,8 +614,9 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10, rounds=3):
     for i in range(3):
         step(i, False)
     torch.cuda.synchronize()
-    round_s = []
+    round_s, durs = [], None
     for _ in range(rounds):
+        timer = Timer()  # per round: the launch durations come from the best round, like the step time
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         for i in range(steps):
@@ -623,9 +624,10 @@ def row_llama(heal, workloads, dev, rotate, with_cpu, steps=10, rounds=3):
         t1.record()
         torch.cuda.synchronize()
         round_s.append(t0.elapsed_time(t1) * 1e-3 / steps)
+        if round_s[-1] == min(round_s):
+            durs = timer.durations()
     step_s = min(round_s)
     flops_step = sum(2.0 * M * N * K for (M, K, N) in shapes)
-    durs = timer.durations()
     graph_s = per_launch_in_graph(heal, bufs, weights, fused, derived, ws)
     per_shape, by_variant = {}, {}
     for (M, K, N) in shapes:
